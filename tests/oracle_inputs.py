@@ -1,0 +1,47 @@
+"""Host-side inputs for the oracle: the seeded draws (synth) encoded to Q2 bytes
+by the oracle's own quantizer.  Nothing here comes from the HIP library."""
+import functools
+
+import numpy as np
+
+from oracle import q2
+from synth import workloads as W
+from synth.gen import bf16_bits_to_f32
+
+
+class HostLayer:
+    """Lazily generated host copy of one layer of a workload."""
+
+    def __init__(self, wl, layer=0):
+        self.wl = wl
+        self.layer = layer
+        self.router_w = W.router_weights(wl, layer)
+        self.router_b = W.router_bias(wl, layer)
+        bits = W.shared_bf16_bits(wl, layer)
+        self.shared_bits = bits
+        self.shared = None if bits is None else tuple(bf16_bits_to_f32(b) for b in bits)
+        self._cache = {}
+
+    def expert_bytes(self, e):
+        """(gate, up, down) Q2 bytes of routed expert e, quantized on the host."""
+        if e not in self._cache:
+            wl = self.wl
+            self._cache[e] = tuple(q2.encode_matrix(W.expert_f32(wl, self.layer, e, m))
+                                   for m in range(3))
+        return self._cache[e]
+
+    def all_expert_bytes(self):
+        """All experts back to back in the library's order (gate, up, down per expert)."""
+        parts = []
+        for e in range(self.wl.n_experts):
+            parts.extend(b.reshape(-1) for b in self.expert_bytes(e))
+        return np.concatenate(parts)
+
+    def oracle_layer(self):
+        return dict(router_w=self.router_w, router_b=self.router_b,
+                    expert_bytes=self.expert_bytes, shared=self.shared)
+
+
+@functools.lru_cache(maxsize=8)
+def host_layer(name, layer=0):
+    return HostLayer(W.WORKLOADS[name], layer)

@@ -1,0 +1,246 @@
+"""Pins of the oracle's MoE layer: brute force on tiny inputs, closed forms,
+special cases that reduce to a dense mixture, and exact invariants (no GPU)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import moe, q2
+from tests.oracle_inputs import host_layer
+from synth import workloads as W
+
+
+# ----------------------------------------------------------------- routing
+def _route_bruteforce(logits, K):
+    T, E = logits.shape
+    idx, g = [], []
+    for t in range(T):
+        pairs = sorted(((-logits[t, e], e) for e in range(E)))
+        sel = [e for _, e in pairs[:K]]
+        mx = max(logits[t])
+        p = [math.exp(logits[t, e] - mx) for e in range(E)]
+        z = sum(p)
+        p = [v / z for v in p]
+        zs = sum(p[e] for e in sel)
+        idx.append(sel)
+        g.append([p[e] / zs for e in sel])
+    return np.array(idx), np.array(g)
+
+
+def test_route_matches_bruteforce():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((7, 32))
+    Wr = rng.standard_normal((9, 32)) * 0.3
+    b = rng.standard_normal(9) * 0.1
+    for K in (1, 2, 3, 9):
+        idx, g, logits, margin = moe.route(x, Wr, b, K)
+        bi, bg = _route_bruteforce(x @ Wr.T + b, K)
+        assert np.array_equal(idx, bi)
+        assert np.allclose(g, bg, rtol=0, atol=1e-14)
+        assert np.allclose(g.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        if K < 9:
+            srt = np.sort(logits, axis=1)[:, ::-1]
+            assert np.allclose(margin, srt[:, K - 1] - srt[:, K])
+        else:
+            assert np.all(np.isinf(margin))
+
+
+def test_route_k1_and_k_equals_e():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 16))
+    Wr = rng.standard_normal((6, 16))
+    _, g, _, _ = moe.route(x, Wr, None, 1)
+    assert np.all(g == 1.0)
+    idx, g, logits, _ = moe.route(x, Wr, None, 6)
+    full = np.exp(logits - logits.max(axis=1, keepdims=True))
+    full /= full.sum(axis=1, keepdims=True)
+    assert np.allclose(np.take_along_axis(full, idx.astype(np.int64), axis=1), g, atol=1e-15)
+
+
+def test_route_ties_go_to_lower_index():
+    x = np.ones((1, 4))
+    Wr = np.array([[1, 0, 0, 0], [0, 0, 0, 1], [1, 0, 0, 0], [0, 1, 0, 0], [0, 0, 1, 0.0]])
+    idx, g, _, margin = moe.route(x, Wr, None, 2)
+    assert idx.tolist() == [[0, 1]]          # all logits equal to 1: lowest indices
+    assert margin[0] == 0.0
+    assert np.allclose(g, 0.5)
+
+
+def test_route_bias_enters_gates():
+    x = np.zeros((1, 4))
+    Wr = np.zeros((3, 4))
+    b = np.array([0.0, math.log(3.0), -5.0])
+    idx, g, _, _ = moe.route(x, Wr, b, 2)
+    assert idx.tolist() == [[1, 0]]
+    assert np.allclose(g, [[0.75, 0.25]], atol=1e-15)
+
+
+# ----------------------------------------------------------------- bucketing
+def test_bucket_matches_loops():
+    rng = np.random.default_rng(2)
+    T, K, E = 37, 4, 11
+    idx = np.array([rng.choice(E, K, replace=False) for _ in range(T)])
+    counts, offsets, perm, inv = moe.bucket(idx, E)
+    flat = idx.reshape(-1)
+    want_perm = [s for e in range(E) for s in range(T * K) if flat[s] == e]
+    assert perm.tolist() == want_perm
+    assert counts.tolist() == [int((flat == e).sum()) for e in range(E)]
+    assert offsets[0] == 0 and offsets[-1] == T * K
+    assert np.all(offsets[1:] - offsets[:-1] == counts)
+    assert np.array_equal(perm[inv], np.arange(T * K))
+
+
+# ----------------------------------------------------------------- FFN closed form
+def _onehot_q2(rows, cols, colmap, value):
+    """Q2 bytes of a [rows, cols] matrix with one nonzero per row: W[r, colmap[r]] = value.
+    value = d * sc * q with d = value / 3, sc = 1, q = 3 (exact); all mins 0."""
+    raw = np.zeros((rows, cols // 256, 84), dtype=np.uint8)
+    d16 = np.float16(value / 3)
+    assert float(d16) * 3 == value
+    for r in range(rows):
+        c = colmap[r]
+        blk = raw[r, c // 256]
+        i = c % 256
+        blk[i // 16] = 1                              # sc_j = 1, m_j = 0
+        blk[16 + i // 4] |= 3 << (2 * (i % 4))
+        blk[80:82] = np.frombuffer(d16.tobytes(), dtype=np.uint8)
+    for r in range(rows):                             # d on the other blocks of the row too
+        for b in range(cols // 256):
+            raw[r, b, 80:82] = np.frombuffer(d16.tobytes(), dtype=np.uint8)
+    return raw.reshape(-1, 84)
+
+
+def test_ffn_closed_form_permutations():
+    # H = 256, I = 512: gate row i reads x[pg(i)] * 0.75, up row i reads x[pu(i)] * 1.5,
+    # down row k reads h[pd(k)] * 0.375.  y_k = 0.375 * silu(0.75 x[pg(j)]) * 1.5 x[pu(j)],
+    # j = pd(k): the gate gets the SiLU, the up the linear term, both read x along H.
+    H, I = 256, 512
+    rng = np.random.default_rng(3)
+    pg = rng.integers(0, H, I)
+    pu = rng.integers(0, H, I)
+    pd = rng.permutation(I)[:H]
+    raw = (_onehot_q2(I, H, pg, 0.75), _onehot_q2(I, H, pu, 1.5), _onehot_q2(H, I, pd, 0.375))
+    x = rng.standard_normal((3, H))
+    wg, wu, wd = moe.expert_weights(*raw, H, I)
+    y = moe.ffn(x, wg, wu, wd)
+    for t in range(3):
+        for k in range(H):
+            j = pd[k]
+            a = 0.75 * x[t, pg[j]]
+            want = 0.375 * (a / (1 + math.exp(-a))) * 1.5 * x[t, pu[j]]
+            assert abs(y[t, k] - want) <= 1e-14 * max(1.0, abs(want))
+
+
+def test_silu_values():
+    assert moe.silu(np.array([0.0]))[0] == 0.0
+    assert abs(moe.silu(np.array([1.0]))[0] - 1 / (1 + math.exp(-1))) < 1e-16
+    assert moe.silu(np.array([-1000.0]))[0] == 0.0
+    assert moe.silu(np.array([1000.0]))[0] == 1000.0
+
+
+# ----------------------------------------------------------------- layer identities
+def _tiny():
+    return host_layer("tiny")
+
+
+def test_k_equals_e_is_dense_mixture():
+    L = _tiny()
+    wl = L.wl
+    x, _ = W.activations(wl)
+    E, H, I = wl.n_experts, wl.hidden, wl.inter
+    out, r = moe.layer(x, L.router_w, None, L.expert_bytes, None, E, H, I)
+    # independent path: stack all experts, einsum over e
+    Wg = np.stack([q2.decode_matrix(L.expert_bytes(e)[0], I, H) for e in range(E)]).astype(np.float64)
+    Wu = np.stack([q2.decode_matrix(L.expert_bytes(e)[1], I, H) for e in range(E)]).astype(np.float64)
+    Wd = np.stack([q2.decode_matrix(L.expert_bytes(e)[2], H, I) for e in range(E)]).astype(np.float64)
+    lg = x.astype(np.float64) @ L.router_w.astype(np.float64).T
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    a = np.einsum("th,eih->tei", x.astype(np.float64), Wg)
+    c = np.einsum("th,eih->tei", x.astype(np.float64), Wu)
+    h = a / (1 + np.exp(-a)) * c
+    y = np.einsum("tei,ehi->teh", h, Wd)
+    want = np.einsum("te,teh->th", p, y)
+    assert np.allclose(out, want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+def test_single_expert_with_shared_is_sum():
+    L = _tiny()
+    wl = L.wl
+    x, _ = W.activations(wl)
+    H, I = wl.hidden, wl.inter
+    one = L.expert_bytes(3)
+    Wr = np.zeros((1, H))
+    rng = np.random.default_rng(4)
+    shared = (rng.standard_normal((I, H)) * 0.02, rng.standard_normal((I, H)) * 0.02,
+              rng.standard_normal((H, I)) * 0.02)
+    out, r = moe.layer(x, Wr, None, lambda e: one, shared, 1, H, I)
+    assert np.all(r["g"] == 1.0)
+    want = moe.ffn(x, *shared) + moe.ffn(x, *moe.expert_weights(*one, H, I))
+    assert np.allclose(out, want, rtol=0, atol=1e-13)
+
+
+def test_identical_experts_make_routing_irrelevant():
+    L = _tiny()
+    wl = L.wl
+    x, _ = W.activations(wl)
+    H, I = wl.hidden, wl.inter
+    same = L.expert_bytes(5)
+    rng = np.random.default_rng(5)
+    o1, _ = moe.layer(x, L.router_w, None, lambda e: same, None, 2, H, I)
+    o2, _ = moe.layer(x, rng.standard_normal(L.router_w.shape), None, lambda e: same, None, 2, H, I)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-13)
+
+
+def _scale_down(raw_down):
+    d = raw_down.copy()
+    for lo in (80, 82):
+        v = d[:, lo:lo + 2].copy().view("<f2").astype(np.float32) * 2
+        d[:, lo:lo + 2] = v.astype(np.float16).view(np.uint8).reshape(-1, 2)
+    return d
+
+
+def test_doubling_down_scales_doubles_output_exactly():
+    L = _tiny()
+    wl = L.wl
+    x, _ = W.activations(wl)
+    H, I = wl.hidden, wl.inter
+    o1, _ = moe.layer(x, L.router_w, None, L.expert_bytes, None, wl.topk, H, I)
+    dbl = lambda e: (L.expert_bytes(e)[0], L.expert_bytes(e)[1], _scale_down(L.expert_bytes(e)[2]))
+    o2, _ = moe.layer(x, L.router_w, None, dbl, None, wl.topk, H, I)
+    assert np.array_equal(o2, 2 * o1)
+
+
+# ----------------------------------------------------------------- RMSNorm / stack
+def test_rmsnorm_closed_forms():
+    h = np.array([[1.0, -1.0] * 128, [3.0] * 256, [0.0] * 255 + [16.0]])
+    x = moe.rmsnorm_bf16(h, 1e-6)
+    assert np.array_equal(x[0], np.sign(h[0]))                    # 1/sqrt(1+1e-6) -> bf16 1.0
+    assert np.array_equal(x[1], np.ones(256))
+    assert x[2, -1] == 16.0 and np.all(x[2, :-1] == 0)            # sqrt(1 + 1e-6) * ... -> 16
+    tiny = moe.rmsnorm_bf16(np.zeros((1, 4)), 1e-6)
+    assert np.all(tiny == 0)
+
+
+def test_round_bf16_known_values():
+    v = np.array([1.0, 1 + 2**-8, 1 + 3 * 2**-8, 1 + 2**-8 + 2**-40, -(1 + 2**-8), 2.0**-130 * 1.75])
+    want = np.array([1.0, 1.0, 1 + 2**-6, 1 + 2**-7, -1.0, 2.0**-130 * 1.75])
+    assert np.array_equal(moe._round_bf16(v), want)
+
+
+def test_stack_with_zero_down_is_identity_and_one_layer_matches():
+    L = _tiny()
+    wl = L.wl
+    H, I = wl.hidden, wl.inter
+    rng = np.random.default_rng(6)
+    h0 = rng.standard_normal((3, H))
+    zero = lambda e: (L.expert_bytes(e)[0], L.expert_bytes(e)[1],
+                      np.zeros_like(L.expert_bytes(e)[2]))
+    layer0 = dict(router_w=L.router_w, router_b=None, expert_bytes=zero, shared=None)
+    h, _ = moe.stack(h0, [layer0, layer0], wl.topk, H, I, 1e-6)
+    assert np.array_equal(h, h0)
+    layer1 = L.oracle_layer()
+    h, _ = moe.stack(h0, [layer1], wl.topk, H, I, 1e-6)
+    want = h0 + moe.layer(moe.rmsnorm_bf16(h0, 1e-6), L.router_w, None, L.expert_bytes,
+                          None, wl.topk, H, I)[0]
+    assert np.array_equal(h, want)
