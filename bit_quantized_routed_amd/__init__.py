@@ -1,0 +1,149 @@
+"""Python binding of libmoe_q2 (the 2-bit routed-expert MoE layer for MI355X).
+
+Argument marshalling only: torch tensors are passed as raw device pointers and
+every step of the layer runs in the HIP library.  The library must be built
+(`python -m bit_quantized_routed_amd.build` or __graft_entry__.build()); there is
+no fallback path.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_q2.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+PATH_AUTO, PATH_DECODE, PATH_PREFILL, PRE_RMSNORM, RESIDUAL_ADD = 0, 1, 2, 4, 8
+PREFILL_MIN_TOKENS = 256
+BLOCK_BYTES = 84
+
+EXPORTS = ["moe_q2_block_bytes", "moe_q2_expert_bytes", "moe_q2_workspace_size",
+           "moe_q2_forward", "moe_q2_quantize", "moe_q2_synth_normal",
+           "moe_q2_status_string", "moe_q2_last_hip_error"]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float)]
+
+
+class Trace(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("perm", ctypes.c_void_p)]
+
+
+class MoeQ2Error(RuntimeError):
+    def __init__(self, status, what):
+        lib = _lib()
+        msg = lib.moe_q2_status_string(status).decode()
+        if status == EHIP:
+            msg += " (hipError %d)" % lib.moe_q2_last_hip_error()
+        super().__init__("%s: status %d, %s" % (what, status, msg))
+        self.status = status
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmoe_q2.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, u64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_uint64, ctypes.c_size_t)
+        lib.moe_q2_block_bytes.restype = sz
+        lib.moe_q2_block_bytes.argtypes = []
+        lib.moe_q2_expert_bytes.restype = sz
+        lib.moe_q2_expert_bytes.argtypes = [ctypes.POINTER(Shape)]
+        lib.moe_q2_workspace_size.restype = ctypes.c_int
+        lib.moe_q2_workspace_size.argtypes = [ctypes.POINTER(Shape), i32, i32, ctypes.POINTER(sz)]
+        lib.moe_q2_forward.restype = ctypes.c_int
+        lib.moe_q2_forward.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.POINTER(Shape), i32, vp,
+                                       vp, sz, ctypes.POINTER(Trace), vp]
+        lib.moe_q2_quantize.restype = ctypes.c_int
+        lib.moe_q2_quantize.argtypes = [vp, i64, vp, vp]
+        lib.moe_q2_synth_normal.restype = ctypes.c_int
+        lib.moe_q2_synth_normal.argtypes = [u64, u64, u64, i64, ctypes.c_float, i32, vp, vp]
+        lib.moe_q2_status_string.restype = ctypes.c_char_p
+        lib.moe_q2_status_string.argtypes = [ctypes.c_int]
+        lib.moe_q2_last_hip_error.restype = ctypes.c_int
+        lib.moe_q2_last_hip_error.argtypes = []
+        _LIB = lib
+    return _LIB
+
+
+def library():
+    return _lib()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_shape(hidden, inter, n_experts, shared_inter=0, act_dtype=BF16, flags=0, rms_eps=1e-6):
+    return Shape(hidden, inter, n_experts, shared_inter, act_dtype, flags, rms_eps)
+
+
+def block_bytes():
+    return int(_lib().moe_q2_block_bytes())
+
+
+def expert_bytes(shape):
+    return int(_lib().moe_q2_expert_bytes(ctypes.byref(shape)))
+
+
+def workspace_size(shape, n_tokens, topk):
+    n = ctypes.c_size_t(0)
+    rc = _lib().moe_q2_workspace_size(ctypes.byref(shape), n_tokens, topk, ctypes.byref(n))
+    if rc:
+        raise MoeQ2Error(rc, "moe_q2_workspace_size")
+    return int(n.value)
+
+
+def forward(x, router_w, experts_q2, shared_w, topk, out, shape, n_tokens, router_b=None,
+            workspace=None, trace=None, stream=None, check=True):
+    """moe_q2_forward on torch device tensors (raw pointers are passed through).
+
+    trace: optional dict with any of topk_idx, topk_w, counts, offsets, perm tensors."""
+    tr = None
+    if trace:
+        tr = Trace(*[_ptr(trace.get(k)) for k in ("topk_idx", "topk_w", "counts", "offsets", "perm")])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib().moe_q2_forward(_ptr(x), _ptr(router_w), _ptr(experts_q2), _ptr(shared_w), topk,
+                               _ptr(out), ctypes.byref(shape), n_tokens, _ptr(router_b),
+                               _ptr(workspace), ws_bytes, ctypes.byref(tr) if tr else None,
+                               _stream(stream))
+    if rc and check:
+        raise MoeQ2Error(rc, "moe_q2_forward")
+    return rc
+
+
+def quantize(w, n_blocks, blocks_out, stream=None):
+    rc = _lib().moe_q2_quantize(_ptr(w), n_blocks, _ptr(blocks_out), _stream(stream))
+    if rc:
+        raise MoeQ2Error(rc, "moe_q2_quantize")
+
+
+def synth_normal(seed, stream_id, start, n, scale, out, out_dtype=F32, stream=None):
+    rc = _lib().moe_q2_synth_normal(seed, stream_id, start, n, float(scale), out_dtype, _ptr(out),
+                                    _stream(stream))
+    if rc:
+        raise MoeQ2Error(rc, "moe_q2_synth_normal")

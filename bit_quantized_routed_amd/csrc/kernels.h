@@ -1,0 +1,25 @@
+// Launchers of the device kernels (host side, internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define FD_TCH 4   // slots per decode work unit
+
+int mq_launch_router(const void *x, int bf16, const float *wr, const float *bias, int T, int H,
+                     int E, float *logits, hipStream_t st);
+int mq_launch_topk(const float *logits, int T, int E, int K, int32_t *idx, float *gate,
+                   int32_t *trace_idx, float *trace_w, hipStream_t st);
+int mq_launch_bucket(const int32_t *idx, int T, int K, int E, int unit_tokens, int32_t *counts,
+                     int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr,
+                     int4 *units, hipStream_t st);
+size_t mq_bucket_lds_bytes(int E);
+int mq_launch_prep(const void *src, int src_bf16, int nrows, int len, int64_t src_ld, uint32_t *xq,
+                   float2 *gsum, float *scale, hipStream_t st);
+int mq_launch_rmsnorm(const float *h, int T, int H, float eps, uint16_t *x, hipStream_t st);
+int mq_launch_q2_dec(int swiglu, const void *experts, int64_t expert_bytes, int64_t off_a,
+                     int64_t off_b, int rows, int kblocks, const int32_t *units_hdr,
+                     const int4 *units, int max_units, const int32_t *perm, int topk,
+                     const uint32_t *xq, const float2 *gsum, const float *xscale, float *out,
+                     int n_cu, hipStream_t st);
+int mq_launch_combine(const float *y, const int32_t *inv, const float *gate, const float *shared,
+                      int T, int H, int K, int accumulate, float *out, hipStream_t st);

@@ -1,0 +1,209 @@
+// Host side of the MoE-Q2 C ABI: validation, workspace carving, path choice and
+// stream-ordered launches.  No allocation, no host synchronisation.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+
+static thread_local int g_last_hip_error = 0;
+
+int mq_fail_hip(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return MOE_Q2_EHIP;
+}
+
+extern "C" int moe_q2_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" const char *moe_q2_status_string(int status) {
+    switch (status) {
+    case MOE_Q2_OK: return "ok";
+    case MOE_Q2_EINVAL: return "invalid argument";
+    case MOE_Q2_EUNSUPPORTED: return "unsupported shape or option";
+    case MOE_Q2_EWORKSPACE: return "workspace missing or too small";
+    case MOE_Q2_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+extern "C" size_t moe_q2_block_bytes(void) { return MQ_BLOCK_BYTES; }
+
+static bool shape_ok(const moe_q2_shape *s) {
+    if (!s) return false;
+    if (s->hidden <= 0 || s->hidden % 256 || s->hidden > 16384) return false;
+    if (s->inter <= 0 || s->inter % 256 || s->inter > 16384) return false;
+    if (s->n_experts < 1 || s->n_experts > 512) return false;
+    if (s->shared_inter < 0 || s->shared_inter % 256 || s->shared_inter > 16384) return false;
+    return true;
+}
+
+extern "C" size_t moe_q2_expert_bytes(const moe_q2_shape *s) {
+    if (!shape_ok(s)) return 0;
+    return (size_t)3 * s->hidden * s->inter / MQ_QK * MQ_BLOCK_BYTES;
+}
+
+namespace {
+struct Workspace {
+    size_t total = 0;
+    size_t logits, idx, gate, counts, offsets, perm, inv, units_hdr, units, xbf, xq, xg, xs, h,
+        hq, hg, hs, y;
+    int max_units = 0;
+};
+
+size_t take(size_t &cursor, size_t bytes) {
+    const size_t at = cursor;
+    cursor += (bytes + 255) & ~(size_t)255;
+    return at;
+}
+
+Workspace carve(const moe_q2_shape *s, int T, int K) {
+    Workspace w;
+    const size_t H = s->hidden, I = s->inter, E = s->n_experts;
+    const size_t S = (size_t)T * K;
+    size_t c = 0;
+    w.max_units = (int)((S + FD_TCH - 1) / FD_TCH + (S < E ? S : E));
+    w.logits = take(c, (size_t)T * E * 4);
+    w.idx = take(c, S * 4);
+    w.gate = take(c, S * 4);
+    w.counts = take(c, E * 4);
+    w.offsets = take(c, (E + 1) * 4);
+    w.perm = take(c, S * 4);
+    w.inv = take(c, S * 4);
+    w.units_hdr = take(c, 16);
+    w.units = take(c, (size_t)w.max_units * 16);
+    w.xbf = take(c, (size_t)T * H * 2);
+    w.xq = take(c, (size_t)T * H * 2);
+    w.xg = take(c, (size_t)T * (H / 16) * 8);
+    w.xs = take(c, (size_t)T * 4);
+    w.h = take(c, S * I * 4);
+    w.hq = take(c, S * I * 2);
+    w.hg = take(c, S * (I / 16) * 8);
+    w.hs = take(c, S * 4);
+    w.y = take(c, S * H * 4);
+    w.total = c;
+    return w;
+}
+
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+}  // namespace
+
+static const int KNOWN_FLAGS = MOE_Q2_PATH_DECODE | MOE_Q2_PATH_PREFILL | MOE_Q2_PRE_RMSNORM |
+                               MOE_Q2_RESIDUAL_ADD;
+
+static int check_common(const moe_q2_shape *s, int32_t n_tokens, int32_t topk) {
+    if (!s) return MOE_Q2_EINVAL;
+    if (!shape_ok(s)) return MOE_Q2_EUNSUPPORTED;
+    if (n_tokens < 0 || n_tokens > (1 << 20)) return MOE_Q2_EINVAL;
+    if (topk < 1 || topk > 16 || topk > s->n_experts) return MOE_Q2_EINVAL;
+    if (s->flags & ~KNOWN_FLAGS) return MOE_Q2_EINVAL;
+    if ((s->flags & MOE_Q2_PATH_DECODE) && (s->flags & MOE_Q2_PATH_PREFILL)) return MOE_Q2_EINVAL;
+    if (!(s->flags & MOE_Q2_PRE_RMSNORM) && s->act_dtype != MOE_Q2_F32 && s->act_dtype != MOE_Q2_BF16)
+        return MOE_Q2_EINVAL;
+    if ((s->flags & MOE_Q2_PRE_RMSNORM) && !(s->rms_eps >= 0.0f && s->rms_eps < 1e30f))
+        return MOE_Q2_EINVAL;
+    return MOE_Q2_OK;
+}
+
+extern "C" int moe_q2_workspace_size(const moe_q2_shape *s, int32_t n_tokens, int32_t topk,
+                                     size_t *bytes) {
+    if (!bytes) return MOE_Q2_EINVAL;
+    const int rc = check_common(s, n_tokens, topk);
+    if (rc) return rc;
+    *bytes = carve(s, n_tokens, topk).total;
+    return MOE_Q2_OK;
+}
+
+static bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *experts_q2,
+                              const uint16_t *shared_w, int32_t topk, float *out,
+                              const moe_q2_shape *s, int32_t n_tokens, const float *router_b,
+                              void *workspace, size_t workspace_bytes, const moe_q2_trace *trace,
+                              void *stream) {
+    int rc = check_common(s, n_tokens, topk);
+    if (rc) return rc;
+    if (!x || !router_w || !experts_q2 || !out) return MOE_Q2_EINVAL;
+    if ((s->shared_inter > 0) != (shared_w != nullptr)) return MOE_Q2_EINVAL;
+    if (((uintptr_t)x & 15) || ((uintptr_t)experts_q2 & 15) || ((uintptr_t)out & 15) ||
+        ((uintptr_t)router_w & 15) || ((uintptr_t)shared_w & 15))
+        return MOE_Q2_EINVAL;
+    const bool rms = (s->flags & MOE_Q2_PRE_RMSNORM) != 0;
+    const bool accum = (s->flags & MOE_Q2_RESIDUAL_ADD) != 0;
+    const int T = n_tokens, K = topk, H = s->hidden, I = s->inter, E = s->n_experts;
+    const size_t xbytes = (size_t)T * H * ((rms || s->act_dtype == MOE_Q2_F32) ? 4 : 2);
+    if (ranges_overlap(x, xbytes, out, (size_t)T * H * 4)) {
+        if (!(x == (const void *)out && rms && accum)) return MOE_Q2_EINVAL;
+    }
+    if (T == 0) return MOE_Q2_OK;
+    const Workspace w = carve(s, T, K);
+    if (!workspace || workspace_bytes < w.total) return MOE_Q2_EWORKSPACE;
+    if ((uintptr_t)workspace & 255) return MOE_Q2_EINVAL;
+    const bool prefill = (s->flags & MOE_Q2_PATH_PREFILL) ||
+                         (!(s->flags & MOE_Q2_PATH_DECODE) && T >= MOE_Q2_PREFILL_MIN_TOKENS);
+    if (prefill) return MOE_Q2_EUNSUPPORTED;
+    if (s->shared_inter > 0) return MOE_Q2_EUNSUPPORTED;
+
+    hipStream_t st = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    float *logits = (float *)(ws + w.logits);
+    int32_t *idx = (int32_t *)(ws + w.idx);
+    float *gate = (float *)(ws + w.gate);
+    int32_t *counts = trace && trace->counts ? trace->counts : (int32_t *)(ws + w.counts);
+    int32_t *offsets = trace && trace->offsets ? trace->offsets : (int32_t *)(ws + w.offsets);
+    int32_t *perm = trace && trace->perm ? trace->perm : (int32_t *)(ws + w.perm);
+    int32_t *inv = (int32_t *)(ws + w.inv);
+    int32_t *units_hdr = (int32_t *)(ws + w.units_hdr);
+    int4 *units = (int4 *)(ws + w.units);
+
+    // layer input
+    const void *xin = x;
+    int xin_bf16 = s->act_dtype == MOE_Q2_BF16;
+    if (rms) {
+        uint16_t *xbf = (uint16_t *)(ws + w.xbf);
+        if ((rc = mq_launch_rmsnorm((const float *)x, T, H, s->rms_eps, xbf, st))) return rc;
+        xin = xbf;
+        xin_bf16 = 1;
+    }
+    // routing
+    if ((rc = mq_launch_router(xin, xin_bf16, router_w, router_b, T, H, E, logits, st))) return rc;
+    if ((rc = mq_launch_topk(logits, T, E, K, idx, gate, trace ? trace->topk_idx : nullptr,
+                             trace ? trace->topk_w : nullptr, st)))
+        return rc;
+    if ((rc = mq_launch_bucket(idx, T, K, E, FD_TCH, counts, offsets, perm, inv, units_hdr, units, st)))
+        return rc;
+    // routed experts, decode path
+    const int ncu = device_cus();
+    const int64_t ebytes = (int64_t)moe_q2_expert_bytes(s);
+    const int64_t mat_gu = (int64_t)I * (H / MQ_QK) * MQ_BLOCK_BYTES;
+    uint32_t *xq = (uint32_t *)(ws + w.xq);
+    float2 *xg = (float2 *)(ws + w.xg);
+    float *xs = (float *)(ws + w.xs);
+    if ((rc = mq_launch_prep(xin, xin_bf16, T, H, H, xq, xg, xs, st))) return rc;
+    float *h = (float *)(ws + w.h);
+    if ((rc = mq_launch_q2_dec(1, experts_q2, ebytes, 0, mat_gu, I, H / MQ_QK, units_hdr, units,
+                               w.max_units, perm, K, xq, xg, xs, h, ncu, st)))
+        return rc;
+    uint32_t *hq = (uint32_t *)(ws + w.hq);
+    float2 *hg = (float2 *)(ws + w.hg);
+    float *hsc = (float *)(ws + w.hs);
+    if ((rc = mq_launch_prep(h, 0, T * K, I, I, hq, hg, hsc, st))) return rc;
+    float *y = (float *)(ws + w.y);
+    if ((rc = mq_launch_q2_dec(0, experts_q2, ebytes, 2 * mat_gu, 0, H, I / MQ_QK, units_hdr, units,
+                               w.max_units, perm, K, hq, hg, hsc, y, ncu, st)))
+        return rc;
+    return mq_launch_combine(y, inv, gate, nullptr, T, H, K, accum ? 1 : 0, out, st);
+}

@@ -1,0 +1,235 @@
+// Routing: router logits, softmax top-K with renormalised gates, and the
+// deterministic token-by-expert bucketing (histogram, exclusive scan, stable
+// permutation, touched-expert work units).
+#include "common.h"
+#include "kernels.h"
+
+// ---------------------------------------------------------------- logits
+// One wave per (expert, token tile of RT_TT tokens); lanes stride the hidden
+// dimension in float4 steps; fp32 FMA, then a butterfly sum across the wave.
+#define RT_TT 8
+template <bool BF16>
+__global__ void __launch_bounds__(256) k_router_logits(const void *__restrict__ x,
+                                                       const float *__restrict__ wr,
+                                                       const float *__restrict__ bias, int T,
+                                                       int H, int E, float *__restrict__ logits) {
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t0 = blockIdx.y * RT_TT;
+    if (e >= E) return;
+    const int nt = min(RT_TT, T - t0);
+    float acc[RT_TT];
+#pragma unroll
+    for (int t = 0; t < RT_TT; ++t) acc[t] = 0.0f;
+    const float4 *w4 = (const float4 *)(wr + (int64_t)e * H);
+    for (int c = lane; c < H / 4; c += 64) {
+        const float4 w = w4[c];
+#pragma unroll
+        for (int t = 0; t < RT_TT; ++t) {
+            if (t < nt) {
+                float4 v;
+                if (BF16) {
+                    const uint2 b = ((const uint2 *)((const uint16_t *)x + (int64_t)(t0 + t) * H))[c];
+                    v = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                                    __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+                } else {
+                    v = ((const float4 *)((const float *)x + (int64_t)(t0 + t) * H))[c];
+                }
+                acc[t] = fmaf(w.x, v.x, acc[t]);
+                acc[t] = fmaf(w.y, v.y, acc[t]);
+                acc[t] = fmaf(w.z, v.z, acc[t]);
+                acc[t] = fmaf(w.w, v.w, acc[t]);
+            }
+        }
+    }
+    const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < RT_TT; ++t) {
+        const float s = mq_wave_sum(acc[t]);
+        if (lane == 0 && t < nt) logits[(int64_t)(t0 + t) * E + e] = s + b;
+    }
+}
+
+// ---------------------------------------------------------------- top-K
+// One wave per token.  K rounds of a wave arg-max over the unselected logits
+// (ties: lower expert index); gates are the softmax over the selected logits,
+// which equals the full softmax renormalised over the selection.
+__global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, int T, int E, int K,
+                                              int32_t *__restrict__ idx, float *__restrict__ gate,
+                                              int32_t *__restrict__ trace_idx,
+                                              float *__restrict__ trace_w) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? logits[(int64_t)t * E + e] : -INFINITY;
+    }
+    uint32_t taken = 0;
+    float sel_v[16];
+    int sel_e[16];
+    for (int k = 0; k < K; ++k) {
+        float bv = -INFINITY;
+        int be = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
+                bv = v[i];
+                be = e;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oe = __shfl_xor(be, o, 64);
+            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+        }
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        sel_v[k] = bv;
+        sel_e[k] = be;
+    }
+    if (lane == 0) {
+        const float mx = sel_v[0];
+        float z = 0.0f, p[16];
+        for (int k = 0; k < K; ++k) { p[k] = expf(sel_v[k] - mx); z += p[k]; }
+        for (int k = 0; k < K; ++k) {
+            const float g = p[k] / z;
+            idx[t * K + k] = sel_e[k];
+            gate[t * K + k] = g;
+            if (trace_idx) trace_idx[t * K + k] = sel_e[k];
+            if (trace_w) trace_w[t * K + k] = g;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- bucketing
+// Single work-group.  counts by LDS atomics (commutative), offsets by a scan,
+// and the stable position of slot s = t*K + k inside expert e's bucket as
+//   offsets[e] + #{t' < t : e chosen by t'}
+// read from a per-expert token bitmap (bits set with atomic OR, so the result
+// does not depend on thread order).  Tokens are processed in chunks of BK_CH.
+// Also emits the touched experts as work units of at most `unit_tokens` slots:
+//   units[u] = (expert, first bucket position, slot count, 0), units_hdr[0] = U.
+#define BK_CH 512
+#define BK_THREADS 1024
+__global__ void __launch_bounds__(BK_THREADS) k_bucket(const int32_t *__restrict__ idx, int T, int K,
+                                                       int E, int unit_tokens,
+                                                       int32_t *__restrict__ counts_out,
+                                                       int32_t *__restrict__ offsets_out,
+                                                       int32_t *__restrict__ perm,
+                                                       int32_t *__restrict__ inv,
+                                                       int32_t *__restrict__ units_hdr,
+                                                       int4 *__restrict__ units) {
+    extern __shared__ uint32_t sm[];
+    const int tid = threadIdx.x;
+    const int W = BK_CH / 32;                 // bitmap words per expert
+    int32_t *cnt = (int32_t *)sm;             // [E]
+    int32_t *off = cnt + E;                   // [E + 1]
+    int32_t *run = off + E + 1;               // [E]
+    int32_t *scan = run + E;                  // [E + 1] (unit scan)
+    uint32_t *bm = (uint32_t *)(scan + E + 1);// [E][W]
+    const int S = T * K;
+
+    for (int e = tid; e < E; e += BK_THREADS) { cnt[e] = 0; run[e] = 0; }
+    __syncthreads();
+    for (int s = tid; s < S; s += BK_THREADS) atomicAdd(&cnt[idx[s]], 1);
+    __syncthreads();
+    {   // exclusive scans of cnt[e] (-> off) and of the unit count per expert (-> scan)
+        __shared__ int wsum[2][BK_THREADS / 64];
+        const int lane = tid & 63, wv = tid >> 6;
+        const int c = tid < E ? cnt[tid] : 0;
+        int a = c, b = (c + unit_tokens - 1) / unit_tokens;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int pa = __shfl_up(a, o, 64), pb = __shfl_up(b, o, 64);
+            if (lane >= o) { a += pa; b += pb; }
+        }
+        if (lane == 63) { wsum[0][wv] = a; wsum[1][wv] = b; }
+        __syncthreads();
+        int ba = 0, bb = 0;
+        for (int w = 0; w < wv; ++w) { ba += wsum[0][w]; bb += wsum[1][w]; }
+        if (tid < E) {
+            off[tid] = ba + a - c;
+            scan[tid] = bb + b - (c + unit_tokens - 1) / unit_tokens;
+        }
+        if (tid == BK_THREADS - 1) {
+            off[E] = ba + a;
+            scan[E] = bb + b;
+            units_hdr[0] = bb + b;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += BK_THREADS) {
+        counts_out[e] = cnt[e];
+        offsets_out[e] = off[e];
+        const int n = cnt[e];
+        for (int c = 0, u = scan[e]; c < n; c += unit_tokens, ++u)
+            units[u] = make_int4(e, off[e] + c, min(unit_tokens, n - c), 0);
+    }
+    if (tid == 0) offsets_out[E] = off[E];
+
+    for (int t0 = 0; t0 < T; t0 += BK_CH) {
+        const int tn = min(BK_CH, T - t0);
+        for (int i = tid; i < E * W; i += BK_THREADS) bm[i] = 0u;
+        __syncthreads();
+        for (int s = t0 * K + tid; s < (t0 + tn) * K; s += BK_THREADS) {
+            const int tl = s / K - t0;
+            atomicOr(&bm[idx[s] * W + (tl >> 5)], 1u << (tl & 31));
+        }
+        __syncthreads();
+        for (int s = t0 * K + tid; s < (t0 + tn) * K; s += BK_THREADS) {
+            const int e = idx[s];
+            const int tl = s / K - t0;
+            const uint32_t *row = bm + e * W;
+            int r = 0;
+            for (int w = 0; w < (tl >> 5); ++w) r += __popc(row[w]);
+            r += __popc(row[tl >> 5] & ((1u << (tl & 31)) - 1u));
+            const int pos = off[e] + run[e] + r;
+            perm[pos] = s;
+            inv[s] = pos;
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += BK_THREADS) {
+            int c = 0;
+            for (int w = 0; w < W; ++w) c += __popc(bm[e * W + w]);
+            run[e] += c;
+        }
+        __syncthreads();
+    }
+}
+
+size_t mq_bucket_lds_bytes(int E) {
+    return (size_t)(4 * E + 2) * 4 + (size_t)E * (BK_CH / 32) * 4;
+}
+
+int mq_launch_router(const void *x, int bf16, const float *wr, const float *bias, int T, int H,
+                     int E, float *logits, hipStream_t st) {
+    dim3 grid((E + 3) / 4, (T + RT_TT - 1) / RT_TT);
+    if (bf16)
+        hipLaunchKernelGGL(k_router_logits<true>, grid, dim3(256), 0, st, x, wr, bias, T, H, E, logits);
+    else
+        hipLaunchKernelGGL(k_router_logits<false>, grid, dim3(256), 0, st, x, wr, bias, T, H, E, logits);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}
+
+int mq_launch_topk(const float *logits, int T, int E, int K, int32_t *idx, float *gate,
+                   int32_t *trace_idx, float *trace_w, hipStream_t st) {
+    hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, K, idx, gate,
+                       trace_idx, trace_w);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}
+
+int mq_launch_bucket(const int32_t *idx, int T, int K, int E, int unit_tokens, int32_t *counts,
+                     int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr,
+                     int4 *units, hipStream_t st) {
+    const size_t lds = mq_bucket_lds_bytes(E);
+    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(BK_THREADS), lds, st, idx, T, K, E, unit_tokens,
+                       counts, offsets, perm, inv, units_hdr, units);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}

@@ -1,0 +1,82 @@
+"""Device-side materialisation of the seeded synthetic workloads (tests, bench).
+
+Every tensor is drawn on the GPU with moe_q2_synth_normal from the same
+(seed, stream, index) definition as the host generator in `synth`, and routed
+expert matrices are encoded with moe_q2_quantize.  The router bias (E floats,
+a logarithm of seeded ranks) is made on the host and uploaded.
+"""
+import numpy as np
+import torch
+
+from synth import workloads as W
+from synth.gen import normal_scale
+
+from . import (BF16, F32, PRE_RMSNORM, make_shape, quantize, synth_normal, workspace_size,
+               expert_bytes as _expert_bytes)
+
+
+def _normal(wl, stream_id, n, sigma, dtype, out=None, start=0):
+    dev = torch.device("cuda")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32 if dtype == F32 else torch.bfloat16, device=dev)
+    synth_normal(wl.seed, stream_id, start, n, float(normal_scale(sigma)), out, out_dtype=dtype)
+    return out
+
+
+class DeviceLayer:
+    """Weights of one layer of a workload, resident in HBM."""
+
+    def __init__(self, wl, layer=0, tmp=None, experts_out=None):
+        self.wl, self.layer = wl, layer
+        E, H, I = wl.n_experts, wl.hidden, wl.inter
+        self.router_w = _normal(wl, W.stream_id(layer, W.TENSOR_ROUTER_W), E * H,
+                                wl.router_sigma, F32).view(E, H)
+        b = W.router_bias(wl, layer)
+        self.router_b = None if b is None else torch.from_numpy(b).cuda()
+        self.shared_w = None
+        if wl.shared_inter:
+            Is = wl.shared_inter
+            self.shared_w = torch.empty(3 * Is * H, dtype=torch.bfloat16, device="cuda")
+            for m in range(3):
+                _normal(wl, W.stream_id(layer, W.TENSOR_SHARED + m), Is * H, wl.shared_sigma, BF16,
+                        out=self.shared_w[m * Is * H:(m + 1) * Is * H])
+        ebytes = wl.expert_bytes
+        self.experts = experts_out if experts_out is not None else \
+            torch.empty(E * ebytes, dtype=torch.uint8, device="cuda")
+        own_tmp = tmp is None
+        if own_tmp:
+            tmp = torch.empty(H * I, dtype=torch.float32, device="cuda")
+        mat_bytes = ebytes // 3
+        for e in range(E):
+            for m in range(3):
+                _normal(wl, W.expert_stream(layer, e, m), H * I, wl.expert_sigma, F32, out=tmp)
+                off = e * ebytes + m * mat_bytes
+                quantize(tmp, H * I // 256, self.experts[off:off + mat_bytes])
+        if own_tmp:
+            del tmp
+
+    def shape(self, flags=0):
+        wl = self.wl
+        act = BF16 if wl.act == "bf16" else F32
+        if wl.rmsnorm:
+            flags |= PRE_RMSNORM
+        return make_shape(wl.hidden, wl.inter, wl.n_experts, wl.shared_inter, act, flags,
+                          wl.rms_eps)
+
+
+def activations(wl, tokens=None):
+    """x [T, H] on the device: fp32, or bf16 for bf16 workloads;
+    for the residual stack this is the initial residual stream (fp32 holding bf16 values)."""
+    T = wl.tokens if tokens is None else tokens
+    n = T * wl.hidden
+    sid = W.stream_id(0, W.TENSOR_X)
+    if wl.rmsnorm:
+        return _normal(wl, sid, n, 1.0, BF16).float().view(T, wl.hidden).contiguous()
+    if wl.act == "bf16":
+        return _normal(wl, sid, n, 1.0, BF16).view(T, wl.hidden)
+    return _normal(wl, sid, n, 1.0, F32).view(T, wl.hidden)
+
+
+def workspace(shape, tokens, topk):
+    n = workspace_size(shape, tokens, topk)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")

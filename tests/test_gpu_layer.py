@@ -1,0 +1,46 @@
+"""GPU parity of the whole layer against the oracle (HIP path through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe
+from synth import workloads as W
+from tests.gpu_util import need_gpu, make_trace, trace_np, check_routing, rel_err
+from tests.oracle_inputs import host_layer
+
+pytestmark = pytest.mark.gpu
+
+TOL_DECODE = 2e-3
+
+
+def _run(mq, dl, x, T, flags=0, out=None):
+    from bit_quantized_routed_amd import workload as dw
+    wl = dl.wl
+    shape = dl.shape(flags)
+    ws = dw.workspace(shape, T, wl.topk)
+    tr = make_trace(T, wl.topk, wl.n_experts)
+    if out is None:
+        out = torch.zeros((T, wl.hidden), dtype=torch.float32, device="cuda")
+    mq.forward(x, dl.router_w, dl.experts, dl.shared_w, wl.topk, out, shape, T,
+               router_b=dl.router_b, workspace=ws, trace=tr)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), trace_np(tr)
+
+
+def test_tiny_layer():
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.WORKLOADS["tiny"]
+    dl = dw.DeviceLayer(wl)
+    hl = host_layer("tiny")
+    assert np.array_equal(dl.experts.cpu().numpy(), hl.all_expert_bytes())
+    x = dw.activations(wl)
+    out, tr = _run(mq, dl, x, wl.tokens)
+    xh, _ = W.activations(wl)
+    assert np.array_equal(x.cpu().numpy(), xh)
+    ref, route = moe.layer(xh, hl.router_w, hl.router_b, hl.expert_bytes, hl.shared, wl.topk,
+                           wl.hidden, wl.inter)
+    excluded, rep = check_routing(tr, route, wl.n_experts, wl.topk)
+    err = rel_err(out, ref, ~excluded)
+    print("tiny", rep, "rel_err", err)
+    assert err <= TOL_DECODE
