@@ -1,0 +1,235 @@
+#!/usr/bin/env python
+"""Benchmark of the 2-bit routed-expert MoE layer on one MI355X.
+
+Metric: MoE-layer tokens/s plus achieved HBM GB/s on the quantized expert bytes,
+for decode and prefill.  A step is one pass of the whole layer (routing,
+bucketing, routed Q2 experts, bf16 shared expert, combine; for the residual
+stack also RMSNorm and the residual add) over one batch of synthetic input with
+all weights resident in HBM.  Decode steps rotate over several distinct layers
+of the same shape (as a model's layer stack does), so each step streams its
+weights from HBM rather than from the 256 MB last-level cache.
+
+Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+EXPERT_BYTES_FULL = 14_450_688
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (2-bit experts), decode and prefill"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode1")
+    ap.add_argument("--extra", default="decode32_zipf",
+                    help="comma-separated extra workloads reported in the same line ('' for none)")
+    ap.add_argument("--rotate", type=int, default=8, help="distinct layers cycled by decode steps")
+    ap.add_argument("--cpu-baseline", type=int, default=1)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_bytes(wl, touched):
+    """Algorithmic HBM bytes of one layer step: touched Q2 experts, bf16 shared
+    expert, fp32 router, activations in (bf16/fp32) and output out (fp32)."""
+    act_in = 4 if (wl.act == "f32" or wl.rmsnorm) else 2
+    b = touched * wl.expert_bytes + 3 * wl.shared_inter * wl.hidden * 2 \
+        + wl.n_experts * wl.hidden * 4 + wl.tokens * wl.hidden * (act_in + 4)
+    if wl.rmsnorm:
+        b += wl.tokens * wl.hidden * 4      # residual read-modify-write
+    return b
+
+
+def traffic_record(kernel):
+    """HBM traffic per launch from committed rocprofv3 counter runs, valid only while
+    the kernel source is unchanged (sha256 recorded with the counters)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != rec["source_sha256"]:
+        return None
+    return rec
+
+
+def run_workload(name, steps, warmup, rotate):
+    import torch
+    import bit_quantized_routed_amd as mq
+    from bit_quantized_routed_amd import workload as dw
+    from synth import workloads as W
+
+    wl = W.WORKLOADS[name]
+    L = wl.layers if wl.layers > 1 else rotate
+    t0 = time.time()
+    tmp = torch.empty(wl.hidden * wl.inter, dtype=torch.float32, device="cuda")
+    layers = [dw.DeviceLayer(wl, layer=l, tmp=tmp) for l in range(L)]
+    del tmp
+    torch.cuda.synchronize()
+    log("[bench] %s: %d layer(s) generated in %.1fs" % (name, L, time.time() - t0))
+    T, K, E = wl.tokens, wl.topk, wl.n_experts
+    flags = mq.RESIDUAL_ADD if wl.rmsnorm else 0
+    shape = layers[0].shape(flags)
+    ws = dw.workspace(shape, T, K)
+    x = dw.activations(wl)
+    out = x if wl.rmsnorm else torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")
+    counts = [torch.zeros(E, dtype=torch.int32, device="cuda") for _ in range(L)]
+    stack = wl.layers > 1            # one step = the whole residual stack
+
+    def one_pass(i, events=None):
+        l = i % L
+        tr = {"counts": counts[l]}
+        if events is not None:
+            tr["events"] = events
+        mq.forward(x, layers[l].router_w, layers[l].experts, layers[l].shared_w, K, out, shape, T,
+                   router_b=layers[l].router_b, workspace=ws, trace=tr)
+
+    def step(i, evs=None):
+        if stack:
+            for l in range(L):
+                one_pass(l, None if evs is None else evs[l])
+        else:
+            one_pass(i, evs)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n_ev = L if stack else 1
+    evsets = [[mq.EventSet() for _ in range(n_ev)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        step(i, evsets[i] if stack else evsets[i][0])
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    ms_per_step = (t2 - t1) * 1e3 / steps
+    phase = {p: [] for p in mq.PHASES}
+    for es in evsets:
+        for e in es:
+            for p, v in e.elapsed().items():
+                phase[p].append(v)
+        for e in es:
+            e.close()
+    touched = [int((c > 0).sum().item()) for c in counts]
+    # per-pass averages
+    phase_ms = {p: float(np.mean(v)) for p, v in phase.items()}
+    d_mean = float(np.mean(touched))
+    passes = L if stack else 1
+    tokens_per_step = T * (1 if not stack else 1)
+    bytes_per_pass = layer_bytes(wl, d_mean)
+    res = {
+        "workload": name, "tokens": T, "layers_in_step": passes, "layers_resident": L,
+        "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_step / (ms_per_step * 1e-3),
+        "layer_tokens_per_s": T * passes / (ms_per_step * 1e-3),
+        "touched_experts_mean": d_mean, "touched_experts_per_layer": touched,
+        "algorithmic_bytes_per_pass": bytes_per_pass,
+        "hbm_gbs": bytes_per_pass * passes / (ms_per_step * 1e-3) / 1e9,
+        "phases_ms_per_pass": phase_ms,
+    }
+    # dominant kernel roofline
+    dom = max(phase_ms, key=phase_ms.get)
+    gu_bytes = d_mean * 2 * (wl.expert_bytes // 3)
+    dn_bytes = d_mean * (wl.expert_bytes // 3)
+    kbytes = {"gate_up": gu_bytes + T * wl.hidden * 2.5 + T * K * wl.inter * 4,
+              "down": dn_bytes + T * K * wl.inter * 2.5 + T * K * wl.hidden * 4,
+              "shared": 3 * wl.shared_inter * wl.hidden * 2}.get(dom)
+    if kbytes is not None and phase_ms[dom] > 0:
+        ach = kbytes / (phase_ms[dom] * 1e-3) / 1e9
+        tr = traffic_record({"gate_up": "k_q2_dec<SWIGLU>", "down": "k_q2_dec<PLAIN>"}.get(dom, dom))
+        res["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                           "traffic": None if tr is None else tr.get("bytes_per_launch"),
+                           "algorithmic_bytes_per_launch": kbytes,
+                           "avg_launch_ms": phase_ms[dom]}
+    del layers, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(name):
+    """The oracle, untuned, on the host cores for a bounded sample: one token of one
+    layer (its routed experts' Q2 bytes prepared beforehand, untimed)."""
+    from oracle import moe
+    from tests.oracle_inputs import HostLayer
+    from synth import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        thr = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        thr = 1
+    wl = W.WORKLOADS[name]
+    hl = HostLayer(wl, 0)
+    xh, _ = W.activations(wl, tokens=1)
+    idx, _, _, _ = moe.route(xh, hl.router_w, hl.router_b, wl.topk)
+    for e in idx[0]:
+        hl.expert_bytes(int(e))          # untimed: input preparation
+    t = time.perf_counter()
+    moe.layer(xh, hl.router_w, hl.router_b, hl.expert_bytes, hl.shared, wl.topk, wl.hidden, wl.inter)
+    dt = time.perf_counter() - t
+    return {"value": round(1.0 / dt, 4), "unit": "tokens/s", "cores": int(thr),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": "1 token of layer 0 of %s (routing, dequantisation of its %d experts, fp64 "
+                      "FFNs, shared expert, combine); %.2f s" % (name, wl.topk, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    head = run_workload(args.workload, args.steps, args.warmup, args.rotate)
+    extras = {}
+    for name in [n for n in args.extra.split(",") if n and n != args.workload]:
+        extras[name] = run_workload(name, args.steps, args.warmup, args.rotate)
+    cpu = cpu_baseline(args.workload) if args.cpu_baseline else None
+    from synth import workloads as W
+    wl = W.WORKLOADS[args.workload]
+    line = {
+        "metric": METRIC, "value": round(head["tokens_per_s"], 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": wl.tokens, "hidden": wl.hidden,
+                   "n_experts": wl.n_experts, "topk": wl.topk, "inter": wl.inter,
+                   "shared_inter": wl.shared_inter, "weights": "q2 routed (84 B/256), bf16 shared, fp32 router",
+                   "layers_rotated": head["layers_resident"],
+                   "touched_experts_mean": head["touched_experts_mean"]},
+        "hbm_gbs": round(head["hbm_gbs"], 1),
+        "roofline": head.get("roofline"),
+        "cpu_baseline": cpu,
+        "phases_ms": {k: round(v, 5) for k, v in head["phases_ms_per_pass"].items()},
+        "workloads": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
+                          for kk, vv in v.items() if kk != "touched_experts_per_layer"}
+                      for k, v in extras.items()},
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

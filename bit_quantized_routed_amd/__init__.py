@@ -18,7 +18,7 @@ PREFILL_MIN_TOKENS = 256
 BLOCK_BYTES = 84
 
 EXPORTS = ["moe_q2_block_bytes", "moe_q2_expert_bytes", "moe_q2_workspace_size",
-           "moe_q2_forward", "moe_q2_quantize", "moe_q2_synth_normal",
+           "moe_q2_forward", "moe_q2_quantize", "moe_q2_pack_expert", "moe_q2_synth_normal",
            "moe_q2_status_string", "moe_q2_last_hip_error"]
 
 
@@ -32,7 +32,11 @@ class Shape(ctypes.Structure):
 class Trace(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
                 ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
-                ("perm", ctypes.c_void_p)]
+                ("perm", ctypes.c_void_p), ("events", ctypes.c_void_p)]
+
+
+PHASES = ["rmsnorm", "router", "topk", "bucket", "prep_x", "gate_up", "prep_h", "down",
+          "shared", "combine"]
 
 
 class MoeQ2Error(RuntimeError):
@@ -67,6 +71,8 @@ def _lib():
                                        vp, sz, ctypes.POINTER(Trace), vp]
         lib.moe_q2_quantize.restype = ctypes.c_int
         lib.moe_q2_quantize.argtypes = [vp, i64, vp, vp]
+        lib.moe_q2_pack_expert.restype = ctypes.c_int
+        lib.moe_q2_pack_expert.argtypes = [vp, vp, vp, i32, i32, vp, vp]
         lib.moe_q2_synth_normal.restype = ctypes.c_int
         lib.moe_q2_synth_normal.argtypes = [u64, u64, u64, i64, ctypes.c_float, i32, vp, vp]
         lib.moe_q2_status_string.restype = ctypes.c_char_p
@@ -122,10 +128,13 @@ def forward(x, router_w, experts_q2, shared_w, topk, out, shape, n_tokens, route
             workspace=None, trace=None, stream=None, check=True):
     """moe_q2_forward on torch device tensors (raw pointers are passed through).
 
-    trace: optional dict with any of topk_idx, topk_w, counts, offsets, perm tensors."""
+    trace: optional dict with any of topk_idx, topk_w, counts, offsets, perm tensors, and
+    `events`: an EventSet whose 2 * len(PHASES) HIP events bracket the phases."""
     tr = None
     if trace:
-        tr = Trace(*[_ptr(trace.get(k)) for k in ("topk_idx", "topk_w", "counts", "offsets", "perm")])
+        ev = trace.get("events")
+        tr = Trace(*[_ptr(trace.get(k)) for k in ("topk_idx", "topk_w", "counts", "offsets", "perm")],
+                   ev.array_ptr() if ev is not None else None)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _lib().moe_q2_forward(_ptr(x), _ptr(router_w), _ptr(experts_q2), _ptr(shared_w), topk,
                                _ptr(out), ctypes.byref(shape), n_tokens, _ptr(router_b),
@@ -142,8 +151,57 @@ def quantize(w, n_blocks, blocks_out, stream=None):
         raise MoeQ2Error(rc, "moe_q2_quantize")
 
 
+def pack_expert(gate, up, down, hidden, inter, out, stream=None):
+    rc = _lib().moe_q2_pack_expert(_ptr(gate), _ptr(up), _ptr(down), hidden, inter, _ptr(out),
+                                   _stream(stream))
+    if rc:
+        raise MoeQ2Error(rc, "moe_q2_pack_expert")
+
+
 def synth_normal(seed, stream_id, start, n, scale, out, out_dtype=F32, stream=None):
     rc = _lib().moe_q2_synth_normal(seed, stream_id, start, n, float(scale), out_dtype, _ptr(out),
                                     _stream(stream))
     if rc:
         raise MoeQ2Error(rc, "moe_q2_synth_normal")
+
+
+class EventSet:
+    """2 * len(PHASES) hipEvent_t handles (created with the HIP runtime directly) that
+    moe_q2_forward records around its phases; elapsed() returns per-phase ms."""
+
+    def __init__(self):
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip = hip
+        n = 2 * len(PHASES)
+        self._arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            rc = hip.hipEventCreate(ctypes.byref(h))
+            if rc:
+                raise RuntimeError("hipEventCreate failed: %d" % rc)
+            self._arr[i] = h
+
+    def array_ptr(self):
+        return ctypes.cast(self._arr, ctypes.c_void_p).value
+
+    def elapsed(self):
+        """Per-phase durations in ms of the last recorded forward (synchronises)."""
+        for i in range(len(self._arr)):
+            self._hip.hipEventSynchronize(self._arr[i])
+        out = {}
+        for i, name in enumerate(PHASES):
+            ms = ctypes.c_float()
+            rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self._arr[2 * i], self._arr[2 * i + 1])
+            out[name] = ms.value if rc == 0 else float("nan")
+        return out
+
+    def close(self):
+        for i in range(len(self._arr)):
+            if self._arr[i]:
+                self._hip.hipEventDestroy(self._arr[i])
+                self._arr[i] = None

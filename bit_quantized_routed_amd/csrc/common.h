@@ -16,6 +16,9 @@
 typedef _Float16 mq_half2 __attribute__((ext_vector_type(2)));
 typedef short mq_bf16x2_raw __attribute__((ext_vector_type(2)));
 typedef float mq_f32x4 __attribute__((ext_vector_type(4)));
+// Native 128-bit vector (HIP's uint4 class copies through memcpy and can end up in
+// scratch memory; this type stays in registers).
+typedef uint32_t mq_u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float mq_bf16_to_f32(uint16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);

@@ -7,13 +7,13 @@
 // the grid is persistent and strides over the unit x tile space (the unit count
 // is produced on the device by the bucketing kernel).
 //
-// Per work-group (4 waves, 64 matrix rows: SWIGLU pairs 32 gate rows with the
-// same 32 up rows): the K dimension is walked in chunks of 4 super-blocks.  A
-// chunk of the 64 rows is staged HBM -> LDS with coalesced dword loads (rows of
-// 84-byte blocks, repacked at a 96-byte block / 100-dword row stride so that the
-// per-row 16-byte LDS reads of a wave hit 64 distinct banks), then wave w
-// decodes block w of the chunk: lane l owns matrix row l.  The activations of
-// the unit's slots are wave-uniform and are read as scalars.
+// Per work-group (4 waves, one 64-row tile of the tiled expert layout: SWIGLU
+// tiles pair 32 gate rows with the same 32 up rows): the K dimension is walked
+// in chunks of 4 block columns.  A chunk is one contiguous 21 KB span, streamed
+// HBM -> registers with 16-byte loads one chunk ahead of the compute and then
+// copied to LDS; wave w decodes block column w of the chunk, lane l owns tile
+// row l (its block sits at an odd 21-dword stride: conflict-free LDS reads).
+// The activations of the unit's slots are wave-uniform and read as scalars.
 //
 // Dot product per 16-weight group (see prep.hip for the activation side): the
 // code dword holds weights i and i+8 at bits 2i and 2i+16, so
@@ -28,8 +28,6 @@
 #include "kernels.h"
 
 #define FD_ROWS 64
-#define FD_RS 100
-#define FD_BS 24
 
 // Wave-uniform data read through the scalar unit (constant address space).
 #define MQ_CONST __attribute__((address_space(4)))
@@ -49,15 +47,17 @@ __device__ __forceinline__ uint32_t mq_and_or(uint32_t a, uint32_t m, uint32_t o
 // Decode one 84-byte block (lane's row) against NT activation rows whose group
 // records start at xb[t] (8 dwords per group) and gb[t] (2 floats per group).
 template <int NT>
-__device__ __forceinline__ void mq_block_dot(const uint32_t *__restrict__ blk, const uint32_t *xb[NT],
-                                             const float *gb[NT], const uint32_t (&mask)[5],
-                                             uint32_t magic, float (&tot)[FD_TCH]) {
-    const uint4 *bp = (const uint4 *)blk;
-    const uint4 q0 = bp[0], q1 = bp[1], q2 = bp[2], q3 = bp[3], q4 = bp[4];
-    const uint32_t dd = blk[20];
-    const uint32_t sw[4] = {q0.x, q0.y, q0.z, q0.w};
-    const uint32_t cw[16] = {q1.x, q1.y, q1.z, q1.w, q2.x, q2.y, q2.z, q2.w,
-                             q3.x, q3.y, q3.z, q3.w, q4.x, q4.y, q4.z, q4.w};
+__device__ __forceinline__ void mq_block_dot(const uint32_t *__restrict__ bl,
+                                             const uint32_t *__restrict__ xq,
+                                             const float *__restrict__ gs, const uint32_t (&xo)[FD_TCH],
+                                             const uint32_t (&mask)[5], uint32_t magic,
+                                             float (&tot)[FD_TCH]) {
+    uint32_t sw[4], cw[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sw[i] = bl[i];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cw[i] = bl[4 + i];
+    const uint32_t dd = bl[20];
     const float d = mq_h2f((uint16_t)(dd & 0xFFFFu));
     const float dmin = mq_h2f((uint16_t)(dd >> 16));
     float accB[NT], accM[NT];
@@ -79,8 +79,8 @@ __device__ __forceinline__ void mq_block_dot(const uint32_t *__restrict__ blk, c
             for (int p = 5; p < 8; ++p) A[p] = mq_and_or(c10, mask[p - 5], magic);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const MQ_CONST uint32_t *xr = (const MQ_CONST uint32_t *)(xb[t] + 8 * j);
-                const MQ_CONST float *gp = (const MQ_CONST float *)(gb[t] + 2 * j);
+                const MQ_CONST uint32_t *xr = (const MQ_CONST uint32_t *)(xq + xo[t] + 8 * j);
+                const MQ_CONST float *gp = (const MQ_CONST float *)(gs + (xo[t] >> 2) + 2 * j);
                 float S = gp[0];
 #pragma unroll
                 for (int p = 0; p < 8; ++p) S = mq_dot2(A[p], xr[p], S);
@@ -96,18 +96,50 @@ __device__ __forceinline__ void mq_block_dot(const uint32_t *__restrict__ blk, c
     }
 }
 
+// Chunk = up to 4 block columns of one 64-row tile: nb * 64 * 84 bytes, contiguous
+// in the tiled expert layout (nb * 336 uint4).  Each thread owns uint4 i = tid + 256 n
+// (indices past the chunk re-read its last uint4, which keeps every load in bounds
+// and the prefetch registers unconditionally written).
+struct mq_pf6 { mq_u32x4 a, b, c, d, e, f; };
+__device__ __forceinline__ void mq_chunk_load(const mq_u32x4 *__restrict__ src, int n16, int tid,
+                                              mq_pf6 &pf) {
+    pf.a = src[min(tid, n16 - 1)];
+    pf.b = src[min(tid + 256, n16 - 1)];
+    pf.c = src[min(tid + 512, n16 - 1)];
+    pf.d = src[min(tid + 768, n16 - 1)];
+    pf.e = src[min(tid + 1024, n16 - 1)];
+    pf.f = src[min(tid + 1280, n16 - 1)];
+}
+__device__ __forceinline__ void mq_chunk_store(mq_u32x4 *__restrict__ dst, int n16, int tid,
+                                               const mq_pf6 &pf) {
+    if (n16 == 4 * 336) {          // full chunk: mq_u32x4 1280..1343 belong to wave 0 only
+        dst[tid] = pf.a;
+        dst[tid + 256] = pf.b;
+        dst[tid + 512] = pf.c;
+        dst[tid + 768] = pf.d;
+        dst[tid + 1024] = pf.e;
+        if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) dst[tid + 1280] = pf.f;
+        return;
+    }
+    if (tid < n16) dst[tid] = pf.a;
+    if (tid + 256 < n16) dst[tid + 256] = pf.b;
+    if (tid + 512 < n16) dst[tid + 512] = pf.c;
+    if (tid + 768 < n16) dst[tid + 768] = pf.d;
+    if (tid + 1024 < n16) dst[tid + 1024] = pf.e;
+    if (tid + 1280 < n16) dst[tid + 1280] = pf.f;
+}
+
 template <bool SWIGLU>
 __global__ void __launch_bounds__(256) k_q2_dec(const uint8_t *__restrict__ experts,
-                                                int64_t expert_bytes, int64_t off_a, int64_t off_b,
-                                                int rows, int kblocks,
-                                                const int32_t *__restrict__ units_hdr,
+                                                int64_t expert_bytes, int64_t mat_off, int rows,
+                                                int kblocks, const int32_t *__restrict__ units_hdr,
                                                 const int4 *__restrict__ units,
                                                 const int32_t *__restrict__ perm, int topk,
                                                 const uint32_t *__restrict__ xq,
                                                 const float2 *__restrict__ gsum,
                                                 const float *__restrict__ xscale,
                                                 float *__restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint32_t stage[FD_ROWS * FD_RS];
+    __shared__ __attribute__((aligned(16))) uint32_t stage[4 * 64 * MQ_BLOCK_DWORDS];
     __shared__ float red[4][FD_TCH][FD_ROWS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, known uniform
@@ -116,7 +148,7 @@ __global__ void __launch_bounds__(256) k_q2_dec(const uint8_t *__restrict__ expe
     const int U = units_hdr[0];
     const int G = kblocks * 16;
     const int nchunks = (kblocks + 3) >> 2;
-    const int64_t row_bytes = (int64_t)kblocks * MQ_BLOCK_BYTES;
+    const int64_t tile_bytes = (int64_t)kblocks * 64 * MQ_BLOCK_BYTES;
     uint32_t mask[5];
 #pragma unroll
     for (int p = 0; p < 5; ++p) mask[p] = __builtin_amdgcn_readfirstlane(0x00030003u << (2 * p)) + 0u * lane;
@@ -133,43 +165,35 @@ __global__ void __launch_bounds__(256) k_q2_dec(const uint8_t *__restrict__ expe
             const int p = p0 + (t < nt ? t : 0);
             arow[t] = __builtin_amdgcn_readfirstlane(SWIGLU ? perm[p] / topk : p);
         }
-        const uint8_t *ebase = experts + (int64_t)e * expert_bytes;
+        const mq_u32x4 *tbase = (const mq_u32x4 *)(experts + (int64_t)e * expert_bytes + mat_off +
+                                             (int64_t)tile * tile_bytes);
         float tot[FD_TCH];
 #pragma unroll
         for (int t = 0; t < FD_TCH; ++t) tot[t] = 0.0f;
 
+        mq_pf6 pf;
+        mq_chunk_load(tbase, min(4, kblocks) * 336, tid, pf);
         for (int c = 0; c < nchunks; ++c) {
             const int nb = min(4, kblocks - 4 * c);
-            const int per_row = nb * MQ_BLOCK_DWORDS;
             __syncthreads();
-            for (int i = tid; i < FD_ROWS * per_row; i += 256) {
-                const int r = i / per_row, rem = i - r * per_row;
-                const int b = rem / MQ_BLOCK_DWORDS, k = rem - b * MQ_BLOCK_DWORDS;
-                int64_t moff;
-                int grow;
-                if (SWIGLU) { moff = r < 32 ? off_a : off_b; grow = r0 + (r & 31); }
-                else { moff = off_a; grow = r0 + r; }
-                const uint32_t *src = (const uint32_t *)(ebase + moff + grow * row_bytes +
-                                                         (int64_t)(4 * c + b) * MQ_BLOCK_BYTES);
-                stage[r * FD_RS + b * FD_BS + k] = src[k];
-            }
+            mq_chunk_store((mq_u32x4 *)stage, nb * 336, tid, pf);
             __syncthreads();
+            if (c + 1 < nchunks)
+                mq_chunk_load(tbase + (int64_t)(c + 1) * 4 * 336, min(4, kblocks - 4 * (c + 1)) * 336,
+                              tid, pf);
             if (wv < nb) {
                 const int cb = 4 * c + wv;
-                const uint32_t *blk = stage + lane * FD_RS + wv * FD_BS;
-                const uint32_t *xb[FD_TCH];
-                const float *gb[FD_TCH];
+                const uint32_t *bl = stage + (wv * 64 + lane) * MQ_BLOCK_DWORDS;
+                // per-token dword offset of group record (row, cb*16) in xq (gsum is at 1/4)
+                uint32_t xo[FD_TCH];
 #pragma unroll
-                for (int t = 0; t < FD_TCH; ++t) {
-                    const int64_t g0 = (int64_t)arow[t] * G + cb * 16;
-                    xb[t] = xq + g0 * 8;
-                    gb[t] = (const float *)(gsum + g0);
-                }
+                for (int t = 0; t < FD_TCH; ++t) xo[t] = (uint32_t)(arow[t] * G + cb * 16) * 8u;
+                const float *gs = (const float *)gsum;
                 switch (nt) {
-                case 1: mq_block_dot<1>(blk, xb, gb, mask, magic, tot); break;
-                case 2: mq_block_dot<2>(blk, xb, gb, mask, magic, tot); break;
-                case 3: mq_block_dot<3>(blk, xb, gb, mask, magic, tot); break;
-                default: mq_block_dot<4>(blk, xb, gb, mask, magic, tot); break;
+                case 1: mq_block_dot<1>(bl, xq, gs, xo, mask, magic, tot); break;
+                case 2: mq_block_dot<2>(bl, xq, gs, xo, mask, magic, tot); break;
+                case 3: mq_block_dot<3>(bl, xq, gs, xo, mask, magic, tot); break;
+                default: mq_block_dot<4>(bl, xq, gs, xo, mask, magic, tot); break;
                 }
             }
         }
@@ -198,11 +222,10 @@ __global__ void __launch_bounds__(256) k_q2_dec(const uint8_t *__restrict__ expe
     }
 }
 
-int mq_launch_q2_dec(int swiglu, const void *experts, int64_t expert_bytes, int64_t off_a,
-                     int64_t off_b, int rows, int kblocks, const int32_t *units_hdr,
-                     const int4 *units, int max_units, const int32_t *perm, int topk,
-                     const uint32_t *xq, const float2 *gsum, const float *xscale, float *out,
-                     int n_cu, hipStream_t st) {
+int mq_launch_q2_dec(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
+                     int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
+                     int max_units, const int32_t *perm, int topk, const uint32_t *xq,
+                     const float2 *gsum, const float *xscale, float *out, int n_cu, hipStream_t st) {
     const int tiles = rows / (swiglu ? 32 : 64);
     int64_t want = (int64_t)max_units * tiles;
     int64_t cap = (int64_t)n_cu * 8;
@@ -210,12 +233,12 @@ int mq_launch_q2_dec(int swiglu, const void *experts, int64_t expert_bytes, int6
     if (grid <= 0) return MOE_Q2_OK;
     if (swiglu)
         hipLaunchKernelGGL(k_q2_dec<true>, dim3(grid), dim3(256), 0, st, (const uint8_t *)experts,
-                           expert_bytes, off_a, off_b, rows, kblocks, units_hdr, units, perm, topk,
-                           xq, gsum, xscale, out);
+                           expert_bytes, mat_off, rows, kblocks, units_hdr, units, perm, topk, xq,
+                           gsum, xscale, out);
     else
         hipLaunchKernelGGL(k_q2_dec<false>, dim3(grid), dim3(256), 0, st, (const uint8_t *)experts,
-                           expert_bytes, off_a, off_b, rows, kblocks, units_hdr, units, perm, topk,
-                           xq, gsum, xscale, out);
+                           expert_bytes, mat_off, rows, kblocks, units_hdr, units, perm, topk, xq,
+                           gsum, xscale, out);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

@@ -16,10 +16,16 @@ size_t mq_bucket_lds_bytes(int E);
 int mq_launch_prep(const void *src, int src_bf16, int nrows, int len, int64_t src_ld, uint32_t *xq,
                    float2 *gsum, float *scale, hipStream_t st);
 int mq_launch_rmsnorm(const float *h, int T, int H, float eps, uint16_t *x, hipStream_t st);
-int mq_launch_q2_dec(int swiglu, const void *experts, int64_t expert_bytes, int64_t off_a,
-                     int64_t off_b, int rows, int kblocks, const int32_t *units_hdr,
-                     const int4 *units, int max_units, const int32_t *perm, int topk,
-                     const uint32_t *xq, const float2 *gsum, const float *xscale, float *out,
-                     int n_cu, hipStream_t st);
+int mq_launch_q2_dec(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
+                     int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
+                     int max_units, const int32_t *perm, int topk, const uint32_t *xq,
+                     const float2 *gsum, const float *xscale, float *out, int n_cu, hipStream_t st);
 int mq_launch_combine(const float *y, const int32_t *inv, const float *gate, const float *shared,
                       int T, int H, int K, int accumulate, float *out, hipStream_t st);
+int mq_launch_split_bf16(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t st);
+int mq_gemm_splits(int M, int N, int K, int n_cu);
+int mq_launch_gemm_bf16(const uint16_t *A, const uint16_t *Alo, int lda, const uint16_t *B, int ldb,
+                        int M, int N, int K, int nsplit, float *P, hipStream_t st);
+int mq_launch_swiglu_partials(const float *P, int nsplit, int M, int Is, uint16_t *hi, uint16_t *lo,
+                              hipStream_t st);
+int mq_launch_sum_partials(const float *P, int nsplit, int64_t MN, float *out, hipStream_t st);

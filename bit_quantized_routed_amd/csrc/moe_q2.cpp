@@ -46,8 +46,8 @@ namespace {
 struct Workspace {
     size_t total = 0;
     size_t logits, idx, gate, counts, offsets, perm, inv, units_hdr, units, xbf, xq, xg, xs, h,
-        hq, hg, hs, y;
-    int max_units = 0;
+        hq, hg, hs, y, xlo, sp, shi, slo, ysh;
+    int max_units = 0, split_gu = 1, split_d = 1;
 };
 
 size_t take(size_t &cursor, size_t bytes) {
@@ -80,6 +80,18 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     w.hg = take(c, S * (I / 16) * 8);
     w.hs = take(c, S * 4);
     w.y = take(c, S * H * 4);
+    const size_t Is = s->shared_inter;
+    if (Is) {
+        // split-K policy fixed at 256 compute units so the size does not depend on the device
+        w.split_gu = mq_gemm_splits(T, (int)(2 * Is), (int)H, 256);
+        w.split_d = mq_gemm_splits(T, (int)H, (int)Is, 256);
+        const size_t pgu = (size_t)w.split_gu * T * 2 * Is, pd = (size_t)w.split_d * T * H;
+        w.xlo = take(c, (size_t)T * H * 2);
+        w.sp = take(c, (pgu > pd ? pgu : pd) * 4);
+        w.shi = take(c, (size_t)T * Is * 2);
+        w.slo = take(c, (size_t)T * Is * 2);
+        w.ysh = take(c, (size_t)T * H * 4);
+    }
     w.total = c;
     return w;
 }
@@ -155,9 +167,20 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     const bool prefill = (s->flags & MOE_Q2_PATH_PREFILL) ||
                          (!(s->flags & MOE_Q2_PATH_DECODE) && T >= MOE_Q2_PREFILL_MIN_TOKENS);
     if (prefill) return MOE_Q2_EUNSUPPORTED;
-    if (s->shared_inter > 0) return MOE_Q2_EUNSUPPORTED;
 
     hipStream_t st = (hipStream_t)stream;
+    hipEvent_t *ev = trace && trace->events ? (hipEvent_t *)trace->events : nullptr;
+    auto mark = [&](int phase, int end) -> int {
+        if (!ev) return MOE_Q2_OK;
+        const hipError_t e = hipEventRecord(ev[2 * phase + end], st);
+        return e == hipSuccess ? MOE_Q2_OK : mq_fail_hip(e);
+    };
+#define MQ_PHASE(ph, call)                                                                 \
+    do {                                                                                   \
+        if ((rc = mark(ph, 0))) return rc;                                                 \
+        if ((rc = (call))) return rc;                                                      \
+        if ((rc = mark(ph, 1))) return rc;                                                 \
+    } while (0)
     char *ws = (char *)workspace;
     float *logits = (float *)(ws + w.logits);
     int32_t *idx = (int32_t *)(ws + w.idx);
@@ -174,17 +197,16 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     int xin_bf16 = s->act_dtype == MOE_Q2_BF16;
     if (rms) {
         uint16_t *xbf = (uint16_t *)(ws + w.xbf);
-        if ((rc = mq_launch_rmsnorm((const float *)x, T, H, s->rms_eps, xbf, st))) return rc;
+        MQ_PHASE(MOE_Q2_PH_RMSNORM, mq_launch_rmsnorm((const float *)x, T, H, s->rms_eps, xbf, st));
         xin = xbf;
         xin_bf16 = 1;
     }
     // routing
-    if ((rc = mq_launch_router(xin, xin_bf16, router_w, router_b, T, H, E, logits, st))) return rc;
-    if ((rc = mq_launch_topk(logits, T, E, K, idx, gate, trace ? trace->topk_idx : nullptr,
-                             trace ? trace->topk_w : nullptr, st)))
-        return rc;
-    if ((rc = mq_launch_bucket(idx, T, K, E, FD_TCH, counts, offsets, perm, inv, units_hdr, units, st)))
-        return rc;
+    MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router(xin, xin_bf16, router_w, router_b, T, H, E, logits, st));
+    MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk(logits, T, E, K, idx, gate, trace ? trace->topk_idx : nullptr,
+                                            trace ? trace->topk_w : nullptr, st));
+    MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket(idx, T, K, E, FD_TCH, counts, offsets, perm, inv,
+                                                units_hdr, units, st));
     // routed experts, decode path
     const int ncu = device_cus();
     const int64_t ebytes = (int64_t)moe_q2_expert_bytes(s);
@@ -192,18 +214,45 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     uint32_t *xq = (uint32_t *)(ws + w.xq);
     float2 *xg = (float2 *)(ws + w.xg);
     float *xs = (float *)(ws + w.xs);
-    if ((rc = mq_launch_prep(xin, xin_bf16, T, H, H, xq, xg, xs, st))) return rc;
+    MQ_PHASE(MOE_Q2_PH_PREP_X, mq_launch_prep(xin, xin_bf16, T, H, H, xq, xg, xs, st));
     float *h = (float *)(ws + w.h);
-    if ((rc = mq_launch_q2_dec(1, experts_q2, ebytes, 0, mat_gu, I, H / MQ_QK, units_hdr, units,
-                               w.max_units, perm, K, xq, xg, xs, h, ncu, st)))
-        return rc;
+    MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_dec(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr,
+                                                 units, w.max_units, perm, K, xq, xg, xs, h, ncu, st));
     uint32_t *hq = (uint32_t *)(ws + w.hq);
     float2 *hg = (float2 *)(ws + w.hg);
     float *hsc = (float *)(ws + w.hs);
-    if ((rc = mq_launch_prep(h, 0, T * K, I, I, hq, hg, hsc, st))) return rc;
+    MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep(h, 0, T * K, I, I, hq, hg, hsc, st));
     float *y = (float *)(ws + w.y);
-    if ((rc = mq_launch_q2_dec(0, experts_q2, ebytes, 2 * mat_gu, 0, H, I / MQ_QK, units_hdr, units,
-                               w.max_units, perm, K, hq, hg, hsc, y, ncu, st)))
-        return rc;
-    return mq_launch_combine(y, inv, gate, nullptr, T, H, K, accum ? 1 : 0, out, st);
+    MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_dec(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr,
+                                              units, w.max_units, perm, K, hq, hg, hsc, y, ncu, st));
+    // shared expert: full-precision bf16 weights on MFMA, weight 1
+    float *ysh = nullptr;
+    if ((rc = mark(MOE_Q2_PH_SHARED, 0))) return rc;
+    if (s->shared_inter > 0) {
+        const int Is = s->shared_inter;
+        const uint16_t *xa = (const uint16_t *)xin, *xa_lo = nullptr;
+        if (!xin_bf16) {
+            uint16_t *hi = (uint16_t *)(ws + w.xbf), *lo = (uint16_t *)(ws + w.xlo);
+            if ((rc = mq_launch_split_bf16((const float *)xin, (int64_t)T * H, hi, lo, st))) return rc;
+            xa = hi;
+            xa_lo = lo;
+        }
+        float *P = (float *)(ws + w.sp);
+        uint16_t *shi = (uint16_t *)(ws + w.shi), *slo = (uint16_t *)(ws + w.slo);
+        if ((rc = mq_launch_gemm_bf16(xa, xa_lo, H, shared_w, H, T, 2 * Is, H, w.split_gu, P, st)))
+            return rc;
+        if ((rc = mq_launch_swiglu_partials(P, w.split_gu, T, Is, shi, slo, st))) return rc;
+        if ((rc = mq_launch_gemm_bf16(shi, slo, Is, shared_w + (size_t)2 * Is * H, Is, T, H, Is,
+                                      w.split_d, P, st)))
+            return rc;
+        ysh = (float *)(ws + w.ysh);
+        if ((rc = mq_launch_sum_partials(P, w.split_d, (int64_t)T * H, ysh, st))) return rc;
+    }
+    if ((rc = mark(MOE_Q2_PH_SHARED, 1))) return rc;
+    MQ_PHASE(MOE_Q2_PH_COMBINE, mq_launch_combine(y, inv, gate, ysh, T, H, K, accum ? 1 : 0, out, st));
+    if (!rms && ev) {
+        if ((rc = mark(MOE_Q2_PH_RMSNORM, 0)) || (rc = mark(MOE_Q2_PH_RMSNORM, 1))) return rc;
+    }
+    return MOE_Q2_OK;
+#undef MQ_PHASE
 }

@@ -126,3 +126,22 @@ int mq_launch_rmsnorm(const float *h, int T, int H, float eps, uint16_t *x, hipS
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
+
+// fp32 -> two bf16 planes: hi = bf16(x), lo = bf16(x - hi) (x = hi + lo to ~16 bits).
+__global__ void k_split_bf16(const float *__restrict__ x, int64_t n, uint16_t *__restrict__ hi,
+                             uint16_t *__restrict__ lo) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const float v = x[i];
+        const uint16_t h = mq_f32_to_bf16(v);
+        hi[i] = h;
+        lo[i] = mq_f32_to_bf16(v - mq_bf16_to_f32(h));
+    }
+}
+
+int mq_launch_split_bf16(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t st) {
+    const int grid = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(k_split_bf16, dim3(grid), dim3(256), 0, st, x, n, hi, lo);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}

@@ -122,3 +122,50 @@ extern "C" int moe_q2_quantize(const float *w, int64_t n_blocks, void *blocks_ou
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
+
+// Tiled expert layout: out block o of the gate/up part is (tile t, column b, slot s)
+// with o = (t * nbh + b) * 64 + s; slot s < 32 is gate row 32t + s, else up row
+// 32t + s - 32.  Down part: o = (t * nbi + b) * 64 + s, row 64t + s.
+__global__ void k_pack_expert(const uint32_t *__restrict__ gate, const uint32_t *__restrict__ up,
+                              const uint32_t *__restrict__ down, int H, int I,
+                              uint32_t *__restrict__ out) {
+    const int nbh = H / MQ_QK, nbi = I / MQ_QK;
+    const int64_t ngu = (int64_t)2 * I * nbh, ntot = ngu + (int64_t)H * nbi;
+    const int64_t ndw = ntot * MQ_BLOCK_DWORDS;
+    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < ndw;
+         w += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t o = w / MQ_BLOCK_DWORDS;
+        const int k = (int)(w - o * MQ_BLOCK_DWORDS);
+        const uint32_t *src;
+        int64_t sblk;
+        if (o < ngu) {
+            const int64_t s = o & 63, tb = o >> 6;
+            const int64_t t = tb / nbh, b = tb - t * nbh;
+            const int64_t row = 32 * t + (s & 31);
+            src = s < 32 ? gate : up;
+            sblk = row * nbh + b;
+        } else {
+            const int64_t od = o - ngu;
+            const int64_t s = od & 63, tb = od >> 6;
+            const int64_t t = tb / nbi, b = tb - t * nbi;
+            src = down;
+            sblk = (64 * t + s) * nbi + b;
+        }
+        out[w] = src[sblk * MQ_BLOCK_DWORDS + k];
+    }
+}
+
+extern "C" int moe_q2_pack_expert(const void *gate, const void *up, const void *down, int32_t hidden,
+                                  int32_t inter, void *out, void *stream) {
+    if (!gate || !up || !down || !out) return MOE_Q2_EINVAL;
+    if (hidden <= 0 || hidden % 256 || inter <= 0 || inter % 256) return MOE_Q2_EUNSUPPORTED;
+    if (((uintptr_t)gate | (uintptr_t)up | (uintptr_t)down | (uintptr_t)out) & 3) return MOE_Q2_EINVAL;
+    const int64_t ndw = (int64_t)3 * hidden / MQ_QK * inter * MQ_BLOCK_DWORDS;
+    int64_t grid = (ndw + 255) / 256;
+    if (grid > 65536) grid = 65536;
+    hipLaunchKernelGGL(k_pack_expert, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
+                       (const uint32_t *)gate, (const uint32_t *)up, (const uint32_t *)down, hidden,
+                       inter, (uint32_t *)out);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}

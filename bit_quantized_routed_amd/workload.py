@@ -12,7 +12,7 @@ from synth import workloads as W
 from synth.gen import normal_scale
 
 from . import (BF16, F32, PRE_RMSNORM, make_shape, quantize, synth_normal, workspace_size,
-               expert_bytes as _expert_bytes)
+               pack_expert)
 
 
 def _normal(wl, stream_id, n, sigma, dtype, out=None, start=0):
@@ -43,17 +43,17 @@ class DeviceLayer:
         ebytes = wl.expert_bytes
         self.experts = experts_out if experts_out is not None else \
             torch.empty(E * ebytes, dtype=torch.uint8, device="cuda")
-        own_tmp = tmp is None
-        if own_tmp:
+        if tmp is None:
             tmp = torch.empty(H * I, dtype=torch.float32, device="cuda")
         mat_bytes = ebytes // 3
+        rm = torch.empty(ebytes, dtype=torch.uint8, device="cuda")     # row-major staging
         for e in range(E):
             for m in range(3):
                 _normal(wl, W.expert_stream(layer, e, m), H * I, wl.expert_sigma, F32, out=tmp)
-                off = e * ebytes + m * mat_bytes
-                quantize(tmp, H * I // 256, self.experts[off:off + mat_bytes])
-        if own_tmp:
-            del tmp
+                quantize(tmp, H * I // 256, rm[m * mat_bytes:(m + 1) * mat_bytes])
+            pack_expert(rm[:mat_bytes], rm[mat_bytes:2 * mat_bytes], rm[2 * mat_bytes:], H, I,
+                        self.experts[e * ebytes:(e + 1) * ebytes])
+        del rm
 
     def shape(self, flags=0):
         wl = self.wl

@@ -22,6 +22,14 @@
  *   w_i = d * sc_j * q_i - dmin * m_j
  * Blocks run along each matrix's reduction dimension.
  *
+ * Routed expert layout (row tiles, so that a run of block columns of 64 rows is
+ * one contiguous span and streams from HBM with plain 16-byte loads):
+ *   gate/up: I/32 tiles; tile t = block columns b = 0..H/256-1 of 64 rows, slots
+ *            0..31 = gate rows 32t.., slots 32..63 = up rows 32t..  ([t][b][slot][84 B])
+ *   down:    H/64 tiles; tile t = block columns b = 0..I/256-1 of down rows 64t..64t+63
+ *   expert = gate/up tiles, then down tiles; experts back to back.
+ * moe_q2_pack_expert builds it from row-major matrices.
+ *
  * Conventions for every entry point:
  *   - pointers marked "device" must be device memory of the current HIP device;
  *     the caller owns every buffer; the library never allocates in moe_q2_forward
@@ -76,14 +84,33 @@ typedef struct {
 } moe_q2_shape;
 
 /* Optional device outputs of the routing and bucketing (each pointer nullable).
- * Slot s = t*K + k; bucket order sorts slots by (expert, token). */
+ * Slot s = t*K + k; bucket order sorts slots by (expert, token).
+ * events: nullable host array of 2 * MOE_Q2_N_PHASES hipEvent_t created by the caller;
+ * when set, events[2i] / events[2i+1] are recorded on the stream before / after
+ * phase i (phases that do not run record both events back to back). */
 typedef struct {
     int32_t *topk_idx;     /* [T, K]  selected experts, descending logit */
     float   *topk_w;       /* [T, K]  renormalised gate weights */
     int32_t *counts;       /* [E]     slots per expert */
     int32_t *offsets;      /* [E + 1] exclusive prefix sum of counts */
     int32_t *perm;         /* [T * K] slot at each bucket position */
+    void   **events;       /* [2 * MOE_Q2_N_PHASES] hipEvent_t, nullable */
 } moe_q2_trace;
+
+/* Phases of moe_q2_forward, in launch order (for moe_q2_trace.events). */
+enum {
+    MOE_Q2_PH_RMSNORM = 0,      /* RMSNorm of the residual stream -> bf16 */
+    MOE_Q2_PH_ROUTER,           /* router logits */
+    MOE_Q2_PH_TOPK,             /* softmax top-K */
+    MOE_Q2_PH_BUCKET,           /* histogram, scan, stable permutation, work units */
+    MOE_Q2_PH_PREP_X,           /* activation preparation for the routed experts */
+    MOE_Q2_PH_GATE_UP,          /* routed Q2 gate/up + SwiGLU */
+    MOE_Q2_PH_PREP_H,           /* intermediate preparation */
+    MOE_Q2_PH_DOWN,             /* routed Q2 down projection */
+    MOE_Q2_PH_SHARED,           /* shared expert (bf16 MFMA) */
+    MOE_Q2_PH_COMBINE,          /* weighted combine (+ residual) */
+    MOE_Q2_N_PHASES
+};
 
 /* Bytes of one 84-byte super-block. */
 size_t moe_q2_block_bytes(void);
@@ -99,8 +126,8 @@ int moe_q2_workspace_size(const moe_q2_shape *s, int32_t n_tokens, int32_t topk,
 /* One MoE layer for n_tokens tokens.
  *   x          device [T, H], act_dtype (fp32 under PRE_RMSNORM); 16-byte aligned
  *   router_w   device [E, H] fp32 row-major
- *   experts_q2 device, E experts back to back, each gate [I rows x H/256 blocks],
- *              up [I x H/256], down [H x I/256] of 84-byte blocks; 16-byte aligned
+ *   experts_q2 device, E experts back to back in the tiled layout above (each
+ *              3 * H * I / 256 blocks of 84 bytes); 16-byte aligned
  *   shared_w   device bf16 gate [Is, H], up [Is, H], down [H, Is] back to back;
  *              NULL iff shared_inter == 0
  *   topk       K, 1 <= K <= min(E, 16)
@@ -126,6 +153,12 @@ int moe_q2_forward(const void *x, const float *router_w, const void *experts_q2,
  * Setup helper, not part of the layer.  Blocks whose scale would overflow fp16 are
  * written with d = dmin = +inf. */
 int moe_q2_quantize(const float *w, int64_t n_blocks, void *blocks_out, void *stream);
+
+/* Pack one routed expert from row-major Q2 matrices (device): gate [I rows x H/256
+ * blocks], up [I x H/256], down [H x I/256] -> out (device, moe_q2_expert_bytes bytes)
+ * in the tiled layout above.  Setup helper, not part of the layer. */
+int moe_q2_pack_expert(const void *gate, const void *up, const void *down, int32_t hidden,
+                       int32_t inter, void *out, void *stream);
 
 /* Seeded synthetic inputs for tests and benchmarks (not part of the layer):
  * value j = float(S(start + j) - 262140) * scale, where S(i) is the sum of the eight

@@ -122,3 +122,38 @@ def encode_matrix(w):
     w = np.ascontiguousarray(w, dtype=np.float32)
     assert w.shape[-1] % QK == 0
     return encode_blocks(w.reshape(-1, QK))
+
+
+# ------------------------------------------------------------------ expert layout
+# A routed expert is stored as row tiles so that any run of consecutive block
+# columns of 64 rows is one contiguous span of bytes:
+#   gate/up: I/32 tiles; tile t holds block column b = 0..H/256-1 of 64 rows,
+#            slots 0..31 = gate rows 32t..32t+31, slots 32..63 = up rows 32t..32t+31
+#            (byte order [t][b][slot][84]);
+#   down:    H/64 tiles; tile t holds block column b = 0..I/256-1 of down rows
+#            64t..64t+63 ([t][b][slot][84]).
+# The expert is the gate/up tiles followed by the down tiles.
+
+
+def pack_expert(gate, up, down, hidden, inter):
+    """Row-major Q2 bytes of gate [I rows x H/256], up [I x H/256], down [H x I/256]
+    -> the expert's tiled bytes (1-D uint8)."""
+    nbh, nbi = hidden // QK, inter // QK
+    g = np.asarray(gate, np.uint8).reshape(inter // 32, 32, nbh, BLOCK_BYTES)
+    u = np.asarray(up, np.uint8).reshape(inter // 32, 32, nbh, BLOCK_BYTES)
+    gu = np.concatenate([g, u], axis=1)                  # [t, slot 64, b, 84]
+    gu = gu.transpose(0, 2, 1, 3)                         # [t, b, slot, 84]
+    d = np.asarray(down, np.uint8).reshape(hidden // 64, 64, nbi, BLOCK_BYTES).transpose(0, 2, 1, 3)
+    return np.concatenate([gu.reshape(-1), d.reshape(-1)])
+
+
+def unpack_expert(raw, hidden, inter):
+    """Inverse of pack_expert: tiled expert bytes -> row-major (gate, up, down) bytes."""
+    nbh, nbi = hidden // QK, inter // QK
+    raw = np.asarray(raw, np.uint8).reshape(-1)
+    ngu = 2 * inter * nbh * BLOCK_BYTES
+    gu = raw[:ngu].reshape(inter // 32, nbh, 64, BLOCK_BYTES).transpose(0, 2, 1, 3)
+    gate = gu[:, :32].reshape(inter * nbh, BLOCK_BYTES)
+    up = gu[:, 32:].reshape(inter * nbh, BLOCK_BYTES)
+    d = raw[ngu:].reshape(hidden // 64, nbi, 64, BLOCK_BYTES).transpose(0, 2, 1, 3)
+    return gate, up, d.reshape(hidden * nbi, BLOCK_BYTES)

@@ -30,12 +30,13 @@ class HostLayer:
                                    for m in range(3))
         return self._cache[e]
 
+    def packed_expert(self, e):
+        """Expert e in the library's tiled layout."""
+        return q2.pack_expert(*self.expert_bytes(e), self.wl.hidden, self.wl.inter)
+
     def all_expert_bytes(self):
-        """All experts back to back in the library's order (gate, up, down per expert)."""
-        parts = []
-        for e in range(self.wl.n_experts):
-            parts.extend(b.reshape(-1) for b in self.expert_bytes(e))
-        return np.concatenate(parts)
+        """All experts back to back in the library's tiled layout."""
+        return np.concatenate([self.packed_expert(e) for e in range(self.wl.n_experts)])
 
     def oracle_layer(self):
         return dict(router_w=self.router_w, router_b=self.router_b,

@@ -44,3 +44,34 @@ def test_tiny_layer():
     err = rel_err(out, ref, ~excluded)
     print("tiny", rep, "rel_err", err)
     assert err <= TOL_DECODE
+
+
+def _full_check(name, sample=None, flags=0):
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.WORKLOADS[name]
+    dl = dw.DeviceLayer(wl)
+    hl = host_layer(name)
+    x = dw.activations(wl)
+    out, tr = _run(mq, dl, x, wl.tokens, flags=flags)
+    xh, _ = W.activations(wl)
+    # routing for every token (router only), bucketing exactly
+    idx, g, logits, margin = moe.route(xh, hl.router_w, hl.router_b, wl.topk)
+    route = {"idx": idx, "g": g, "logits": logits, "margin": margin}
+    excluded, rep = check_routing(tr, route, wl.n_experts, wl.topk)
+    toks = np.arange(wl.tokens) if sample is None else np.asarray(sample)
+    toks = toks[~excluded[toks]]
+    ref, _ = moe.layer(xh[toks], hl.router_w, hl.router_b, hl.expert_bytes, hl.shared, wl.topk,
+                       wl.hidden, wl.inter)
+    err = rel_err(out[toks], ref)
+    print(name, rep, "tokens", toks.tolist(), "rel_err", err)
+    assert err <= TOL_DECODE
+    return err
+
+
+def test_decode1_layer():
+    _full_check("decode1")
+
+
+def test_decode32_zipf_layer_sampled():
+    _full_check("decode32_zipf", sample=[0, 17])

@@ -52,3 +52,16 @@ def test_device_quantizer_matches_oracle_on_workload(name, e, m):
     wl = W.WORKLOADS[name]
     w = W.expert_f32(wl, 0, e, m)
     assert np.array_equal(_dev_quant(mq, w), q2.encode_matrix(w))
+
+
+def test_device_pack_matches_oracle_layout():
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    from tests.oracle_inputs import host_layer
+    wl = W.WORKLOADS["decode1"]
+    hl = host_layer("decode1")
+    g, u, d = hl.expert_bytes(3)
+    dev = [torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda() for a in (g, u, d)]
+    out = torch.empty(wl.expert_bytes, dtype=torch.uint8, device="cuda")
+    mq.pack_expert(dev[0], dev[1], dev[2], wl.hidden, wl.inter, out)
+    assert np.array_equal(out.cpu().numpy(), hl.packed_expert(3))

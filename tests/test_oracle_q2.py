@@ -171,3 +171,24 @@ def test_quantizer_codes_and_nibbles_in_range():
 def test_overflowing_block_is_rejected():
     with pytest.raises(ValueError):
         q2.encode_blocks(np.full((1, 256), 1e7, dtype=np.float32))
+
+
+def test_pack_expert_positions_and_roundtrip():
+    H, I = 512, 256        # 2 blocks per gate/up row, 1 per down row
+    rng = np.random.default_rng(7)
+    g = rng.integers(0, 256, (I * 2, 84), dtype=np.uint8)
+    u = rng.integers(0, 256, (I * 2, 84), dtype=np.uint8)
+    d = rng.integers(0, 256, (H * 1, 84), dtype=np.uint8)
+    packed = q2.pack_expert(g, u, d, H, I)
+    assert packed.size == (g.size + u.size + d.size)
+    blk = lambda i: packed[84 * i: 84 * (i + 1)]
+    # gate row r, block b -> tile r // 32, column b, slot r % 32
+    for r, b in [(0, 0), (31, 1), (32, 0), (255, 1)]:
+        t, slot = r // 32, r % 32
+        assert np.array_equal(blk((t * 2 + b) * 64 + slot), g[r * 2 + b])
+        assert np.array_equal(blk((t * 2 + b) * 64 + 32 + slot), u[r * 2 + b])
+    off = 2 * I * 2          # blocks of the gate/up part
+    for r in [0, 63, 64, 511]:
+        assert np.array_equal(blk(off + (r // 64) * 64 + r % 64), d[r])
+    g2, u2, d2 = q2.unpack_expert(packed, H, I)
+    assert np.array_equal(g2, g) and np.array_equal(u2, u) and np.array_equal(d2, d)
