@@ -3,7 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#define FD_TCH 4   // slots per decode work unit
+#define FD_TCH 4        // slots per work unit of the vector-ALU decode kernel
+#define MMA_TCH 16      // slots per work unit of the matrix-core kernel
 
 int mq_launch_router(const void *x, int bf16, const float *wr, const float *bias, int T, int H,
                      int E, float *logits, hipStream_t st);
@@ -29,3 +30,10 @@ int mq_launch_gemm_bf16(const uint16_t *A, const uint16_t *Alo, int lda, const u
 int mq_launch_swiglu_partials(const float *P, int nsplit, int M, int Is, uint16_t *hi, uint16_t *lo,
                               hipStream_t st);
 int mq_launch_sum_partials(const float *P, int nsplit, int64_t MN, float *out, hipStream_t st);
+int mq_launch_prep_digits(const void *src, int src_bf16, int nrows, int len, int64_t src_ld,
+                          void *xdig, uint32_t *xsum, float *scale, hipStream_t st);
+int mq_launch_q2_mma(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
+                     int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
+                     int max_units, const int32_t *perm, int topk, const void *xdig,
+                     const uint32_t *xsum, const float *xscale, float *out, int n_cu,
+                     hipStream_t st);

@@ -61,6 +61,7 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     const size_t H = s->hidden, I = s->inter, E = s->n_experts;
     const size_t S = (size_t)T * K;
     size_t c = 0;
+    // work units: at most ceil(S / tch) + min(E, S) for either kernel's unit size
     w.max_units = (int)((S + FD_TCH - 1) / FD_TCH + (S < E ? S : E));
     w.logits = take(c, (size_t)T * E * 4);
     w.idx = take(c, S * 4);
@@ -72,7 +73,7 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     w.units_hdr = take(c, 16);
     w.units = take(c, (size_t)w.max_units * 16);
     w.xbf = take(c, (size_t)T * H * 2);
-    w.xq = take(c, (size_t)T * H * 2);
+    w.xq = take(c, (size_t)T * H * 2);          // fp16 pairs, or the two int8 digits
     w.xg = take(c, (size_t)T * (H / 16) * 8);
     w.xs = take(c, (size_t)T * 4);
     w.h = take(c, S * I * 4);
@@ -111,7 +112,7 @@ int device_cus() {
 }  // namespace
 
 static const int KNOWN_FLAGS = MOE_Q2_PATH_DECODE | MOE_Q2_PATH_PREFILL | MOE_Q2_PRE_RMSNORM |
-                               MOE_Q2_RESIDUAL_ADD;
+                               MOE_Q2_RESIDUAL_ADD | MOE_Q2_DECODE_VALU;
 
 static int check_common(const moe_q2_shape *s, int32_t n_tokens, int32_t topk) {
     if (!s) return MOE_Q2_EINVAL;
@@ -205,26 +206,39 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router(xin, xin_bf16, router_w, router_b, T, H, E, logits, st));
     MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk(logits, T, E, K, idx, gate, trace ? trace->topk_idx : nullptr,
                                             trace ? trace->topk_w : nullptr, st));
-    MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket(idx, T, K, E, FD_TCH, counts, offsets, perm, inv,
+    const bool valu = (s->flags & MOE_Q2_DECODE_VALU) != 0;
+    const int tch = valu ? FD_TCH : MMA_TCH;
+    MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket(idx, T, K, E, tch, counts, offsets, perm, inv,
                                                 units_hdr, units, st));
-    // routed experts, decode path
+    // routed experts
     const int ncu = device_cus();
     const int64_t ebytes = (int64_t)moe_q2_expert_bytes(s);
     const int64_t mat_gu = (int64_t)I * (H / MQ_QK) * MQ_BLOCK_BYTES;
+    float *h = (float *)(ws + w.h);
+    float *y = (float *)(ws + w.y);
     uint32_t *xq = (uint32_t *)(ws + w.xq);
     float2 *xg = (float2 *)(ws + w.xg);
     float *xs = (float *)(ws + w.xs);
-    MQ_PHASE(MOE_Q2_PH_PREP_X, mq_launch_prep(xin, xin_bf16, T, H, H, xq, xg, xs, st));
-    float *h = (float *)(ws + w.h);
-    MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_dec(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr,
-                                                 units, w.max_units, perm, K, xq, xg, xs, h, ncu, st));
     uint32_t *hq = (uint32_t *)(ws + w.hq);
     float2 *hg = (float2 *)(ws + w.hg);
     float *hsc = (float *)(ws + w.hs);
-    MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep(h, 0, T * K, I, I, hq, hg, hsc, st));
-    float *y = (float *)(ws + w.y);
-    MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_dec(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr,
-                                              units, w.max_units, perm, K, hq, hg, hsc, y, ncu, st));
+    if (valu) {
+        MQ_PHASE(MOE_Q2_PH_PREP_X, mq_launch_prep(xin, xin_bf16, T, H, H, xq, xg, xs, st));
+        MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_dec(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr,
+                                                     units, w.max_units, perm, K, xq, xg, xs, h, ncu, st));
+        MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep(h, 0, T * K, I, I, hq, hg, hsc, st));
+        MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_dec(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr,
+                                                  units, w.max_units, perm, K, hq, hg, hsc, y, ncu, st));
+    } else {
+        MQ_PHASE(MOE_Q2_PH_PREP_X, mq_launch_prep_digits(xin, xin_bf16, T, H, H, xq, (uint32_t *)xg, xs, st));
+        MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr, units,
+                                                     w.max_units, perm, K, xq, (const uint32_t *)xg, xs, h,
+                                                     ncu, st));
+        MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_digits(h, 0, T * K, I, I, hq, (uint32_t *)hg, hsc, st));
+        MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_mma(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr,
+                                                  units, w.max_units, perm, K, hq, (const uint32_t *)hg, hsc, y,
+                                                  ncu, st));
+    }
     // shared expert: full-precision bf16 weights on MFMA, weight 1
     float *ysh = nullptr;
     if ((rc = mark(MOE_Q2_PH_SHARED, 0))) return rc;

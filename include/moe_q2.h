@@ -69,7 +69,9 @@ enum {
     MOE_Q2_PATH_PREFILL = 2,   /* force the bf16 MFMA grouped-GEMM path */
     MOE_Q2_PRE_RMSNORM = 4,    /* x is the fp32 residual stream h; the layer input is
                                   bf16(h / sqrt(mean(h^2) + rms_eps)) (unit gain) */
-    MOE_Q2_RESIDUAL_ADD = 8    /* out += layer(...) instead of out = layer(...) */
+    MOE_Q2_RESIDUAL_ADD = 8,   /* out += layer(...) instead of out = layer(...) */
+    MOE_Q2_DECODE_VALU = 16    /* decode path: routed experts on the vector-ALU dot-product
+                                  kernel instead of the integer matrix-core kernel */
 };
 #define MOE_Q2_PREFILL_MIN_TOKENS 256
 

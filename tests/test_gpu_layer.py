@@ -27,7 +27,8 @@ def _run(mq, dl, x, T, flags=0, out=None):
     return out.cpu().numpy().astype(np.float64), trace_np(tr)
 
 
-def test_tiny_layer():
+@pytest.mark.parametrize("kernel", ["mma", "valu"])
+def test_tiny_layer(kernel):
     mq = need_gpu()
     from bit_quantized_routed_amd import workload as dw
     wl = W.WORKLOADS["tiny"]
@@ -35,7 +36,7 @@ def test_tiny_layer():
     hl = host_layer("tiny")
     assert np.array_equal(dl.experts.cpu().numpy(), hl.all_expert_bytes())
     x = dw.activations(wl)
-    out, tr = _run(mq, dl, x, wl.tokens)
+    out, tr = _run(mq, dl, x, wl.tokens, flags=mq.DECODE_VALU if kernel == "valu" else 0)
     xh, _ = W.activations(wl)
     assert np.array_equal(x.cpu().numpy(), xh)
     ref, route = moe.layer(xh, hl.router_w, hl.router_b, hl.expert_bytes, hl.shared, wl.topk,
@@ -69,9 +70,13 @@ def _full_check(name, sample=None, flags=0):
     return err
 
 
-def test_decode1_layer():
-    _full_check("decode1")
+@pytest.mark.parametrize("kernel", ["mma", "valu"])
+def test_decode1_layer(kernel):
+    import bit_quantized_routed_amd as mq
+    _full_check("decode1", flags=mq.DECODE_VALU if kernel == "valu" else 0)
 
 
-def test_decode32_zipf_layer_sampled():
-    _full_check("decode32_zipf", sample=[0, 17])
+@pytest.mark.parametrize("kernel", ["mma", "valu"])
+def test_decode32_zipf_layer_sampled(kernel):
+    import bit_quantized_routed_amd as mq
+    _full_check("decode32_zipf", sample=[0, 17], flags=mq.DECODE_VALU if kernel == "valu" else 0)
