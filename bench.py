@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode1")
-    ap.add_argument("--extra", default="decode32_zipf",
+    ap.add_argument("--extra", default="decode32_zipf,prefill2048,stack40_t64_zipf",
                     help="comma-separated extra workloads reported in the same line ('' for none)")
     ap.add_argument("--rotate", type=int, default=8, help="distinct layers cycled by decode steps")
     ap.add_argument("--cpu-baseline", type=int, default=1)

@@ -167,7 +167,6 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     if ((uintptr_t)workspace & 255) return MOE_Q2_EINVAL;
     const bool prefill = (s->flags & MOE_Q2_PATH_PREFILL) ||
                          (!(s->flags & MOE_Q2_PATH_DECODE) && T >= MOE_Q2_PREFILL_MIN_TOKENS);
-    if (prefill) return MOE_Q2_EUNSUPPORTED;
 
     hipStream_t st = (hipStream_t)stream;
     hipEvent_t *ev = trace && trace->events ? (hipEvent_t *)trace->events : nullptr;
@@ -206,7 +205,7 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router(xin, xin_bf16, router_w, router_b, T, H, E, logits, st));
     MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk(logits, T, E, K, idx, gate, trace ? trace->topk_idx : nullptr,
                                             trace ? trace->topk_w : nullptr, st));
-    const bool valu = (s->flags & MOE_Q2_DECODE_VALU) != 0;
+    const bool valu = !prefill && (s->flags & MOE_Q2_DECODE_VALU) != 0;
     const int tch = valu ? FD_TCH : MMA_TCH;
     MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket(idx, T, K, E, tch, counts, offsets, perm, inv,
                                                 units_hdr, units, st));

@@ -95,12 +95,15 @@ def expert_weights(raw_gate, raw_up, raw_down, hidden, inter):
             q2.decode_matrix(raw_down, hidden, inter))
 
 
-def layer(x, router_w, router_b, expert_bytes, shared, topk, hidden, inter):
+def layer(x, router_w, router_b, expert_bytes, shared, topk, hidden, inter, ffn_map=None):
     """One MoE layer in fp64.
 
     x            [T, H] activations (fp32 values, or bf16 values widened)
     expert_bytes callable e -> (gate, up, down) Q2 bytes of routed expert e
     shared       None, or (Wg [Is,H], Wu [Is,H], Wd [H,Is]) full-precision weights
+    ffn_map      optional evaluator of the routed FFNs: called with a list of
+                 (expert, token rows [n, H]) and returning the list of FFN outputs;
+                 by default each is ffn(rows, *expert_weights(*expert_bytes(e))).
     Returns out [T, H] fp64 and the routing dict."""
     x = _f64(x)
     idx, g, logits, margin = route(x, router_w, router_b, topk)
@@ -109,11 +112,15 @@ def layer(x, router_w, router_b, expert_bytes, shared, topk, hidden, inter):
         out += ffn(x, *shared)
     # Each (token, expert) pair is an independent FFN evaluation; evaluating all
     # tokens of one expert together only shares the decoded weights.
+    work = []
     for e in np.unique(idx):
-        rows = np.nonzero(idx == e)
-        toks, ks = rows
-        wg, wu, wd = expert_weights(*expert_bytes(int(e)), hidden, inter)
-        y = ffn(x[toks], wg, wu, wd)
+        toks, ks = np.nonzero(idx == e)
+        work.append((int(e), toks, ks))
+    if ffn_map is None:
+        ys = [ffn(x[toks], *expert_weights(*expert_bytes(e), hidden, inter)) for e, toks, _ in work]
+    else:
+        ys = ffn_map([(e, x[toks]) for e, toks, _ in work])
+    for (e, toks, ks), y in zip(work, ys):
         out[toks] += g[toks, ks][:, None] * y
     return out, {"idx": idx, "g": g, "logits": logits, "margin": margin}
 
@@ -142,14 +149,15 @@ def _round_bf16(y):
 def stack(h0, layers, topk, hidden, inter, eps):
     """Residual stack: h_{l+1} = h_l + layer_l(rmsnorm_bf16(h_l)).
 
-    layers: list of dicts with router_w, router_b, expert_bytes, shared.
+    layers: list of dicts with router_w, router_b, expert_bytes, shared and
+    optionally ffn_map (see layer()).
     Returns the final residual stream [T, H] fp64 and per-layer routings."""
     h = _f64(h0)
     routings = []
     for L in layers:
         x = rmsnorm_bf16(h, eps)
         y, r = layer(x, L["router_w"], L["router_b"], L["expert_bytes"], L["shared"],
-                     topk, hidden, inter)
+                     topk, hidden, inter, ffn_map=L.get("ffn_map"))
         h = h + y
         routings.append(r)
     return h, routings

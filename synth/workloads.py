@@ -91,6 +91,9 @@ WORKLOADS = {
                             1.0 / math.sqrt(H_DS)),
     "stack40_t64_zipf": Workload("stack40_t64_zipf", 4, 64, H_DS, E_DS, K_DS, I_DS, I_DS,
                                  "bf16", 0.02, zipf=True, layers=40, rmsnorm=True),
+    # small residual stack for exhaustive checks of RMSNorm + residual over many layers
+    "tiny_stack": Workload("tiny_stack", 5, 16, 256, 8, 2, 512, 256, "bf16", 0.05,
+                           layers=12, rmsnorm=True),
 }
 ORDER = ["tiny", "decode1", "decode32_zipf", "prefill2048", "stack40_t64_zipf"]
 
