@@ -169,7 +169,8 @@ class EventSet:
     """2 * len(PHASES) hipEvent_t handles (created with the HIP runtime directly) that
     moe_q2_forward records around its phases; elapsed() returns per-phase ms."""
 
-    def __init__(self):
+    def __init__(self, phases=None):
+        """phases: names of the phases to bracket (default: all)."""
         hip = ctypes.CDLL("libamdhip64.so")
         hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
@@ -179,7 +180,11 @@ class EventSet:
         self._hip = hip
         n = 2 * len(PHASES)
         self._arr = (ctypes.c_void_p * n)()
+        want = set(PHASES if phases is None else phases)
         for i in range(n):
+            if PHASES[i // 2] not in want:
+                self._arr[i] = None
+                continue
             h = ctypes.c_void_p()
             rc = hip.hipEventCreate(ctypes.byref(h))
             if rc:
@@ -192,9 +197,12 @@ class EventSet:
     def elapsed(self):
         """Per-phase durations in ms of the last recorded forward (synchronises)."""
         for i in range(len(self._arr)):
-            self._hip.hipEventSynchronize(self._arr[i])
+            if self._arr[i]:
+                self._hip.hipEventSynchronize(self._arr[i])
         out = {}
         for i, name in enumerate(PHASES):
+            if not self._arr[2 * i]:
+                continue
             ms = ctypes.c_float()
             rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self._arr[2 * i], self._arr[2 * i + 1])
             out[name] = ms.value if rc == 0 else float("nan")

@@ -9,10 +9,11 @@ __global__ void __launch_bounds__(256) k_combine(const float *__restrict__ y,
                                                  const float *__restrict__ gate,
                                                  const float *__restrict__ shared, int H, int K,
                                                  int accumulate, float *out) {
-    const int t = blockIdx.x;
+    const int t = blockIdx.y;
     const float4 *sh = shared ? (const float4 *)(shared + (int64_t)t * H) : nullptr;
     float4 *o = (float4 *)(out + (int64_t)t * H);
-    for (int c = threadIdx.x; c < H / 4; c += 256) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c < H / 4) {
         float4 v = sh ? sh[c] : make_float4(0.f, 0.f, 0.f, 0.f);
         for (int k = 0; k < K; ++k) {
             const float g = gate[t * K + k];
@@ -30,7 +31,8 @@ __global__ void __launch_bounds__(256) k_combine(const float *__restrict__ y,
 
 int mq_launch_combine(const float *y, const int32_t *inv, const float *gate, const float *shared,
                       int T, int H, int K, int accumulate, float *out, hipStream_t st) {
-    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, st, y, inv, gate, shared, H, K, accumulate, out);
+    hipLaunchKernelGGL(k_combine, dim3((H / 4 + 255) / 256, T), dim3(256), 0, st, y, inv, gate, shared, H,
+                       K, accumulate, out);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

@@ -333,3 +333,187 @@ int mq_launch_q2_mma(int swiglu, const void *experts, int64_t expert_bytes, int6
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
+
+// ------------------------------------------------------------------ prefill variant
+// Same arithmetic as k_q2_mma, shaped for many tokens per expert.  Work unit =
+// (expert, up to 16*MF slots); work item = (unit, super-tile of 4 consecutive
+// 64-row tiles = 256 matrix rows).  Work-group = 8 waves: wave w owns tile w/2 and
+// two 16-row fragments (SWIGLU: the gate fragment 16*(w%2).. and the up fragment
+// 32 + 16*(w%2)..  of the same rows; PLAIN: fragments 2*(w%2), 2*(w%2)+1), times
+// all MF token fragments.  Per block column, the 4 tiles' weights (21 KB) and the
+// unit's activation digits + group sums (576 B per token) are staged in LDS, so a
+// token's activations are read once per 256 rows; the next block column is
+// prefetched into registers during the compute.
+#define PF_TS 148   // LDS token stride in dwords: 576 B of data + 16 B pad (conflict-free reads)
+
+template <bool SWIGLU, int MF>
+__global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ experts,
+                                                   int64_t expert_bytes, int64_t mat_off, int rows,
+                                                   int kblocks, const int32_t *__restrict__ units_hdr,
+                                                   const int4 *__restrict__ units,
+                                                   const int32_t *__restrict__ perm, int topk,
+                                                   const mq_u32x4 *__restrict__ xdig,
+                                                   const uint32_t *__restrict__ xsum,
+                                                   const float *__restrict__ xscale,
+                                                   float *__restrict__ out) {
+    constexpr int NTOK = 16 * MF;
+    constexpr int NPB = (4 * 336 + 511) / 512;          // weight pieces per thread
+    constexpr int NPA = (NTOK * 36 + 511) / 512;        // activation pieces per thread
+    __shared__ __attribute__((aligned(16))) uint32_t sB[4 * 64 * MQ_BLOCK_DWORDS];
+    __shared__ __attribute__((aligned(16))) uint32_t sA[NTOK * PF_TS];
+    __shared__ int arow_s[NTOK];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, q4 = lane >> 4;
+    const int tw = wv >> 1, hw = wv & 1;
+    const int nslot0 = SWIGLU ? 16 * hw : 32 * hw;       // first fragment's slot
+    const int nslot1 = SWIGLU ? 32 + 16 * hw : 32 * hw + 16;
+    const int stiles = rows / (SWIGLU ? 32 : 64) / 4;
+    const int U = units_hdr[0];
+    const int G = kblocks * 16;
+    const int64_t tile_bytes = (int64_t)kblocks * 64 * MQ_BLOCK_BYTES;
+
+    for (int wu = blockIdx.x; wu < U * stiles; wu += gridDim.x) {
+        const int u = wu / stiles, st = wu - u * stiles;
+        const int4 un = units[u];
+        const int e = un.x, p0 = un.y, nt = un.z;
+        __syncthreads();
+        for (int i = tid; i < NTOK; i += 512)
+            arow_s[i] = i < nt ? (SWIGLU ? perm[p0 + i] / topk : p0 + i) : -1;
+        __syncthreads();
+        const uint8_t *tb = experts + (int64_t)e * expert_bytes + mat_off + (int64_t)(4 * st) * tile_bytes;
+        const int nA = nt * 36;
+        mq_u32x4 pb[NPB], pa[NPA];
+        auto load = [&](int b) {
+#pragma unroll
+            for (int n = 0; n < NPB; ++n) {
+                const int j = min(tid + 512 * n, 4 * 336 - 1);
+                const int tl = j / 336, w = j - tl * 336;
+                pb[n] = *(const mq_u32x4 *)(tb + (int64_t)tl * tile_bytes + (int64_t)b * 5376 + w * 16);
+            }
+#pragma unroll
+            for (int n = 0; n < NPA; ++n) {
+                const int j = min(tid + 512 * n, max(nA, 1) - 1);
+                const int i = j / 36, w = j - i * 36;
+                const int ar = max(arow_s[i], 0);
+                if (w < 32)
+                    pa[n] = xdig[((int64_t)ar * G + 16 * b) * 2 + w];
+                else
+                    pa[n] = *(const mq_u32x4 *)(xsum + ((int64_t)ar * kblocks + b) * 16 + (w - 32) * 4);
+            }
+        };
+        mq_f32x4 tot[MF][2];
+#pragma unroll
+        for (int m = 0; m < MF; ++m) { tot[m][0] = (mq_f32x4){0.f, 0.f, 0.f, 0.f}; tot[m][1] = tot[m][0]; }
+        load(0);
+        for (int b = 0; b < kblocks; ++b) {
+            __syncthreads();
+#pragma unroll
+            for (int n = 0; n < NPB; ++n) {
+                const int j = tid + 512 * n;
+                if (j < 4 * 336) *(mq_u32x4 *)(sB + 4 * j) = pb[n];
+            }
+#pragma unroll
+            for (int n = 0; n < NPA; ++n) {
+                const int j = tid + 512 * n;
+                if (j < nA) {
+                    const int i = j / 36, w = j - i * 36;
+                    *(mq_u32x4 *)(sA + i * PF_TS + 4 * w) = pa[n];
+                }
+            }
+            __syncthreads();
+            if (b + 1 < kblocks) load(b + 1);
+            const uint32_t *blk0 = sB + (tw * 64 + nslot0 + r16) * MQ_BLOCK_DWORDS;
+            const uint32_t *blk1 = sB + (tw * 64 + nslot1 + r16) * MQ_BLOCK_DWORDS;
+            mq_i32x4 hi[MF][2], lo[MF][2];
+#pragma unroll
+            for (int m = 0; m < MF; ++m)
+#pragma unroll
+                for (int f = 0; f < 2; ++f) { hi[m][f] = (mq_i32x4){0, 0, 0, 0}; lo[m][f] = hi[m][f]; }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int g = 4 * kk + q4;
+                const mq_i32x4 b0 = mq_codes_x_scale(blk0[4 + g], (blk0[kk] >> (8 * q4)) & 0xFu);
+                const mq_i32x4 b1 = mq_codes_x_scale(blk1[4 + g], (blk1[kk] >> (8 * q4)) & 0xFu);
+#pragma unroll
+                for (int m = 0; m < MF; ++m) {
+                    if (16 * m < nt) {
+                        const uint32_t *ap = sA + (16 * m + r16) * PF_TS + 8 * g;
+                        const mq_i32x4 ah = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)ap);
+                        const mq_i32x4 al = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(ap + 4));
+                        hi[m][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b0, hi[m][0], 0, 0, 0);
+                        lo[m][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b0, lo[m][0], 0, 0, 0);
+                        hi[m][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b1, hi[m][1], 0, 0, 0);
+                        lo[m][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b1, lo[m][1], 0, 0, 0);
+                    }
+                }
+            }
+            const mq_s16x4 bm0 = mq_mins_bf16(blk0[q4]), bm1 = mq_mins_bf16(blk1[q4]);
+            const uint32_t dd0 = blk0[20], dd1 = blk1[20];
+            const float d0 = mq_h2f((uint16_t)(dd0 & 0xFFFFu)), m0 = mq_h2f((uint16_t)(dd0 >> 16));
+            const float d1 = mq_h2f((uint16_t)(dd1 & 0xFFFFu)), m1 = mq_h2f((uint16_t)(dd1 >> 16));
+#pragma unroll
+            for (int m = 0; m < MF; ++m) {
+                if (16 * m < nt) {
+                    const uint32_t *xp = sA + (16 * m + r16) * PF_TS + 128;
+                    const mq_s16x4 xh = __builtin_bit_cast(mq_s16x4, *(const uint2 *)(xp + 2 * q4));
+                    const mq_s16x4 xl = __builtin_bit_cast(mq_s16x4, *(const uint2 *)(xp + 8 + 2 * q4));
+                    mq_f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+                    a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, bm0, a0, 0, 0, 0);
+                    a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, bm0, a0, 0, 0, 0);
+                    a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, bm1, a1, 0, 0, 0);
+                    a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, bm1, a1, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        tot[m][0][i] = fmaf(d0, (float)((hi[m][0][i] << 8) + lo[m][0][i]),
+                                            fmaf(-m0, a0[i], tot[m][0][i]));
+                        tot[m][1][i] = fmaf(d1, (float)((hi[m][1][i] << 8) + lo[m][1][i]),
+                                            fmaf(-m1, a1[i], tot[m][1][i]));
+                    }
+                }
+            }
+        }
+        // outputs: lane holds tokens 16m + 4*q4 + i of row slots (nslot0|nslot1) + r16
+        const int trow = (4 * st + tw) * (SWIGLU ? 32 : 64);
+#pragma unroll
+        for (int m = 0; m < MF; ++m) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * m + 4 * q4 + i;
+                if (t < nt) {
+                    const float s = xscale[arow_s[t]];
+                    float *o = out + (int64_t)(p0 + t) * rows + trow;
+                    if (SWIGLU) {
+                        const float g = tot[m][0][i] * s, up = tot[m][1][i] * s;
+                        o[16 * hw + r16] = g / (1.0f + expf(-g)) * up;
+                    } else {
+                        o[nslot0 + r16] = tot[m][0][i] * s;
+                        o[nslot1 + r16] = tot[m][1][i] * s;
+                    }
+                }
+            }
+        }
+    }
+}
+
+int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
+                        int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
+                        int max_units, const int32_t *perm, int topk, const void *xdig,
+                        const uint32_t *xsum, const float *xscale, float *out, int n_cu,
+                        hipStream_t st) {
+    const int stiles = rows / (swiglu ? 32 : 64) / 4;
+    int64_t want = (int64_t)max_units * stiles;
+    int64_t cap = (int64_t)n_cu * 2;
+    const int grid = (int)(want < cap ? want : cap);
+    if (grid <= 0) return MOE_Q2_OK;
+    if (swiglu)
+        hipLaunchKernelGGL((k_q2_mma_pf<true, PF_MF>), dim3(grid), dim3(512), 0, st,
+                           (const uint8_t *)experts, expert_bytes, mat_off, rows, kblocks, units_hdr,
+                           units, perm, topk, (const mq_u32x4 *)xdig, xsum, xscale, out);
+    else
+        hipLaunchKernelGGL((k_q2_mma_pf<false, PF_MF>), dim3(grid), dim3(512), 0, st,
+                           (const uint8_t *)experts, expert_bytes, mat_off, rows, kblocks, units_hdr,
+                           units, perm, topk, (const mq_u32x4 *)xdig, xsum, xscale, out);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}

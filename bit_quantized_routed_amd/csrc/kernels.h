@@ -4,12 +4,17 @@
 #include <stdint.h>
 
 #define FD_TCH 4        // slots per work unit of the vector-ALU decode kernel
-#define MMA_TCH 16      // slots per work unit of the matrix-core kernel
+#define MMA_TCH 16      // slots per work unit of the matrix-core decode kernel
+#define PF_MF 4         // token fragments per unit of the prefill kernel
+#define PF_TCH (16 * PF_MF)
 
 int mq_launch_router(const void *x, int bf16, const float *wr, const float *bias, int T, int H,
                      int E, float *logits, hipStream_t st);
-int mq_launch_topk(const float *logits, int T, int E, int K, int32_t *idx, float *gate,
-                   int32_t *trace_idx, float *trace_w, hipStream_t st);
+int mq_launch_topk(const float *logits, int nsplit, const float *bias, int T, int E, int K,
+                   int32_t *idx, float *gate, int32_t *trace_idx, float *trace_w, hipStream_t st);
+int mq_router_splits(int T, int H, int E);
+int mq_launch_router_mma(const uint16_t *x, const float *wr, int T, int H, int E, int nsplit,
+                         float *P, hipStream_t st);
 int mq_launch_bucket(const int32_t *idx, int T, int K, int E, int unit_tokens, int32_t *counts,
                      int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr,
                      int4 *units, hipStream_t st);
@@ -37,3 +42,8 @@ int mq_launch_q2_mma(int swiglu, const void *experts, int64_t expert_bytes, int6
                      int max_units, const int32_t *perm, int topk, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out, int n_cu,
                      hipStream_t st);
+int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
+                        int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
+                        int max_units, const int32_t *perm, int topk, const void *xdig,
+                        const uint32_t *xsum, const float *xscale, float *out, int n_cu,
+                        hipStream_t st);

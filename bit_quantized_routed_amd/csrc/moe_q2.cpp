@@ -47,7 +47,7 @@ struct Workspace {
     size_t total = 0;
     size_t logits, idx, gate, counts, offsets, perm, inv, units_hdr, units, xbf, xq, xg, xs, h,
         hq, hg, hs, y, xlo, sp, shi, slo, ysh;
-    int max_units = 0, split_gu = 1, split_d = 1;
+    int max_units = 0, split_gu = 1, split_d = 1, rsplit = 1;
 };
 
 size_t take(size_t &cursor, size_t bytes) {
@@ -63,7 +63,8 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     size_t c = 0;
     // work units: at most ceil(S / tch) + min(E, S) for either kernel's unit size
     w.max_units = (int)((S + FD_TCH - 1) / FD_TCH + (S < E ? S : E));
-    w.logits = take(c, (size_t)T * E * 4);
+    w.rsplit = mq_router_splits(T, (int)H, (int)E);
+    w.logits = take(c, (size_t)w.rsplit * T * E * 4);
     w.idx = take(c, S * 4);
     w.gate = take(c, S * 4);
     w.counts = take(c, E * 4);
@@ -171,7 +172,7 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     hipStream_t st = (hipStream_t)stream;
     hipEvent_t *ev = trace && trace->events ? (hipEvent_t *)trace->events : nullptr;
     auto mark = [&](int phase, int end) -> int {
-        if (!ev) return MOE_Q2_OK;
+        if (!ev || !ev[2 * phase + end]) return MOE_Q2_OK;
         const hipError_t e = hipEventRecord(ev[2 * phase + end], st);
         return e == hipSuccess ? MOE_Q2_OK : mq_fail_hip(e);
     };
@@ -202,11 +203,20 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         xin_bf16 = 1;
     }
     // routing
-    MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router(xin, xin_bf16, router_w, router_b, T, H, E, logits, st));
-    MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk(logits, T, E, K, idx, gate, trace ? trace->topk_idx : nullptr,
+    // bf16 activations: MFMA router (split-K partials); fp32 activations: vector-ALU router
+    int nsplit = 1;
+    if (xin_bf16) {
+        nsplit = w.rsplit;
+        MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router_mma((const uint16_t *)xin, router_w, T, H, E, nsplit,
+                                                        logits, st));
+    } else {
+        MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router(xin, 0, router_w, nullptr, T, H, E, logits, st));
+    }
+    MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk(logits, nsplit, router_b, T, E, K, idx, gate,
+                                            trace ? trace->topk_idx : nullptr,
                                             trace ? trace->topk_w : nullptr, st));
     const bool valu = !prefill && (s->flags & MOE_Q2_DECODE_VALU) != 0;
-    const int tch = valu ? FD_TCH : MMA_TCH;
+    const int tch = valu ? FD_TCH : (prefill ? PF_TCH : MMA_TCH);
     MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket(idx, T, K, E, tch, counts, offsets, perm, inv,
                                                 units_hdr, units, st));
     // routed experts
@@ -228,6 +238,15 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep(h, 0, T * K, I, I, hq, hg, hsc, st));
         MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_dec(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr,
                                                   units, w.max_units, perm, K, hq, hg, hsc, y, ncu, st));
+    } else if (prefill) {
+        MQ_PHASE(MOE_Q2_PH_PREP_X, mq_launch_prep_digits(xin, xin_bf16, T, H, H, xq, (uint32_t *)xg, xs, st));
+        MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma_pf(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr,
+                                                        units, w.max_units, perm, K, xq, (const uint32_t *)xg,
+                                                        xs, h, ncu, st));
+        MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_digits(h, 0, T * K, I, I, hq, (uint32_t *)hg, hsc, st));
+        MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_mma_pf(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK,
+                                                     units_hdr, units, w.max_units, perm, K, hq,
+                                                     (const uint32_t *)hg, hsc, y, ncu, st));
     } else {
         MQ_PHASE(MOE_Q2_PH_PREP_X, mq_launch_prep_digits(xin, xin_bf16, T, H, H, xq, (uint32_t *)xg, xs, st));
         MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr, units,

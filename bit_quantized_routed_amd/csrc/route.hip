@@ -50,27 +50,141 @@ __global__ void __launch_bounds__(256) k_router_logits(const void *__restrict__ 
     }
 }
 
+// ---------------------------------------------------------------- logits on MFMA
+// bf16 activations x fp32 router weights.  Each weight is split exactly into three
+// bf16 terms w = hi + mid + lo (8 + 8 + 8 significant bits, round-to-nearest at
+// each step), so every product with a bf16 activation is exact in fp32 and the
+// MFMA accumulates in fp32 (v_mfma_f32_16x16x32_bf16, three per fragment pair).
+// Tile: 64 tokens x 64 experts per work-group, wave w owns experts 16w..16w+15
+// and the 4 token fragments; fragments are loaded straight from global memory.
+// Split-K partial logits go to P[split][T][E] (summed in order by top-K).
+typedef __bf16 mq_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short mq_s16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void mq_split3(const float (&w)[8], mq_s16x8 &hi, mq_s16x8 &mid, mq_s16x8 &lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint16_t h = mq_f32_to_bf16(w[i]);
+        const float r1 = w[i] - mq_bf16_to_f32(h);
+        const uint16_t m = mq_f32_to_bf16(r1);
+        const float r2 = r1 - mq_bf16_to_f32(m);
+        hi[i] = (short)h;
+        mid[i] = (short)m;
+        lo[i] = (short)mq_f32_to_bf16(r2);
+    }
+}
+
+__global__ void __launch_bounds__(256) k_router_mma(const uint16_t *__restrict__ x,
+                                                    const float *__restrict__ wr, int T, int H, int E,
+                                                    int k_per_split, float *__restrict__ P) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int e0 = blockIdx.x * 64 + wv * 16, t0 = blockIdx.y * 64;
+    const int split = blockIdx.z;
+    const int k0 = split * k_per_split, k1 = min(H, k0 + k_per_split);
+    const int r16 = lane & 15, q = lane >> 4;
+    const int e = e0 + r16;
+    mq_f32x4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = (mq_f32x4){0.f, 0.f, 0.f, 0.f};
+    const float *wrow = wr + (int64_t)min(e, E - 1) * H;
+    for (int k = k0; k < k1; k += 32) {
+        const int kk = k + 8 * q;
+        float w[8];
+        const float4 w0 = *(const float4 *)(wrow + kk), w1 = *(const float4 *)(wrow + kk + 4);
+        w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+        w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+        if (e >= E) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[i] = 0.0f;
+        }
+        mq_s16x8 bh, bm, bl;
+        mq_split3(w, bh, bm, bl);
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+            const int t = t0 + 16 * mf + r16;
+            mq_u32x4 a = {0u, 0u, 0u, 0u};
+            if (t < T) a = *(const mq_u32x4 *)(x + (int64_t)t * H + kk);
+            const mq_bf16x8 av = __builtin_bit_cast(mq_bf16x8, a);
+            acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(mq_bf16x8, bh), acc[mf], 0, 0, 0);
+            acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(mq_bf16x8, bm), acc[mf], 0, 0, 0);
+            acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(mq_bf16x8, bl), acc[mf], 0, 0, 0);
+        }
+    }
+    float *Ps = P + (int64_t)split * T * E;
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 16 * mf + 4 * q + i;
+            if (t < T && e < E) Ps[(int64_t)t * E + e] = acc[mf][i];
+        }
+}
+
+int mq_router_splits(int T, int H, int E) {
+    const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
+    int s = (512 + tiles - 1) / tiles;
+    const int smax = H / 128;
+    if (s > smax) s = smax;
+    return s < 1 ? 1 : s;
+}
+
+int mq_launch_router_mma(const uint16_t *x, const float *wr, int T, int H, int E, int nsplit,
+                         float *P, hipStream_t st) {
+    int kps = (H + nsplit - 1) / nsplit;
+    kps = (kps + 31) / 32 * 32;
+    dim3 grid((E + 63) / 64, (T + 63) / 64, nsplit);
+    hipLaunchKernelGGL(k_router_mma, grid, dim3(256), 0, st, x, wr, T, H, E, kps, P);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}
+
 // ---------------------------------------------------------------- top-K
 // One wave per token.  K rounds of a wave arg-max over the unselected logits
 // (ties: lower expert index); gates are the softmax over the selected logits,
 // which equals the full softmax renormalised over the selection.
-__global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, int T, int E, int K,
+// One work-group per token.  Every thread adds the split-K partial logits of up to
+// two experts (fixed order) and the bias; wave 0 then runs K rounds of a wave
+// arg-max over the unselected logits (ties: lower expert index).  Gates are the
+// softmax over the selected logits, which equals the full softmax renormalised
+// over the selection.
+__global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, int nsplit,
+                                              const float *__restrict__ bias, int T, int E, int K,
                                               int32_t *__restrict__ idx, float *__restrict__ gate,
                                               int32_t *__restrict__ trace_idx,
                                               float *__restrict__ trace_w) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
+    __shared__ float lg[512];
+    const int t = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const float *p = logits + (int64_t)t * E + e;
+        const int64_t stride = (int64_t)T * E;
+        float a = 0.0f;
+        int sp = 0;
+        for (; sp + 8 <= nsplit; sp += 8) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = p[(sp + i) * stride];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a += v[i];
+        }
+        for (; sp < nsplit; ++sp) a += p[sp * stride];
+        lg[e] = a + (bias ? bias[e] : 0.0f);
+    }
+    __syncthreads();
+    if (threadIdx.x >= 64) return;
+    const int lane = threadIdx.x;
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? logits[(int64_t)t * E + e] : -INFINITY;
+        v[i] = e < E ? lg[e] : -INFINITY;
     }
     uint32_t taken = 0;
     float sel_v[16];
     int sel_e[16];
-    for (int k = 0; k < K; ++k) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if (k >= K) break;
         float bv = -INFINITY;
         int be = 0x7FFFFFFF;
 #pragma unroll
@@ -91,17 +205,25 @@ __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, 
         sel_v[k] = bv;
         sel_e[k] = be;
     }
-    if (lane == 0) {
+    if (lane < K) {
         const float mx = sel_v[0];
-        float z = 0.0f, p[16];
-        for (int k = 0; k < K; ++k) { p[k] = expf(sel_v[k] - mx); z += p[k]; }
-        for (int k = 0; k < K; ++k) {
-            const float g = p[k] / z;
-            idx[t * K + k] = sel_e[k];
-            gate[t * K + k] = g;
-            if (trace_idx) trace_idx[t * K + k] = sel_e[k];
-            if (trace_w) trace_w[t * K + k] = g;
+        float z = 0.0f, mine = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (k >= K) break;
+            const float pk = expf(sel_v[k] - mx);
+            z += pk;
+            if (k == lane) mine = pk;
         }
+        int me = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (k == lane) me = sel_e[k];
+        const float g = mine / z;
+        idx[t * K + lane] = me;
+        gate[t * K + lane] = g;
+        if (trace_idx) trace_idx[t * K + lane] = me;
+        if (trace_w) trace_w[t * K + lane] = g;
     }
 }
 
@@ -216,10 +338,10 @@ int mq_launch_router(const void *x, int bf16, const float *wr, const float *bias
     return MOE_Q2_OK;
 }
 
-int mq_launch_topk(const float *logits, int T, int E, int K, int32_t *idx, float *gate,
-                   int32_t *trace_idx, float *trace_w, hipStream_t st) {
-    hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, K, idx, gate,
-                       trace_idx, trace_w);
+int mq_launch_topk(const float *logits, int nsplit, const float *bias, int T, int E, int K,
+                   int32_t *idx, float *gate, int32_t *trace_idx, float *trace_w, hipStream_t st) {
+    hipLaunchKernelGGL(k_topk, dim3(T), dim3(256), 0, st, logits, nsplit, bias, T, E, K,
+                       idx, gate, trace_idx, trace_w);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

@@ -88,8 +88,8 @@ typedef struct {
 /* Optional device outputs of the routing and bucketing (each pointer nullable).
  * Slot s = t*K + k; bucket order sorts slots by (expert, token).
  * events: nullable host array of 2 * MOE_Q2_N_PHASES hipEvent_t created by the caller;
- * when set, events[2i] / events[2i+1] are recorded on the stream before / after
- * phase i (phases that do not run record both events back to back). */
+ * when set, each non-null events[2i] / events[2i+1] is recorded on the stream before /
+ * after phase i (phases that do not run record both events back to back). */
 typedef struct {
     int32_t *topk_idx;     /* [T, K]  selected experts, descending logit */
     float   *topk_w;       /* [T, K]  renormalised gate weights */

@@ -80,3 +80,17 @@ def test_decode1_layer(kernel):
 def test_decode32_zipf_layer_sampled(kernel):
     import bit_quantized_routed_amd as mq
     _full_check("decode32_zipf", sample=[0, 17], flags=mq.DECODE_VALU if kernel == "valu" else 0)
+
+
+def test_decode32_forced_prefill_kernels():
+    """The prefill kernels on a decode-sized batch (PATH_PREFILL), all 32 tokens sampled
+    through the oracle: covers partial token fragments and buckets of 1..18 slots."""
+    import bit_quantized_routed_amd as mq
+    _full_check("decode32_zipf", sample=[1, 9, 30], flags=mq.PATH_PREFILL)
+
+
+def test_tiny_forced_prefill_kernels():
+    """Prefill kernels at the tiny shape: 1-block reduction rows (H = 256) and a
+    2-block down projection, fewer rows than one 256-row super-tile."""
+    import bit_quantized_routed_amd as mq
+    _full_check("tiny", flags=mq.PATH_PREFILL)
