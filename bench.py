@@ -39,6 +39,8 @@ def parse():
                     help="comma-separated extra workloads reported in the same line ('' for none)")
     ap.add_argument("--rotate", type=int, default=8, help="distinct layers cycled by decode steps")
     ap.add_argument("--cpu-baseline", type=int, default=1)
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -127,8 +129,8 @@ def run_workload(name, steps, warmup, rotate):
                 phase[p].append(v)
             e.close()
     phase_ms = {p: float(np.mean(v)) for p, v in phase.items() if v}
-    routed = ("gate_up", "down", "shared")
-    dom = max(routed, key=lambda p: phase_ms.get(p, 0.0))
+    # roofline kernel: the larger of the two routed-expert kernels (single launches)
+    dom = max(("gate_up", "down"), key=lambda p: phase_ms.get(p, 0.0))
     # timed region: only the dominant kernel's phase is bracketed by events
     evsets = [[mq.EventSet(phases=[dom]) for _ in range(n_ev)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -181,7 +183,7 @@ def run_workload(name, steps, warmup, rotate):
                                 T * 3 * wl.shared_inter * wl.hidden * 2) / (ms_per_step * 1e-3) / 1e12
     elif kbytes is not None and dom_avg > 0:
         ach = kbytes / (dom_avg * 1e-3) / 1e9
-        tr = traffic_record(dom)
+        tr = traffic_record("%s/%s" % (name, dom))
         res["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                            "traffic": None if tr is None else tr.get("bytes_per_launch"),
@@ -232,6 +234,14 @@ def main():
     extras = {}
     for name in [n for n in args.extra.split(",") if n and n != args.workload]:
         extras[name] = run_workload(name, args.steps, args.warmup, args.rotate)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cpu = cpu_baseline(args.workload) if args.cpu_baseline else None
     from synth import workloads as W
     wl = W.WORKLOADS[args.workload]
