@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_q2.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
-PATH_AUTO, PATH_DECODE, PATH_PREFILL, PRE_RMSNORM, RESIDUAL_ADD, DECODE_VALU = 0, 1, 2, 4, 8, 16
+PATH_AUTO, PATH_DECODE, PATH_PREFILL, PRE_RMSNORM, RESIDUAL_ADD, DECODE_VALU, SERIAL = 0, 1, 2, 4, 8, 16, 32
 PREFILL_MIN_TOKENS = 256
 BLOCK_BYTES = 84
 

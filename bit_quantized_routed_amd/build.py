@@ -12,6 +12,9 @@ SOURCES = ["moe_q2.cpp", "setup.hip", "route.hip", "prep.hip", "ffn_dec.hip", "f
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-munsafe-fp-atomics", "-Wno-unused-command-line-argument"]
+# Matrix-core kernels keep their accumulators in ordinary VGPRs (no copies out of
+# the accumulation registers in the per-block fold).
+FILE_FLAGS = {"ffn_mma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose=False, jobs=8):
@@ -23,7 +26,7 @@ def build(verbose=False, jobs=8):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"]
-        cmd = ["hipcc", *lang, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ["hipcc", *lang, *DEVICE_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd))
         procs.append(subprocess.Popen(cmd))

@@ -37,10 +37,12 @@ int mq_launch_swiglu_partials(const float *P, int nsplit, int M, int Is, uint16_
 int mq_launch_sum_partials(const float *P, int nsplit, int64_t MN, float *out, hipStream_t st);
 int mq_launch_prep_digits(const void *src, int src_bf16, int nrows, int len, int64_t src_ld,
                           void *xdig, uint32_t *xsum, float *scale, hipStream_t st);
+// zrow: index of the all-zero activation row (written by mq_launch_prep_digits after
+// the nrows real rows); trash_row: an output row that absorbs padding-token writes.
 int mq_launch_q2_mma(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
                      int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
-                     int max_units, const int32_t *perm, int topk, const void *xdig,
-                     const uint32_t *xsum, const float *xscale, float *out, int n_cu,
+                     int max_units, const int32_t *perm, int topk, int zrow, int trash_row,
+                     const void *xdig, const uint32_t *xsum, const float *xscale, float *out, int n_cu,
                      hipStream_t st);
 int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
                         int rows, int kblocks, const int32_t *units_hdr, const int4 *units,

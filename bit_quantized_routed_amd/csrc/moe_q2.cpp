@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -73,15 +75,17 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     w.inv = take(c, S * 4);
     w.units_hdr = take(c, 16);
     w.units = take(c, (size_t)w.max_units * 16);
+    // activation buffers hold one extra row: the all-zero row that padding tokens
+    // of the decode kernels read; h and y one extra row that absorbs their writes
     w.xbf = take(c, (size_t)T * H * 2);
-    w.xq = take(c, (size_t)T * H * 2);          // fp16 pairs, or the two int8 digits
-    w.xg = take(c, (size_t)T * (H / 16) * 8);
-    w.xs = take(c, (size_t)T * 4);
-    w.h = take(c, S * I * 4);
-    w.hq = take(c, S * I * 2);
-    w.hg = take(c, S * (I / 16) * 8);
-    w.hs = take(c, S * 4);
-    w.y = take(c, S * H * 4);
+    w.xq = take(c, (size_t)(T + 1) * H * 2);    // fp16 pairs, or the two int8 digits
+    w.xg = take(c, (size_t)(T + 1) * (H / 16) * 8);
+    w.xs = take(c, (size_t)(T + 1) * 4);
+    w.h = take(c, (S + 1) * I * 4);
+    w.hq = take(c, (S + 1) * I * 2);
+    w.hg = take(c, (S + 1) * (I / 16) * 8);
+    w.hs = take(c, (S + 1) * 4);
+    w.y = take(c, (S + 1) * H * 4);
     const size_t Is = s->shared_inter;
     if (Is) {
         // split-K policy fixed at 256 compute units so the size does not depend on the device
@@ -113,7 +117,50 @@ int device_cus() {
 }  // namespace
 
 static const int KNOWN_FLAGS = MOE_Q2_PATH_DECODE | MOE_Q2_PATH_PREFILL | MOE_Q2_PRE_RMSNORM |
-                               MOE_Q2_RESIDUAL_ADD | MOE_Q2_DECODE_VALU;
+                               MOE_Q2_RESIDUAL_ADD | MOE_Q2_DECODE_VALU | MOE_Q2_SERIAL;
+
+namespace {
+// The concurrent branch (activation preparation + shared expert): one internal
+// stream and fork / prep / join events per device, created on first use and kept
+// for the process.  `mu`
+// makes the enqueue of one forward call atomic with respect to other host
+// threads, so each join waited on is the one its own call recorded.
+struct SideBranch {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, prep = nullptr, join = nullptr;
+    bool ready = false;
+    std::mutex mu;
+};
+SideBranch g_side[64];
+std::mutex g_side_init;
+
+SideBranch *side_branch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    SideBranch &b = g_side[dev];
+    std::lock_guard<std::mutex> g(g_side_init);
+    if (!b.ready) {
+        if (!b.s && hipStreamCreateWithFlags(&b.s, hipStreamNonBlocking) != hipSuccess) {
+            b.s = nullptr;
+            return nullptr;
+        }
+        if (!b.fork && hipEventCreateWithFlags(&b.fork, hipEventDisableTiming) != hipSuccess) {
+            b.fork = nullptr;
+            return nullptr;
+        }
+        if (!b.prep && hipEventCreateWithFlags(&b.prep, hipEventDisableTiming) != hipSuccess) {
+            b.prep = nullptr;
+            return nullptr;
+        }
+        if (!b.join && hipEventCreateWithFlags(&b.join, hipEventDisableTiming) != hipSuccess) {
+            b.join = nullptr;
+            return nullptr;
+        }
+        b.ready = true;
+    }
+    return &b;
+}
+}  // namespace
 
 static int check_common(const moe_q2_shape *s, int32_t n_tokens, int32_t topk) {
     if (!s) return MOE_Q2_EINVAL;
@@ -171,11 +218,12 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
 
     hipStream_t st = (hipStream_t)stream;
     hipEvent_t *ev = trace && trace->events ? (hipEvent_t *)trace->events : nullptr;
-    auto mark = [&](int phase, int end) -> int {
+    auto mark_on = [&](int phase, int end, hipStream_t on) -> int {
         if (!ev || !ev[2 * phase + end]) return MOE_Q2_OK;
-        const hipError_t e = hipEventRecord(ev[2 * phase + end], st);
+        const hipError_t e = hipEventRecord(ev[2 * phase + end], on);
         return e == hipSuccess ? MOE_Q2_OK : mq_fail_hip(e);
     };
+    auto mark = [&](int phase, int end) -> int { return mark_on(phase, end, st); };
 #define MQ_PHASE(ph, call)                                                                 \
     do {                                                                                   \
         if ((rc = mark(ph, 0))) return rc;                                                 \
@@ -202,6 +250,67 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         xin = xbf;
         xin_bf16 = 1;
     }
+    // Work that depends on the layer input only -- the routed experts' activation
+    // preparation and the shared expert (full-precision bf16 weights on MFMA,
+    // weight 1) -- runs as a branch concurrent with the routing (forked here; the
+    // routed experts wait for the preparation, the combine for the whole branch)
+    // unless MOE_Q2_SERIAL is set.
+    const bool valu = !prefill && (s->flags & MOE_Q2_DECODE_VALU) != 0;
+    float *ysh = nullptr;
+    SideBranch *side = nullptr;
+    std::unique_lock<std::mutex> side_lock;
+    hipStream_t sst = st;
+    if (!(s->flags & MOE_Q2_SERIAL)) {
+        side = side_branch();
+        if (side) {
+            side_lock = std::unique_lock<std::mutex>(side->mu);
+            hipError_t e = hipEventRecord(side->fork, st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+            if (e != hipSuccess) return mq_fail_hip(e);
+            sst = side->s;
+        }
+    }
+    uint32_t *xq = (uint32_t *)(ws + w.xq);
+    float2 *xg = (float2 *)(ws + w.xg);
+    float *xs = (float *)(ws + w.xs);
+    if ((rc = mark_on(MOE_Q2_PH_PREP_X, 0, sst))) return rc;
+    if (valu)
+        rc = mq_launch_prep(xin, xin_bf16, T, H, H, xq, xg, xs, sst);
+    else
+        rc = mq_launch_prep_digits(xin, xin_bf16, T, H, H, xq, (uint32_t *)xg, xs, sst);
+    if (rc) return rc;
+    if ((rc = mark_on(MOE_Q2_PH_PREP_X, 1, sst))) return rc;
+    if (side) {
+        const hipError_t e = hipEventRecord(side->prep, sst);
+        if (e != hipSuccess) return mq_fail_hip(e);
+    }
+    if ((rc = mark_on(MOE_Q2_PH_SHARED, 0, sst))) return rc;
+    if (s->shared_inter > 0) {
+        const int Is = s->shared_inter;
+        const uint16_t *xa = (const uint16_t *)xin, *xa_lo = nullptr;
+        if (!xin_bf16) {
+            uint16_t *hi = (uint16_t *)(ws + w.xbf), *lo = (uint16_t *)(ws + w.xlo);
+            if ((rc = mq_launch_split_bf16((const float *)xin, (int64_t)T * H, hi, lo, sst))) return rc;
+            xa = hi;
+            xa_lo = lo;
+        }
+        float *P = (float *)(ws + w.sp);
+        uint16_t *shi = (uint16_t *)(ws + w.shi), *slo = (uint16_t *)(ws + w.slo);
+        if ((rc = mq_launch_gemm_bf16(xa, xa_lo, H, shared_w, H, T, 2 * Is, H, w.split_gu, P, sst)))
+            return rc;
+        if ((rc = mq_launch_swiglu_partials(P, w.split_gu, T, Is, shi, slo, sst))) return rc;
+        if ((rc = mq_launch_gemm_bf16(shi, slo, Is, shared_w + (size_t)2 * Is * H, Is, T, H, Is,
+                                      w.split_d, P, sst)))
+            return rc;
+        ysh = (float *)(ws + w.ysh);
+        if ((rc = mq_launch_sum_partials(P, w.split_d, (int64_t)T * H, ysh, sst))) return rc;
+    }
+    if ((rc = mark_on(MOE_Q2_PH_SHARED, 1, sst))) return rc;
+    if (side) {
+        const hipError_t e = hipEventRecord(side->join, sst);
+        if (e != hipSuccess) return mq_fail_hip(e);
+    }
+
     // routing
     // bf16 activations: MFMA router (split-K partials); fp32 activations: vector-ALU router
     int nsplit = 1;
@@ -215,31 +324,29 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk(logits, nsplit, router_b, T, E, K, idx, gate,
                                             trace ? trace->topk_idx : nullptr,
                                             trace ? trace->topk_w : nullptr, st));
-    const bool valu = !prefill && (s->flags & MOE_Q2_DECODE_VALU) != 0;
     const int tch = valu ? FD_TCH : (prefill ? PF_TCH : MMA_TCH);
     MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket(idx, T, K, E, tch, counts, offsets, perm, inv,
                                                 units_hdr, units, st));
+    if (side) {
+        const hipError_t e = hipStreamWaitEvent(st, side->prep, 0);
+        if (e != hipSuccess) return mq_fail_hip(e);
+    }
     // routed experts
     const int ncu = device_cus();
     const int64_t ebytes = (int64_t)moe_q2_expert_bytes(s);
     const int64_t mat_gu = (int64_t)I * (H / MQ_QK) * MQ_BLOCK_BYTES;
     float *h = (float *)(ws + w.h);
     float *y = (float *)(ws + w.y);
-    uint32_t *xq = (uint32_t *)(ws + w.xq);
-    float2 *xg = (float2 *)(ws + w.xg);
-    float *xs = (float *)(ws + w.xs);
     uint32_t *hq = (uint32_t *)(ws + w.hq);
     float2 *hg = (float2 *)(ws + w.hg);
     float *hsc = (float *)(ws + w.hs);
     if (valu) {
-        MQ_PHASE(MOE_Q2_PH_PREP_X, mq_launch_prep(xin, xin_bf16, T, H, H, xq, xg, xs, st));
         MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_dec(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr,
                                                      units, w.max_units, perm, K, xq, xg, xs, h, ncu, st));
         MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep(h, 0, T * K, I, I, hq, hg, hsc, st));
         MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_dec(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr,
                                                   units, w.max_units, perm, K, hq, hg, hsc, y, ncu, st));
     } else if (prefill) {
-        MQ_PHASE(MOE_Q2_PH_PREP_X, mq_launch_prep_digits(xin, xin_bf16, T, H, H, xq, (uint32_t *)xg, xs, st));
         MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma_pf(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr,
                                                         units, w.max_units, perm, K, xq, (const uint32_t *)xg,
                                                         xs, h, ncu, st));
@@ -248,39 +355,18 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
                                                      units_hdr, units, w.max_units, perm, K, hq,
                                                      (const uint32_t *)hg, hsc, y, ncu, st));
     } else {
-        MQ_PHASE(MOE_Q2_PH_PREP_X, mq_launch_prep_digits(xin, xin_bf16, T, H, H, xq, (uint32_t *)xg, xs, st));
         MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr, units,
-                                                     w.max_units, perm, K, xq, (const uint32_t *)xg, xs, h,
-                                                     ncu, st));
+                                                     w.max_units, perm, K, T, T * K, xq,
+                                                     (const uint32_t *)xg, xs, h, ncu, st));
         MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_digits(h, 0, T * K, I, I, hq, (uint32_t *)hg, hsc, st));
         MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_mma(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr,
-                                                  units, w.max_units, perm, K, hq, (const uint32_t *)hg, hsc, y,
-                                                  ncu, st));
+                                                  units, w.max_units, perm, K, T * K, T * K, hq,
+                                                  (const uint32_t *)hg, hsc, y, ncu, st));
     }
-    // shared expert: full-precision bf16 weights on MFMA, weight 1
-    float *ysh = nullptr;
-    if ((rc = mark(MOE_Q2_PH_SHARED, 0))) return rc;
-    if (s->shared_inter > 0) {
-        const int Is = s->shared_inter;
-        const uint16_t *xa = (const uint16_t *)xin, *xa_lo = nullptr;
-        if (!xin_bf16) {
-            uint16_t *hi = (uint16_t *)(ws + w.xbf), *lo = (uint16_t *)(ws + w.xlo);
-            if ((rc = mq_launch_split_bf16((const float *)xin, (int64_t)T * H, hi, lo, st))) return rc;
-            xa = hi;
-            xa_lo = lo;
-        }
-        float *P = (float *)(ws + w.sp);
-        uint16_t *shi = (uint16_t *)(ws + w.shi), *slo = (uint16_t *)(ws + w.slo);
-        if ((rc = mq_launch_gemm_bf16(xa, xa_lo, H, shared_w, H, T, 2 * Is, H, w.split_gu, P, st)))
-            return rc;
-        if ((rc = mq_launch_swiglu_partials(P, w.split_gu, T, Is, shi, slo, st))) return rc;
-        if ((rc = mq_launch_gemm_bf16(shi, slo, Is, shared_w + (size_t)2 * Is * H, Is, T, H, Is,
-                                      w.split_d, P, st)))
-            return rc;
-        ysh = (float *)(ws + w.ysh);
-        if ((rc = mq_launch_sum_partials(P, w.split_d, (int64_t)T * H, ysh, st))) return rc;
+    if (side) {
+        const hipError_t e = hipStreamWaitEvent(st, side->join, 0);
+        if (e != hipSuccess) return mq_fail_hip(e);
     }
-    if ((rc = mark(MOE_Q2_PH_SHARED, 1))) return rc;
     MQ_PHASE(MOE_Q2_PH_COMBINE, mq_launch_combine(y, inv, gate, ysh, T, H, K, accum ? 1 : 0, out, st));
     if (!rms && ev) {
         if ((rc = mark(MOE_Q2_PH_RMSNORM, 0)) || (rc = mark(MOE_Q2_PH_RMSNORM, 1))) return rc;

@@ -74,46 +74,63 @@ __device__ __forceinline__ void mq_split3(const float (&w)[8], mq_s16x8 &hi, mq_
     }
 }
 
+// The k range of a split is walked in chunks of RT_KC 32-wide steps whose weight
+// and activation loads are all issued before the chunk's multiplies; MF = token
+// fragments per work-group (1 for up to 16 tokens, else 4).
+#define RT_KC 8
+template <int MF>
 __global__ void __launch_bounds__(256) k_router_mma(const uint16_t *__restrict__ x,
                                                     const float *__restrict__ wr, int T, int H, int E,
                                                     int k_per_split, float *__restrict__ P) {
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int e0 = blockIdx.x * 64 + wv * 16, t0 = blockIdx.y * 64;
+    const int e0 = blockIdx.x * 64 + wv * 16, t0 = blockIdx.y * 16 * MF;
     const int split = blockIdx.z;
     const int k0 = split * k_per_split, k1 = min(H, k0 + k_per_split);
     const int r16 = lane & 15, q = lane >> 4;
     const int e = e0 + r16;
-    mq_f32x4 acc[4];
+    mq_f32x4 acc[MF];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = (mq_f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < MF; ++i) acc[i] = (mq_f32x4){0.f, 0.f, 0.f, 0.f};
     const float *wrow = wr + (int64_t)min(e, E - 1) * H;
-    for (int k = k0; k < k1; k += 32) {
-        const int kk = k + 8 * q;
-        float w[8];
-        const float4 w0 = *(const float4 *)(wrow + kk), w1 = *(const float4 *)(wrow + kk + 4);
-        w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
-        w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
-        if (e >= E) {
+    for (int kc = k0; kc < k1; kc += 32 * RT_KC) {
+        float4 w0[RT_KC], w1[RT_KC];
+        mq_u32x4 a[RT_KC][MF];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) w[i] = 0.0f;
+        for (int s = 0; s < RT_KC; ++s) {
+            const int kk = kc + 32 * s + 8 * q;
+            const bool ok = kc + 32 * s < k1;
+            w0[s] = ok ? *(const float4 *)(wrow + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+            w1[s] = ok ? *(const float4 *)(wrow + kk + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf) {
+                const int t = t0 + 16 * mf + r16;
+                a[s][mf] = (ok && t < T) ? *(const mq_u32x4 *)(x + (int64_t)t * H + kk)
+                                         : (mq_u32x4){0u, 0u, 0u, 0u};
+            }
         }
-        mq_s16x8 bh, bm, bl;
-        mq_split3(w, bh, bm, bl);
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
-            const int t = t0 + 16 * mf + r16;
-            mq_u32x4 a = {0u, 0u, 0u, 0u};
-            if (t < T) a = *(const mq_u32x4 *)(x + (int64_t)t * H + kk);
-            const mq_bf16x8 av = __builtin_bit_cast(mq_bf16x8, a);
-            acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(mq_bf16x8, bh), acc[mf], 0, 0, 0);
-            acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(mq_bf16x8, bm), acc[mf], 0, 0, 0);
-            acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(mq_bf16x8, bl), acc[mf], 0, 0, 0);
+        for (int s = 0; s < RT_KC; ++s) {
+            if (kc + 32 * s >= k1) break;
+            float w[8] = {w0[s].x, w0[s].y, w0[s].z, w0[s].w, w1[s].x, w1[s].y, w1[s].z, w1[s].w};
+            if (e >= E) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w[i] = 0.0f;
+            }
+            mq_s16x8 bh, bm, bl;
+            mq_split3(w, bh, bm, bl);
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf) {
+                const mq_bf16x8 av = __builtin_bit_cast(mq_bf16x8, a[s][mf]);
+                acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(mq_bf16x8, bh), acc[mf], 0, 0, 0);
+                acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(mq_bf16x8, bm), acc[mf], 0, 0, 0);
+                acc[mf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(mq_bf16x8, bl), acc[mf], 0, 0, 0);
+            }
         }
     }
     float *Ps = P + (int64_t)split * T * E;
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+    for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + 16 * mf + 4 * q + i;
@@ -133,8 +150,12 @@ int mq_launch_router_mma(const uint16_t *x, const float *wr, int T, int H, int E
                          float *P, hipStream_t st) {
     int kps = (H + nsplit - 1) / nsplit;
     kps = (kps + 31) / 32 * 32;
-    dim3 grid((E + 63) / 64, (T + 63) / 64, nsplit);
-    hipLaunchKernelGGL(k_router_mma, grid, dim3(256), 0, st, x, wr, T, H, E, kps, P);
+    if (T <= 16)
+        hipLaunchKernelGGL(k_router_mma<1>, dim3((E + 63) / 64, 1, nsplit), dim3(256), 0, st, x, wr, T, H,
+                           E, kps, P);
+    else
+        hipLaunchKernelGGL(k_router_mma<4>, dim3((E + 63) / 64, (T + 63) / 64, nsplit), dim3(256), 0, st,
+                           x, wr, T, H, E, kps, P);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
@@ -144,81 +165,81 @@ int mq_launch_router_mma(const uint16_t *x, const float *wr, int T, int H, int E
 // (ties: lower expert index); gates are the softmax over the selected logits,
 // which equals the full softmax renormalised over the selection.
 // One work-group per token.  Every thread adds the split-K partial logits of up to
-// two experts (fixed order) and the bias; wave 0 then runs K rounds of a wave
-// arg-max over the unselected logits (ties: lower expert index).  Gates are the
-// softmax over the selected logits, which equals the full softmax renormalised
-// over the selection.
+// two experts (fixed order) and the bias.  The selection order is value
+// descending, ties to the lower expert index; it is the order of the 64-bit keys
+// (order-preserving bits of the logit, then the complemented expert index), all
+// distinct, so an expert's rank is the number of larger keys: every thread counts
+// it for its experts against the whole key table in LDS, and the experts of rank
+// < K are the selection, in order.  Gates are the softmax over the selected
+// logits, which equals the full softmax renormalised over the selection.
+__device__ __forceinline__ uint32_t mq_order_key(float v) {
+    const uint32_t u = __float_as_uint(v + 0.0f);    // -0 -> +0: equal floats, equal keys
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, int nsplit,
                                               const float *__restrict__ bias, int T, int E, int K,
                                               int32_t *__restrict__ idx, float *__restrict__ gate,
                                               int32_t *__restrict__ trace_idx,
                                               float *__restrict__ trace_w) {
+    __shared__ __attribute__((aligned(16))) uint64_t key[512];
     __shared__ float lg[512];
+    __shared__ float sv[16];
+    __shared__ int se[16];
     const int t = blockIdx.x;
-    for (int e = threadIdx.x; e < E; e += 256) {
+    const int E2 = (E + 1) & ~1;
+    for (int e = threadIdx.x; e < E2; e += 256) {
+        if (e >= E) {
+            key[e] = 0;                               // below every real key
+            continue;
+        }
         const float *p = logits + (int64_t)t * E + e;
         const int64_t stride = (int64_t)T * E;
+        const float be = bias ? bias[e] : 0.0f;     // loaded together with the partials
+        // partials added in split order; up to 64 of them are loaded at once (the
+        // indices are clamped so that every load is unconditional)
         float a = 0.0f;
-        int sp = 0;
-        for (; sp + 8 <= nsplit; sp += 8) {
-            float v[8];
+        for (int sp = 0; sp < nsplit; sp += 64) {
+            float v[64];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = p[(sp + i) * stride];
+            for (int i = 0; i < 64; ++i) v[i] = p[(int64_t)min(sp + i, nsplit - 1) * stride];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a += v[i];
+            for (int i = 0; i < 64; ++i) a = sp + i < nsplit ? a + v[i] : a;
         }
-        for (; sp < nsplit; ++sp) a += p[sp * stride];
-        lg[e] = a + (bias ? bias[e] : 0.0f);
+        a += be;
+        lg[e] = a;
+        key[e] = ((uint64_t)mq_order_key(a) << 32) | (uint32_t)(0xFFFFu - e);
     }
     __syncthreads();
-    if (threadIdx.x >= 64) return;
-    const int lane = threadIdx.x;
-    float v[8];
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const uint64_t my = key[e];
+        int r[8] = {0, 0, 0, 0, 0, 0, 0, 0};       // independent counters (short chains)
+        int m = 0;
+        for (; m + 16 <= E2; m += 16) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? lg[e] : -INFINITY;
-    }
-    uint32_t taken = 0;
-    float sel_v[16];
-    int sel_e[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        if (k >= K) break;
-        float bv = -INFINITY;
-        int be = 0x7FFFFFFF;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-                bv = v[i];
-                be = e;
+            for (int j = 0; j < 8; ++j) {
+                const ulonglong2 k2 = *(const ulonglong2 *)&key[m + 2 * j];
+                r[j] += (k2.x > my ? 1 : 0) + (k2.y > my ? 1 : 0);
             }
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oe = __shfl_xor(be, o, 64);
-            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+        for (; m < E2; m += 2) r[0] += (key[m] > my ? 1 : 0) + (key[m + 1] > my ? 1 : 0);
+        const int rank = ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
+        if (rank < K) {
+            sv[rank] = lg[e];
+            se[rank] = e;
         }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        sel_v[k] = bv;
-        sel_e[k] = be;
     }
+    __syncthreads();
+    const int lane = threadIdx.x;
     if (lane < K) {
-        const float mx = sel_v[0];
+        const float mx = sv[0];
         float z = 0.0f, mine = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            if (k >= K) break;
-            const float pk = expf(sel_v[k] - mx);
+        for (int k = 0; k < K; ++k) {
+            const float pk = expf(sv[k] - mx);
             z += pk;
             if (k == lane) mine = pk;
         }
-        int me = 0;
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-            if (k == lane) me = sel_e[k];
+        const int me = se[lane];
         const float g = mine / z;
         idx[t * K + lane] = me;
         gate[t * K + lane] = g;

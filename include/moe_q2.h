@@ -32,10 +32,19 @@
  *
  * Conventions for every entry point:
  *   - pointers marked "device" must be device memory of the current HIP device;
- *     the caller owns every buffer; the library never allocates in moe_q2_forward
- *     and keeps no state between calls (it is reentrant across streams);
+ *     the caller owns every buffer; moe_q2_forward allocates no memory;
  *   - work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and
- *     is asynchronous: a device fault surfaces at the caller's next sync;
+ *     is asynchronous: a device fault surfaces at the caller's next sync.  The
+ *     work that needs only the layer input (the routed experts' activation
+ *     preparation and the shared expert) runs as a concurrent branch:
+ *     moe_q2_forward forks it onto an internal stream with an event recorded on
+ *     `stream` and joins it back with events before the routed experts and the
+ *     combine, so the caller sees ordinary stream-ordered semantics (and the
+ *     fork/join is legal under graph capture).  The internal stream and its
+ *     three events are created by the first call on a device and kept until
+ *     the process ends; calls from several host threads on one device enqueue
+ *     one at a time.  MOE_Q2_SERIAL keeps every launch on `stream` and touches
+ *     no internal state;
  *   - arguments are validated before anything is enqueued; a non-zero status
  *     means nothing was enqueued (except MOE_Q2_EHIP, raised when a launch
  *     fails, after which earlier launches of the same call may have run);
@@ -65,13 +74,14 @@ enum { MOE_Q2_F32 = 0, MOE_Q2_BF16 = 1 };
 /* moe_q2_shape.flags */
 enum {
     MOE_Q2_PATH_AUTO = 0,      /* decode kernels below MOE_Q2_PREFILL_MIN_TOKENS tokens, else prefill */
-    MOE_Q2_PATH_DECODE = 1,    /* force the fp32-accumulate vector-ALU path */
-    MOE_Q2_PATH_PREFILL = 2,   /* force the bf16 MFMA grouped-GEMM path */
+    MOE_Q2_PATH_DECODE = 1,    /* force the decode kernels (up to 16 slots per work unit) */
+    MOE_Q2_PATH_PREFILL = 2,   /* force the prefill kernels (up to 64 slots per work unit) */
     MOE_Q2_PRE_RMSNORM = 4,    /* x is the fp32 residual stream h; the layer input is
                                   bf16(h / sqrt(mean(h^2) + rms_eps)) (unit gain) */
     MOE_Q2_RESIDUAL_ADD = 8,   /* out += layer(...) instead of out = layer(...) */
-    MOE_Q2_DECODE_VALU = 16    /* decode path: routed experts on the vector-ALU dot-product
+    MOE_Q2_DECODE_VALU = 16,   /* decode path: routed experts on the vector-ALU dot-product
                                   kernel instead of the integer matrix-core kernel */
+    MOE_Q2_SERIAL = 32         /* run every launch on `stream` (no internal stream) */
 };
 #define MOE_Q2_PREFILL_MIN_TOKENS 256
 
@@ -81,7 +91,8 @@ typedef struct {
     int32_t n_experts;     /* E: 1..512 */
     int32_t shared_inter;  /* Is: shared expert intermediate, multiple of 256, or 0 = none */
     int32_t act_dtype;     /* MOE_Q2_F32 or MOE_Q2_BF16 (ignored under PRE_RMSNORM: x is fp32) */
-    int32_t flags;         /* MOE_Q2_PATH_* | MOE_Q2_PRE_RMSNORM | MOE_Q2_RESIDUAL_ADD */
+    int32_t flags;         /* MOE_Q2_PATH_* | MOE_Q2_PRE_RMSNORM | MOE_Q2_RESIDUAL_ADD |
+                              MOE_Q2_DECODE_VALU | MOE_Q2_SERIAL */
     float   rms_eps;       /* used under MOE_Q2_PRE_RMSNORM */
 } moe_q2_shape;
 
@@ -89,7 +100,9 @@ typedef struct {
  * Slot s = t*K + k; bucket order sorts slots by (expert, token).
  * events: nullable host array of 2 * MOE_Q2_N_PHASES hipEvent_t created by the caller;
  * when set, each non-null events[2i] / events[2i+1] is recorded on the stream before /
- * after phase i (phases that do not run record both events back to back). */
+ * after phase i (phases that do not run record both events back to back; the
+ * activation-preparation and shared-expert phases are recorded on the stream
+ * they run on). */
 typedef struct {
     int32_t *topk_idx;     /* [T, K]  selected experts, descending logit */
     float   *topk_w;       /* [T, K]  renormalised gate weights */
@@ -99,7 +112,8 @@ typedef struct {
     void   **events;       /* [2 * MOE_Q2_N_PHASES] hipEvent_t, nullable */
 } moe_q2_trace;
 
-/* Phases of moe_q2_forward, in launch order (for moe_q2_trace.events). */
+/* Phases of moe_q2_forward (for moe_q2_trace.events); PREP_X and SHARED run on the
+ * concurrent branch, the others in this order on the calling stream. */
 enum {
     MOE_Q2_PH_RMSNORM = 0,      /* RMSNorm of the residual stream -> bf16 */
     MOE_Q2_PH_ROUTER,           /* router logits */

@@ -70,10 +70,25 @@ def _full_check(name, sample=None, flags=0):
     return err
 
 
-@pytest.mark.parametrize("kernel", ["mma", "valu"])
+@pytest.mark.parametrize("kernel", ["mma", "valu", "mma_serial"])
 def test_decode1_layer(kernel):
     import bit_quantized_routed_amd as mq
-    _full_check("decode1", flags=mq.DECODE_VALU if kernel == "valu" else 0)
+    flags = {"mma": 0, "valu": mq.DECODE_VALU, "mma_serial": mq.SERIAL}[kernel]
+    _full_check("decode1", flags=flags)
+
+
+def test_shared_branch_concurrent_equals_serial():
+    """The shared expert forked onto the internal stream gives the same bits as the
+    all-on-one-stream order, over several back-to-back calls."""
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.WORKLOADS["decode32_zipf"]
+    dl = dw.DeviceLayer(wl)
+    x = dw.activations(wl)
+    ser, _ = _run(mq, dl, x, wl.tokens, flags=mq.SERIAL)
+    for _ in range(3):
+        con, _ = _run(mq, dl, x, wl.tokens, flags=0)
+        assert np.array_equal(con, ser)
 
 
 @pytest.mark.parametrize("kernel", ["mma", "valu"])
