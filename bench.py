@@ -9,6 +9,12 @@ all weights resident in HBM.  Decode steps rotate over several distinct layers
 of the same shape (as a model's layer stack does), so each step streams its
 weights from HBM rather than from the 256 MB last-level cache.
 
+Steps are timed as HIP graph replays by default (one captured graph per step;
+exactly K replays), which removes the host-side launch cost of the ~15 kernels of
+a decode step; the dominant routed kernel's duration comes from HIP events in a
+separate eager loop of the same K steps, which is also reported
+(eager_ms_per_step).  --graph 0 times the eager loop only.
+
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
@@ -39,6 +45,7 @@ def parse():
                     help="comma-separated extra workloads reported in the same line ('' for none)")
     ap.add_argument("--rotate", type=int, default=8, help="distinct layers cycled by decode steps")
     ap.add_argument("--cpu-baseline", type=int, default=1)
+    ap.add_argument("--graph", type=int, default=1, help="time steps as HIP graph replays")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -76,7 +83,7 @@ def traffic_record(kernel):
     return rec
 
 
-def run_workload(name, steps, warmup, rotate):
+def run_workload(name, steps, warmup, rotate, graph=True):
     import torch
     import bit_quantized_routed_amd as mq
     from bit_quantized_routed_amd import workload as dw
@@ -146,6 +153,35 @@ def run_workload(name, steps, warmup, rotate):
             dom_ms.append(e.elapsed()[dom])
             e.close()
     dom_avg = float(np.mean(dom_ms))
+    eager_ms = ms_per_step
+    launch = "eager"
+    if graph:
+        # one graph per distinct step (layer rotation), captured on a side stream
+        n_graphs = 1 if stack else L
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for i in range(n_graphs):
+                step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        for i in range(n_graphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(max(warmup, n_graphs)):
+            graphs[i % n_graphs].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(steps):
+            graphs[i % n_graphs].replay()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        ms_per_step = (t2 - t1) * 1e3 / steps
+        launch = "hip_graph"
+        del graphs
     touched = [int((c > 0).sum().item()) for c in counts]
     d_mean = float(np.mean(touched))
     passes = L if stack else 1
@@ -153,7 +189,8 @@ def run_workload(name, steps, warmup, rotate):
     bytes_per_pass = layer_bytes(wl, d_mean)
     res = {
         "workload": name, "tokens": T, "layers_in_step": passes, "layers_resident": L,
-        "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_step / (ms_per_step * 1e-3),
+        "ms_per_step": ms_per_step, "eager_ms_per_step": eager_ms, "launch": launch,
+        "tokens_per_s": tokens_per_step / (ms_per_step * 1e-3),
         "layer_tokens_per_s": T * passes / (ms_per_step * 1e-3),
         "touched_experts_mean": d_mean, "touched_experts_per_layer": touched,
         "algorithmic_bytes_per_pass": bytes_per_pass,
@@ -230,10 +267,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
-    head = run_workload(args.workload, args.steps, args.warmup, args.rotate)
+    head = run_workload(args.workload, args.steps, args.warmup, args.rotate, bool(args.graph))
     extras = {}
     for name in [n for n in args.extra.split(",") if n and n != args.workload]:
-        extras[name] = run_workload(name, args.steps, args.warmup, args.rotate)
+        extras[name] = run_workload(name, args.steps, args.warmup, args.rotate, bool(args.graph))
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -253,7 +290,8 @@ def main():
         "config": {"workload": args.workload, "tokens": wl.tokens, "hidden": wl.hidden,
                    "n_experts": wl.n_experts, "topk": wl.topk, "inter": wl.inter,
                    "shared_inter": wl.shared_inter, "weights": "q2 routed (84 B/256), bf16 shared, fp32 router",
-                   "layers_rotated": head["layers_resident"],
+                   "layers_rotated": head["layers_resident"], "launch": head["launch"],
+                   "eager_ms_per_step": round(head["eager_ms_per_step"], 5),
                    "touched_experts_mean": head["touched_experts_mean"]},
         "hbm_gbs": round(head["hbm_gbs"], 1),
         "roofline": head.get("roofline"),

@@ -108,24 +108,10 @@ __device__ __forceinline__ void mq_bcol_store(mq_u32x4 *__restrict__ dst, int la
     dst[lane + 320] = v.f;
 }
 
-// Activation operands of one block column for the lane's token: digits of groups
-// 4kk + q4 (hi, lo), the two bf16 planes of the group sums 4q4 .. 4q4+3, and the
-// row's scale.  Lanes without a token read an all-zero activation row.
-struct mq_acol { mq_i32x4 hi[4], lo[4]; mq_s16x4 sh, sl; float sc; };
-
-__device__ __forceinline__ void mq_acol_load(const mq_u32x4 *__restrict__ xd, const uint32_t *__restrict__ xs,
-                                             const float *__restrict__ xsc, int cb, int q4, mq_acol &a) {
-    a.sc = *xsc;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const int g = cb * 16 + 4 * kk + q4;
-        a.hi[kk] = __builtin_bit_cast(mq_i32x4, xd[2 * g]);
-        a.lo[kk] = __builtin_bit_cast(mq_i32x4, xd[2 * g + 1]);
-    }
-    const uint32_t *p = xs + cb * 16;
-    a.sh = __builtin_bit_cast(mq_s16x4, *(const uint2 *)(p + 2 * q4));
-    a.sl = __builtin_bit_cast(mq_s16x4, *(const uint2 *)(p + 8 + 2 * q4));
-}
+// Activation operands of one block column for one MFMA lane (token l % 16, group
+// quad q4 = l / 16): digits of groups 4kk + q4 (hi, lo) and the two bf16 planes of
+// the group sums 4q4 .. 4q4+3.
+struct mq_acol { mq_i32x4 hi[4], lo[4]; mq_s16x4 sh, sl; };
 
 // One 64-row block column from the wave's LDS slice into the 4 N fragments:
 // integer products of both activation digits on the i8 matrix cores, the min
@@ -159,211 +145,204 @@ __device__ __forceinline__ void mq_mma_column(const uint32_t *__restrict__ my, i
     }
 }
 
-// Where a work unit's operands live, per lane: its weight tile and the lane's
-// activation row (digits, group sums, scale).
-struct mq_cursor {
-    const mq_u32x4 *w;
-    const mq_u32x4 *xd;
-    const uint32_t *xs;
-    const float *xsc;
-    int p0, nt, r0;
-};
-
-#define MQ_DEC_PASSES 6
-#define MQ_DEC_MAX_UNITS (16 * MQ_DEC_PASSES)    // work units per work-group
-
-// Work unit = (touched expert, 64-row tile of the tiled layout, up to 16 slots);
-// work-group g takes units g, g + grid, ... (at most MQ_DEC_MAX_UNITS of them).
-// Per work-group (4 waves): wave w takes block columns w, w+4, ... of the tile for
-// all 64 rows (4 N fragments).  Each wave streams its own block columns (5376
-// contiguous bytes each) HBM -> registers one column ahead, together with the
-// activation digits of that column (two register sets used alternately), and
-// copies the weights to its private LDS slice.  The four waves' partial sums are
-// added in a fixed order at the end of each unit.
+// Work unit = (touched expert's unit of up to 16 slots, group of 4 consecutive row
+// tiles, k-split s).  Wave w streams tile 4g + w -- 64 rows, all 4 N fragments --
+// over block columns [s * cps, (s + 1) * cps) and owns those rows' sums, so no
+// reduction across waves is needed; the 4 waves step through the columns
+// together and share one copy of each column's activation operands (16 tokens x
+// 16 groups: two 16-byte digit vectors per lane and MFMA step, plus the group-sum
+// planes), which the work-group loads cooperatively into LDS already arranged in
+// MFMA lane order (one 16-byte LDS read per operand, lane-contiguous).  A wave's
+// weight column (5376 contiguous bytes) goes through registers into its private
+// LDS slice.  Both are prefetched one column ahead; the activation buffer is
+// double-buffered, so one barrier per column suffices.
 //
-// The stream runs across work units: the last column of a unit prefetches the
-// first column of the work-group's next unit.  The work-group's unit records and
-// per-token activation rows are gathered into LDS once, up front, so no memory
-// load inside the stream depends on another one; every load is unconditional
-// (padding tokens read an all-zero activation row, padding outputs go to a
-// discard row).  The compiler's memory waits then only ever wait for the oldest
-// column in flight, never drain the prefetch.
-template <bool SWIGLU>
+// Outputs are per-split partial sums, scaled by the token's activation scale:
+//   GU  : gate rows -> out0[s][slot][row], up rows -> out1[s][slot][row]
+//   down: out0[s][slot][row]
+// Padding tokens (beyond the unit's count) read the all-zero activation row zrow
+// and write to the discard row trash_row.
+#define DM_AITEMS 576          // 512 digit vectors + 64 sum vectors per column
+
+template <bool GU>
 __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ experts, int64_t expert_bytes,
-                                                int64_t mat_off, int rows, int kblocks,
-                                                const int32_t *__restrict__ units_hdr,
+                                                int64_t mat_off, int tiles, int kblocks, int nsplit,
+                                                int cps, const int32_t *__restrict__ units_hdr,
                                                 const int4 *__restrict__ units,
                                                 const int32_t *__restrict__ perm, int topk, int zrow,
                                                 int trash_row, const mq_u32x4 *__restrict__ xdig,
                                                 const uint32_t *__restrict__ xsum,
-                                                const float *__restrict__ xscale,
-                                                float *__restrict__ out) {
-    __shared__ __attribute__((aligned(16))) mq_u32x4 stage[4][384];   // one slice per wave
-    __shared__ float red[4][16][64];
-    __shared__ int4 t_unit[MQ_DEC_MAX_UNITS];                          // expert, p0, nt, r0
-    __shared__ int t_row[MQ_DEC_MAX_UNITS][16];                        // activation row per token
-    constexpr int ROW_TILE = SWIGLU ? 32 : 64;
+                                                const float *__restrict__ xscale, float *__restrict__ out0,
+                                                float *__restrict__ out1, int out_ld, int64_t split_stride) {
+    __shared__ __attribute__((aligned(16))) mq_u32x4 sW[4][384];           // weight slices, one per wave
+    __shared__ __attribute__((aligned(16))) mq_u32x4 sA[2][DM_AITEMS];     // activation operands
+    __shared__ int s_row[16];
+    __shared__ float s_sc[16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, q4 = lane >> 4;
-    const int tiles = rows / ROW_TILE;
-    const int nwu = units_hdr[0] * tiles;
-    const int G = kblocks * 16;                  // groups per activation row
+    const int groups = tiles >> 2;
+    const int tg = blockIdx.x % groups;
+    const int rest = blockIdx.x / groups;
+    const int ks = rest % nsplit, u = rest / nsplit;
+    if (u >= units_hdr[0]) return;
+    const int c0 = ks * cps, c1 = min(kblocks, c0 + cps);
+    if (c0 >= c1) return;
+    const int4 un = units[u];
+    const int e = un.x, p0 = un.y, nt = un.z;
+    const int tile = 4 * tg + wv;
+    const int G = kblocks * 16;
     const int64_t tile_bytes = (int64_t)kblocks * 64 * MQ_BLOCK_BYTES;
-    const int ncol = wv < kblocks ? (kblocks - wv + 3) / 4 : 0;   // this wave's columns per unit
-    const int gsz = (int)gridDim.x;
-    if ((int)blockIdx.x >= nwu) return;
-    const int nj = (nwu - (int)blockIdx.x + gsz - 1) / gsz;      // units of this work-group
-    mq_u32x4 *my = stage[wv];
-    const uint32_t *myd = (const uint32_t *)my;
-
-    // gather: thread (j, r) = (tid / 16 + 16 p, tid % 16)
-    {
-        const int r = tid & 15;
-        int4 un[MQ_DEC_PASSES];
-        int sl[MQ_DEC_PASSES];
-#pragma unroll
-        for (int p = 0; p < MQ_DEC_PASSES; ++p) {
-            const int j = (tid >> 4) + 16 * p;
-            un[p] = make_int4(0, 0, 1, 0);
-            if (j < nj) un[p] = units[((int)blockIdx.x + j * gsz) / tiles];
-        }
-#pragma unroll
-        for (int p = 0; p < MQ_DEC_PASSES; ++p) {
-            const int j = (tid >> 4) + 16 * p;
-            sl[p] = un[p].y + (r < un[p].z ? r : 0);
-            if (SWIGLU && j < nj) sl[p] = perm[sl[p]];
-        }
-#pragma unroll
-        for (int p = 0; p < MQ_DEC_PASSES; ++p) {
-            const int j = (tid >> 4) + 16 * p;
-            if (j < nj) {
-                t_row[j][r] = r < un[p].z ? (SWIGLU ? sl[p] / topk : sl[p]) : zrow;
-                if (r == 0) {
-                    const int wu = (int)blockIdx.x + j * gsz;
-                    t_unit[j] = make_int4(un[p].x, un[p].y, un[p].z, (wu - (wu / tiles) * tiles) * ROW_TILE);
-                }
-            }
-        }
+    const mq_u32x4 *tb = (const mq_u32x4 *)(experts + (int64_t)e * expert_bytes + mat_off +
+                                            (int64_t)tile * tile_bytes);
+    mq_bcol wb;
+    mq_bcol_load(tb + (int64_t)c0 * 336, lane, wb);      // weights first: needs only the unit
+    if (tid < 16) {
+        const bool ok = tid < nt;
+        const int slot = p0 + (ok ? tid : 0);            // always a valid slot: nt >= 1
+        int ar = GU ? perm[slot] / topk : slot;
+        ar = ok ? ar : zrow;
+        s_row[tid] = ar;
+        s_sc[tid] = xscale[ar];
     }
     __syncthreads();
-
-    auto open = [&](mq_cursor &c, int j) {
-        const int4 t = t_unit[j];
-        const int e = __builtin_amdgcn_readfirstlane(t.x);
-        c.p0 = __builtin_amdgcn_readfirstlane(t.y);
-        c.nt = __builtin_amdgcn_readfirstlane(t.z);
-        c.r0 = __builtin_amdgcn_readfirstlane(t.w);
-        c.w = (const mq_u32x4 *)(experts + (int64_t)e * expert_bytes + mat_off +
-                                 (int64_t)(c.r0 / ROW_TILE) * tile_bytes);
-        const int arow = t_row[j][r16];
-        c.xd = xdig + (int64_t)arow * G * 2;
-        c.xs = xsum + (int64_t)arow * G;
-        c.xsc = xscale + arow;
-    };
-    // reduction of one finished unit and its stores; sc = the lane's row scale
-    auto finish = [&](const mq_cursor &c, const mq_f32x4 (&tot)[4], float sc) {
-        // D layout: lane l, element i -> token 4*(l/16) + i, row slot 16*nf + l%16
+    // this thread's three activation items, one per LDS slot so that a wave's
+    // stores are lane-contiguous (the last ones clamped: duplicate writes of
+    // identical data).  Slot i < 512 = (kk * 2 + digit) * 64 + lane holds the digit
+    // vector of MFMA step kk for lane (token l % 16, group 4 kk + l / 16); slot
+    // 512 + l the group-sum vector of lane l (token l % 16, quad l / 16).
+    // global address space stated explicitly: a generic (flat) load would also count
+    // against the LDS counter and make every LDS wait in the column wait for it
+    typedef const __attribute__((address_space(1))) mq_u32x4 *gvec;
+    gvec asrc[3];
+    int aslot[3], astep[3];
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) red[wv][4 * nf + i][lane] = tot[nf][i];
-        __syncthreads();
-        if (SWIGLU) {
-            // thread -> output row j (0..31), tokens t0 and t0 + 8
-            const int j = tid & 31, t0 = tid >> 5;
-            const int nfg = j >> 4, rr = j & 15;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int t = t0 + 8 * h;
-                const int src = 16 * (t >> 2) + rr, i = t & 3;
-                const float g = (red[0][4 * nfg + i][src] + red[1][4 * nfg + i][src]) +
-                                (red[2][4 * nfg + i][src] + red[3][4 * nfg + i][src]);
-                const float up = (red[0][4 * (nfg + 2) + i][src] + red[1][4 * (nfg + 2) + i][src]) +
-                                 (red[2][4 * (nfg + 2) + i][src] + red[3][4 * (nfg + 2) + i][src]);
-                const float st = __shfl(sc, t, 64);
-                const float gs = g * st, us = up * st;
-                out[(int64_t)(t < c.nt ? c.p0 + t : trash_row) * rows + c.r0 + j] =
-                    gs / (1.0f + expf(-gs)) * us;
-            }
+    for (int n = 0; n < 3; ++n) {
+        const int it = min(tid + 256 * n, DM_AITEMS - 1);
+        if (it < 512) {
+            const int l = it & 63, d = (it >> 6) & 1, kk = it >> 7;
+            const int tk = l & 15, g = 4 * kk + (l >> 4);
+            asrc[n] = (gvec)(xdig + (int64_t)s_row[tk] * G * 2 + g * 2 + d);
+            aslot[n] = it;
+            astep[n] = 32;
         } else {
-            // thread -> output row slot j (0..63), tokens t0, t0 + 4, t0 + 8, t0 + 12
-            const int j = tid & 63, t0 = tid >> 6;
-            const int nfj = j >> 4, rr = j & 15;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const int t = t0 + 4 * h;
-                const int src = 16 * (t >> 2) + rr, i = t & 3;
-                const float v = (red[0][4 * nfj + i][src] + red[1][4 * nfj + i][src]) +
-                                (red[2][4 * nfj + i][src] + red[3][4 * nfj + i][src]);
-                out[(int64_t)(t < c.nt ? c.p0 + t : trash_row) * rows + c.r0 + j] = v * __shfl(sc, t, 64);
-            }
+            const int l = it - 512;
+            asrc[n] = (gvec)((const mq_u32x4 *)(xsum + (int64_t)s_row[l & 15] * G) + (l >> 4));
+            aslot[n] = it;
+            astep[n] = 4;
         }
-        __syncthreads();
-    };
+    }
+    mq_u32x4 ab[3];
+#pragma unroll
+    for (int n = 0; n < 3; ++n) ab[n] = asrc[n][c0 * astep[n]];
 
-    mq_cursor cur;
-    open(cur, 0);
     mq_f32x4 tot[4];
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) tot[nf] = (mq_f32x4){0.f, 0.f, 0.f, 0.f};
-
-    if (ncol == 0) {
-        // fewer than 4 block columns: this wave only joins the reductions
-        for (int j = 0; j < nj; ++j) {
-            open(cur, j);
-            finish(cur, tot, *cur.xsc);
-        }
-        return;
-    }
-
-    mq_bcol wb;
-    mq_acol aA, aB;
-    mq_bcol_load(cur.w + (int64_t)wv * 336, lane, wb);
-    mq_acol_load(cur.xd, cur.xs, cur.xsc, wv, q4, aA);
-    int i = 0, j = 0;
-    // one block column; returns false when the stream has ended
-    auto step = [&](const mq_acol &acur, mq_acol &anext) -> bool {
-        mq_bcol_store(my, lane, wb);
-        // the item after this one: the next column of this unit, or the first
-        // column of the next unit (past the end: this column again, L2 hits whose
-        // values are never used)
-        mq_cursor nxt;
-        const bool more = j + 1 < nj;
-        open(nxt, more ? j + 1 : j);
-        const bool last = i + 1 == ncol;
-        const int cb = wv + 4 * i;
-        const int cn = last ? (more ? wv : cb) : cb + 4;
-        mq_bcol_load((last ? nxt.w : cur.w) + (int64_t)cn * 336, lane, wb);
-        mq_acol_load(last ? nxt.xd : cur.xd, last ? nxt.xs : cur.xs, last ? nxt.xsc : cur.xsc, cn, q4, anext);
-        mq_mma_column(myd, r16, q4, acur, tot);
-        if (!last) {
-            ++i;
-            return true;
-        }
-        finish(cur, tot, acur.sc);
+    const uint32_t *myd = (const uint32_t *)sW[wv];
+    int buf = 0;
+    for (int c = c0; c < c1; ++c) {
+        mq_bcol_store(sW[wv], lane, wb);
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) tot[nf] = (mq_f32x4){0.f, 0.f, 0.f, 0.f};
-        cur = nxt;
-        i = 0;
-        return ++j < nj;
-    };
-    while (step(aA, aB) && step(aB, aA)) {
+        for (int n = 0; n < 3; ++n) sA[buf][aslot[n]] = ab[n];
+        __syncthreads();
+        if (c + 1 < c1) {
+            mq_bcol_load(tb + (int64_t)(c + 1) * 336, lane, wb);
+#pragma unroll
+            for (int n = 0; n < 3; ++n) ab[n] = asrc[n][(c + 1) * astep[n]];
+        }
+        mq_acol a;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            a.hi[kk] = __builtin_bit_cast(mq_i32x4, sA[buf][(kk * 2) * 64 + lane]);
+            a.lo[kk] = __builtin_bit_cast(mq_i32x4, sA[buf][(kk * 2 + 1) * 64 + lane]);
+        }
+        const mq_u32x4 sv = sA[buf][512 + lane];
+        a.sh = __builtin_bit_cast(mq_s16x4, (uint2){sv[0], sv[1]});
+        a.sl = __builtin_bit_cast(mq_s16x4, (uint2){sv[2], sv[3]});
+        mq_mma_column(myd, r16, q4, a, tot);
+        buf ^= 1;
     }
+    // D layout: lane l, element i -> token 4*(l/16) + i, row slot 16*nf + l%16
+    float *o0 = out0 + (int64_t)ks * split_stride;
+    float *o1 = GU ? out1 + (int64_t)ks * split_stride : nullptr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * q4 + i;
+        const float sc = s_sc[t];
+        const int64_t orow = (int64_t)(t < nt ? p0 + t : trash_row) * out_ld;
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+            const float v = tot[nf][i] * sc;
+            if (GU) {
+                // slots 0..31: gate rows 32*tile + slot; 32..63: up rows 32*tile + slot - 32
+                float *o = nf < 2 ? o0 : o1;
+                o[orow + 32 * tile + 16 * (nf & 1) + r16] = v;
+            } else {
+                o0[orow + 64 * tile + 16 * nf + r16] = v;
+            }
+        }
+    }
+}
+
+// Split count along the reduction for the decode kernel: enough work-groups for
+// one resident round at three per compute unit of a 256-CU device, at most
+// max_split, and at least 2 block columns per split.
+void mq_dec_split(int max_units, int tiles, int kblocks, int max_split, int *nsplit, int *cps) {
+    const int64_t wgs = (int64_t)max_units * (tiles / 4);
+    int s = (int)(768 / (wgs > 0 ? wgs : 1));
+    const int smax = kblocks / 2 > 1 ? kblocks / 2 : 1;
+    if (s > smax) s = smax;
+    if (s > max_split) s = max_split;
+    if (s < 1) s = 1;
+    const int c = (kblocks + s - 1) / s;
+    *cps = c;
+    *nsplit = (kblocks + c - 1) / c;
+}
+
+int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t mat_off, int tiles,
+                     int kblocks, const int32_t *units_hdr, const int4 *units, int max_units,
+                     const int32_t *perm, int topk, int zrow, int trash_row, const void *xdig,
+                     const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
+                     int64_t split_stride, hipStream_t st) {
+    if (tiles % 4) return MOE_Q2_EUNSUPPORTED;
+    int nsplit = 1, cps = kblocks;
+    mq_dec_split(max_units, tiles, kblocks, gu ? MQ_DEC_SPLIT_GU : MQ_DEC_SPLIT_D, &nsplit, &cps);
+    const int64_t grid = (int64_t)max_units * nsplit * (tiles / 4);
+    if (grid <= 0) return MOE_Q2_OK;
+    if (grid > 0x7fffffff) return MOE_Q2_EUNSUPPORTED;
+    if (gu)
+        hipLaunchKernelGGL(k_q2_mma<true>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
+                           expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units_hdr, units, perm, topk,
+                           zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
+                           split_stride);
+    else
+        hipLaunchKernelGGL(k_q2_mma<false>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
+                           expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units_hdr, units, perm, topk,
+                           zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
+                           split_stride);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
 }
 
 // ------------------------------------------------------------------ activation digits
 // Per row: s = 2^(e - 14) with max|x| in (2^(e-1), 2^e] (1 for an all-zero row);
 // a = rint(x / s) (|a| <= 2^14), hi = floor((a + 128) / 256), lo = a - 256 hi.
 // xdig[row][group][digit] = 16 bytes, byte b of dword s = digit of element 4b + s;
-// xsum[row][block][plane][16] = bf16 planes of A_j = sum of the group's a (hi plane
-// bf16(A_j), lo plane bf16(A_j - hi)).
+// xsum[row][block][quad][plane][4] = bf16 planes of A_j = sum of the group's a for
+// the groups j = 4 quad .. 4 quad + 3 (hi plane bf16(A_j), lo plane bf16(A_j - hi)):
+// one 16-byte vector per MFMA lane quad.
 // One work-group per row (row == nrows: the all-zero row read by padding tokens).
 // Thread i holds groups i, i + 256, ... (at most PD_NG) in registers: one pass of
 // loads, a work-group max, then the digits from the registers.
+// SRC 0: fp32 rows; 1: bf16 rows; 2: SwiGLU of split partial sums, row values
+// silu(sum_s gate[s][row]) * sum_s up[s][row] (splits added in order; src = gate
+// partials, src2 = up partials, split_stride apart).
 #define PD_NG 4
-template <int SRC>  // 0: fp32 rows, 1: bf16 rows
-__global__ void __launch_bounds__(256) k_prep_digits(const void *__restrict__ src, int nrows, int len,
+template <int SRC>
+__global__ void __launch_bounds__(256) k_prep_digits(const void *__restrict__ src,
+                                                     const void *__restrict__ src2, int nsplit,
+                                                     int64_t split_stride, int nrows, int len,
                                                      int64_t src_ld, mq_u32x4 *__restrict__ xdig,
                                                      uint32_t *__restrict__ xsum,
                                                      float *__restrict__ scale) {
@@ -379,6 +358,37 @@ __global__ void __launch_bounds__(256) k_prep_digits(const void *__restrict__ sr
         if (zero_row || g >= G) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) v[n][i] = 0.0f;
+        } else if (SRC == 2) {
+            float gs[16], us[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) { gs[i] = 0.0f; us[i] = 0.0f; }
+            // splits in order, two at a time with both loads in flight
+            for (int sp = 0; sp < nsplit; sp += 2) {
+                float4 a[2][4], b[2][4];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int64_t off = min(sp + j, nsplit - 1) * split_stride + row * src_ld + g * 16;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        a[j][i] = ((const float4 *)((const float *)src + off))[i];
+                        b[j][i] = ((const float4 *)((const float *)src2 + off))[i];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if (sp + j < nsplit) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            gs[4 * i] += a[j][i].x; gs[4 * i + 1] += a[j][i].y;
+                            gs[4 * i + 2] += a[j][i].z; gs[4 * i + 3] += a[j][i].w;
+                            us[4 * i] += b[j][i].x; us[4 * i + 1] += b[j][i].y;
+                            us[4 * i + 2] += b[j][i].z; us[4 * i + 3] += b[j][i].w;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[n][i] = gs[i] / (1.0f + expf(-gs[i])) * us[i];
         } else if (SRC == 0) {
             const float4 *p = (const float4 *)((const float *)src + row * src_ld + g * 16);
 #pragma unroll
@@ -447,8 +457,8 @@ __global__ void __launch_bounds__(256) k_prep_digits(const void *__restrict__ sr
         const uint16_t bh = mq_f32_to_bf16(fs);
         const uint16_t bl = mq_f32_to_bf16(fs - mq_bf16_to_f32(bh));
         const int blk = g >> 4, j = g & 15;
-        sr[blk * 32 + j] = bh;
-        sr[blk * 32 + 16 + j] = bl;
+        sr[blk * 32 + (j >> 2) * 8 + (j & 3)] = bh;
+        sr[blk * 32 + (j >> 2) * 8 + 4 + (j & 3)] = bl;
     }
 }
 
@@ -458,38 +468,23 @@ int mq_launch_prep_digits(const void *src, int src_bf16, int nrows, int len, int
     if (len / 16 > 256 * PD_NG) return MOE_Q2_EUNSUPPORTED;
     dim3 grid(nrows + 1);                        // nrows rows + the zero row
     if (src_bf16)
-        hipLaunchKernelGGL(k_prep_digits<1>, grid, dim3(256), 0, st, src, nrows, len, src_ld,
-                           (mq_u32x4 *)xdig, xsum, scale);
+        hipLaunchKernelGGL(k_prep_digits<1>, grid, dim3(256), 0, st, src, nullptr, 1, (int64_t)0, nrows, len,
+                           src_ld, (mq_u32x4 *)xdig, xsum, scale);
     else
-        hipLaunchKernelGGL(k_prep_digits<0>, grid, dim3(256), 0, st, src, nrows, len, src_ld,
-                           (mq_u32x4 *)xdig, xsum, scale);
+        hipLaunchKernelGGL(k_prep_digits<0>, grid, dim3(256), 0, st, src, nullptr, 1, (int64_t)0, nrows, len,
+                           src_ld, (mq_u32x4 *)xdig, xsum, scale);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
 
-int mq_launch_q2_mma(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
-                     int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
-                     int max_units, const int32_t *perm, int topk, int zrow, int trash_row,
-                     const void *xdig, const uint32_t *xsum, const float *xscale, float *out, int n_cu,
-                     hipStream_t st) {
-    const int tiles = rows / (swiglu ? 32 : 64);
-    const int64_t want = (int64_t)max_units * tiles;
-    // resident work-groups (2 per compute unit), but never more than
-    // MQ_DEC_MAX_UNITS work units per work-group
-    int64_t g = (int64_t)n_cu * 2;
-    if (g > want) g = want;
-    if (g * MQ_DEC_MAX_UNITS < want) g = (want + MQ_DEC_MAX_UNITS - 1) / MQ_DEC_MAX_UNITS;
-    if (g > 0x7fffffff) return MOE_Q2_EUNSUPPORTED;
-    const int grid = (int)g;
-    if (grid <= 0) return MOE_Q2_OK;
-    if (swiglu)
-        hipLaunchKernelGGL(k_q2_mma<true>, dim3(grid), dim3(256), 0, st, (const uint8_t *)experts,
-                           expert_bytes, mat_off, rows, kblocks, units_hdr, units, perm, topk, zrow,
-                           trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out);
-    else
-        hipLaunchKernelGGL(k_q2_mma<false>, dim3(grid), dim3(256), 0, st, (const uint8_t *)experts,
-                           expert_bytes, mat_off, rows, kblocks, units_hdr, units, perm, topk, zrow,
-                           trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out);
+int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit, int64_t split_stride,
+                                 int nrows, int len, int64_t src_ld, void *xdig, uint32_t *xsum,
+                                 float *scale, hipStream_t st) {
+    if (nrows <= 0) return MOE_Q2_OK;
+    if (len / 16 > 256 * PD_NG) return MOE_Q2_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_prep_digits<2>, dim3(nrows + 1), dim3(256), 0, st, (const void *)gate,
+                       (const void *)up, nsplit, split_stride, nrows, len, src_ld, (mq_u32x4 *)xdig, xsum,
+                       scale);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
@@ -615,9 +610,9 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
 #pragma unroll
             for (int m = 0; m < MF; ++m) {
                 if (16 * m < nt) {
-                    const uint32_t *xp = sA + (16 * m + r16) * PF_TS + 128;
-                    const mq_s16x4 xh = __builtin_bit_cast(mq_s16x4, *(const uint2 *)(xp + 2 * q4));
-                    const mq_s16x4 xl = __builtin_bit_cast(mq_s16x4, *(const uint2 *)(xp + 8 + 2 * q4));
+                    const mq_u32x4 xv = *(const mq_u32x4 *)(sA + (16 * m + r16) * PF_TS + 128 + 4 * q4);
+                    const mq_s16x4 xh = __builtin_bit_cast(mq_s16x4, (uint2){xv[0], xv[1]});
+                    const mq_s16x4 xl = __builtin_bit_cast(mq_s16x4, (uint2){xv[2], xv[3]});
                     mq_f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
                     a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, bm0, a0, 0, 0, 0);
                     a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, bm0, a0, 0, 0, 0);

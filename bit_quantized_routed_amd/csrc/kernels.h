@@ -26,8 +26,9 @@ int mq_launch_q2_dec(int swiglu, const void *experts, int64_t expert_bytes, int6
                      int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                      int max_units, const int32_t *perm, int topk, const uint32_t *xq,
                      const float2 *gsum, const float *xscale, float *out, int n_cu, hipStream_t st);
-int mq_launch_combine(const float *y, const int32_t *inv, const float *gate, const float *shared,
-                      int T, int H, int K, int accumulate, float *out, hipStream_t st);
+int mq_launch_combine(const float *y, int nsplit, int64_t split_stride, const int32_t *inv,
+                      const float *gate, const float *shared, int T, int H, int K, int accumulate, float *out,
+                      hipStream_t st);
 int mq_launch_split_bf16(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t st);
 int mq_gemm_splits(int M, int N, int K, int n_cu);
 int mq_launch_gemm_bf16(const uint16_t *A, const uint16_t *Alo, int lda, const uint16_t *B, int ldb,
@@ -37,13 +38,23 @@ int mq_launch_swiglu_partials(const float *P, int nsplit, int M, int Is, uint16_
 int mq_launch_sum_partials(const float *P, int nsplit, int64_t MN, float *out, hipStream_t st);
 int mq_launch_prep_digits(const void *src, int src_bf16, int nrows, int len, int64_t src_ld,
                           void *xdig, uint32_t *xsum, float *scale, hipStream_t st);
-// zrow: index of the all-zero activation row (written by mq_launch_prep_digits after
-// the nrows real rows); trash_row: an output row that absorbs padding-token writes.
-int mq_launch_q2_mma(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
-                     int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
-                     int max_units, const int32_t *perm, int topk, int zrow, int trash_row,
-                     const void *xdig, const uint32_t *xsum, const float *xscale, float *out, int n_cu,
-                     hipStream_t st);
+int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit, int64_t split_stride,
+                                 int nrows, int len, int64_t src_ld, void *xdig, uint32_t *xsum,
+                                 float *scale, hipStream_t st);
+// Decode kernel: split count along the reduction (shared by the workspace sizing).
+// Gate/up splits are summed by the intermediate preparation; the down projection
+// is not split (its partials would cost the combine more than they save).
+#define MQ_DEC_SPLIT_GU 4
+#define MQ_DEC_SPLIT_D 1
+void mq_dec_split(int max_units, int tiles, int kblocks, int max_split, int *nsplit, int *cps);
+// zrow: index of the all-zero activation row (written by the digit preparation after
+// the real rows); trash_row: an output row that absorbs padding-token writes; outputs
+// are per-split partial sums split_stride floats apart (gu: gate -> out0, up -> out1).
+int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t mat_off, int tiles,
+                     int kblocks, const int32_t *units_hdr, const int4 *units, int max_units,
+                     const int32_t *perm, int topk, int zrow, int trash_row, const void *xdig,
+                     const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
+                     int64_t split_stride, hipStream_t st);
 int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
                         int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                         int max_units, const int32_t *perm, int topk, const void *xdig,

@@ -50,7 +50,15 @@ struct Workspace {
     size_t logits, idx, gate, counts, offsets, perm, inv, units_hdr, units, xbf, xq, xg, xs, h,
         hq, hg, hs, y, xlo, sp, shi, slo, ysh;
     int max_units = 0, split_gu = 1, split_d = 1, rsplit = 1;
+    // routed path and, for the matrix-core decode kernels, their reduction splits
+    bool prefill = false, valu = false;
+    int dec_units = 0, dsplit_gu = 1, dsplit_d = 1;
 };
+
+// Upper bound on the work units of a bucketing with `tch` slots per unit.
+int units_bound(size_t S, size_t E, int tch) {
+    return (int)((S + tch - 1) / tch + (S < E ? S : E));
+}
 
 size_t take(size_t &cursor, size_t bytes) {
     const size_t at = cursor;
@@ -64,7 +72,16 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     const size_t S = (size_t)T * K;
     size_t c = 0;
     // work units: at most ceil(S / tch) + min(E, S) for either kernel's unit size
-    w.max_units = (int)((S + FD_TCH - 1) / FD_TCH + (S < E ? S : E));
+    w.max_units = units_bound(S, E, FD_TCH);
+    w.prefill = (s->flags & MOE_Q2_PATH_PREFILL) ||
+                (!(s->flags & MOE_Q2_PATH_DECODE) && T >= MOE_Q2_PREFILL_MIN_TOKENS);
+    w.valu = !w.prefill && (s->flags & MOE_Q2_DECODE_VALU) != 0;
+    int cps = 0;
+    if (!w.prefill && !w.valu) {
+        w.dec_units = units_bound(S, E, MMA_TCH);
+        mq_dec_split(w.dec_units, (int)(I / 32), (int)(H / MQ_QK), MQ_DEC_SPLIT_GU, &w.dsplit_gu, &cps);
+        mq_dec_split(w.dec_units, (int)(H / 64), (int)(I / MQ_QK), MQ_DEC_SPLIT_D, &w.dsplit_d, &cps);
+    }
     w.rsplit = mq_router_splits(T, (int)H, (int)E);
     w.logits = take(c, (size_t)w.rsplit * T * E * 4);
     w.idx = take(c, S * 4);
@@ -81,11 +98,13 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     w.xq = take(c, (size_t)(T + 1) * H * 2);    // fp16 pairs, or the two int8 digits
     w.xg = take(c, (size_t)(T + 1) * (H / 16) * 8);
     w.xs = take(c, (size_t)(T + 1) * 4);
-    w.h = take(c, (S + 1) * I * 4);
+    // h: the intermediate (S + 1 rows), or for the matrix-core decode kernels the
+    // gate and up split partial sums; y: the routed outputs, or their split partials
+    w.h = take(c, (w.prefill || w.valu ? 1 : 2 * (size_t)w.dsplit_gu) * (S + 1) * I * 4);
     w.hq = take(c, (S + 1) * I * 2);
     w.hg = take(c, (S + 1) * (I / 16) * 8);
     w.hs = take(c, (S + 1) * 4);
-    w.y = take(c, (S + 1) * H * 4);
+    w.y = take(c, (size_t)w.dsplit_d * (S + 1) * H * 4);
     const size_t Is = s->shared_inter;
     if (Is) {
         // split-K policy fixed at 256 compute units so the size does not depend on the device
@@ -213,8 +232,7 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     const Workspace w = carve(s, T, K);
     if (!workspace || workspace_bytes < w.total) return MOE_Q2_EWORKSPACE;
     if ((uintptr_t)workspace & 255) return MOE_Q2_EINVAL;
-    const bool prefill = (s->flags & MOE_Q2_PATH_PREFILL) ||
-                         (!(s->flags & MOE_Q2_PATH_DECODE) && T >= MOE_Q2_PREFILL_MIN_TOKENS);
+    const bool prefill = w.prefill;
 
     hipStream_t st = (hipStream_t)stream;
     hipEvent_t *ev = trace && trace->events ? (hipEvent_t *)trace->events : nullptr;
@@ -255,7 +273,7 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     // weight 1) -- runs as a branch concurrent with the routing (forked here; the
     // routed experts wait for the preparation, the combine for the whole branch)
     // unless MOE_Q2_SERIAL is set.
-    const bool valu = !prefill && (s->flags & MOE_Q2_DECODE_VALU) != 0;
+    const bool valu = w.valu;
     float *ysh = nullptr;
     SideBranch *side = nullptr;
     std::unique_lock<std::mutex> side_lock;
@@ -355,19 +373,27 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
                                                      units_hdr, units, w.max_units, perm, K, hq,
                                                      (const uint32_t *)hg, hsc, y, ncu, st));
     } else {
-        MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr, units,
-                                                     w.max_units, perm, K, T, T * K, xq,
-                                                     (const uint32_t *)xg, xs, h, ncu, st));
-        MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_digits(h, 0, T * K, I, I, hq, (uint32_t *)hg, hsc, st));
-        MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_mma(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr,
-                                                  units, w.max_units, perm, K, T * K, T * K, hq,
-                                                  (const uint32_t *)hg, hsc, y, ncu, st));
+        // split partial sums: gate and up [dsplit_gu][S + 1][I], y [dsplit_d][S + 1][H]
+        const int S = T * K;
+        const int64_t gstride = (int64_t)(S + 1) * I, ystride = (int64_t)(S + 1) * H;
+        float *gp = h, *up = h + (int64_t)w.dsplit_gu * gstride;
+        MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma(1, experts_q2, ebytes, 0, I / 32, H / MQ_QK, units_hdr,
+                                                     units, w.dec_units, perm, K, T, S, xq,
+                                                     (const uint32_t *)xg, xs, gp, up, I, gstride, st));
+        MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_swiglu_digits(gp, up, w.dsplit_gu, gstride, S, I, I, hq,
+                                                                (uint32_t *)hg, hsc, st));
+        MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_mma(0, experts_q2, ebytes, 2 * mat_gu, H / 64, I / MQ_QK,
+                                                  units_hdr, units, w.dec_units, perm, K, S, S, hq,
+                                                  (const uint32_t *)hg, hsc, y, nullptr, H, ystride, st));
     }
+    const int ysplit = (prefill || valu) ? 1 : w.dsplit_d;
+    const int64_t ystride = (int64_t)(T * K + 1) * H;
     if (side) {
         const hipError_t e = hipStreamWaitEvent(st, side->join, 0);
         if (e != hipSuccess) return mq_fail_hip(e);
     }
-    MQ_PHASE(MOE_Q2_PH_COMBINE, mq_launch_combine(y, inv, gate, ysh, T, H, K, accum ? 1 : 0, out, st));
+    MQ_PHASE(MOE_Q2_PH_COMBINE, mq_launch_combine(y, ysplit, ystride, inv, gate, ysh, T, H, K, accum ? 1 : 0,
+                                                  out, st));
     if (!rms && ev) {
         if ((rc = mark(MOE_Q2_PH_RMSNORM, 0)) || (rc = mark(MOE_Q2_PH_RMSNORM, 1))) return rc;
     }

@@ -177,6 +177,19 @@ __device__ __forceinline__ uint32_t mq_order_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+template <int B>
+__device__ __forceinline__ float mq_sum_partials(const float *__restrict__ p, int64_t stride, int nsplit) {
+    float a = 0.0f;
+    for (int sp = 0; sp < nsplit; sp += B) {
+        float v[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) v[i] = p[(int64_t)min(sp + i, nsplit - 1) * stride];
+#pragma unroll
+        for (int i = 0; i < B; ++i) a = sp + i < nsplit ? a + v[i] : a;
+    }
+    return a;
+}
+
 __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, int nsplit,
                                               const float *__restrict__ bias, int T, int E, int K,
                                               int32_t *__restrict__ idx, float *__restrict__ gate,
@@ -196,17 +209,10 @@ __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, 
         const float *p = logits + (int64_t)t * E + e;
         const int64_t stride = (int64_t)T * E;
         const float be = bias ? bias[e] : 0.0f;     // loaded together with the partials
-        // partials added in split order; up to 64 of them are loaded at once (the
+        // partials added in split order; a batch of them is loaded at once (the
         // indices are clamped so that every load is unconditional)
-        float a = 0.0f;
-        for (int sp = 0; sp < nsplit; sp += 64) {
-            float v[64];
-#pragma unroll
-            for (int i = 0; i < 64; ++i) v[i] = p[(int64_t)min(sp + i, nsplit - 1) * stride];
-#pragma unroll
-            for (int i = 0; i < 64; ++i) a = sp + i < nsplit ? a + v[i] : a;
-        }
-        a += be;
+        const float a = (nsplit <= 8 ? mq_sum_partials<8>(p, stride, nsplit)
+                                     : mq_sum_partials<64>(p, stride, nsplit)) + be;
         lg[e] = a;
         key[e] = ((uint64_t)mq_order_key(a) << 32) | (uint32_t)(0xFFFFu - e);
     }

@@ -1,0 +1,50 @@
+"""HIP graph capture of moe_q2_forward (with its concurrent branch): every replay,
+with eager calls and synchronisations in between, equals the eager result bit for
+bit."""
+import pytest
+import torch
+
+from synth import workloads as W
+from tests.gpu_util import need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["decode1", "decode32_zipf", "tiny_stack"])
+def test_graph_replays_equal_eager(name):
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.WORKLOADS[name]
+    dl = dw.DeviceLayer(wl)
+    T, K = wl.tokens, wl.topk
+    shape = dl.shape(0)                  # PRE_RMSNORM for the residual-stack shape
+    ws = dw.workspace(shape, T, K)
+    x = dw.activations(wl)
+    out_e = torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")
+    out_g = torch.empty_like(out_e)
+
+    def fwd(out):
+        mq.forward(x, dl.router_w, dl.experts, dl.shared_w, K, out, shape, T,
+                   router_b=dl.router_b, workspace=ws)
+
+    fwd(out_e)
+    torch.cuda.synchronize()
+    ref = out_e.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd(out_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd(out_g)
+    for rep in range(4):
+        out_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref), "replay %d differs from the eager result" % rep
+        fwd(out_e)                       # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out_e, ref)
