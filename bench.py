@@ -9,9 +9,9 @@ all weights resident in HBM.  Decode steps rotate over several distinct layers
 of the same shape (as a model's layer stack does), so each step streams its
 weights from HBM rather than from the 256 MB last-level cache.
 
-Steps are timed as HIP graph replays by default (one captured graph per step;
-exactly K replays), which removes the host-side launch cost of the ~15 kernels of
-a decode step; the dominant routed kernel's duration comes from HIP events in a
+Steps are timed as HIP graph replays by default (one captured graph holds one
+pass over the rotated layers, or one step; exactly K steps are replayed), which
+removes the host-side launch cost of the ~15 kernels of a decode step; the dominant routed kernel's duration comes from HIP events in a
 separate eager loop of the same K steps, which is also reported
 (eager_ms_per_step).  --graph 0 times the eager loop only.
 
@@ -156,31 +156,36 @@ def run_workload(name, steps, warmup, rotate, graph=True):
     eager_ms = ms_per_step
     launch = "eager"
     if graph:
-        # one graph per distinct step (layer rotation), captured on a side stream
-        n_graphs = 1 if stack else L
+        # G consecutive steps per captured graph (one pass over the rotated layers
+        # when that divides the step count, else one step), replayed steps / G times:
+        # exactly `steps` steps, with one host launch per G steps
+        G = L if (not stack and steps % L == 0) else 1
+        n_graphs = 1 if (stack or G == L) else L
         graphs = []
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
-            for i in range(n_graphs):
+            for i in range(max(G, n_graphs)):
                 step(i)
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        for i in range(n_graphs):
+        for j in range(n_graphs):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(i)
+                for i in range(G):
+                    step(j + i)
             graphs.append(g)
-        for i in range(max(warmup, n_graphs)):
-            graphs[i % n_graphs].replay()
+        n_rep = steps // G
+        for r in range(max(1, warmup // G)):
+            graphs[r % n_graphs].replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        for i in range(steps):
-            graphs[i % n_graphs].replay()
+        for r in range(n_rep):
+            graphs[r % n_graphs].replay()
         torch.cuda.synchronize()
         t2 = time.perf_counter()
-        ms_per_step = (t2 - t1) * 1e3 / steps
-        launch = "hip_graph"
+        ms_per_step = (t2 - t1) * 1e3 / (n_rep * G)
+        launch = "hip_graph x%d steps" % G
         del graphs
     touched = [int((c > 0).sum().item()) for c in counts]
     d_mean = float(np.mean(touched))
@@ -198,9 +203,14 @@ def run_workload(name, steps, warmup, rotate, graph=True):
         "phases_ms_per_pass": phase_ms,
         "phases_note": "separate instrumented pass; each phase includes ~4 us of event overhead",
     }
-    # dominant kernel roofline (duration from the timed region's events)
+    # dominant kernel roofline (duration from the timed region's events); on the
+    # matrix-core decode path with a bf16 layer input the routed launches also
+    # stream the shared expert's gate/up and down rows
     gu_bytes = d_mean * 2 * (wl.expert_bytes // 3)
     dn_bytes = d_mean * (wl.expert_bytes // 3)
+    if T < 256 and wl.shared_inter and (wl.act == "bf16" or wl.rmsnorm):
+        gu_bytes += 2 * wl.shared_inter * wl.hidden * 2
+        dn_bytes += wl.shared_inter * wl.hidden * 2
     kbytes = {"gate_up": gu_bytes + T * wl.hidden * 2.5 + T * K * wl.inter * 4,
               "down": dn_bytes + T * K * wl.inter * 2.5 + T * K * wl.hidden * 4,
               "shared": 3 * wl.shared_inter * wl.hidden * 2}.get(dom)

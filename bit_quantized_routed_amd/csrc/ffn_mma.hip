@@ -164,6 +164,133 @@ __device__ __forceinline__ void mq_mma_column(const uint32_t *__restrict__ my, i
 // and write to the discard row trash_row.
 #define DM_AITEMS 576          // 512 digit vectors + 64 sum vectors per column
 
+// ------------------------------------------------------------------ dense rows
+// The shared expert's bf16 rows for up to 255 tokens, in the same launch as the
+// routed experts (work-groups appended to the grid), so the two overlap without a
+// second stream.  Work-group = (block of 4 * 16 NF rows, k-split); wave w takes
+// rows 16 NF w .. +16 NF - 1 of the block over the split's k range in steps of 32
+// on v_mfma_f32_16x16x32_bf16 (B: 16 bytes of a weight row per lane, A: 16 bytes
+// of a token row; with A2 also the token row's low bf16 plane), tokens in chunks
+// of up to 64 (MF fragments of 16).  Operands come straight from global memory,
+// two k-steps in flight (register ping-pong, unconditional clamped loads).  Token
+// rows beyond T read row T - 1 and are never stored.  Outputs are per-split
+// partial sums: row r < half -> out0[s][t][r], else out1[s][t][r - half].
+struct MqDense {
+    const uint16_t *w;       // [rows][K] bf16, row-major
+    const uint16_t *x;       // [T][K] bf16
+    const uint16_t *xlo;     // [T][K] bf16 low plane (A2) or null
+    float *out0, *out1;
+    int T, rows, K, half, nsplit, kps, out_ld, grid;
+    int64_t split_stride;
+};
+
+typedef __bf16 mq_bf16x8 __attribute__((ext_vector_type(8)));
+
+template <int NF, int MF, bool A2>
+__device__ __forceinline__ void mq_dense_chunk(const MqDense &d, int row0, int k0, int k1, int t0, int ks,
+                                               int lane) {
+    typedef const __attribute__((address_space(1))) mq_u32x4 *gvec;
+    const int r16 = lane & 15, q4 = lane >> 4;
+    gvec wp[NF], xp[MF], xl[MF];
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf)
+        wp[nf] = (gvec)(d.w + (int64_t)(row0 + 16 * nf + r16) * d.K + 8 * q4);
+#pragma unroll
+    for (int m = 0; m < MF; ++m) {
+        const int tok = min(t0 + 16 * m + r16, d.T - 1);
+        xp[m] = (gvec)(d.x + (int64_t)tok * d.K + 8 * q4);
+        xl[m] = A2 ? (gvec)(d.xlo + (int64_t)tok * d.K + 8 * q4) : xp[m];
+    }
+    mq_f32x4 acc[NF][MF];
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+        for (int m = 0; m < MF; ++m) acc[nf][m] = (mq_f32x4){0.f, 0.f, 0.f, 0.f};
+    mq_u32x4 b0[NF], b1[NF], a0[MF], a1[MF], l0[MF], l1[MF];
+    auto load = [&](mq_u32x4 (&b)[NF], mq_u32x4 (&a)[MF], mq_u32x4 (&l)[MF], int k) {
+        const int o = k >> 3;                      // 16-byte units
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) b[nf] = wp[nf][o];
+#pragma unroll
+        for (int m = 0; m < MF; ++m) {
+            a[m] = xp[m][o];
+            if (A2) l[m] = xl[m][o];
+        }
+    };
+    auto mma = [&](const mq_u32x4 (&b)[NF], const mq_u32x4 (&a)[MF], const mq_u32x4 (&l)[MF]) {
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+            for (int m = 0; m < MF; ++m) {
+                acc[nf][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mq_bf16x8, a[m]),
+                                                                     __builtin_bit_cast(mq_bf16x8, b[nf]),
+                                                                     acc[nf][m], 0, 0, 0);
+                if (A2)
+                    acc[nf][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mq_bf16x8, l[m]),
+                                                                         __builtin_bit_cast(mq_bf16x8, b[nf]),
+                                                                         acc[nf][m], 0, 0, 0);
+            }
+    };
+    // k1 - k0 is a multiple of 64: steps k (set 0) and k + 32 (set 1)
+    load(b0, a0, l0, k0);
+    load(b1, a1, l1, k0 + 32);
+    for (int k = k0; k < k1; k += 64) {
+        mma(b0, a0, l0);
+        load(b0, a0, l0, min(k + 64, k1 - 64));
+        mma(b1, a1, l1);
+        load(b1, a1, l1, min(k + 96, k1 - 32));
+    }
+    // D layout: lane l, element i -> token 4*(l/16) + i of fragment m, row 16*nf + l%16
+#pragma unroll
+    for (int m = 0; m < MF; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 16 * m + 4 * q4 + i;
+            if (t < d.T) {
+#pragma unroll
+                for (int nf = 0; nf < NF; ++nf) {
+                    const int r = row0 + 16 * nf + r16;
+                    float *o = r < d.half ? d.out0 + (int64_t)ks * d.split_stride + (int64_t)t * d.out_ld + r
+                                          : d.out1 + (int64_t)ks * d.split_stride + (int64_t)t * d.out_ld +
+                                                (r - d.half);
+                    *o = acc[nf][m][i];
+                }
+            }
+        }
+}
+
+template <int NF, bool A2>
+__device__ __forceinline__ void mq_dense_wg(const MqDense &d, int wg, int wv, int lane) {
+    const int rblocks = d.rows / (64 * NF);
+    const int rb = wg % rblocks, ks = wg / rblocks;
+    const int k0 = ks * d.kps, k1 = min(d.K, k0 + d.kps);
+    if (k0 >= k1) return;
+    const int row0 = rb * 64 * NF + wv * 16 * NF;
+    for (int t0 = 0; t0 < d.T; t0 += 64) {
+        const int nt = d.T - t0;
+        if (nt > 48)
+            mq_dense_chunk<NF, 4, A2>(d, row0, k0, k1, t0, ks, lane);
+        else if (nt > 32)
+            mq_dense_chunk<NF, 3, A2>(d, row0, k0, k1, t0, ks, lane);
+        else if (nt > 16)
+            mq_dense_chunk<NF, 2, A2>(d, row0, k0, k1, t0, ks, lane);
+        else
+            mq_dense_chunk<NF, 1, A2>(d, row0, k0, k1, t0, ks, lane);
+    }
+}
+
+// Rows per work-group of the dense path and its k-split: about 256 work-groups.
+void mq_dense_split(int rows, int K, int nf, int *nsplit, int *kps) {
+    const int rblocks = rows / (64 * nf);
+    int s = 256 / (rblocks > 0 ? rblocks : 1);
+    if (s > K / 64) s = K / 64;
+    if (s < 1) s = 1;
+    int k = (K + s - 1) / s;
+    k = (k + 63) / 64 * 64;
+    *kps = k;
+    *nsplit = (K + k - 1) / k;
+}
+
 template <bool GU>
 __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ experts, int64_t expert_bytes,
                                                 int64_t mat_off, int tiles, int kblocks, int nsplit,
@@ -173,7 +300,8 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
                                                 int trash_row, const mq_u32x4 *__restrict__ xdig,
                                                 const uint32_t *__restrict__ xsum,
                                                 const float *__restrict__ xscale, float *__restrict__ out0,
-                                                float *__restrict__ out1, int out_ld, int64_t split_stride) {
+                                                float *__restrict__ out1, int out_ld, int64_t split_stride,
+                                                int q2_grid, const MqDense dn) {
     __shared__ __attribute__((aligned(16))) mq_u32x4 sW[4][384];           // weight slices, one per wave
     __shared__ __attribute__((aligned(16))) mq_u32x4 sA[2][DM_AITEMS];     // activation operands
     __shared__ int s_row[16];
@@ -181,6 +309,14 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, q4 = lane >> 4;
+    if ((int)blockIdx.x >= q2_grid) {
+        // appended work-groups: the shared expert's dense rows
+        if (GU)
+            mq_dense_wg<4, false>(dn, (int)blockIdx.x - q2_grid, wv, lane);
+        else
+            mq_dense_wg<2, true>(dn, (int)blockIdx.x - q2_grid, wv, lane);
+        return;
+    }
     const int groups = tiles >> 2;
     const int tg = blockIdx.x % groups;
     const int rest = blockIdx.x / groups;
@@ -245,12 +381,14 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
         mq_bcol_store(sW[wv], lane, wb);
 #pragma unroll
         for (int n = 0; n < 3; ++n) sA[buf][aslot[n]] = ab[n];
-        __syncthreads();
+        // the registers are free again: the next column's loads go out before the
+        // barrier, so its latency overlaps the wait for the other waves
         if (c + 1 < c1) {
             mq_bcol_load(tb + (int64_t)(c + 1) * 336, lane, wb);
 #pragma unroll
             for (int n = 0; n < 3; ++n) ab[n] = asrc[n][(c + 1) * astep[n]];
         }
+        __syncthreads();
         mq_acol a;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -304,23 +442,45 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
                      int kblocks, const int32_t *units_hdr, const int4 *units, int max_units,
                      const int32_t *perm, int topk, int zrow, int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
-                     int64_t split_stride, hipStream_t st) {
+                     int64_t split_stride, const MqDenseSpec *dense, hipStream_t st) {
     if (tiles % 4) return MOE_Q2_EUNSUPPORTED;
     int nsplit = 1, cps = kblocks;
     mq_dec_split(max_units, tiles, kblocks, gu ? MQ_DEC_SPLIT_GU : MQ_DEC_SPLIT_D, &nsplit, &cps);
-    const int64_t grid = (int64_t)max_units * nsplit * (tiles / 4);
+    const int64_t q2_grid = (int64_t)max_units * nsplit * (tiles / 4);
+    MqDense dn = {};
+    int64_t dgrid = 0;
+    if (dense) {
+        const int nf = gu ? 4 : 2;
+        if (dense->rows % (64 * nf) || dense->K % 64 || dense->T < 1) return MOE_Q2_EUNSUPPORTED;
+        dn.w = dense->w;
+        dn.x = dense->x;
+        dn.xlo = dense->xlo;
+        dn.out0 = dense->out0;
+        dn.out1 = dense->out1;
+        dn.T = dense->T;
+        dn.rows = dense->rows;
+        dn.K = dense->K;
+        dn.half = dense->half;
+        dn.out_ld = dense->out_ld;
+        dn.split_stride = dense->split_stride;
+        mq_dense_split(dense->rows, dense->K, nf, &dn.nsplit, &dn.kps);
+        if (dn.nsplit != dense->nsplit) return MOE_Q2_EINVAL;       // workspace sized for another split
+        dgrid = (int64_t)(dense->rows / (64 * nf)) * dn.nsplit;
+        dn.grid = (int)dgrid;
+    }
+    const int64_t grid = q2_grid + dgrid;
     if (grid <= 0) return MOE_Q2_OK;
     if (grid > 0x7fffffff) return MOE_Q2_EUNSUPPORTED;
     if (gu)
         hipLaunchKernelGGL(k_q2_mma<true>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
                            expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units_hdr, units, perm, topk,
                            zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
-                           split_stride);
+                           split_stride, (int)q2_grid, dn);
     else
         hipLaunchKernelGGL(k_q2_mma<false>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
                            expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units_hdr, units, perm, topk,
                            zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
-                           split_stride);
+                           split_stride, (int)q2_grid, dn);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
@@ -339,16 +499,56 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
 // silu(sum_s gate[s][row]) * sum_s up[s][row] (splits added in order; src = gate
 // partials, src2 = up partials, split_stride apart).
 #define PD_NG 4
+// Work-groups after the zero row (SRC 2 only): the shared expert's SwiGLU, 256
+// columns of one token each, h = silu(sum_s g[s][t]) * sum_s u[s][t] (splits in
+// order, all partial loads in flight together), written as two bf16 planes
+// (hi = bf16(h), lo = bf16(h - hi)).
+struct MqSharedRows {
+    const float *g, *u;
+    int nsplit;
+    int64_t split_stride;
+    int Is;
+    uint16_t *hi, *lo;
+};
+
 template <int SRC>
 __global__ void __launch_bounds__(256) k_prep_digits(const void *__restrict__ src,
                                                      const void *__restrict__ src2, int nsplit,
                                                      int64_t split_stride, int nrows, int len,
                                                      int64_t src_ld, mq_u32x4 *__restrict__ xdig,
                                                      uint32_t *__restrict__ xsum,
-                                                     float *__restrict__ scale) {
+                                                     float *__restrict__ scale, const MqSharedRows sh) {
     __shared__ float wmax[4];
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
+    if (SRC == 2 && row > nrows) {
+        const int cb = (sh.Is + 255) / 256;
+        const int t = (row - nrows - 1) / cb;
+        const int c = ((row - nrows - 1) % cb) * 256 + tid;
+        if (c >= sh.Is) return;
+        const int64_t o = (int64_t)t * sh.Is + c;
+        float g = 0.0f, u = 0.0f;
+        for (int sp0 = 0; sp0 < sh.nsplit; sp0 += 16) {
+            float gv[16], uv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t so = min(sp0 + j, sh.nsplit - 1) * sh.split_stride + o;
+                gv[j] = sh.g[so];
+                uv[j] = sh.u[so];
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (sp0 + j < sh.nsplit) {
+                    g += gv[j];
+                    u += uv[j];
+                }
+        }
+        const float h = g / (1.0f + expf(-g)) * u;
+        const uint16_t hb = mq_f32_to_bf16(h);
+        sh.hi[o] = hb;
+        sh.lo[o] = mq_f32_to_bf16(h - mq_bf16_to_f32(hb));
+        return;
+    }
     const bool zero_row = row == nrows;
     const int G = len / 16;
     float v[PD_NG][16];
@@ -469,22 +669,29 @@ int mq_launch_prep_digits(const void *src, int src_bf16, int nrows, int len, int
     dim3 grid(nrows + 1);                        // nrows rows + the zero row
     if (src_bf16)
         hipLaunchKernelGGL(k_prep_digits<1>, grid, dim3(256), 0, st, src, nullptr, 1, (int64_t)0, nrows, len,
-                           src_ld, (mq_u32x4 *)xdig, xsum, scale);
+                           src_ld, (mq_u32x4 *)xdig, xsum, scale, MqSharedRows{});
     else
         hipLaunchKernelGGL(k_prep_digits<0>, grid, dim3(256), 0, st, src, nullptr, 1, (int64_t)0, nrows, len,
-                           src_ld, (mq_u32x4 *)xdig, xsum, scale);
+                           src_ld, (mq_u32x4 *)xdig, xsum, scale, MqSharedRows{});
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
 
 int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit, int64_t split_stride,
                                  int nrows, int len, int64_t src_ld, void *xdig, uint32_t *xsum,
-                                 float *scale, hipStream_t st) {
+                                 float *scale, const MqSharedSwiglu *shared, hipStream_t st) {
     if (nrows <= 0) return MOE_Q2_OK;
     if (len / 16 > 256 * PD_NG) return MOE_Q2_EUNSUPPORTED;
-    hipLaunchKernelGGL(k_prep_digits<2>, dim3(nrows + 1), dim3(256), 0, st, (const void *)gate,
+    MqSharedRows sh = {};
+    int extra = 0;
+    if (shared) {
+        sh = MqSharedRows{shared->g, shared->u, shared->nsplit, shared->split_stride, shared->Is, shared->hi,
+                          shared->lo};
+        extra = shared->T * ((shared->Is + 255) / 256);
+    }
+    hipLaunchKernelGGL(k_prep_digits<2>, dim3(nrows + 1 + extra), dim3(256), 0, st, (const void *)gate,
                        (const void *)up, nsplit, split_stride, nrows, len, src_ld, (mq_u32x4 *)xdig, xsum,
-                       scale);
+                       scale, sh);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

@@ -26,9 +26,10 @@ int mq_launch_q2_dec(int swiglu, const void *experts, int64_t expert_bytes, int6
                      int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                      int max_units, const int32_t *perm, int topk, const uint32_t *xq,
                      const float2 *gsum, const float *xscale, float *out, int n_cu, hipStream_t st);
+// shared: the shared expert's output as sh_nsplit partial sums sh_stride floats apart
 int mq_launch_combine(const float *y, int nsplit, int64_t split_stride, const int32_t *inv,
-                      const float *gate, const float *shared, int T, int H, int K, int accumulate, float *out,
-                      hipStream_t st);
+                      const float *gate, const float *shared, int sh_nsplit, int64_t sh_stride, int T, int H,
+                      int K, int accumulate, float *out, hipStream_t st);
 int mq_launch_split_bf16(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, hipStream_t st);
 int mq_gemm_splits(int M, int N, int K, int n_cu);
 int mq_launch_gemm_bf16(const uint16_t *A, const uint16_t *Alo, int lda, const uint16_t *B, int ldb,
@@ -38,9 +39,18 @@ int mq_launch_swiglu_partials(const float *P, int nsplit, int M, int Is, uint16_
 int mq_launch_sum_partials(const float *P, int nsplit, int64_t MN, float *out, hipStream_t st);
 int mq_launch_prep_digits(const void *src, int src_bf16, int nrows, int len, int64_t src_ld,
                           void *xdig, uint32_t *xsum, float *scale, hipStream_t st);
+// Optional shared-expert rows of the same launch: SwiGLU of the dense split partials
+// g/u [nsplit][T][Is] into two bf16 planes hi/lo [T][Is].
+struct MqSharedSwiglu {
+    const float *g, *u;
+    int nsplit;
+    int64_t split_stride;
+    int Is, T;
+    uint16_t *hi, *lo;
+};
 int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit, int64_t split_stride,
                                  int nrows, int len, int64_t src_ld, void *xdig, uint32_t *xsum,
-                                 float *scale, hipStream_t st);
+                                 float *scale, const MqSharedSwiglu *shared, hipStream_t st);
 // Decode kernel: split count along the reduction (shared by the workspace sizing).
 // Gate/up splits are summed by the intermediate preparation; the down projection
 // is not split (its partials would cost the combine more than they save).
@@ -50,11 +60,21 @@ void mq_dec_split(int max_units, int tiles, int kblocks, int max_split, int *nsp
 // zrow: index of the all-zero activation row (written by the digit preparation after
 // the real rows); trash_row: an output row that absorbs padding-token writes; outputs
 // are per-split partial sums split_stride floats apart (gu: gate -> out0, up -> out1).
+// Optional dense rows (the shared expert) appended to a decode launch: bf16 weights
+// [rows][K], bf16 activations [T][K] (+ low plane), per-split partial outputs
+// (rows below `half` -> out0, the rest -> out1, split_stride floats apart).
+struct MqDenseSpec {
+    const uint16_t *w, *x, *xlo;
+    float *out0, *out1;
+    int T, rows, K, half, out_ld, nsplit;
+    int64_t split_stride;
+};
+void mq_dense_split(int rows, int K, int nf, int *nsplit, int *kps);
 int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t mat_off, int tiles,
                      int kblocks, const int32_t *units_hdr, const int4 *units, int max_units,
                      const int32_t *perm, int topk, int zrow, int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
-                     int64_t split_stride, hipStream_t st);
+                     int64_t split_stride, const MqDenseSpec *dense, hipStream_t st);
 int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
                         int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                         int max_units, const int32_t *perm, int topk, const void *xdig,

@@ -53,6 +53,10 @@ struct Workspace {
     // routed path and, for the matrix-core decode kernels, their reduction splits
     bool prefill = false, valu = false;
     int dec_units = 0, dsplit_gu = 1, dsplit_d = 1;
+    // shared expert fused into the matrix-core decode launches (bf16 layer input)
+    bool fused = false;
+    int fsplit_gu = 1, fsplit_d = 1;
+    size_t fgu = 0, fd = 0;
 };
 
 // Upper bound on the work units of a bucketing with `tch` slots per unit.
@@ -106,7 +110,18 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     w.hs = take(c, (S + 1) * 4);
     w.y = take(c, (size_t)w.dsplit_d * (S + 1) * H * 4);
     const size_t Is = s->shared_inter;
-    if (Is) {
+    const bool in_bf16 = (s->flags & MOE_Q2_PRE_RMSNORM) || s->act_dtype == MOE_Q2_BF16;
+    w.fused = Is > 0 && !w.prefill && !w.valu && in_bf16;
+    if (w.fused) {
+        // dense partial sums of the shared expert: gate and up [split][T][Is], down [split][T][H]
+        int kps = 0;
+        mq_dense_split((int)(2 * Is), (int)H, 4, &w.fsplit_gu, &kps);
+        mq_dense_split((int)H, (int)Is, 2, &w.fsplit_d, &kps);
+        w.fgu = take(c, (size_t)w.fsplit_gu * T * 2 * Is * 4);
+        w.fd = take(c, (size_t)w.fsplit_d * T * H * 4);
+        w.shi = take(c, (size_t)T * Is * 2);
+        w.slo = take(c, (size_t)T * Is * 2);
+    } else if (Is) {
         // split-K policy fixed at 256 compute units so the size does not depend on the device
         w.split_gu = mq_gemm_splits(T, (int)(2 * Is), (int)H, 256);
         w.split_d = mq_gemm_splits(T, (int)H, (int)Is, 256);
@@ -268,17 +283,21 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         xin = xbf;
         xin_bf16 = 1;
     }
-    // Work that depends on the layer input only -- the routed experts' activation
-    // preparation and the shared expert (full-precision bf16 weights on MFMA,
-    // weight 1) -- runs as a branch concurrent with the routing (forked here; the
-    // routed experts wait for the preparation, the combine for the whole branch)
-    // unless MOE_Q2_SERIAL is set.
+    // The matrix-core decode path with a bf16 layer input runs the shared expert
+    // inside the routed launches (appended dense work-groups), all on `stream`.
+    // Otherwise the work that depends on the layer input only -- the routed
+    // experts' activation preparation and the shared expert (full-precision bf16
+    // weights on MFMA, weight 1) -- runs as a branch concurrent with the routing
+    // (forked here; the routed experts wait for the preparation, the combine for
+    // the whole branch) unless MOE_Q2_SERIAL is set.
     const bool valu = w.valu;
     float *ysh = nullptr;
+    int ysh_split = 1;
+    int64_t ysh_stride = 0;
     SideBranch *side = nullptr;
     std::unique_lock<std::mutex> side_lock;
     hipStream_t sst = st;
-    if (!(s->flags & MOE_Q2_SERIAL)) {
+    if (!(s->flags & MOE_Q2_SERIAL) && !w.fused) {
         side = side_branch();
         if (side) {
             side_lock = std::unique_lock<std::mutex>(side->mu);
@@ -303,7 +322,7 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         if (e != hipSuccess) return mq_fail_hip(e);
     }
     if ((rc = mark_on(MOE_Q2_PH_SHARED, 0, sst))) return rc;
-    if (s->shared_inter > 0) {
+    if (s->shared_inter > 0 && !w.fused) {
         const int Is = s->shared_inter;
         const uint16_t *xa = (const uint16_t *)xin, *xa_lo = nullptr;
         if (!xin_bf16) {
@@ -377,14 +396,34 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         const int S = T * K;
         const int64_t gstride = (int64_t)(S + 1) * I, ystride = (int64_t)(S + 1) * H;
         float *gp = h, *up = h + (int64_t)w.dsplit_gu * gstride;
+        MqDenseSpec dgu = {}, dd = {};
+        MqSharedSwiglu shs = {};
+        if (w.fused) {
+            // shared expert rows in the same launches; its outputs are dense partials
+            const int Is = s->shared_inter;
+            float *fg = (float *)(ws + w.fgu);
+            float *fu = fg + (int64_t)w.fsplit_gu * T * Is;
+            uint16_t *shi = (uint16_t *)(ws + w.shi), *slo = (uint16_t *)(ws + w.slo);
+            dgu = MqDenseSpec{shared_w, (const uint16_t *)xin, nullptr, fg, fu, T, 2 * Is, H, Is, Is,
+                              w.fsplit_gu, (int64_t)T * Is};
+            shs = MqSharedSwiglu{fg, fu, w.fsplit_gu, (int64_t)T * Is, Is, T, shi, slo};
+            ysh = (float *)(ws + w.fd);
+            ysh_split = w.fsplit_d;
+            ysh_stride = (int64_t)T * H;
+            dd = MqDenseSpec{shared_w + (size_t)2 * Is * H, shi, slo, ysh, ysh, T, H, Is, H, H, w.fsplit_d,
+                             ysh_stride};
+        }
         MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma(1, experts_q2, ebytes, 0, I / 32, H / MQ_QK, units_hdr,
                                                      units, w.dec_units, perm, K, T, S, xq,
-                                                     (const uint32_t *)xg, xs, gp, up, I, gstride, st));
+                                                     (const uint32_t *)xg, xs, gp, up, I, gstride,
+                                                     w.fused ? &dgu : nullptr, st));
         MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_swiglu_digits(gp, up, w.dsplit_gu, gstride, S, I, I, hq,
-                                                                (uint32_t *)hg, hsc, st));
+                                                                (uint32_t *)hg, hsc, w.fused ? &shs : nullptr,
+                                                                st));
         MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_mma(0, experts_q2, ebytes, 2 * mat_gu, H / 64, I / MQ_QK,
                                                   units_hdr, units, w.dec_units, perm, K, S, S, hq,
-                                                  (const uint32_t *)hg, hsc, y, nullptr, H, ystride, st));
+                                                  (const uint32_t *)hg, hsc, y, nullptr, H, ystride,
+                                                  w.fused ? &dd : nullptr, st));
     }
     const int ysplit = (prefill || valu) ? 1 : w.dsplit_d;
     const int64_t ystride = (int64_t)(T * K + 1) * H;
@@ -392,8 +431,8 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         const hipError_t e = hipStreamWaitEvent(st, side->join, 0);
         if (e != hipSuccess) return mq_fail_hip(e);
     }
-    MQ_PHASE(MOE_Q2_PH_COMBINE, mq_launch_combine(y, ysplit, ystride, inv, gate, ysh, T, H, K, accum ? 1 : 0,
-                                                  out, st));
+    MQ_PHASE(MOE_Q2_PH_COMBINE, mq_launch_combine(y, ysplit, ystride, inv, gate, ysh, ysh_split, ysh_stride, T,
+                                                  H, K, accum ? 1 : 0, out, st));
     if (!rms && ev) {
         if ((rc = mark(MOE_Q2_PH_RMSNORM, 0)) || (rc = mark(MOE_Q2_PH_RMSNORM, 1))) return rc;
     }
