@@ -5,6 +5,7 @@
 
 #define FD_TCH 4        // slots per work unit of the vector-ALU decode kernel
 #define MMA_TCH 16      // slots per work unit of the matrix-core decode kernel
+#define MQ_TOPK_BUCKET_MAX_T 4   // largest batch whose bucketing runs in the top-K launch
 #define PF_MF 4         // token fragments per unit of the prefill kernel
 #define PF_TCH (16 * PF_MF)
 
@@ -19,6 +20,10 @@ int mq_launch_bucket(const int32_t *idx, int T, int K, int E, int unit_tokens, i
                      int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr,
                      int4 *units, hipStream_t st);
 size_t mq_bucket_lds_bytes(int E);
+// Top-K and bucketing in one work-group (T <= MQ_TOPK_BUCKET_MAX_T).
+int mq_launch_topk_bucket(const float *logits, int nsplit, const float *bias, int T, int E, int K,
+                          int32_t *idx, float *gate, int32_t *trace_idx, float *trace_w, int unit_tokens, int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                          int32_t *units_hdr, int4 *units, hipStream_t st);
 int mq_launch_prep(const void *src, int src_bf16, int nrows, int len, int64_t src_ld, uint32_t *xq,
                    float2 *gsum, float *scale, hipStream_t st);
 int mq_launch_rmsnorm(const float *h, int T, int H, float eps, uint16_t *x, hipStream_t st);
@@ -37,6 +42,9 @@ int mq_launch_gemm_bf16(const uint16_t *A, const uint16_t *Alo, int lda, const u
 int mq_launch_swiglu_partials(const float *P, int nsplit, int M, int Is, uint16_t *hi, uint16_t *lo,
                               hipStream_t st);
 int mq_launch_sum_partials(const float *P, int nsplit, int64_t MN, float *out, hipStream_t st);
+// Router (bf16 layer input) and the layer input's activation digits in one launch.
+int mq_launch_router_prep(const uint16_t *x, const float *wr, int T, int H, int E, int nsplit, float *P,
+                          void *xdig, uint32_t *xsum, float *xscale, hipStream_t st);
 int mq_launch_prep_digits(const void *src, int src_bf16, int nrows, int len, int64_t src_ld,
                           void *xdig, uint32_t *xsum, float *scale, hipStream_t st);
 // Optional shared-expert rows of the same launch: SwiGLU of the dense split partials

@@ -310,10 +310,12 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     uint32_t *xq = (uint32_t *)(ws + w.xq);
     float2 *xg = (float2 *)(ws + w.xg);
     float *xs = (float *)(ws + w.xs);
+    // on one stream with a bf16 input, the router launch also prepares the digits
+    const bool prep_in_router = !side && !valu && xin_bf16;
     if ((rc = mark_on(MOE_Q2_PH_PREP_X, 0, sst))) return rc;
     if (valu)
         rc = mq_launch_prep(xin, xin_bf16, T, H, H, xq, xg, xs, sst);
-    else
+    else if (!prep_in_router)
         rc = mq_launch_prep_digits(xin, xin_bf16, T, H, H, xq, (uint32_t *)xg, xs, sst);
     if (rc) return rc;
     if ((rc = mark_on(MOE_Q2_PH_PREP_X, 1, sst))) return rc;
@@ -351,19 +353,32 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     // routing
     // bf16 activations: MFMA router (split-K partials); fp32 activations: vector-ALU router
     int nsplit = 1;
-    if (xin_bf16) {
+    if (xin_bf16 && prep_in_router) {
+        nsplit = w.rsplit;
+        MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router_prep((const uint16_t *)xin, router_w, T, H, E, nsplit,
+                                                         logits, xq, (uint32_t *)xg, xs, st));
+    } else if (xin_bf16) {
         nsplit = w.rsplit;
         MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router_mma((const uint16_t *)xin, router_w, T, H, E, nsplit,
                                                         logits, st));
     } else {
         MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router(xin, 0, router_w, nullptr, T, H, E, logits, st));
     }
-    MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk(logits, nsplit, router_b, T, E, K, idx, gate,
-                                            trace ? trace->topk_idx : nullptr,
-                                            trace ? trace->topk_w : nullptr, st));
+    // few tokens: the bucketing runs in the top-K launch (its phase then reads zero)
     const int tch = valu ? FD_TCH : (prefill ? PF_TCH : MMA_TCH);
-    MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket(idx, T, K, E, tch, counts, offsets, perm, inv,
-                                                units_hdr, units, st));
+    if (T <= MQ_TOPK_BUCKET_MAX_T) {
+        MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk_bucket(logits, nsplit, router_b, T, E, K, idx, gate,
+                                                       trace ? trace->topk_idx : nullptr,
+                                                       trace ? trace->topk_w : nullptr, tch, counts,
+                                                       offsets, perm, inv, units_hdr, units, st));
+        MQ_PHASE(MOE_Q2_PH_BUCKET, MOE_Q2_OK);
+    } else {
+        MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk(logits, nsplit, router_b, T, E, K, idx, gate,
+                                                trace ? trace->topk_idx : nullptr,
+                                                trace ? trace->topk_w : nullptr, st));
+        MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket(idx, T, K, E, tch, counts, offsets, perm, inv,
+                                                    units_hdr, units, st));
+    }
     if (side) {
         const hipError_t e = hipStreamWaitEvent(st, side->prep, 0);
         if (e != hipSuccess) return mq_fail_hip(e);

@@ -3,6 +3,7 @@
 // permutation, touched-expert work units).
 #include "common.h"
 #include "kernels.h"
+#include "prep_rows.h"
 
 // ---------------------------------------------------------------- logits
 // One wave per (expert, token tile of RT_TT tokens); lanes stride the hidden
@@ -79,13 +80,13 @@ __device__ __forceinline__ void mq_split3(const float (&w)[8], mq_s16x8 &hi, mq_
 // fragments per work-group (1 for up to 16 tokens, else 4).
 #define RT_KC 8
 template <int MF>
-__global__ void __launch_bounds__(256) k_router_mma(const uint16_t *__restrict__ x,
-                                                    const float *__restrict__ wr, int T, int H, int E,
-                                                    int k_per_split, float *__restrict__ P) {
+__device__ __forceinline__ void mq_router_wg(const uint16_t *__restrict__ x, const float *__restrict__ wr,
+                                             int T, int H, int E, int k_per_split, float *__restrict__ P,
+                                             int bx, int by, int bz) {
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int e0 = blockIdx.x * 64 + wv * 16, t0 = blockIdx.y * 16 * MF;
-    const int split = blockIdx.z;
+    const int e0 = bx * 64 + wv * 16, t0 = by * 16 * MF;
+    const int split = bz;
     const int k0 = split * k_per_split, k1 = min(H, k0 + k_per_split);
     const int r16 = lane & 15, q = lane >> 4;
     const int e = e0 + r16;
@@ -138,6 +139,50 @@ __global__ void __launch_bounds__(256) k_router_mma(const uint16_t *__restrict__
         }
 }
 
+template <int MF>
+__global__ void __launch_bounds__(256) k_router_mma(const uint16_t *__restrict__ x,
+                                                    const float *__restrict__ wr, int T, int H, int E,
+                                                    int k_per_split, float *__restrict__ P) {
+    mq_router_wg<MF>(x, wr, T, H, E, k_per_split, P, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// One launch for the two consumers of the bf16 layer input: the router
+// work-groups (gx * gy * gz of them, flattened) and then one work-group per row of
+// activation digits (T rows + the zero row).
+template <int MF>
+__global__ void __launch_bounds__(256) k_router_prep(const uint16_t *__restrict__ x,
+                                                     const float *__restrict__ wr, int T, int H, int E,
+                                                     int k_per_split, float *__restrict__ P, int gx, int gy,
+                                                     int gz, mq_u32x4 *__restrict__ xdig,
+                                                     uint32_t *__restrict__ xsum, float *__restrict__ xscale) {
+    const int nr = gx * gy * gz;
+    const int b = blockIdx.x;
+    if (b < nr) {
+        mq_router_wg<MF>(x, wr, T, H, E, k_per_split, P, b % gx, (b / gx) % gy, b / (gx * gy));
+    } else {
+        mq_prep_digits_wg<1>(x, nullptr, 1, 0, T, H, H, xdig, xsum, xscale, MqSharedRows{}, b - nr);
+    }
+}
+
+int mq_launch_router_prep(const uint16_t *x, const float *wr, int T, int H, int E, int nsplit, float *P,
+                          void *xdig, uint32_t *xsum, float *xscale, hipStream_t st) {
+    if (H / 16 > 256 * PD_NG) return MOE_Q2_EUNSUPPORTED;
+    int kps = (H + nsplit - 1) / nsplit;
+    kps = (kps + 31) / 32 * 32;
+    const int gx = (E + 63) / 64, gz = nsplit;
+    const int gy = T <= 16 ? 1 : (T + 63) / 64;
+    const int64_t grid = (int64_t)gx * gy * gz + T + 1;
+    if (grid > 0x7fffffff) return MOE_Q2_EUNSUPPORTED;
+    if (T <= 16)
+        hipLaunchKernelGGL(k_router_prep<1>, dim3((unsigned)grid), dim3(256), 0, st, x, wr, T, H, E, kps, P, gx,
+                           gy, gz, (mq_u32x4 *)xdig, xsum, xscale);
+    else
+        hipLaunchKernelGGL(k_router_prep<4>, dim3((unsigned)grid), dim3(256), 0, st, x, wr, T, H, E, kps, P, gx,
+                           gy, gz, (mq_u32x4 *)xdig, xsum, xscale);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}
+
 int mq_router_splits(int T, int H, int E) {
     const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
     int s = (512 + tiles - 1) / tiles;
@@ -161,9 +206,6 @@ int mq_launch_router_mma(const uint16_t *x, const float *wr, int T, int H, int E
 }
 
 // ---------------------------------------------------------------- top-K
-// One wave per token.  K rounds of a wave arg-max over the unselected logits
-// (ties: lower expert index); gates are the softmax over the selected logits,
-// which equals the full softmax renormalised over the selection.
 // One work-group per token.  Every thread adds the split-K partial logits of up to
 // two experts (fixed order) and the bias.  The selection order is value
 // descending, ties to the lower expert index; it is the order of the 64-bit keys
@@ -190,20 +232,25 @@ __device__ __forceinline__ float mq_sum_partials(const float *__restrict__ p, in
     return a;
 }
 
-__global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, int nsplit,
-                                              const float *__restrict__ bias, int T, int E, int K,
-                                              int32_t *__restrict__ idx, float *__restrict__ gate,
-                                              int32_t *__restrict__ trace_idx,
+// LDS of one token's selection
+struct MqTopkLds {
+    __attribute__((aligned(16))) uint64_t key[512];
+    float lg[512];
+    float sv[16];
+    int se[16];
+};
+
+// Token t by NT threads (thread index i); valid false: only the barriers.
+template <int NT>
+__device__ __forceinline__ void mq_topk_token(const float *__restrict__ logits, int nsplit,
+                                              const float *__restrict__ bias, int T, int E, int K, int t,
+                                              bool valid, int i, MqTopkLds &L, int32_t *__restrict__ idx,
+                                              float *__restrict__ gate, int32_t *__restrict__ trace_idx,
                                               float *__restrict__ trace_w) {
-    __shared__ __attribute__((aligned(16))) uint64_t key[512];
-    __shared__ float lg[512];
-    __shared__ float sv[16];
-    __shared__ int se[16];
-    const int t = blockIdx.x;
     const int E2 = (E + 1) & ~1;
-    for (int e = threadIdx.x; e < E2; e += 256) {
+    for (int e = i; valid && e < E2; e += NT) {
         if (e >= E) {
-            key[e] = 0;                               // below every real key
+            L.key[e] = 0;                             // below every real key
             continue;
         }
         const float *p = logits + (int64_t)t * E + e;
@@ -213,45 +260,54 @@ __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, 
         // indices are clamped so that every load is unconditional)
         const float a = (nsplit <= 8 ? mq_sum_partials<8>(p, stride, nsplit)
                                      : mq_sum_partials<64>(p, stride, nsplit)) + be;
-        lg[e] = a;
-        key[e] = ((uint64_t)mq_order_key(a) << 32) | (uint32_t)(0xFFFFu - e);
+        L.lg[e] = a;
+        L.key[e] = ((uint64_t)mq_order_key(a) << 32) | (uint32_t)(0xFFFFu - e);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) {
-        const uint64_t my = key[e];
+    for (int e = i; valid && e < E; e += NT) {
+        const uint64_t my = L.key[e];
         int r[8] = {0, 0, 0, 0, 0, 0, 0, 0};       // independent counters (short chains)
         int m = 0;
         for (; m + 16 <= E2; m += 16) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const ulonglong2 k2 = *(const ulonglong2 *)&key[m + 2 * j];
+                const ulonglong2 k2 = *(const ulonglong2 *)&L.key[m + 2 * j];
                 r[j] += (k2.x > my ? 1 : 0) + (k2.y > my ? 1 : 0);
             }
         }
-        for (; m < E2; m += 2) r[0] += (key[m] > my ? 1 : 0) + (key[m + 1] > my ? 1 : 0);
+        for (; m < E2; m += 2) r[0] += (L.key[m] > my ? 1 : 0) + (L.key[m + 1] > my ? 1 : 0);
         const int rank = ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
         if (rank < K) {
-            sv[rank] = lg[e];
-            se[rank] = e;
+            L.sv[rank] = L.lg[e];
+            L.se[rank] = e;
         }
     }
     __syncthreads();
-    const int lane = threadIdx.x;
-    if (lane < K) {
-        const float mx = sv[0];
+    if (valid && i < K) {
+        const float mx = L.sv[0];
         float z = 0.0f, mine = 0.0f;
         for (int k = 0; k < K; ++k) {
-            const float pk = expf(sv[k] - mx);
+            const float pk = expf(L.sv[k] - mx);
             z += pk;
-            if (k == lane) mine = pk;
+            if (k == i) mine = pk;
         }
-        const int me = se[lane];
+        const int me = L.se[i];
         const float g = mine / z;
-        idx[t * K + lane] = me;
-        gate[t * K + lane] = g;
-        if (trace_idx) trace_idx[t * K + lane] = me;
-        if (trace_w) trace_w[t * K + lane] = g;
+        idx[t * K + i] = me;
+        gate[t * K + i] = g;
+        if (trace_idx) trace_idx[t * K + i] = me;
+        if (trace_w) trace_w[t * K + i] = g;
     }
+}
+
+__global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, int nsplit,
+                                              const float *__restrict__ bias, int T, int E, int K,
+                                              int32_t *__restrict__ idx, float *__restrict__ gate,
+                                              int32_t *__restrict__ trace_idx,
+                                              float *__restrict__ trace_w) {
+    __shared__ MqTopkLds L;
+    mq_topk_token<256>(logits, nsplit, bias, T, E, K, blockIdx.x, true, threadIdx.x, L, idx, gate, trace_idx,
+                       trace_w);
 }
 
 // ---------------------------------------------------------------- bucketing
@@ -264,15 +320,11 @@ __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, 
 //   units[u] = (expert, first bucket position, slot count, 0), units_hdr[0] = U.
 #define BK_CH 512
 #define BK_THREADS 1024
-__global__ void __launch_bounds__(BK_THREADS) k_bucket(const int32_t *__restrict__ idx, int T, int K,
-                                                       int E, int unit_tokens,
-                                                       int32_t *__restrict__ counts_out,
-                                                       int32_t *__restrict__ offsets_out,
-                                                       int32_t *__restrict__ perm,
-                                                       int32_t *__restrict__ inv,
-                                                       int32_t *__restrict__ units_hdr,
-                                                       int4 *__restrict__ units) {
-    extern __shared__ uint32_t sm[];
+// (run by a work-group of BK_THREADS threads; sm = mq_bucket_lds_bytes(E) of LDS)
+__device__ void mq_bucket_wg(const int32_t *__restrict__ idx, int T, int K, int E, int unit_tokens,
+                             int32_t *__restrict__ counts_out, int32_t *__restrict__ offsets_out,
+                             int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+                             int32_t *__restrict__ units_hdr, int4 *__restrict__ units, uint32_t *sm) {
     const int tid = threadIdx.x;
     const int W = BK_CH / 32;                 // bitmap words per expert
     int32_t *cnt = (int32_t *)sm;             // [E]
@@ -350,8 +402,107 @@ __global__ void __launch_bounds__(BK_THREADS) k_bucket(const int32_t *__restrict
     }
 }
 
+__global__ void __launch_bounds__(BK_THREADS) k_bucket(const int32_t *__restrict__ idx, int T, int K,
+                                                       int E, int unit_tokens,
+                                                       int32_t *__restrict__ counts_out,
+                                                       int32_t *__restrict__ offsets_out,
+                                                       int32_t *__restrict__ perm,
+                                                       int32_t *__restrict__ inv,
+                                                       int32_t *__restrict__ units_hdr,
+                                                       int4 *__restrict__ units) {
+    extern __shared__ uint32_t sm[];
+    mq_bucket_wg(idx, T, K, E, unit_tokens, counts_out, offsets_out, perm, inv, units_hdr, units, sm);
+}
+
 size_t mq_bucket_lds_bytes(int E) {
     return (size_t)(4 * E + 2) * 4 + (size_t)E * (BK_CH / 32) * 4;
+}
+
+// Bucketing of a small batch whose selections sit in LDS (sidx[S], S <= 256),
+// same results as mq_bucket_wg: every expert counts its slots by a scan of sidx,
+// the offsets and unit starts are exclusive scans over the experts, and slot s
+// lands at offsets[e] + #{s' < s : sidx[s'] = e} (stable in slot order).
+__device__ __forceinline__ void mq_bucket_small_wg(const int *sidx, int S, int E, int unit_tokens,
+                                                   int32_t *__restrict__ counts_out,
+                                                   int32_t *__restrict__ offsets_out,
+                                                   int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+                                                   int32_t *__restrict__ units_hdr, int4 *__restrict__ units,
+                                                   int *soff) {
+    __shared__ int wsum[2][BK_THREADS / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int c = 0;
+    if (tid < E)
+        for (int s = 0; s < S; ++s) c += sidx[s] == tid ? 1 : 0;
+    const int nu = (c + unit_tokens - 1) / unit_tokens;
+    int a = c, b = nu;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int pa = __shfl_up(a, o, 64), pb = __shfl_up(b, o, 64);
+        if (lane >= o) { a += pa; b += pb; }
+    }
+    if (lane == 63) { wsum[0][wv] = a; wsum[1][wv] = b; }
+    __syncthreads();
+    int ba = 0, bb = 0;
+    for (int w = 0; w < wv; ++w) { ba += wsum[0][w]; bb += wsum[1][w]; }
+    const int off = ba + a - c, u0 = bb + b - nu;
+    if (tid < E) {
+        soff[tid] = off;
+        counts_out[tid] = c;
+        offsets_out[tid] = off;
+        for (int k = 0, u = u0; k < c; k += unit_tokens, ++u)
+            units[u] = make_int4(tid, off + k, min(unit_tokens, c - k), 0);
+    }
+    if (tid == BK_THREADS - 1) {
+        offsets_out[E] = ba + a;
+        units_hdr[0] = bb + b;
+    }
+    __syncthreads();
+    if (tid < S) {
+        const int e = sidx[tid];
+        int r = 0;
+        for (int s = 0; s < tid; ++s) r += sidx[s] == e ? 1 : 0;
+        const int pos = soff[e] + r;
+        perm[pos] = tid;
+        inv[tid] = pos;
+    }
+}
+
+// Top-K and bucketing in one work-group, for batches of at most TB_TOKENS
+// tokens: one group of 256 threads selects for each token, the selections stay
+// in LDS, then the whole work-group buckets them.
+#define TB_TOKENS (BK_THREADS / 256)
+__global__ void __launch_bounds__(BK_THREADS) k_topk_bucket(const float *__restrict__ logits, int nsplit,
+                                                            const float *__restrict__ bias, int T, int E,
+                                                            int K, int32_t *__restrict__ idx,
+                                                            float *__restrict__ gate,
+                                                            int32_t *__restrict__ trace_idx,
+                                                            float *__restrict__ trace_w, int unit_tokens,
+                                                            int32_t *__restrict__ counts,
+                                                            int32_t *__restrict__ offsets,
+                                                            int32_t *__restrict__ perm,
+                                                            int32_t *__restrict__ inv,
+                                                            int32_t *__restrict__ units_hdr,
+                                                            int4 *__restrict__ units) {
+    __shared__ MqTopkLds L[TB_TOKENS];
+    __shared__ int sidx[TB_TOKENS * 16];
+    __shared__ int soff[BK_THREADS];
+    const int g = threadIdx.x >> 8, i = threadIdx.x & 255;
+    mq_topk_token<256>(logits, nsplit, bias, T, E, K, g, g < T, i, L[g], idx, gate, trace_idx, trace_w);
+    if (g < T && i < K) sidx[g * K + i] = L[g].se[i];
+    __syncthreads();
+    mq_bucket_small_wg(sidx, T * K, E, unit_tokens, counts, offsets, perm, inv, units_hdr, units, soff);
+}
+
+int mq_launch_topk_bucket(const float *logits, int nsplit, const float *bias, int T, int E, int K,
+                          int32_t *idx, float *gate, int32_t *trace_idx, float *trace_w, int unit_tokens,
+                          int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr,
+                          int4 *units, hipStream_t st) {
+    if (E > BK_THREADS || T > TB_TOKENS || K > 16) return MOE_Q2_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_topk_bucket, dim3(1), dim3(BK_THREADS), 0, st, logits, nsplit,
+                       bias, T, E, K, idx, gate, trace_idx, trace_w, unit_tokens, counts, offsets, perm, inv,
+                       units_hdr, units);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
 }
 
 int mq_launch_router(const void *x, int bf16, const float *wr, const float *bias, int T, int H,

@@ -97,6 +97,30 @@ def test_decode32_zipf_layer_sampled(kernel):
     _full_check("decode32_zipf", sample=[0, 17], flags=mq.DECODE_VALU if kernel == "valu" else 0)
 
 
+@pytest.mark.parametrize("T", [2, 3, 4, 5])
+def test_small_batches(T):
+    """Batches of 2..5 tokens of the decode shape: up to 4 tokens the top-K and the
+    bucketing run as one work-group (4 tokens per selection round), from 5 on as
+    two launches.  Routing and bucketing of every token, the output of the last."""
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.WORKLOADS["decode32_zipf"]
+    dl = dw.DeviceLayer(wl)
+    hl = host_layer("decode32_zipf")
+    x = dw.activations(wl, tokens=T)
+    out, tr = _run(mq, dl, x, T)
+    xh, _ = W.activations(wl, tokens=T)
+    idx, g, logits, margin = moe.route(xh, hl.router_w, hl.router_b, wl.topk)
+    excluded, rep = check_routing(tr, {"idx": idx, "g": g, "logits": logits, "margin": margin},
+                                  wl.n_experts, wl.topk)
+    assert not excluded[T - 1]
+    ref, _ = moe.layer(xh[T - 1:T], hl.router_w, hl.router_b, hl.expert_bytes, hl.shared, wl.topk,
+                       wl.hidden, wl.inter)
+    err = rel_err(out[T - 1:T], ref)
+    print("decode32_zipf first", T, rep, "rel_err", err)
+    assert err <= TOL_DECODE
+
+
 def test_decode32_forced_prefill_kernels():
     """The prefill kernels on a decode-sized batch (PATH_PREFILL), all 32 tokens sampled
     through the oracle: covers partial token fragments and buckets of 1..18 slots."""
