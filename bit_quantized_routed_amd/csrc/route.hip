@@ -139,11 +139,67 @@ __device__ __forceinline__ void mq_router_wg(const uint16_t *__restrict__ x, con
         }
 }
 
+// Batches of at most RT_SMALL_T tokens: one work-group per expert e over the
+// whole hidden dimension (thread i takes the float4 columns i, i + 256, ...;
+// fp32 FMA of the bf16 activations, loads of 8 columns issued together), wave
+// sums, then the 4 wave sums added in wave order.  The logits are final
+// (P[t][e], one split).
+#define RT_SMALL_T 8
+__device__ __forceinline__ void mq_router_small_wg(const uint16_t *__restrict__ x,
+                                                   const float *__restrict__ wr, int T, int H, int E,
+                                                   float *__restrict__ P, int e) {
+    __shared__ float red[4][RT_SMALL_T];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int C = H >> 2;
+    const float4 *w4 = (const float4 *)(wr + (int64_t)e * H);
+    float acc[RT_SMALL_T];
+#pragma unroll
+    for (int t = 0; t < RT_SMALL_T; ++t) acc[t] = 0.0f;
+    for (int c0 = 0; c0 < C; c0 += 256 * 8) {
+        float4 w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = c0 + tid + 256 * j;
+            w[j] = c < C ? w4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int t = 0; t < RT_SMALL_T; ++t) {
+            if (t >= T) break;
+            const uint2 *x4 = (const uint2 *)(x + (int64_t)t * H);
+            uint2 b[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = c0 + tid + 256 * j;
+                b[j] = c < C ? x4[c] : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                acc[t] = fmaf(w[j].x, __uint_as_float(b[j].x << 16), acc[t]);
+                acc[t] = fmaf(w[j].y, __uint_as_float(b[j].x & 0xFFFF0000u), acc[t]);
+                acc[t] = fmaf(w[j].z, __uint_as_float(b[j].y << 16), acc[t]);
+                acc[t] = fmaf(w[j].w, __uint_as_float(b[j].y & 0xFFFF0000u), acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < RT_SMALL_T; ++t) {
+        if (t >= T) break;
+        const float v = mq_wave_sum(acc[t]);
+        if (lane == 0) red[wv][t] = v;
+    }
+    __syncthreads();
+    if (tid < T) P[(int64_t)tid * E + e] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
+// MF = 0: mq_router_small_wg, one work-group per expert
 template <int MF>
 __global__ void __launch_bounds__(256) k_router_mma(const uint16_t *__restrict__ x,
                                                     const float *__restrict__ wr, int T, int H, int E,
                                                     int k_per_split, float *__restrict__ P) {
-    mq_router_wg<MF>(x, wr, T, H, E, k_per_split, P, blockIdx.x, blockIdx.y, blockIdx.z);
+    if constexpr (MF == 0)
+        mq_router_small_wg(x, wr, T, H, E, P, blockIdx.x);
+    else
+        mq_router_wg<MF>(x, wr, T, H, E, k_per_split, P, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // One launch for the two consumers of the bf16 layer input: the router
@@ -158,7 +214,10 @@ __global__ void __launch_bounds__(256) k_router_prep(const uint16_t *__restrict_
     const int nr = gx * gy * gz;
     const int b = blockIdx.x;
     if (b < nr) {
-        mq_router_wg<MF>(x, wr, T, H, E, k_per_split, P, b % gx, (b / gx) % gy, b / (gx * gy));
+        if constexpr (MF == 0)
+            mq_router_small_wg(x, wr, T, H, E, P, b);
+        else
+            mq_router_wg<MF>(x, wr, T, H, E, k_per_split, P, b % gx, (b / gx) % gy, b / (gx * gy));
     } else {
         mq_prep_digits_wg<1>(x, nullptr, 1, 0, T, H, H, xdig, xsum, xscale, MqSharedRows{}, b - nr);
     }
@@ -169,11 +228,16 @@ int mq_launch_router_prep(const uint16_t *x, const float *wr, int T, int H, int 
     if (H / 16 > 256 * PD_NG) return MOE_Q2_EUNSUPPORTED;
     int kps = (H + nsplit - 1) / nsplit;
     kps = (kps + 31) / 32 * 32;
-    const int gx = (E + 63) / 64, gz = nsplit;
+    const bool small = T <= RT_SMALL_T;
+    if (small && nsplit != 1) return MOE_Q2_EINVAL;
+    const int gx = small ? E : (E + 63) / 64, gz = nsplit;
     const int gy = T <= 16 ? 1 : (T + 63) / 64;
     const int64_t grid = (int64_t)gx * gy * gz + T + 1;
     if (grid > 0x7fffffff) return MOE_Q2_EUNSUPPORTED;
-    if (T <= 16)
+    if (small)
+        hipLaunchKernelGGL(k_router_prep<0>, dim3((unsigned)grid), dim3(256), 0, st, x, wr, T, H, E, kps, P, gx,
+                           gy, gz, (mq_u32x4 *)xdig, xsum, xscale);
+    else if (T <= 16)
         hipLaunchKernelGGL(k_router_prep<1>, dim3((unsigned)grid), dim3(256), 0, st, x, wr, T, H, E, kps, P, gx,
                            gy, gz, (mq_u32x4 *)xdig, xsum, xscale);
     else
@@ -184,6 +248,7 @@ int mq_launch_router_prep(const uint16_t *x, const float *wr, int T, int H, int 
 }
 
 int mq_router_splits(int T, int H, int E) {
+    if (T <= RT_SMALL_T) return 1;
     const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
     int s = (512 + tiles - 1) / tiles;
     const int smax = H / 128;
@@ -195,7 +260,10 @@ int mq_launch_router_mma(const uint16_t *x, const float *wr, int T, int H, int E
                          float *P, hipStream_t st) {
     int kps = (H + nsplit - 1) / nsplit;
     kps = (kps + 31) / 32 * 32;
-    if (T <= 16)
+    if (T <= RT_SMALL_T) {
+        if (nsplit != 1) return MOE_Q2_EINVAL;
+        hipLaunchKernelGGL(k_router_mma<0>, dim3(E), dim3(256), 0, st, x, wr, T, H, E, kps, P);
+    } else if (T <= 16)
         hipLaunchKernelGGL(k_router_mma<1>, dim3((E + 63) / 64, 1, nsplit), dim3(256), 0, st, x, wr, T, H,
                            E, kps, P);
     else
@@ -210,10 +278,13 @@ int mq_launch_router_mma(const uint16_t *x, const float *wr, int T, int H, int E
 // two experts (fixed order) and the bias.  The selection order is value
 // descending, ties to the lower expert index; it is the order of the 64-bit keys
 // (order-preserving bits of the logit, then the complemented expert index), all
-// distinct, so an expert's rank is the number of larger keys: every thread counts
-// it for its experts against the whole key table in LDS, and the experts of rank
-// < K are the selection, in order.  Gates are the softmax over the selected
-// logits, which equals the full softmax renormalised over the selection.
+// distinct, so an expert's rank is the number of larger keys.  Two levels: each
+// chunk of 64 experts ranks its own keys and keeps those of rank < K as
+// candidates (every member of the overall top K is in its chunk's top K), then
+// the candidates are ranked among themselves; an expert of the overall top K has
+// the same rank there, every other candidate a rank >= K.  Gates are the softmax
+// over the selected logits, which equals the full softmax renormalised over the
+// selection.
 __device__ __forceinline__ uint32_t mq_order_key(float v) {
     const uint32_t u = __float_as_uint(v + 0.0f);    // -0 -> +0: equal floats, equal keys
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -232,13 +303,29 @@ __device__ __forceinline__ float mq_sum_partials(const float *__restrict__ p, in
     return a;
 }
 
-// LDS of one token's selection
+// LDS of one token's selection (experts padded to a multiple of 64, at most 512)
 struct MqTopkLds {
     __attribute__((aligned(16))) uint64_t key[512];
+    __attribute__((aligned(16))) uint64_t cand[8 * 16];   // [chunk][local rank < K]
     float lg[512];
     float sv[16];
     int se[16];
 };
+
+// Number of keys of key[0..n) (n even, 16-byte aligned) above `my`.
+__device__ __forceinline__ int mq_count_above(const uint64_t *key, int n, uint64_t my) {
+    int r[8] = {0, 0, 0, 0, 0, 0, 0, 0};           // independent counters (short chains)
+    int m = 0;
+    for (; m + 16 <= n; m += 16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const ulonglong2 k2 = *(const ulonglong2 *)&key[m + 2 * j];
+            r[j] += (k2.x > my ? 1 : 0) + (k2.y > my ? 1 : 0);
+        }
+    }
+    for (; m < n; m += 2) r[0] += (key[m] > my ? 1 : 0) + (key[m + 1] > my ? 1 : 0);
+    return ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
+}
 
 // Token t by NT threads (thread index i); valid false: only the barriers.
 template <int NT>
@@ -247,8 +334,11 @@ __device__ __forceinline__ void mq_topk_token(const float *__restrict__ logits, 
                                               bool valid, int i, MqTopkLds &L, int32_t *__restrict__ idx,
                                               float *__restrict__ gate, int32_t *__restrict__ trace_idx,
                                               float *__restrict__ trace_w) {
-    const int E2 = (E + 1) & ~1;
-    for (int e = i; valid && e < E2; e += NT) {
+    static_assert(NT >= 128, "one thread per candidate slot");
+    const int E64 = (E + 63) & ~63;
+    const int ncand = (E64 >> 6) * K;
+    if (valid && i < 128) L.cand[i] = 0;             // empty candidate slots
+    for (int e = i; valid && e < E64; e += NT) {
         if (e >= E) {
             L.key[e] = 0;                             // below every real key
             continue;
@@ -264,39 +354,37 @@ __device__ __forceinline__ void mq_topk_token(const float *__restrict__ logits, 
         L.key[e] = ((uint64_t)mq_order_key(a) << 32) | (uint32_t)(0xFFFFu - e);
     }
     __syncthreads();
-    for (int e = i; valid && e < E; e += NT) {
+    for (int e = i; valid && e < E; e += NT) {       // rank inside the chunk
         const uint64_t my = L.key[e];
-        int r[8] = {0, 0, 0, 0, 0, 0, 0, 0};       // independent counters (short chains)
-        int m = 0;
-        for (; m + 16 <= E2; m += 16) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const ulonglong2 k2 = *(const ulonglong2 *)&L.key[m + 2 * j];
-                r[j] += (k2.x > my ? 1 : 0) + (k2.y > my ? 1 : 0);
-            }
-        }
-        for (; m < E2; m += 2) r[0] += (L.key[m] > my ? 1 : 0) + (L.key[m + 1] > my ? 1 : 0);
-        const int rank = ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
-        if (rank < K) {
-            L.sv[rank] = L.lg[e];
-            L.se[rank] = e;
+        const int c = e >> 6;
+        const int r = mq_count_above(L.key + 64 * c, 64, my);
+        if (r < K) L.cand[c * K + r] = my;
+    }
+    __syncthreads();
+    if (valid && i < ncand) {                        // rank among the candidates
+        const uint64_t my = L.cand[i];
+        const int r = mq_count_above(L.cand, (ncand + 1) & ~1, my);
+        if (my != 0 && r < K) {
+            const int e = 0xFFFF - (int)(my & 0xFFFFu);
+            L.sv[r] = L.lg[e];
+            L.se[r] = e;
         }
     }
     __syncthreads();
-    if (valid && i < K) {
+    if (valid && i < 64) {                           // softmax over the K selected (one wave)
         const float mx = L.sv[0];
-        float z = 0.0f, mine = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            const float pk = expf(L.sv[k] - mx);
-            z += pk;
-            if (k == i) mine = pk;
+        const float pk = i < K ? expf(L.sv[i] - mx) : 0.0f;
+        float z = pk;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
+        if (i < K) {
+            const int me = L.se[i];
+            const float g = pk / z;
+            idx[t * K + i] = me;
+            gate[t * K + i] = g;
+            if (trace_idx) trace_idx[t * K + i] = me;
+            if (trace_w) trace_w[t * K + i] = g;
         }
-        const int me = L.se[i];
-        const float g = mine / z;
-        idx[t * K + i] = me;
-        gate[t * K + i] = g;
-        if (trace_idx) trace_idx[t * K + i] = me;
-        if (trace_w) trace_w[t * K + i] = g;
     }
 }
 

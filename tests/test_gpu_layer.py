@@ -97,11 +97,12 @@ def test_decode32_zipf_layer_sampled(kernel):
     _full_check("decode32_zipf", sample=[0, 17], flags=mq.DECODE_VALU if kernel == "valu" else 0)
 
 
-@pytest.mark.parametrize("T", [2, 3, 4, 5])
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 8, 9])
 def test_small_batches(T):
-    """Batches of 2..5 tokens of the decode shape: up to 4 tokens the top-K and the
-    bucketing run as one work-group (4 tokens per selection round), from 5 on as
-    two launches.  Routing and bucketing of every token, the output of the last."""
+    """Small batches of the decode shape: up to 4 tokens the top-K and the bucketing
+    run as one work-group, from 5 on as two launches; up to 8 tokens the router
+    runs one work-group per expert, from 9 on on the matrix cores with split-K.
+    Routing and bucketing of every token, the output of the last."""
     mq = need_gpu()
     from bit_quantized_routed_amd import workload as dw
     wl = W.WORKLOADS["decode32_zipf"]
