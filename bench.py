@@ -38,8 +38,8 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (2-bit experts), decode and pre
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", default="decode1")
     ap.add_argument("--extra", default="decode32_zipf,prefill2048,stack40_t64_zipf",
                     help="comma-separated extra workloads reported in the same line ('' for none)")

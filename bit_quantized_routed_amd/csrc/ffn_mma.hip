@@ -190,55 +190,85 @@ template <int NF, int MF, bool A2>
 __device__ __forceinline__ void mq_dense_chunk(const MqDense &d, int row0, int k0, int k1, int t0, int ks,
                                                int lane) {
     typedef const __attribute__((address_space(1))) mq_u32x4 *gvec;
+    typedef const __attribute__((address_space(1))) char *gbyte;
     const int r16 = lane & 15, q4 = lane >> 4;
-    gvec wp[NF], xp[MF], xl[MF];
+    // per-lane 32-bit byte offsets from uniform bases (scalar base + vector offset
+    // addressing; nothing per stage is kept in vector registers)
+    uint32_t wo[NF], xo[MF];
 #pragma unroll
-    for (int nf = 0; nf < NF; ++nf)
-        wp[nf] = (gvec)(d.w + (int64_t)(row0 + 16 * nf + r16) * d.K + 8 * q4);
+    for (int nf = 0; nf < NF; ++nf) wo[nf] = (uint32_t)(((row0 + 16 * nf + r16) * d.K + 8 * q4) * 2);
 #pragma unroll
     for (int m = 0; m < MF; ++m) {
         const int tok = min(t0 + 16 * m + r16, d.T - 1);
-        xp[m] = (gvec)(d.x + (int64_t)tok * d.K + 8 * q4);
-        xl[m] = A2 ? (gvec)(d.xlo + (int64_t)tok * d.K + 8 * q4) : xp[m];
+        xo[m] = (uint32_t)((tok * d.K + 8 * q4) * 2);
     }
     mq_f32x4 acc[NF][MF];
 #pragma unroll
     for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
         for (int m = 0; m < MF; ++m) acc[nf][m] = (mq_f32x4){0.f, 0.f, 0.f, 0.f};
-    mq_u32x4 b0[NF], b1[NF], a0[MF], a1[MF], l0[MF], l1[MF];
-    auto load = [&](mq_u32x4 (&b)[NF], mq_u32x4 (&a)[MF], mq_u32x4 (&l)[MF], int k) {
-        const int o = k >> 3;                      // 16-byte units
+    // ring of D stages of 32 k each in registers: loads run D stages ahead of the
+    // multiplies (deep enough that the weight stream is not latency-bound at one
+    // work-group per compute unit); D is what about 130 registers hold next to the
+    // accumulators, so the kernel keeps the occupancy of its routed path
+    constexpr int PER = NF + MF * (A2 ? 2 : 1);
+    constexpr int DR = (130 - 4 * NF * MF) / (4 * PER);
+    constexpr int D = DR > 8 ? 8 : (DR < 2 ? 2 : DR);
+    mq_u32x4 b[D][NF], a[D][MF], l[D][MF];
+    // an opaque copy of the weight base: the stage addresses are then formed here,
+    // not hoisted out of the token-chunk loop into registers held across it
+    const uint16_t *wbase = d.w;
+    asm volatile("" : "+s"(wbase));
+    auto load = [&](int s, int k) {
+        const gbyte wb = (gbyte)(wbase + k), xb = (gbyte)(d.x + k), lb = (gbyte)((A2 ? d.xlo : d.x) + k);
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) b[nf] = wp[nf][o];
+        for (int nf = 0; nf < NF; ++nf) b[s][nf] = *(gvec)(wb + wo[nf]);
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
-            a[m] = xp[m][o];
-            if (A2) l[m] = xl[m][o];
+            a[s][m] = *(gvec)(xb + xo[m]);
+            if (A2) l[s][m] = *(gvec)(lb + xo[m]);
         }
     };
-    auto mma = [&](const mq_u32x4 (&b)[NF], const mq_u32x4 (&a)[MF], const mq_u32x4 (&l)[MF]) {
+    auto mma = [&](int s) {
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
             for (int m = 0; m < MF; ++m) {
-                acc[nf][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mq_bf16x8, a[m]),
-                                                                     __builtin_bit_cast(mq_bf16x8, b[nf]),
+                acc[nf][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mq_bf16x8, a[s][m]),
+                                                                     __builtin_bit_cast(mq_bf16x8, b[s][nf]),
                                                                      acc[nf][m], 0, 0, 0);
                 if (A2)
-                    acc[nf][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mq_bf16x8, l[m]),
-                                                                         __builtin_bit_cast(mq_bf16x8, b[nf]),
+                    acc[nf][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mq_bf16x8, l[s][m]),
+                                                                         __builtin_bit_cast(mq_bf16x8, b[s][nf]),
                                                                          acc[nf][m], 0, 0, 0);
             }
     };
-    // k1 - k0 is a multiple of 64: steps k (set 0) and k + 32 (set 1)
-    load(b0, a0, l0, k0);
-    load(b1, a1, l1, k0 + 32);
-    for (int k = k0; k < k1; k += 64) {
-        mma(b0, a0, l0);
-        load(b0, a0, l0, min(k + 64, k1 - 64));
-        mma(b1, a1, l1);
-        load(b1, a1, l1, min(k + 96, k1 - 32));
+    // stage j covers k0 + 32 j; slot s holds stage i + s of the block starting at i.
+    // Loads past the last stage are clamped to it (in bounds; those slots are not
+    // multiplied), so every load is unconditional.
+    const int nst = (k1 - k0) >> 5;
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(s, k0 + 32 * min(s, nst - 1));
+    int i = 0;
+    for (; i + D < nst; i += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            mma(s);
+            load(s, k0 + 32 * min(i + D + s, nst - 1));
+            // keep each slot's reload after its multiply: the slot's registers are reused
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // last block: the slots past the last stage multiply a zero activation
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+        const bool live = s < nst - i;
+#pragma unroll
+        for (int m = 0; m < MF; ++m) {
+            a[s][m] = live ? a[s][m] : (mq_u32x4){0u, 0u, 0u, 0u};
+            if (A2) l[s][m] = live ? l[s][m] : (mq_u32x4){0u, 0u, 0u, 0u};
+        }
+        mma(s);
     }
     // D layout: lane l, element i -> token 4*(l/16) + i of fragment m, row 16*nf + l%16
 #pragma unroll
@@ -294,9 +324,8 @@ void mq_dense_split(int rows, int K, int nf, int *nsplit, int *kps) {
 template <bool GU>
 __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ experts, int64_t expert_bytes,
                                                 int64_t mat_off, int tiles, int kblocks, int nsplit,
-                                                int cps, const int32_t *__restrict__ units_hdr,
-                                                const int4 *__restrict__ units,
-                                                const int32_t *__restrict__ perm, int topk, int zrow,
+                                                int cps, const int4 *__restrict__ units,
+                                                const int32_t *__restrict__ urow, int zrow,
                                                 int trash_row, const mq_u32x4 *__restrict__ xdig,
                                                 const uint32_t *__restrict__ xsum,
                                                 const float *__restrict__ xscale, float *__restrict__ out0,
@@ -321,11 +350,14 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
     const int tg = blockIdx.x % groups;
     const int rest = blockIdx.x / groups;
     const int ks = rest % nsplit, u = rest / nsplit;
-    if (u >= units_hdr[0]) return;
     const int c0 = ks * cps, c1 = min(kblocks, c0 + cps);
     if (c0 >= c1) return;
+    // the unit and (gate/up) its row table are independent loads; nothing else
+    // waits on global memory before the first activation loads
     const int4 un = units[u];
+    const int urv = GU && tid < 16 ? urow[(int64_t)u * 16 + tid] : 0;
     const int e = un.x, p0 = un.y, nt = un.z;
+    if (nt == 0) return;                                 // past the last unit
     const int tile = 4 * tg + wv;
     const int G = kblocks * 16;
     const int64_t tile_bytes = (int64_t)kblocks * 64 * MQ_BLOCK_BYTES;
@@ -333,13 +365,11 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
                                             (int64_t)tile * tile_bytes);
     mq_bcol wb;
     mq_bcol_load(tb + (int64_t)c0 * 336, lane, wb);      // weights first: needs only the unit
+    float scv = 0.0f;                                    // row scale, to LDS in the loop
     if (tid < 16) {
-        const bool ok = tid < nt;
-        const int slot = p0 + (ok ? tid : 0);            // always a valid slot: nt >= 1
-        int ar = GU ? perm[slot] / topk : slot;
-        ar = ok ? ar : zrow;
+        const int ar = tid < nt ? (GU ? urv : p0 + tid) : zrow;
         s_row[tid] = ar;
-        s_sc[tid] = xscale[ar];
+        scv = xscale[ar];
     }
     __syncthreads();
     // this thread's three activation items, one per LDS slot so that a wave's
@@ -378,6 +408,7 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
     const uint32_t *myd = (const uint32_t *)sW[wv];
     int buf = 0;
     for (int c = c0; c < c1; ++c) {
+        if (tid < 16) s_sc[tid] = scv;
         mq_bcol_store(sW[wv], lane, wb);
 #pragma unroll
         for (int n = 0; n < 3; ++n) sA[buf][aslot[n]] = ab[n];
@@ -439,11 +470,12 @@ void mq_dec_split(int max_units, int tiles, int kblocks, int max_split, int *nsp
 }
 
 int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t mat_off, int tiles,
-                     int kblocks, const int32_t *units_hdr, const int4 *units, int max_units,
-                     const int32_t *perm, int topk, int zrow, int trash_row, const void *xdig,
+                     int kblocks, const int4 *units, int max_units, const int32_t *urow, int zrow,
+                     int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
                      int64_t split_stride, const MqDenseSpec *dense, hipStream_t st) {
     if (tiles % 4) return MOE_Q2_EUNSUPPORTED;
+    if (gu && !urow) return MOE_Q2_EINVAL;
     int nsplit = 1, cps = kblocks;
     mq_dec_split(max_units, tiles, kblocks, gu ? MQ_DEC_SPLIT_GU : MQ_DEC_SPLIT_D, &nsplit, &cps);
     const int64_t q2_grid = (int64_t)max_units * nsplit * (tiles / 4);
@@ -473,13 +505,13 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
     if (grid > 0x7fffffff) return MOE_Q2_EUNSUPPORTED;
     if (gu)
         hipLaunchKernelGGL(k_q2_mma<true>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
-                           expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units_hdr, units, perm, topk,
-                           zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
+                           expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units, urow, zrow,
+                           trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
                            split_stride, (int)q2_grid, dn);
     else
         hipLaunchKernelGGL(k_q2_mma<false>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
-                           expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units_hdr, units, perm, topk,
-                           zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
+                           expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units, urow, zrow,
+                           trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
                            split_stride, (int)q2_grid, dn);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;

@@ -18,12 +18,13 @@ int mq_launch_router_mma(const uint16_t *x, const float *wr, int T, int H, int E
                          float *P, hipStream_t st);
 int mq_launch_bucket(const int32_t *idx, int T, int K, int E, int unit_tokens, int32_t *counts,
                      int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr,
-                     int4 *units, hipStream_t st);
+                     int4 *units, int fill_units, int32_t *urow, int zrow, hipStream_t st);
 size_t mq_bucket_lds_bytes(int E);
 // Top-K and bucketing in one work-group (T <= MQ_TOPK_BUCKET_MAX_T).
 int mq_launch_topk_bucket(const float *logits, int nsplit, const float *bias, int T, int E, int K,
-                          int32_t *idx, float *gate, int32_t *trace_idx, float *trace_w, int unit_tokens, int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
-                          int32_t *units_hdr, int4 *units, hipStream_t st);
+                          int32_t *idx, float *gate, int32_t *trace_idx, float *trace_w, int unit_tokens,
+                          int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr,
+                          int4 *units, int fill_units, int32_t *urow, int zrow, hipStream_t st);
 int mq_launch_prep(const void *src, int src_bf16, int nrows, int len, int64_t src_ld, uint32_t *xq,
                    float2 *gsum, float *scale, hipStream_t st);
 int mq_launch_rmsnorm(const float *h, int T, int H, float eps, uint16_t *x, hipStream_t st);
@@ -78,9 +79,11 @@ struct MqDenseSpec {
     int64_t split_stride;
 };
 void mq_dense_split(int rows, int K, int nf, int *nsplit, int *kps);
+// units: max_units records, those past the last unit with slot count 0; urow (gate/up):
+// the [max_units][16] row table of the bucketing; down reads the rows of its slots.
 int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t mat_off, int tiles,
-                     int kblocks, const int32_t *units_hdr, const int4 *units, int max_units,
-                     const int32_t *perm, int topk, int zrow, int trash_row, const void *xdig,
+                     int kblocks, const int4 *units, int max_units, const int32_t *urow, int zrow,
+                     int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
                      int64_t split_stride, const MqDenseSpec *dense, hipStream_t st);
 int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,

@@ -47,7 +47,7 @@ extern "C" size_t moe_q2_expert_bytes(const moe_q2_shape *s) {
 namespace {
 struct Workspace {
     size_t total = 0;
-    size_t logits, idx, gate, counts, offsets, perm, inv, units_hdr, units, xbf, xq, xg, xs, h,
+    size_t logits, idx, gate, counts, offsets, perm, inv, units_hdr, units, urow = 0, xbf, xq, xg, xs, h,
         hq, hg, hs, y, xlo, sp, shi, slo, ysh;
     int max_units = 0, split_gu = 1, split_d = 1, rsplit = 1;
     // routed path and, for the matrix-core decode kernels, their reduction splits
@@ -96,6 +96,7 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     w.inv = take(c, S * 4);
     w.units_hdr = take(c, 16);
     w.units = take(c, (size_t)w.max_units * 16);
+    if (w.dec_units) w.urow = take(c, (size_t)w.dec_units * MMA_TCH * 4);   // row table of the units
     // activation buffers hold one extra row: the all-zero row that padding tokens
     // of the decode kernels read; h and y one extra row that absorbs their writes
     w.xbf = take(c, (size_t)T * H * 2);
@@ -273,6 +274,10 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     int32_t *inv = (int32_t *)(ws + w.inv);
     int32_t *units_hdr = (int32_t *)(ws + w.units_hdr);
     int4 *units = (int4 *)(ws + w.units);
+    // matrix-core decode: unit records padded to the grid's unit count, row table
+    const bool dec_mma = w.dec_units > 0;
+    int32_t *urow = dec_mma ? (int32_t *)(ws + w.urow) : nullptr;
+    const int fill_units = dec_mma ? w.dec_units : 0;
 
     // layer input
     const void *xin = x;
@@ -370,14 +375,15 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk_bucket(logits, nsplit, router_b, T, E, K, idx, gate,
                                                        trace ? trace->topk_idx : nullptr,
                                                        trace ? trace->topk_w : nullptr, tch, counts,
-                                                       offsets, perm, inv, units_hdr, units, st));
+                                                       offsets, perm, inv, units_hdr, units, fill_units,
+                                                       urow, T, st));
         MQ_PHASE(MOE_Q2_PH_BUCKET, MOE_Q2_OK);
     } else {
         MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk(logits, nsplit, router_b, T, E, K, idx, gate,
                                                 trace ? trace->topk_idx : nullptr,
                                                 trace ? trace->topk_w : nullptr, st));
         MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket(idx, T, K, E, tch, counts, offsets, perm, inv,
-                                                    units_hdr, units, st));
+                                                    units_hdr, units, fill_units, urow, T, st));
     }
     if (side) {
         const hipError_t e = hipStreamWaitEvent(st, side->prep, 0);
@@ -428,15 +434,15 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
             dd = MqDenseSpec{shared_w + (size_t)2 * Is * H, shi, slo, ysh, ysh, T, H, Is, H, H, w.fsplit_d,
                              ysh_stride};
         }
-        MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma(1, experts_q2, ebytes, 0, I / 32, H / MQ_QK, units_hdr,
-                                                     units, w.dec_units, perm, K, T, S, xq,
+        MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma(1, experts_q2, ebytes, 0, I / 32, H / MQ_QK, units,
+                                                     w.dec_units, urow, T, S, xq,
                                                      (const uint32_t *)xg, xs, gp, up, I, gstride,
                                                      w.fused ? &dgu : nullptr, st));
         MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_swiglu_digits(gp, up, w.dsplit_gu, gstride, S, I, I, hq,
                                                                 (uint32_t *)hg, hsc, w.fused ? &shs : nullptr,
                                                                 st));
         MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_mma(0, experts_q2, ebytes, 2 * mat_gu, H / 64, I / MQ_QK,
-                                                  units_hdr, units, w.dec_units, perm, K, S, S, hq,
+                                                  units, w.dec_units, nullptr, S, S, hq,
                                                   (const uint32_t *)hg, hsc, y, nullptr, H, ystride,
                                                   w.fused ? &dd : nullptr, st));
     }

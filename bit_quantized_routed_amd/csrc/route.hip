@@ -405,14 +405,18 @@ __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, 
 // read from a per-expert token bitmap (bits set with atomic OR, so the result
 // does not depend on thread order).  Tokens are processed in chunks of BK_CH.
 // Also emits the touched experts as work units of at most `unit_tokens` slots:
-//   units[u] = (expert, first bucket position, slot count, 0), units_hdr[0] = U.
+//   units[u] = (expert, first bucket position, slot count, 0), units_hdr[0] = U,
+// records U .. fill_units - 1 all zero (slot count 0: no unit), and, when urow is
+// given, the row table urow[u][i] = token of the unit's slot i (zrow past the
+// slot count), so that a consumer finds its rows with one load indexed by u.
 #define BK_CH 512
 #define BK_THREADS 1024
 // (run by a work-group of BK_THREADS threads; sm = mq_bucket_lds_bytes(E) of LDS)
 __device__ void mq_bucket_wg(const int32_t *__restrict__ idx, int T, int K, int E, int unit_tokens,
                              int32_t *__restrict__ counts_out, int32_t *__restrict__ offsets_out,
                              int32_t *__restrict__ perm, int32_t *__restrict__ inv,
-                             int32_t *__restrict__ units_hdr, int4 *__restrict__ units, uint32_t *sm) {
+                             int32_t *__restrict__ units_hdr, int4 *__restrict__ units, int fill_units,
+                             int32_t *__restrict__ urow, int zrow, uint32_t *sm) {
     const int tid = threadIdx.x;
     const int W = BK_CH / 32;                 // bitmap words per expert
     int32_t *cnt = (int32_t *)sm;             // [E]
@@ -455,9 +459,13 @@ __device__ void mq_bucket_wg(const int32_t *__restrict__ idx, int T, int K, int 
         counts_out[e] = cnt[e];
         offsets_out[e] = off[e];
         const int n = cnt[e];
-        for (int c = 0, u = scan[e]; c < n; c += unit_tokens, ++u)
+        for (int c = 0, u = scan[e]; c < n; c += unit_tokens, ++u) {
             units[u] = make_int4(e, off[e] + c, min(unit_tokens, n - c), 0);
+            if (urow)
+                for (int i = n - c; i < unit_tokens; ++i) urow[(int64_t)u * unit_tokens + i] = zrow;
+        }
     }
+    for (int u = scan[E] + tid; u < fill_units; u += BK_THREADS) units[u] = make_int4(0, 0, 0, 0);
     if (tid == 0) offsets_out[E] = off[E];
 
     for (int t0 = 0; t0 < T; t0 += BK_CH) {
@@ -479,6 +487,10 @@ __device__ void mq_bucket_wg(const int32_t *__restrict__ idx, int T, int K, int 
             const int pos = off[e] + run[e] + r;
             perm[pos] = s;
             inv[s] = pos;
+            if (urow) {
+                const int local = run[e] + r;
+                urow[(int64_t)(scan[e] + local / unit_tokens) * unit_tokens + local % unit_tokens] = s / K;
+            }
         }
         __syncthreads();
         for (int e = tid; e < E; e += BK_THREADS) {
@@ -497,9 +509,11 @@ __global__ void __launch_bounds__(BK_THREADS) k_bucket(const int32_t *__restrict
                                                        int32_t *__restrict__ perm,
                                                        int32_t *__restrict__ inv,
                                                        int32_t *__restrict__ units_hdr,
-                                                       int4 *__restrict__ units) {
+                                                       int4 *__restrict__ units, int fill_units,
+                                                       int32_t *__restrict__ urow, int zrow) {
     extern __shared__ uint32_t sm[];
-    mq_bucket_wg(idx, T, K, E, unit_tokens, counts_out, offsets_out, perm, inv, units_hdr, units, sm);
+    mq_bucket_wg(idx, T, K, E, unit_tokens, counts_out, offsets_out, perm, inv, units_hdr, units, fill_units,
+                 urow, zrow, sm);
 }
 
 size_t mq_bucket_lds_bytes(int E) {
@@ -515,7 +529,8 @@ __device__ __forceinline__ void mq_bucket_small_wg(const int *sidx, int S, int E
                                                    int32_t *__restrict__ offsets_out,
                                                    int32_t *__restrict__ perm, int32_t *__restrict__ inv,
                                                    int32_t *__restrict__ units_hdr, int4 *__restrict__ units,
-                                                   int *soff) {
+                                                   int fill_units, int32_t *__restrict__ urow, int K, int zrow,
+                                                   int *soff, int *sun) {
     __shared__ int wsum[2][BK_THREADS / 64];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int c = 0;
@@ -535,15 +550,22 @@ __device__ __forceinline__ void mq_bucket_small_wg(const int *sidx, int S, int E
     const int off = ba + a - c, u0 = bb + b - nu;
     if (tid < E) {
         soff[tid] = off;
+        sun[tid] = u0;
         counts_out[tid] = c;
         offsets_out[tid] = off;
-        for (int k = 0, u = u0; k < c; k += unit_tokens, ++u)
+        for (int k = 0, u = u0; k < c; k += unit_tokens, ++u) {
             units[u] = make_int4(tid, off + k, min(unit_tokens, c - k), 0);
+            if (urow)
+                for (int i = c - k; i < unit_tokens; ++i) urow[(int64_t)u * unit_tokens + i] = zrow;
+        }
     }
     if (tid == BK_THREADS - 1) {
         offsets_out[E] = ba + a;
         units_hdr[0] = bb + b;
     }
+    int U = 0;
+    for (int w = 0; w < BK_THREADS / 64; ++w) U += wsum[1][w];
+    for (int u = U + tid; u < fill_units; u += BK_THREADS) units[u] = make_int4(0, 0, 0, 0);
     __syncthreads();
     if (tid < S) {
         const int e = sidx[tid];
@@ -552,6 +574,7 @@ __device__ __forceinline__ void mq_bucket_small_wg(const int *sidx, int S, int E
         const int pos = soff[e] + r;
         perm[pos] = tid;
         inv[tid] = pos;
+        if (urow) urow[(int64_t)(sun[e] + r / unit_tokens) * unit_tokens + r % unit_tokens] = tid / K;
     }
 }
 
@@ -570,25 +593,27 @@ __global__ void __launch_bounds__(BK_THREADS) k_topk_bucket(const float *__restr
                                                             int32_t *__restrict__ perm,
                                                             int32_t *__restrict__ inv,
                                                             int32_t *__restrict__ units_hdr,
-                                                            int4 *__restrict__ units) {
+                                                            int4 *__restrict__ units, int fill_units,
+                                                            int32_t *__restrict__ urow, int zrow) {
     __shared__ MqTopkLds L[TB_TOKENS];
     __shared__ int sidx[TB_TOKENS * 16];
-    __shared__ int soff[BK_THREADS];
+    __shared__ int soff[BK_THREADS], sun[BK_THREADS];
     const int g = threadIdx.x >> 8, i = threadIdx.x & 255;
     mq_topk_token<256>(logits, nsplit, bias, T, E, K, g, g < T, i, L[g], idx, gate, trace_idx, trace_w);
     if (g < T && i < K) sidx[g * K + i] = L[g].se[i];
     __syncthreads();
-    mq_bucket_small_wg(sidx, T * K, E, unit_tokens, counts, offsets, perm, inv, units_hdr, units, soff);
+    mq_bucket_small_wg(sidx, T * K, E, unit_tokens, counts, offsets, perm, inv, units_hdr, units, fill_units,
+                       urow, K, zrow, soff, sun);
 }
 
 int mq_launch_topk_bucket(const float *logits, int nsplit, const float *bias, int T, int E, int K,
                           int32_t *idx, float *gate, int32_t *trace_idx, float *trace_w, int unit_tokens,
                           int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr,
-                          int4 *units, hipStream_t st) {
+                          int4 *units, int fill_units, int32_t *urow, int zrow, hipStream_t st) {
     if (E > BK_THREADS || T > TB_TOKENS || K > 16) return MOE_Q2_EUNSUPPORTED;
     hipLaunchKernelGGL(k_topk_bucket, dim3(1), dim3(BK_THREADS), 0, st, logits, nsplit,
                        bias, T, E, K, idx, gate, trace_idx, trace_w, unit_tokens, counts, offsets, perm, inv,
-                       units_hdr, units);
+                       units_hdr, units, fill_units, urow, zrow);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
@@ -614,10 +639,10 @@ int mq_launch_topk(const float *logits, int nsplit, const float *bias, int T, in
 
 int mq_launch_bucket(const int32_t *idx, int T, int K, int E, int unit_tokens, int32_t *counts,
                      int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr,
-                     int4 *units, hipStream_t st) {
+                     int4 *units, int fill_units, int32_t *urow, int zrow, hipStream_t st) {
     const size_t lds = mq_bucket_lds_bytes(E);
     hipLaunchKernelGGL(k_bucket, dim3(1), dim3(BK_THREADS), lds, st, idx, T, K, E, unit_tokens,
-                       counts, offsets, perm, inv, units_hdr, units);
+                       counts, offsets, perm, inv, units_hdr, units, fill_units, urow, zrow);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
