@@ -57,21 +57,22 @@ __device__ __forceinline__ void mq_st6(mq_u32x4 *__restrict__ dst, int n16, int 
 }
 
 // q*sc for the 16 weights of one group: dword s holds weights s, s+4, s+8, s+12.
-// sc2 = sc in both 16-bit halves; every byte product is at most 3 * 15, so one
-// packed 16-bit multiply scales four bytes without carries.
+// Every byte product is at most 3 * 15, so one packed 16-bit multiply (the scale
+// broadcast to both halves by the operand select) scales four bytes without carries.
 typedef uint16_t mq_u16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ int32_t mq_mul_bytes(uint32_t x, uint32_t sc2) {
-    return __builtin_bit_cast(int32_t, __builtin_bit_cast(mq_u16x2, x) * __builtin_bit_cast(mq_u16x2, sc2));
+__device__ __forceinline__ int32_t mq_mul_bytes(uint32_t x, uint16_t sc) {
+    // both 16-bit halves times the same scalar (a broadcast operand, no splat op)
+    return __builtin_bit_cast(int32_t, __builtin_bit_cast(mq_u16x2, x) * (mq_u16x2){sc, sc});
 }
 
 __device__ __forceinline__ mq_i32x4 mq_codes_x_scale(uint32_t cw, uint32_t sc) {
-    const uint32_t sc2 = sc * 0x00010001u;
+    const uint16_t s = (uint16_t)sc;
     mq_i32x4 b;
-    b[0] = mq_mul_bytes(cw & 0x03030303u, sc2);
-    b[1] = mq_mul_bytes((cw >> 2) & 0x03030303u, sc2);
-    b[2] = mq_mul_bytes((cw >> 4) & 0x03030303u, sc2);
-    b[3] = mq_mul_bytes((cw >> 6) & 0x03030303u, sc2);
+    b[0] = mq_mul_bytes(cw & 0x03030303u, s);
+    b[1] = mq_mul_bytes((cw >> 2) & 0x03030303u, s);
+    b[2] = mq_mul_bytes((cw >> 4) & 0x03030303u, s);
+    b[3] = mq_mul_bytes((cw >> 6) & 0x03030303u, s);
     return b;
 }
 
@@ -125,7 +126,7 @@ __device__ __forceinline__ void mq_mma_column(const uint32_t *__restrict__ my, i
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const uint32_t cw = blk[4 + 4 * kk + q4];
-            const uint32_t sc = (blk[kk] >> (8 * q4)) & 0xFu;
+            const uint32_t sc = __builtin_amdgcn_ubfe(blk[kk], 8 * q4, 4);
             const mq_i32x4 b = mq_codes_x_scale(cw, sc);
             ih = __builtin_amdgcn_mfma_i32_16x16x64_i8(a.hi[kk], b, ih, 0, 0, 0);
             il = __builtin_amdgcn_mfma_i32_16x16x64_i8(a.lo[kk], b, il, 0, 0, 0);
@@ -666,8 +667,8 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int g = 4 * kk + q4;
-                const mq_i32x4 b0 = mq_codes_x_scale(blk0[4 + g], (blk0[kk] >> (8 * q4)) & 0xFu);
-                const mq_i32x4 b1 = mq_codes_x_scale(blk1[4 + g], (blk1[kk] >> (8 * q4)) & 0xFu);
+                const mq_i32x4 b0 = mq_codes_x_scale(blk0[4 + g], __builtin_amdgcn_ubfe(blk0[kk], 8 * q4, 4));
+                const mq_i32x4 b1 = mq_codes_x_scale(blk1[4 + g], __builtin_amdgcn_ubfe(blk1[kk], 8 * q4, 4));
 #pragma unroll
                 for (int m = 0; m < MF; ++m) {
                     if (16 * m < nt) {
