@@ -22,6 +22,7 @@
 // how they tile tokens and stage operands; both are described at their
 // definitions below.
 #include "common.h"
+#include <type_traits>
 #include "kernels.h"
 
 typedef int32_t mq_i32x4 __attribute__((ext_vector_type(4)));
@@ -592,8 +593,10 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                                                    float *__restrict__ out) {
     constexpr int NTOK = 16 * MF;
     constexpr int NPB = (4 * 336 + 511) / 512;          // weight pieces per thread
-    constexpr int NPA = (NTOK * 36 + 511) / 512;        // activation pieces per thread
-    __shared__ __attribute__((aligned(16))) uint32_t sB[4 * 64 * MQ_BLOCK_DWORDS];
+    constexpr int NPD = NTOK * 32 / 512;                // digit pieces per thread
+    static_assert(NTOK * 32 % 512 == 0 && NTOK * 4 <= 512, "piece split");
+    // sB is padded to whole pieces so that no store is predicated
+    __shared__ __attribute__((aligned(16))) uint32_t sB[4 * NPB * 512];
     __shared__ __attribute__((aligned(16))) uint32_t sA[NTOK * PF_TS];
     __shared__ int arow_s[NTOK];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -606,18 +609,26 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     const int U = units_hdr[0];
     const int G = kblocks * 16;
     const int64_t tile_bytes = (int64_t)kblocks * 64 * MQ_BLOCK_BYTES;
+    const mq_i32x4 zi = {0, 0, 0, 0};
 
     for (int wu = blockIdx.x; wu < U * stiles; wu += gridDim.x) {
         const int u = wu / stiles, st = wu - u * stiles;
         const int4 un = units[u];
         const int e = un.x, p0 = un.y, nt = un.z;
         __syncthreads();
-        for (int i = tid; i < NTOK; i += 512)
-            arow_s[i] = i < nt ? (SWIGLU ? perm[p0 + i] / topk : p0 + i) : -1;
+        // token rows of the unit; slots past nt repeat the last token (their sums are
+        // computed and never stored)
+        for (int i = tid; i < NTOK; i += 512) {
+            const int slot = p0 + min(i, nt - 1);
+            arow_s[i] = SWIGLU ? perm[slot] / topk : slot;
+        }
         __syncthreads();
         const uint8_t *tb = experts + (int64_t)e * expert_bytes + mat_off + (int64_t)(4 * st) * tile_bytes;
-        const int nA = nt * 36;
-        mq_u32x4 pb[NPB], pa[NPA];
+        // this thread's activation rows: digit pieces j = tid + 512 n (token j / 32, 16-byte
+        // word j % 32), sum piece tid (token tid / 4, word tid % 4) for tid < NTOK * 4
+        const int srow = arow_s[min(tid >> 2, NTOK - 1)];
+        const bool has_sum = tid < NTOK * 4;             // whole waves
+        mq_u32x4 pb[NPB], pd[NPD], ps;
         auto load = [&](int b) {
 #pragma unroll
             for (int n = 0; n < NPB; ++n) {
@@ -626,76 +637,63 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                 pb[n] = *(const mq_u32x4 *)(tb + (int64_t)tl * tile_bytes + (int64_t)b * 5376 + w * 16);
             }
 #pragma unroll
-            for (int n = 0; n < NPA; ++n) {
-                const int j = min(tid + 512 * n, max(nA, 1) - 1);
-                const int i = j / 36, w = j - i * 36;
-                const int ar = max(arow_s[i], 0);
-                if (w < 32)
-                    pa[n] = xdig[((int64_t)ar * G + 16 * b) * 2 + w];
-                else
-                    pa[n] = *(const mq_u32x4 *)(xsum + ((int64_t)ar * kblocks + b) * 16 + (w - 32) * 4);
-            }
+            for (int n = 0; n < NPD; ++n)
+                pd[n] = xdig[((int64_t)arow_s[(tid + 512 * n) >> 5] * G + 16 * b) * 2 + ((tid + 512 * n) & 31)];
+            ps = *(const mq_u32x4 *)(xsum + ((int64_t)srow * kblocks + b) * 16 + (tid & 3) * 4);
         };
-        mq_f32x4 tot[MF][2];
+        // MFC token fragments carry tokens (the rest of MF are skipped): one copy of the
+        // column loop per count, so no fragment test sits in the loop
+        auto run = [&](auto mfc_tag) {
+            constexpr int MFC = decltype(mfc_tag)::value;
+            mq_f32x4 tot[MFC][2];
 #pragma unroll
-        for (int m = 0; m < MF; ++m) { tot[m][0] = (mq_f32x4){0.f, 0.f, 0.f, 0.f}; tot[m][1] = tot[m][0]; }
-        load(0);
-        for (int b = 0; b < kblocks; ++b) {
-            __syncthreads();
+            for (int m = 0; m < MFC; ++m) { tot[m][0] = (mq_f32x4){0.f, 0.f, 0.f, 0.f}; tot[m][1] = tot[m][0]; }
+            load(0);
+            for (int b = 0; b < kblocks; ++b) {
+                __syncthreads();
 #pragma unroll
-            for (int n = 0; n < NPB; ++n) {
-                const int j = tid + 512 * n;
-                if (j < 4 * 336) *(mq_u32x4 *)(sB + 4 * j) = pb[n];
-            }
+                for (int n = 0; n < NPB; ++n) *(mq_u32x4 *)(sB + 4 * (tid + 512 * n)) = pb[n];
 #pragma unroll
-            for (int n = 0; n < NPA; ++n) {
-                const int j = tid + 512 * n;
-                if (j < nA) {
-                    const int i = j / 36, w = j - i * 36;
-                    *(mq_u32x4 *)(sA + i * PF_TS + 4 * w) = pa[n];
+                for (int n = 0; n < NPD; ++n) {
+                    const int j = tid + 512 * n;
+                    *(mq_u32x4 *)(sA + (j >> 5) * PF_TS + 4 * (j & 31)) = pd[n];
                 }
-            }
-            __syncthreads();
-            if (b + 1 < kblocks) load(b + 1);
-            const uint32_t *blk0 = sB + (tw * 64 + nslot0 + r16) * MQ_BLOCK_DWORDS;
-            const uint32_t *blk1 = sB + (tw * 64 + nslot1 + r16) * MQ_BLOCK_DWORDS;
-            mq_i32x4 hi[MF][2], lo[MF][2];
+                if (has_sum) *(mq_u32x4 *)(sA + (tid >> 2) * PF_TS + 128 + 4 * (tid & 3)) = ps;
+                __syncthreads();
+                if (b + 1 < kblocks) load(b + 1);
+                const uint32_t *blk0 = sB + (tw * 64 + nslot0 + r16) * MQ_BLOCK_DWORDS;
+                const uint32_t *blk1 = sB + (tw * 64 + nslot1 + r16) * MQ_BLOCK_DWORDS;
+                mq_i32x4 hi[MFC][2], lo[MFC][2];
 #pragma unroll
-            for (int m = 0; m < MF; ++m)
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int g = 4 * kk + q4;
+                    const mq_i32x4 b0 = mq_codes_x_scale(blk0[4 + g], __builtin_amdgcn_ubfe(blk0[kk], 8 * q4, 4));
+                    const mq_i32x4 b1 = mq_codes_x_scale(blk1[4 + g], __builtin_amdgcn_ubfe(blk1[kk], 8 * q4, 4));
 #pragma unroll
-                for (int f = 0; f < 2; ++f) { hi[m][f] = (mq_i32x4){0, 0, 0, 0}; lo[m][f] = hi[m][f]; }
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int g = 4 * kk + q4;
-                const mq_i32x4 b0 = mq_codes_x_scale(blk0[4 + g], __builtin_amdgcn_ubfe(blk0[kk], 8 * q4, 4));
-                const mq_i32x4 b1 = mq_codes_x_scale(blk1[4 + g], __builtin_amdgcn_ubfe(blk1[kk], 8 * q4, 4));
-#pragma unroll
-                for (int m = 0; m < MF; ++m) {
-                    if (16 * m < nt) {
+                    for (int m = 0; m < MFC; ++m) {
                         const uint32_t *ap = sA + (16 * m + r16) * PF_TS + 8 * g;
                         const mq_i32x4 ah = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)ap);
                         const mq_i32x4 al = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(ap + 4));
-                        hi[m][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b0, hi[m][0], 0, 0, 0);
-                        lo[m][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b0, lo[m][0], 0, 0, 0);
-                        hi[m][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b1, hi[m][1], 0, 0, 0);
-                        lo[m][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b1, lo[m][1], 0, 0, 0);
+                        // the first step of each chain starts from zero (no accumulator to clear)
+                        hi[m][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b0, kk ? hi[m][0] : zi, 0, 0, 0);
+                        lo[m][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b0, kk ? lo[m][0] : zi, 0, 0, 0);
+                        hi[m][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b1, kk ? hi[m][1] : zi, 0, 0, 0);
+                        lo[m][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b1, kk ? lo[m][1] : zi, 0, 0, 0);
                     }
                 }
-            }
-            const mq_s16x4 bm0 = mq_mins_bf16(blk0[q4]), bm1 = mq_mins_bf16(blk1[q4]);
-            const uint32_t dd0 = blk0[20], dd1 = blk1[20];
-            const float d0 = mq_h2f((uint16_t)(dd0 & 0xFFFFu)), m0 = mq_h2f((uint16_t)(dd0 >> 16));
-            const float d1 = mq_h2f((uint16_t)(dd1 & 0xFFFFu)), m1 = mq_h2f((uint16_t)(dd1 >> 16));
+                const mq_s16x4 bm0 = mq_mins_bf16(blk0[q4]), bm1 = mq_mins_bf16(blk1[q4]);
+                const uint32_t dd0 = blk0[20], dd1 = blk1[20];
+                const float d0 = mq_h2f((uint16_t)(dd0 & 0xFFFFu)), m0 = mq_h2f((uint16_t)(dd0 >> 16));
+                const float d1 = mq_h2f((uint16_t)(dd1 & 0xFFFFu)), m1 = mq_h2f((uint16_t)(dd1 >> 16));
 #pragma unroll
-            for (int m = 0; m < MF; ++m) {
-                if (16 * m < nt) {
+                for (int m = 0; m < MFC; ++m) {
                     const mq_u32x4 xv = *(const mq_u32x4 *)(sA + (16 * m + r16) * PF_TS + 128 + 4 * q4);
                     const mq_s16x4 xh = __builtin_bit_cast(mq_s16x4, (uint2){xv[0], xv[1]});
                     const mq_s16x4 xl = __builtin_bit_cast(mq_s16x4, (uint2){xv[2], xv[3]});
-                    mq_f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-                    a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, bm0, a0, 0, 0, 0);
+                    const mq_f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+                    mq_f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, bm0, zf, 0, 0, 0);
                     a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, bm0, a0, 0, 0, 0);
-                    a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, bm1, a1, 0, 0, 0);
+                    mq_f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, bm1, zf, 0, 0, 0);
                     a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, bm1, a1, 0, 0, 0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -706,27 +704,33 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                     }
                 }
             }
-        }
-        // outputs: lane holds tokens 16m + 4*q4 + i of row slots (nslot0|nslot1) + r16
-        const int trow = (4 * st + tw) * (SWIGLU ? 32 : 64);
+            // outputs: lane holds tokens 16m + 4*q4 + i of row slots (nslot0|nslot1) + r16
+            const int trow = (4 * st + tw) * (SWIGLU ? 32 : 64);
 #pragma unroll
-        for (int m = 0; m < MF; ++m) {
+            for (int m = 0; m < MFC; ++m) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * m + 4 * q4 + i;
-                if (t < nt) {
-                    const float s = xscale[arow_s[t]];
-                    float *o = out + (int64_t)(p0 + t) * rows + trow;
-                    if (SWIGLU) {
-                        const float g = tot[m][0][i] * s, up = tot[m][1][i] * s;
-                        o[16 * hw + r16] = g / (1.0f + expf(-g)) * up;
-                    } else {
-                        o[nslot0 + r16] = tot[m][0][i] * s;
-                        o[nslot1 + r16] = tot[m][1][i] * s;
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * m + 4 * q4 + i;
+                    if (t < nt) {
+                        const float sc = xscale[arow_s[t]];
+                        float *o = out + (int64_t)(p0 + t) * rows + trow;
+                        if (SWIGLU) {
+                            const float gt = tot[m][0][i] * sc, up = tot[m][1][i] * sc;
+                            o[16 * hw + r16] = gt / (1.0f + expf(-gt)) * up;
+                        } else {
+                            o[nslot0 + r16] = tot[m][0][i] * sc;
+                            o[nslot1 + r16] = tot[m][1][i] * sc;
+                        }
                     }
                 }
             }
-        }
+        };
+        const int mfa = (nt + 15) >> 4;                  // 1..MF, uniform
+        static_assert(MF == 4, "one loop copy per fragment count 1..4");
+        if (mfa >= 4) run(std::integral_constant<int, 4>{});
+        else if (mfa == 3) run(std::integral_constant<int, 3>{});
+        else if (mfa == 2) run(std::integral_constant<int, 2>{});
+        else run(std::integral_constant<int, 1>{});
     }
 }
 
