@@ -596,8 +596,9 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     constexpr int NPD = NTOK * 32 / 512;                // digit pieces per thread
     static_assert(NTOK * 32 % 512 == 0 && NTOK * 4 <= 512, "piece split");
     // sB is padded to whole pieces so that no store is predicated
-    __shared__ __attribute__((aligned(16))) uint32_t sB[4 * NPB * 512];
-    __shared__ __attribute__((aligned(16))) uint32_t sA[NTOK * PF_TS];
+    // double-buffered: column b + 1 is stored while column b is multiplied
+    __shared__ __attribute__((aligned(16))) uint32_t sB[2][4 * NPB * 512];
+    __shared__ __attribute__((aligned(16))) uint32_t sA[2][NTOK * PF_TS];
     __shared__ int arow_s[NTOK];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -648,21 +649,29 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
             mq_f32x4 tot[MFC][2];
 #pragma unroll
             for (int m = 0; m < MFC; ++m) { tot[m][0] = (mq_f32x4){0.f, 0.f, 0.f, 0.f}; tot[m][1] = tot[m][0]; }
-            load(0);
-            for (int b = 0; b < kblocks; ++b) {
-                __syncthreads();
+            auto store = [&](int buf) {
 #pragma unroll
-                for (int n = 0; n < NPB; ++n) *(mq_u32x4 *)(sB + 4 * (tid + 512 * n)) = pb[n];
+                for (int n = 0; n < NPB; ++n) *(mq_u32x4 *)(sB[buf] + 4 * (tid + 512 * n)) = pb[n];
 #pragma unroll
                 for (int n = 0; n < NPD; ++n) {
                     const int j = tid + 512 * n;
-                    *(mq_u32x4 *)(sA + (j >> 5) * PF_TS + 4 * (j & 31)) = pd[n];
+                    *(mq_u32x4 *)(sA[buf] + (j >> 5) * PF_TS + 4 * (j & 31)) = pd[n];
                 }
-                if (has_sum) *(mq_u32x4 *)(sA + (tid >> 2) * PF_TS + 128 + 4 * (tid & 3)) = ps;
-                __syncthreads();
-                if (b + 1 < kblocks) load(b + 1);
-                const uint32_t *blk0 = sB + (tw * 64 + nslot0 + r16) * MQ_BLOCK_DWORDS;
-                const uint32_t *blk1 = sB + (tw * 64 + nslot1 + r16) * MQ_BLOCK_DWORDS;
+                if (has_sum) *(mq_u32x4 *)(sA[buf] + (tid >> 2) * PF_TS + 128 + 4 * (tid & 3)) = ps;
+            };
+            // One barrier per column: the buffer written in step b (column b + 1) was
+            // last read in step b - 1, which every wave finished before that step's
+            // barrier.  Loads past the last column repeat it (in bounds, stored into
+            // the idle buffer and never read), so no load or store is conditional.
+            load(0);
+            store(0);
+            load(min(1, kblocks - 1));
+            __syncthreads();
+            for (int b = 0; b < kblocks; ++b) {
+                const int cur = b & 1;
+                const uint32_t *blk0 = sB[cur] + (tw * 64 + nslot0 + r16) * MQ_BLOCK_DWORDS;
+                const uint32_t *blk1 = sB[cur] + (tw * 64 + nslot1 + r16) * MQ_BLOCK_DWORDS;
+                const uint32_t *sAc = sA[cur];
                 mq_i32x4 hi[MFC][2], lo[MFC][2];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
@@ -671,7 +680,7 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                     const mq_i32x4 b1 = mq_codes_x_scale(blk1[4 + g], __builtin_amdgcn_ubfe(blk1[kk], 8 * q4, 4));
 #pragma unroll
                     for (int m = 0; m < MFC; ++m) {
-                        const uint32_t *ap = sA + (16 * m + r16) * PF_TS + 8 * g;
+                        const uint32_t *ap = sAc + (16 * m + r16) * PF_TS + 8 * g;
                         const mq_i32x4 ah = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)ap);
                         const mq_i32x4 al = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(ap + 4));
                         // the first step of each chain starts from zero (no accumulator to clear)
@@ -687,7 +696,7 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                 const float d1 = mq_h2f((uint16_t)(dd1 & 0xFFFFu)), m1 = mq_h2f((uint16_t)(dd1 >> 16));
 #pragma unroll
                 for (int m = 0; m < MFC; ++m) {
-                    const mq_u32x4 xv = *(const mq_u32x4 *)(sA + (16 * m + r16) * PF_TS + 128 + 4 * q4);
+                    const mq_u32x4 xv = *(const mq_u32x4 *)(sAc + (16 * m + r16) * PF_TS + 128 + 4 * q4);
                     const mq_s16x4 xh = __builtin_bit_cast(mq_s16x4, (uint2){xv[0], xv[1]});
                     const mq_s16x4 xl = __builtin_bit_cast(mq_s16x4, (uint2){xv[2], xv[3]});
                     const mq_f32x4 zf = {0.f, 0.f, 0.f, 0.f};
@@ -703,6 +712,9 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                                             fmaf(-m1, a1[i], tot[m][1][i]));
                     }
                 }
+                store(cur ^ 1);
+                load(min(b + 2, kblocks - 1));
+                __syncthreads();
             }
             // outputs: lane holds tokens 16m + 4*q4 + i of row slots (nslot0|nslot1) + r16
             const int trow = (4 * st + tw) * (SWIGLU ? 32 : 64);
