@@ -1,13 +1,15 @@
 // Weighted combine of the expert outputs (fixed order, deterministic):
 //   y[slot] = sum_{s=0}^{nsplit-1} yp[s][slot]      (split partial sums, in order)
 //   v[t] = sum_s shared[s][t] + sum_{k=0}^{K-1} g[t,k] * y[inv[t*K+k]]   (shared in partials)
+// (y in slot order when inv is null: y[t*K+k]).
 //   out[t] = v[t]            (or out[t] + v[t] under residual accumulation)
 #include "common.h"
 #include "kernels.h"
 
-// The K slot indices and gates are loaded first, then the K rows (independent
-// loads in flight together), then the sums in fixed order.
+// All loads are issued before the sums (split partials in batches of CB_SB, clamped
+// indices); the sums then run in fixed order.
 #define CB_KMAX 16
+#define CB_SB 8
 __global__ void __launch_bounds__(256) k_combine(const float *__restrict__ y, int nsplit,
                                                  int64_t split_stride, const int32_t *__restrict__ inv,
                                                  const float *__restrict__ gate,
@@ -22,15 +24,19 @@ __global__ void __launch_bounds__(256) k_combine(const float *__restrict__ y, in
 #pragma unroll
     for (int k = 0; k < CB_KMAX; ++k) {
         const int kk = min(k, K - 1);
-        sl[k] = inv[t * K + kk];
+        sl[k] = inv ? inv[t * K + kk] : t * K + kk;
         gk[k] = gate[t * K + kk];
     }
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (shared) {
-        v = ((const float4 *)(shared + (int64_t)t * H))[c];
-        for (int sp = 1; sp < sh_nsplit; ++sp) {
-            const float4 q = ((const float4 *)(shared + sp * sh_stride + (int64_t)t * H))[c];
-            v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+        const float4 *sp4 = (const float4 *)(shared + (int64_t)t * H) + c;
+        for (int s0 = 0; s0 < sh_nsplit; s0 += CB_SB) {
+            float4 q[CB_SB];
+#pragma unroll
+            for (int i = 0; i < CB_SB; ++i) q[i] = sp4[(int64_t)min(s0 + i, sh_nsplit - 1) * (sh_stride / 4)];
+#pragma unroll
+            for (int i = 0; i < CB_SB; ++i)
+                if (s0 + i < sh_nsplit) { v.x += q[i].x; v.y += q[i].y; v.z += q[i].z; v.w += q[i].w; }
         }
     }
     float4 yy[CB_KMAX];

@@ -627,20 +627,32 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
         const uint8_t *tb = experts + (int64_t)e * expert_bytes + mat_off + (int64_t)(4 * st) * tile_bytes;
         // this thread's activation rows: digit pieces j = tid + 512 n (token j / 32, 16-byte
         // word j % 32), sum piece tid (token tid / 4, word tid % 4) for tid < NTOK * 4
-        const int srow = arow_s[min(tid >> 2, NTOK - 1)];
         const bool has_sum = tid < NTOK * 4;             // whole waves
+        // per-thread 32-bit byte offsets from uniform bases (scalar base + vector
+        // offset addressing: the column step only moves the scalar base)
+        typedef const __attribute__((address_space(1))) mq_u32x4 *gvec;
+        typedef const __attribute__((address_space(1))) char *gbyte;
+        uint32_t wo[NPB], dofs[NPD];
+#pragma unroll
+        for (int n = 0; n < NPB; ++n) {
+            const int j = min(tid + 512 * n, 4 * 336 - 1);
+            const int tl = j / 336, w = j - tl * 336;
+            wo[n] = (uint32_t)(tl * tile_bytes + w * 16);
+        }
+#pragma unroll
+        for (int n = 0; n < NPD; ++n)
+            dofs[n] = (uint32_t)((arow_s[(tid + 512 * n) >> 5] * G * 2 + ((tid + 512 * n) & 31)) * 16);
+        const uint32_t so = (uint32_t)((arow_s[min(tid >> 2, NTOK - 1)] * kblocks * 16 + (tid & 3) * 4) * 4);
         mq_u32x4 pb[NPB], pd[NPD], ps;
         auto load = [&](int b) {
+            const gbyte wb = (gbyte)(tb + (int64_t)b * 5376);
+            const gbyte db = (gbyte)(xdig + (int64_t)b * 32);
+            const gbyte sb = (gbyte)(xsum + (int64_t)b * 16);
 #pragma unroll
-            for (int n = 0; n < NPB; ++n) {
-                const int j = min(tid + 512 * n, 4 * 336 - 1);
-                const int tl = j / 336, w = j - tl * 336;
-                pb[n] = *(const mq_u32x4 *)(tb + (int64_t)tl * tile_bytes + (int64_t)b * 5376 + w * 16);
-            }
+            for (int n = 0; n < NPB; ++n) pb[n] = *(gvec)(wb + wo[n]);
 #pragma unroll
-            for (int n = 0; n < NPD; ++n)
-                pd[n] = xdig[((int64_t)arow_s[(tid + 512 * n) >> 5] * G + 16 * b) * 2 + ((tid + 512 * n) & 31)];
-            ps = *(const mq_u32x4 *)(xsum + ((int64_t)srow * kblocks + b) * 16 + (tid & 3) * 4);
+            for (int n = 0; n < NPD; ++n) pd[n] = *(gvec)(db + dofs[n]);
+            ps = *(gvec)(sb + so);
         };
         // MFC token fragments carry tokens (the rest of MF are skipped): one copy of the
         // column loop per count, so no fragment test sits in the loop
