@@ -24,6 +24,7 @@
 #include "common.h"
 #include <type_traits>
 #include "kernels.h"
+#include "topk_dev.h"
 
 typedef int32_t mq_i32x4 __attribute__((ext_vector_type(4)));
 typedef short mq_s16x4 __attribute__((ext_vector_type(4)));
@@ -323,6 +324,57 @@ void mq_dense_split(int rows, int K, int nf, int *nsplit, int *kps) {
     *nsplit = (K + k - 1) / k;
 }
 
+// LDS of the in-launch routing (it aliases the weight slices, which are not in use
+// until the routing is done)
+struct MqRouteLds {
+    MqTopkLds L;
+    int sidx[MQ_TOPK_BUCKET_MAX_T * 16];
+    int soff[MQ_ROUTE_MAX_E], sun[MQ_ROUTE_MAX_E], scnt[MQ_ROUTE_MAX_E];
+    int sU;
+    int4 unit;
+    int rows[MMA_TCH];
+};
+
+// Unit u of the batch -- (expert, first bucket position, slot count, chunk of the
+// expert's slots) -- and, for threads below 16, the token of its slot tid (the zero
+// row past the count): the batch's top-K selection and bucketing done in LDS by the
+// same functions as the top-K + bucketing launch.  Work-group 0 also writes the
+// routing outputs.  256 threads.
+__device__ __forceinline__ int4 mq_route_unit(const MqRoute &rt, int u, MqRouteLds &R, int tid, int &urv) {
+    const bool w0 = blockIdx.x == 0;
+    const int S = rt.T * rt.K;
+    for (int t = 0; t < rt.T; ++t) {
+        mq_topk_token<256>(rt.logits, 1, rt.bias, rt.T, rt.E, rt.K, t, true, tid, R.L, w0 ? rt.idx : nullptr,
+                           w0 ? rt.gate : nullptr, w0 ? rt.trace_idx : nullptr, w0 ? rt.trace_w : nullptr);
+        // the selection of token t is final here; the next token's first writes to
+        // it come two barriers later
+        if (tid < rt.K) R.sidx[t * rt.K + tid] = R.L.se[tid];
+    }
+    __syncthreads();
+    mq_bucket_small_wg<256>(R.sidx, S, rt.E, MMA_TCH, w0, rt.counts, rt.offsets, rt.perm, rt.inv, rt.units_hdr,
+                            rt.units, rt.fill_units, rt.urow, rt.K, rt.zrow, R.soff, R.sun, R.scnt, &R.sU);
+    if (tid == 0) R.unit = make_int4(0, 0, 0, 0);
+    __syncthreads();
+    if (tid < rt.E) {
+        const int c = R.scnt[tid], u0 = R.sun[tid];
+        if (u >= u0 && u < u0 + (c + MMA_TCH - 1) / MMA_TCH) {
+            const int k = u - u0;
+            R.unit = make_int4(tid, R.soff[tid] + MMA_TCH * k, min(MMA_TCH, c - MMA_TCH * k), k);
+        }
+    }
+    __syncthreads();
+    const int4 un = R.unit;
+    if (tid < S && un.z > 0 && R.sidx[tid] == un.x) {    // slots of the unit's expert, in slot order
+        int r = 0;
+        for (int q = 0; q < tid; ++q) r += R.sidx[q] == un.x ? 1 : 0;
+        r -= MMA_TCH * un.w;
+        if (r >= 0 && r < MMA_TCH) R.rows[r] = tid / rt.K;
+    }
+    __syncthreads();
+    urv = tid < un.z ? R.rows[tid] : rt.zrow;
+    return un;
+}
+
 template <bool GU>
 __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ experts, int64_t expert_bytes,
                                                 int64_t mat_off, int tiles, int kblocks, int nsplit,
@@ -332,8 +384,10 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
                                                 const uint32_t *__restrict__ xsum,
                                                 const float *__restrict__ xscale, float *__restrict__ out0,
                                                 float *__restrict__ out1, int out_ld, int64_t split_stride,
-                                                int q2_grid, const MqDense dn) {
+                                                int q2_grid, const MqDense dn, const MqRoute rt,
+                                                int route_on) {
     __shared__ __attribute__((aligned(16))) mq_u32x4 sW[4][384];           // weight slices, one per wave
+    static_assert(sizeof(MqRouteLds) <= sizeof(sW), "routing LDS fits the weight slices");
     __shared__ __attribute__((aligned(16))) mq_u32x4 sA[2][DM_AITEMS];     // activation operands
     __shared__ int s_row[16];
     __shared__ float s_sc[16];
@@ -354,10 +408,16 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
     const int ks = rest % nsplit, u = rest / nsplit;
     const int c0 = ks * cps, c1 = min(kblocks, c0 + cps);
     if (c0 >= c1) return;
-    // the unit and (gate/up) its row table are independent loads; nothing else
-    // waits on global memory before the first activation loads
-    const int4 un = units[u];
-    const int urv = GU && tid < 16 ? urow[(int64_t)u * 16 + tid] : 0;
+    // the unit and (gate/up) its row table: routed here, or two independent loads
+    // (nothing else waits on global memory before the first activation loads)
+    int4 un;
+    int urv = 0;
+    if (GU && route_on) {
+        un = mq_route_unit(rt, u, *reinterpret_cast<MqRouteLds *>(&sW[0][0]), tid, urv);
+    } else {
+        un = units[u];
+        urv = GU && tid < 16 ? urow[(int64_t)u * 16 + tid] : 0;
+    }
     const int e = un.x, p0 = un.y, nt = un.z;
     if (nt == 0) return;                                 // past the last unit
     const int tile = 4 * tg + wv;
@@ -475,9 +535,14 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
                      int kblocks, const int4 *units, int max_units, const int32_t *urow, int zrow,
                      int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
-                     int64_t split_stride, const MqDenseSpec *dense, hipStream_t st) {
+                     int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route, hipStream_t st) {
     if (tiles % 4) return MOE_Q2_EUNSUPPORTED;
     if (gu && !urow) return MOE_Q2_EINVAL;
+    if (route && (!gu || route->T < 1 || route->T > MQ_TOPK_BUCKET_MAX_T || route->E > MQ_ROUTE_MAX_E ||
+                  route->K > 16 || route->K < 1))
+        return MOE_Q2_EINVAL;
+    const MqRoute rt = route ? *route : MqRoute{};
+    const int route_on = route ? 1 : 0;
     int nsplit = 1, cps = kblocks;
     mq_dec_split(max_units, tiles, kblocks, gu ? MQ_DEC_SPLIT_GU : MQ_DEC_SPLIT_D, &nsplit, &cps);
     const int64_t q2_grid = (int64_t)max_units * nsplit * (tiles / 4);
@@ -509,12 +574,12 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
         hipLaunchKernelGGL(k_q2_mma<true>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
                            expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units, urow, zrow,
                            trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
-                           split_stride, (int)q2_grid, dn);
+                           split_stride, (int)q2_grid, dn, rt, route_on);
     else
         hipLaunchKernelGGL(k_q2_mma<false>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
                            expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units, urow, zrow,
                            trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
-                           split_stride, (int)q2_grid, dn);
+                           split_stride, (int)q2_grid, dn, rt, route_on);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

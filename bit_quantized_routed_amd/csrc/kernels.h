@@ -79,13 +79,33 @@ struct MqDenseSpec {
     int64_t split_stride;
 };
 void mq_dense_split(int rows, int K, int nf, int *nsplit, int *kps);
+// Routing done inside the decode gate/up launch (batches of at most
+// MQ_TOPK_BUCKET_MAX_T tokens, E <= MQ_ROUTE_MAX_E, K <= 16): every routed
+// work-group selects and buckets the batch from the final logits in LDS and takes
+// its unit from there; work-group 0 writes the routing outputs (the same arrays the
+// top-K + bucketing launch writes) for the later launches.
+#define MQ_ROUTE_MAX_E 256
+struct MqRoute {
+    const float *logits, *bias;
+    int T, E, K;
+    int32_t *idx;
+    float *gate;
+    int32_t *trace_idx;
+    float *trace_w;
+    int32_t *counts, *offsets, *perm, *inv, *units_hdr;
+    int4 *units;
+    int fill_units;
+    int32_t *urow;
+    int zrow;
+};
 // units: max_units records, those past the last unit with slot count 0; urow (gate/up):
 // the [max_units][16] row table of the bucketing; down reads the rows of its slots.
+// route (gate/up only, optional): route in the launch instead of reading units/urow.
 int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t mat_off, int tiles,
                      int kblocks, const int4 *units, int max_units, const int32_t *urow, int zrow,
                      int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
-                     int64_t split_stride, const MqDenseSpec *dense, hipStream_t st);
+                     int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route, hipStream_t st);
 int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
                         int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                         int max_units, const int32_t *perm, int topk, const void *xdig,

@@ -369,9 +369,19 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     } else {
         MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router(xin, 0, router_w, nullptr, T, H, E, logits, st));
     }
-    // few tokens: the bucketing runs in the top-K launch (its phase then reads zero)
+    // few tokens: the bucketing runs in the top-K launch (its phase then reads zero),
+    // or, on the matrix-core decode path, inside the gate/up launch (both phases zero)
     const int tch = valu ? FD_TCH : (prefill ? PF_TCH : MMA_TCH);
-    if (T <= MQ_TOPK_BUCKET_MAX_T) {
+    const bool route_in_gu = !valu && !prefill && nsplit == 1 && T <= MQ_TOPK_BUCKET_MAX_T &&
+                             E <= MQ_ROUTE_MAX_E && K <= 16;
+    MqRoute rt = {};
+    if (route_in_gu) {
+        rt = MqRoute{logits, router_b, T, (int)E, K, idx, gate, trace ? trace->topk_idx : nullptr,
+                     trace ? trace->topk_w : nullptr, counts, offsets, perm, inv, units_hdr, units, fill_units,
+                     urow, T};
+        MQ_PHASE(MOE_Q2_PH_TOPK, MOE_Q2_OK);
+        MQ_PHASE(MOE_Q2_PH_BUCKET, MOE_Q2_OK);
+    } else if (T <= MQ_TOPK_BUCKET_MAX_T) {
         MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk_bucket(logits, nsplit, router_b, T, E, K, idx, gate,
                                                        trace ? trace->topk_idx : nullptr,
                                                        trace ? trace->topk_w : nullptr, tch, counts,
@@ -437,14 +447,15 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma(1, experts_q2, ebytes, 0, I / 32, H / MQ_QK, units,
                                                      w.dec_units, urow, T, S, xq,
                                                      (const uint32_t *)xg, xs, gp, up, I, gstride,
-                                                     w.fused ? &dgu : nullptr, st));
+                                                     w.fused ? &dgu : nullptr, route_in_gu ? &rt : nullptr,
+                                                     st));
         MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_swiglu_digits(gp, up, w.dsplit_gu, gstride, S, I, I, hq,
                                                                 (uint32_t *)hg, hsc, w.fused ? &shs : nullptr,
                                                                 st));
         MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_mma(0, experts_q2, ebytes, 2 * mat_gu, H / 64, I / MQ_QK,
                                                   units, w.dec_units, nullptr, S, S, hq,
                                                   (const uint32_t *)hg, hsc, y, nullptr, H, ystride,
-                                                  w.fused ? &dd : nullptr, st));
+                                                  w.fused ? &dd : nullptr, nullptr, st));
     }
     const int ysplit = (prefill || valu) ? 1 : w.dsplit_d;
     const int64_t ystride = (int64_t)(T * K + 1) * H;
