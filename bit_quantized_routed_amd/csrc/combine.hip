@@ -17,7 +17,7 @@ __global__ void __launch_bounds__(256) k_combine(const float *__restrict__ y, in
                                                  int64_t sh_stride, int H, int K, int accumulate,
                                                  float *out) {
     const int t = blockIdx.y;
-    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
     if (c >= H / 4) return;
     int sl[CB_KMAX];
     float gk[CB_KMAX];
@@ -39,10 +39,20 @@ __global__ void __launch_bounds__(256) k_combine(const float *__restrict__ y, in
                 if (s0 + i < sh_nsplit) { v.x += q[i].x; v.y += q[i].y; v.z += q[i].z; v.w += q[i].w; }
         }
     }
-    float4 yy[CB_KMAX];
+    // splits 0 and 1 loaded together; further splits (not used by the launches that
+    // split the down projection at most twice) one after another
+    float4 yy[CB_KMAX], y1[CB_KMAX];
 #pragma unroll
     for (int k = 0; k < CB_KMAX; ++k) yy[k] = ((const float4 *)(y + (int64_t)sl[k] * H))[c];
-    for (int sp = 1; sp < nsplit; ++sp) {
+    if (nsplit > 1) {
+#pragma unroll
+        for (int k = 0; k < CB_KMAX; ++k) y1[k] = ((const float4 *)(y + split_stride + (int64_t)sl[k] * H))[c];
+#pragma unroll
+        for (int k = 0; k < CB_KMAX; ++k) {
+            yy[k].x += y1[k].x; yy[k].y += y1[k].y; yy[k].z += y1[k].z; yy[k].w += y1[k].w;
+        }
+    }
+    for (int sp = 2; sp < nsplit; ++sp) {
 #pragma unroll
         for (int k = 0; k < CB_KMAX; ++k) {
             const float4 q = ((const float4 *)(y + sp * split_stride + (int64_t)sl[k] * H))[c];
@@ -67,7 +77,10 @@ __global__ void __launch_bounds__(256) k_combine(const float *__restrict__ y, in
 int mq_launch_combine(const float *y, int nsplit, int64_t split_stride, const int32_t *inv,
                       const float *gate, const float *shared, int sh_nsplit, int64_t sh_stride, int T, int H,
                       int K, int accumulate, float *out, hipStream_t st) {
-    hipLaunchKernelGGL(k_combine, dim3((H / 4 + 255) / 256, T), dim3(256), 0, st, y, nsplit, split_stride,
+    // few tokens: 64-thread work-groups, so that the loads of a row spread over more
+    // compute units (the launch is latency- and load-issue-bound there)
+    const int nb = T <= 8 ? 64 : 256;
+    hipLaunchKernelGGL(k_combine, dim3((H / 4 + nb - 1) / nb, T), dim3(nb), 0, st, y, nsplit, split_stride,
                        inv, gate, shared, sh_nsplit, sh_stride, H, K, accumulate, out);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;

@@ -61,10 +61,12 @@ int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit,
                                  int nrows, int len, int64_t src_ld, void *xdig, uint32_t *xsum,
                                  float *scale, const MqSharedSwiglu *shared, hipStream_t st);
 // Decode kernel: split count along the reduction (shared by the workspace sizing).
-// Gate/up splits are summed by the intermediate preparation; the down projection
-// is not split (its partials would cost the combine more than they save).
+// Gate/up splits are summed by the intermediate preparation, down splits by the
+// combine; a split is taken only while the launch stays within about 768 resident
+// work-groups (in practice: down splits in two for batches of a token or two, whose
+// few work-groups are otherwise latency-bound).
 #define MQ_DEC_SPLIT_GU 4
-#define MQ_DEC_SPLIT_D 1
+#define MQ_DEC_SPLIT_D 2
 void mq_dec_split(int max_units, int tiles, int kblocks, int max_split, int *nsplit, int *cps);
 // zrow: index of the all-zero activation row (written by the digit preparation after
 // the real rows); trash_row: an output row that absorbs padding-token writes; outputs
