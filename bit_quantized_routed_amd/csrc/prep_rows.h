@@ -78,11 +78,11 @@ __device__ __forceinline__ void mq_prep_digits_wg(const void *__restrict__ src, 
             float gs[16], us[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) { gs[i] = 0.0f; us[i] = 0.0f; }
-            // splits in order, two at a time with both loads in flight
-            for (int sp = 0; sp < nsplit; sp += 2) {
-                float4 a[2][4], b[2][4];
+            // splits in order, four at a time with all their loads in flight
+            for (int sp = 0; sp < nsplit; sp += 4) {
+                float4 a[4][4], b[4][4];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < 4; ++j) {
                     const int64_t off = min(sp + j, nsplit - 1) * split_stride + row * src_ld + g * 16;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -91,7 +91,7 @@ __device__ __forceinline__ void mq_prep_digits_wg(const void *__restrict__ src, 
                     }
                 }
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < 4; ++j) {
                     if (sp + j < nsplit) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
