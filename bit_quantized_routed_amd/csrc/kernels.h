@@ -20,6 +20,14 @@ int mq_launch_bucket(const int32_t *idx, int T, int K, int E, int unit_tokens, i
                      int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr,
                      int4 *units, int fill_units, int32_t *urow, int zrow, hipStream_t st);
 size_t mq_bucket_lds_bytes(int E);
+// Large batches: the same bucketing in three launches over chunks of tokens; chunk:
+// workspace of mq_bucket_chunks(T) * E ints.  No row table (prefill and vector-ALU
+// decode kernels read the permutation).
+int mq_bucket_chunks(int T);
+int mq_launch_bucket_par(const int32_t *idx, int T, int K, int E, int unit_tokens, int32_t *counts,
+                         int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr, int4 *units,
+                         int fill_units, int32_t *chunk, hipStream_t st);
+#define MQ_BUCKET_PAR_MIN_T 256   // batches from this size bucket in three launches (no row table)
 // Top-K and bucketing in one work-group (T <= MQ_TOPK_BUCKET_MAX_T).
 int mq_launch_topk_bucket(const float *logits, int nsplit, const float *bias, int T, int E, int K,
                           int32_t *idx, float *gate, int32_t *trace_idx, float *trace_w, int unit_tokens,

@@ -47,7 +47,7 @@ extern "C" size_t moe_q2_expert_bytes(const moe_q2_shape *s) {
 namespace {
 struct Workspace {
     size_t total = 0;
-    size_t logits, idx, gate, counts, offsets, perm, inv, units_hdr, units, urow = 0, xbf, xq, xg, xs, h,
+    size_t logits, idx, gate, counts, offsets, perm, inv, units_hdr, units, urow = 0, bchunk = 0, xbf, xq, xg, xs, h,
         hq, hg, hs, y, xlo, sp, shi, slo, ysh;
     int max_units = 0, split_gu = 1, split_d = 1, rsplit = 1;
     // routed path and, for the matrix-core decode kernels, their reduction splits
@@ -97,6 +97,8 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     w.units_hdr = take(c, 16);
     w.units = take(c, (size_t)w.max_units * 16);
     if (w.dec_units) w.urow = take(c, (size_t)w.dec_units * MMA_TCH * 4);   // row table of the units
+    if (T >= MQ_BUCKET_PAR_MIN_T)                   // per-chunk expert counts of the large-batch bucketing
+        w.bchunk = take(c, (size_t)mq_bucket_chunks(T) * E * 4);
     // activation buffers hold one extra row: the all-zero row that padding tokens
     // of the decode kernels read; h and y one extra row that absorbs their writes
     w.xbf = take(c, (size_t)T * H * 2);
@@ -392,8 +394,13 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         MQ_PHASE(MOE_Q2_PH_TOPK, mq_launch_topk(logits, nsplit, router_b, T, E, K, idx, gate,
                                                 trace ? trace->topk_idx : nullptr,
                                                 trace ? trace->topk_w : nullptr, st));
-        MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket(idx, T, K, E, tch, counts, offsets, perm, inv,
-                                                    units_hdr, units, fill_units, urow, T, st));
+        if (!urow && T >= MQ_BUCKET_PAR_MIN_T)
+            MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket_par(idx, T, K, E, tch, counts, offsets, perm, inv,
+                                                            units_hdr, units, fill_units,
+                                                            (int32_t *)(ws + w.bchunk), st));
+        else
+            MQ_PHASE(MOE_Q2_PH_BUCKET, mq_launch_bucket(idx, T, K, E, tch, counts, offsets, perm, inv,
+                                                        units_hdr, units, fill_units, urow, T, st));
     }
     if (side) {
         const hipError_t e = hipStreamWaitEvent(st, side->prep, 0);

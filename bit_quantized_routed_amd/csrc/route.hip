@@ -404,6 +404,125 @@ __global__ void __launch_bounds__(BK_THREADS) k_bucket(const int32_t *__restrict
                  urow, zrow, sm);
 }
 
+// Large batches (prefill): the same bucketing in three launches over chunks of
+// BKP_CH tokens.  (1) per chunk, the expert histogram (LDS atomics: commutative) into
+// cnt[e][chunk]; (2) one work-group: per expert the exclusive prefix over the chunks
+// in chunk order and the total, exclusive scans over the experts (offsets, unit
+// starts), unit records, and cnt[e][chunk] += offsets[e], the chunk's first bucket
+// position for e; (3) per chunk, slot s = t*K + k of expert e goes to
+// cnt[e][chunk] + #{tokens t' < t of the chunk that chose e} (a per-expert token
+// bitmap in LDS).  Same results as mq_bucket_wg.
+#define BKP_CH 64
+__global__ void __launch_bounds__(256) k_bucket_hist(const int32_t *__restrict__ idx, int T, int K, int E,
+                                                     int C, int32_t *__restrict__ cnt) {
+    extern __shared__ int32_t hc[];                 // [E]
+    const int c = blockIdx.x, tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) hc[e] = 0;
+    __syncthreads();
+    const int s0 = c * BKP_CH * K, s1 = min(T, (c + 1) * BKP_CH) * K;
+    for (int q = s0 + tid; q < s1; q += 256) atomicAdd(&hc[idx[q]], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) cnt[(int64_t)e * C + c] = hc[e];
+}
+
+__global__ void __launch_bounds__(BK_THREADS) k_bucket_scan(int C, int E, int unit_tokens,
+                                                            int32_t *__restrict__ cnt,
+                                                            int32_t *__restrict__ counts_out,
+                                                            int32_t *__restrict__ offsets_out,
+                                                            int32_t *__restrict__ units_hdr,
+                                                            int4 *__restrict__ units, int fill_units) {
+    __shared__ int wsum[2][BK_THREADS / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int c = 0;
+    if (tid < E) {
+        int32_t *row = cnt + (int64_t)tid * C;
+        for (int k0 = 0; k0 < C; k0 += 16) {          // 16 counts loaded at once
+            int v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = row[min(k0 + j, C - 1)];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (k0 + j < C) {
+                    row[k0 + j] = c;                  // exclusive prefix over the chunks
+                    c += v[j];
+                }
+        }
+    }
+    const int nu = (c + unit_tokens - 1) / unit_tokens;
+    int a = c, b = nu;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int pa = __shfl_up(a, o, 64), pb = __shfl_up(b, o, 64);
+        if (lane >= o) { a += pa; b += pb; }
+    }
+    if (lane == 63) { wsum[0][wv] = a; wsum[1][wv] = b; }
+    __syncthreads();
+    int ba = 0, bb = 0;
+    for (int w = 0; w < wv; ++w) { ba += wsum[0][w]; bb += wsum[1][w]; }
+    const int off = ba + a - c, u0 = bb + b - nu;
+    if (tid < E) {
+        counts_out[tid] = c;
+        offsets_out[tid] = off;
+        for (int k = 0, u = u0; k < c; k += unit_tokens, ++u)
+            units[u] = make_int4(tid, off + k, min(unit_tokens, c - k), 0);
+        int32_t *row = cnt + (int64_t)tid * C;
+        for (int k = 0; k < C; ++k) row[k] += off;
+    }
+    if (tid == BK_THREADS - 1) {
+        offsets_out[E] = ba + a;
+        units_hdr[0] = bb + b;
+    }
+    int U = 0;
+    for (int w = 0; w < BK_THREADS / 64; ++w) U += wsum[1][w];
+    for (int u = U + tid; u < fill_units; u += BK_THREADS) units[u] = make_int4(0, 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(256) k_bucket_place(const int32_t *__restrict__ idx, int T, int K, int E,
+                                                      int C, const int32_t *__restrict__ base,
+                                                      int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+    extern __shared__ uint32_t bm[];                // [E][BKP_CH / 32] token bitmaps
+    constexpr int W = BKP_CH / 32;
+    const int c = blockIdx.x, tid = threadIdx.x, t0 = c * BKP_CH;
+    for (int i = tid; i < E * W; i += 256) bm[i] = 0u;
+    __syncthreads();
+    const int s0 = t0 * K, s1 = min(T, t0 + BKP_CH) * K;
+    for (int q = s0 + tid; q < s1; q += 256) {
+        const int tl = q / K - t0;
+        atomicOr(&bm[idx[q] * W + (tl >> 5)], 1u << (tl & 31));
+    }
+    __syncthreads();
+    for (int q = s0 + tid; q < s1; q += 256) {
+        const int e = idx[q], tl = q / K - t0;
+        const uint32_t *row = bm + e * W;
+        int r = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            if (w < (tl >> 5)) r += __popc(row[w]);
+        r += __popc(row[tl >> 5] & ((1u << (tl & 31)) - 1u));
+        const int pos = base[(int64_t)e * C + c] + r;
+        perm[pos] = q;
+        inv[q] = pos;
+    }
+}
+
+int mq_bucket_chunks(int T) { return (T + BKP_CH - 1) / BKP_CH; }
+
+int mq_launch_bucket_par(const int32_t *idx, int T, int K, int E, int unit_tokens, int32_t *counts,
+                         int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr, int4 *units,
+                         int fill_units, int32_t *chunk, hipStream_t st) {
+    if (E > BK_THREADS || T < 1) return MOE_Q2_EUNSUPPORTED;
+    const int C = mq_bucket_chunks(T);
+    hipLaunchKernelGGL(k_bucket_hist, dim3(C), dim3(256), (size_t)E * 4, st, idx, T, K, E, C, chunk);
+    MQ_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(BK_THREADS), 0, st, C, E, unit_tokens, chunk, counts, offsets,
+                       units_hdr, units, fill_units);
+    MQ_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_bucket_place, dim3(C), dim3(256), (size_t)E * (BKP_CH / 32) * 4, st, idx, T, K, E, C,
+                       chunk, perm, inv);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}
+
 size_t mq_bucket_lds_bytes(int E) {
     return (size_t)(4 * E + 2) * 4 + (size_t)E * (BK_CH / 32) * 4;
 }
