@@ -343,6 +343,23 @@ struct MqRouteLds {
 __device__ __forceinline__ int4 mq_route_unit(const MqRoute &rt, int u, MqRouteLds &R, int tid, int &urv) {
     const bool w0 = blockIdx.x == 0;
     const int S = rt.T * rt.K;
+    if (rt.T == 1 && !w0) {
+        // one token: every selected expert is a unit of one slot, in expert order, so
+        // unit u is the selection of rank u by expert index (slot u, token 0)
+        mq_topk_token<256>(rt.logits, 1, rt.bias, 1, rt.E, rt.K, 0, true, tid, R.L, nullptr, nullptr, nullptr,
+                           nullptr);
+        if (tid == 0) R.unit = make_int4(0, 0, 0, 0);
+        __syncthreads();
+        if (tid < rt.K) {
+            const int e = R.L.se[tid];
+            int r = 0;
+            for (int q = 0; q < rt.K; ++q) r += R.L.se[q] < e ? 1 : 0;
+            if (r == u) R.unit = make_int4(e, u, 1, 0);
+        }
+        __syncthreads();
+        urv = tid == 0 ? 0 : rt.zrow;
+        return R.unit;
+    }
     for (int t = 0; t < rt.T; ++t) {
         mq_topk_token<256>(rt.logits, 1, rt.bias, rt.T, rt.E, rt.K, t, true, tid, R.L, w0 ? rt.idx : nullptr,
                            w0 ? rt.gate : nullptr, w0 ? rt.trace_idx : nullptr, w0 ? rt.trace_w : nullptr);

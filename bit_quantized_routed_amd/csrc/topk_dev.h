@@ -101,7 +101,8 @@ __device__ __forceinline__ void mq_topk_token(const float *__restrict__ logits, 
         }
     }
     __syncthreads();
-    if (valid && i < 64) {                           // softmax over the K selected (one wave)
+    // softmax over the K selected (one wave), skipped when no output is asked for
+    if (valid && i < 64 && (idx || gate || trace_idx || trace_w)) {
         const float mx = L.sv[0];
         const float pk = i < K ? expf(L.sv[i] - mx) : 0.0f;
         float z = pk;
@@ -119,8 +120,8 @@ __device__ __forceinline__ void mq_topk_token(const float *__restrict__ logits, 
 }
 
 // Bucketing of a small batch whose selections sit in LDS (sidx[S], S <= 256), by a
-// work-group of NTH >= E threads, same results as mq_bucket_wg: every expert counts its slots by a scan of sidx,
-// the offsets and unit starts are exclusive scans over the experts, and slot s
+// work-group of NTH >= E threads, same results as mq_bucket_wg: every expert counts
+// its slots by a scan of sidx, the offsets and unit starts are exclusive scans over the experts, and slot s
 // lands at offsets[e] + #{s' < s : sidx[s'] = e} (stable in slot order).  The
 // offsets, unit starts (and counts, unit total when given) stay in LDS; the global
 // outputs are written only when `write` is set.
