@@ -408,8 +408,8 @@ __global__ void __launch_bounds__(BK_THREADS) k_bucket(const int32_t *__restrict
 // BKP_CH tokens.  (1) per chunk, the expert histogram (LDS atomics: commutative) into
 // cnt[e][chunk]; (2) one work-group: per expert the exclusive prefix over the chunks
 // in chunk order and the total, exclusive scans over the experts (offsets, unit
-// starts), unit records, and cnt[e][chunk] += offsets[e], the chunk's first bucket
-// position for e; (3) per chunk, slot s = t*K + k of expert e goes to
+// starts), unit records, and cnt[e][chunk] = offsets[e] + that prefix, the chunk's
+// first bucket position for e; (3) per chunk, slot s = t*K + k of expert e goes to
 // cnt[e][chunk] + #{tokens t' < t of the chunk that chose e} (a per-expert token
 // bitmap in LDS).  Same results as mq_bucket_wg.
 #define BKP_CH 64
@@ -425,31 +425,37 @@ __global__ void __launch_bounds__(256) k_bucket_hist(const int32_t *__restrict__
     for (int e = tid; e < E; e += 256) cnt[(int64_t)e * C + c] = hc[e];
 }
 
-__global__ void __launch_bounds__(BK_THREADS) k_bucket_scan(int C, int E, int unit_tokens,
-                                                            int32_t *__restrict__ cnt,
-                                                            int32_t *__restrict__ counts_out,
-                                                            int32_t *__restrict__ offsets_out,
-                                                            int32_t *__restrict__ units_hdr,
-                                                            int4 *__restrict__ units, int fill_units) {
-    __shared__ int wsum[2][BK_THREADS / 64];
+// (256 threads, so that it finds room on a compute unit next to a concurrent
+// launch; thread i owns experts BKP_EPT * i .. + BKP_EPT - 1)
+#define BKP_EPT 4
+__global__ void __launch_bounds__(256) k_bucket_scan(int C, int E, int unit_tokens, int32_t *__restrict__ cnt,
+                                                     int32_t *__restrict__ counts_out,
+                                                     int32_t *__restrict__ offsets_out,
+                                                     int32_t *__restrict__ units_hdr,
+                                                     int4 *__restrict__ units, int fill_units) {
+    __shared__ int wsum[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int c = 0;
-    if (tid < E) {
-        int32_t *row = cnt + (int64_t)tid * C;
-        for (int k0 = 0; k0 < C; k0 += 16) {          // 16 counts loaded at once
-            int v[16];
+    int cn[BKP_EPT];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] = row[min(k0 + j, C - 1)];
+    for (int q = 0; q < BKP_EPT; ++q) {               // expert totals, 16 counts at once
+        const int e = BKP_EPT * tid + q;
+        int c = 0;
+        if (e < E) {
+            const int32_t *row = cnt + (int64_t)e * C;
+            for (int k0 = 0; k0 < C; k0 += 16) {
+                int v[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if (k0 + j < C) {
-                    row[k0 + j] = c;                  // exclusive prefix over the chunks
-                    c += v[j];
-                }
+                for (int j = 0; j < 16; ++j) v[j] = row[min(k0 + j, C - 1)];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) c += k0 + j < C ? v[j] : 0;
+            }
         }
+        cn[q] = c;
     }
-    const int nu = (c + unit_tokens - 1) / unit_tokens;
-    int a = c, b = nu;
+    int tc = 0, tu = 0;                               // this thread's slots and units
+#pragma unroll
+    for (int q = 0; q < BKP_EPT; ++q) { tc += cn[q]; tu += (cn[q] + unit_tokens - 1) / unit_tokens; }
+    int a = tc, b = tu;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int pa = __shfl_up(a, o, 64), pb = __shfl_up(b, o, 64);
@@ -459,22 +465,39 @@ __global__ void __launch_bounds__(BK_THREADS) k_bucket_scan(int C, int E, int un
     __syncthreads();
     int ba = 0, bb = 0;
     for (int w = 0; w < wv; ++w) { ba += wsum[0][w]; bb += wsum[1][w]; }
-    const int off = ba + a - c, u0 = bb + b - nu;
-    if (tid < E) {
-        counts_out[tid] = c;
-        offsets_out[tid] = off;
-        for (int k = 0, u = u0; k < c; k += unit_tokens, ++u)
-            units[u] = make_int4(tid, off + k, min(unit_tokens, c - k), 0);
-        int32_t *row = cnt + (int64_t)tid * C;
-        for (int k = 0; k < C; ++k) row[k] += off;
+    int off = ba + a - tc, u = bb + b - tu;           // exclusive: first slot and unit of the thread
+#pragma unroll
+    for (int q = 0; q < BKP_EPT; ++q) {
+        const int e = BKP_EPT * tid + q, c = cn[q];
+        if (e < E) {
+            counts_out[e] = c;
+            offsets_out[e] = off;
+            for (int k = 0; k < c; k += unit_tokens, ++u)
+                units[u] = make_int4(e, off + k, min(unit_tokens, c - k), 0);
+            // chunk bases: offset plus the exclusive prefix over the chunks (in chunk
+            // order), 16 counts loaded before any is overwritten
+            int32_t *row = cnt + (int64_t)e * C;
+            int run = off;
+            for (int k0 = 0; k0 < C; k0 += 16) {
+                int v[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) v[j] = row[min(k0 + j, C - 1)];
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (k0 + j < C) {
+                        row[k0 + j] = run;
+                        run += v[j];
+                    }
+            }
+        }
+        off += c;
     }
-    if (tid == BK_THREADS - 1) {
+    if (tid == 255) {
         offsets_out[E] = ba + a;
         units_hdr[0] = bb + b;
     }
-    int U = 0;
-    for (int w = 0; w < BK_THREADS / 64; ++w) U += wsum[1][w];
-    for (int u = U + tid; u < fill_units; u += BK_THREADS) units[u] = make_int4(0, 0, 0, 0);
+    const int U = wsum[1][0] + wsum[1][1] + wsum[1][2] + wsum[1][3];
+    for (int q = U + tid; q < fill_units; q += 256) units[q] = make_int4(0, 0, 0, 0);
 }
 
 __global__ void __launch_bounds__(256) k_bucket_place(const int32_t *__restrict__ idx, int T, int K, int E,
@@ -510,11 +533,11 @@ int mq_bucket_chunks(int T) { return (T + BKP_CH - 1) / BKP_CH; }
 int mq_launch_bucket_par(const int32_t *idx, int T, int K, int E, int unit_tokens, int32_t *counts,
                          int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr, int4 *units,
                          int fill_units, int32_t *chunk, hipStream_t st) {
-    if (E > BK_THREADS || T < 1) return MOE_Q2_EUNSUPPORTED;
+    if (E > 256 * BKP_EPT || T < 1) return MOE_Q2_EUNSUPPORTED;
     const int C = mq_bucket_chunks(T);
     hipLaunchKernelGGL(k_bucket_hist, dim3(C), dim3(256), (size_t)E * 4, st, idx, T, K, E, C, chunk);
     MQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(BK_THREADS), 0, st, C, E, unit_tokens, chunk, counts, offsets,
+    hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(256), 0, st, C, E, unit_tokens, chunk, counts, offsets,
                        units_hdr, units, fill_units);
     MQ_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_bucket_place, dim3(C), dim3(256), (size_t)E * (BKP_CH / 32) * 4, st, idx, T, K, E, C,
