@@ -1,9 +1,10 @@
 """GPU parity on small, odd layer shapes: expert counts that leave a partial chunk of
 64 in the top-K ranking, K = 1, K = E, the largest E and K the library accepts, fp32
 and bf16 inputs, with and without a shared expert, Zipf-biased routing, token counts
-on both sides of every launch-shape switch (fused top-K + bucketing up to 4 tokens,
-per-expert router up to 8, decode kernels below 256 tokens, prefill kernels from
-256), and an empty batch.  Every token's routing and the bucketing are checked; the
+on both sides of every launch-shape switch (routing inside the decode gate/up launch
+up to 4 tokens and E <= 256, with its one-token shortcut; per-expert router up to 8;
+decode kernels below 256 tokens; prefill kernels and the chunked bucketing from
+256, also with E > 256), and an empty batch.  Every token's routing and the bucketing are checked; the
 outputs of every token outside the near-tie window are compared with the oracle."""
 import numpy as np
 import pytest
@@ -28,6 +29,8 @@ CASES = [
     ("e512_k16_t2",   15,   2,  256, 512, 16, 256,   0, "bf16", 0.05, False),
     ("e8_k2_t300",    16, 300,  256,   8, 2, 512, 256, "bf16", 0.05, False),
     ("e33_k4_t1_f32", 17,   1,  256,  33, 4, 256, 256, "f32",  0.05, False),
+    ("e16_k16_t1",    18,   1,  256,  16, 16, 256, 256, "bf16", 0.05, False),
+    ("e300_k8_t260",  19, 260,  256, 300, 8, 256, 256, "bf16", 0.05, True),
 ]
 
 
