@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=8, help="distinct layers cycled by decode steps")
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--graph", type=int, default=1, help="time steps as HIP graph replays")
+    ap.add_argument("--ceilings", type=int, default=1, help="measure copy and bf16 GEMM ceilings")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -154,6 +155,7 @@ def run_workload(name, steps, warmup, rotate, graph=True):
             e.close()
     dom_avg = float(np.mean(dom_ms))
     eager_ms = ms_per_step
+    pct = None
     launch = "eager"
     if graph:
         # G consecutive steps per captured graph (one pass over the rotated layers
@@ -186,6 +188,18 @@ def run_workload(name, steps, warmup, rotate, graph=True):
         t2 = time.perf_counter()
         ms_per_step = (t2 - t1) * 1e3 / (n_rep * G)
         launch = "hip_graph x%d steps" % G
+        # spread of the step time: a separate pass of event-bracketed replays
+        n_pct = max(10, min(60, n_rep))
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_pct)]
+        for r in range(n_pct):
+            pev[r][0].record()
+            graphs[r % n_graphs].replay()
+            pev[r][1].record()
+        torch.cuda.synchronize()
+        per_step = [a.elapsed_time(b) / G for a, b in pev]
+        pct = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
+               "p90": float(np.percentile(per_step, 90)), "replays": n_pct}
         del graphs
     touched = [int((c > 0).sum().item()) for c in counts]
     d_mean = float(np.mean(touched))
@@ -201,6 +215,7 @@ def run_workload(name, steps, warmup, rotate, graph=True):
         "algorithmic_bytes_per_pass": bytes_per_pass,
         "hbm_gbs": bytes_per_pass * passes / (ms_per_step * 1e-3) / 1e9,
         "phases_ms_per_pass": phase_ms,
+        "ms_per_step_percentiles": pct,
         "phases_note": "separate instrumented pass; each phase includes ~4 us of event overhead",
     }
     # dominant kernel roofline (duration from the timed region's events); on the
@@ -239,6 +254,41 @@ def run_workload(name, steps, warmup, rotate, graph=True):
     del layers, ws
     torch.cuda.empty_cache()
     return res
+
+
+def measured_ceilings():
+    """Context for the roofline fractions, measured on the same GPU: a 2 GiB
+    device-to-device copy (GB/s counting read + write) and a bf16 8192^3 matrix
+    product through torch's BLAS (TFLOP/s); medians of 10 timed repetitions."""
+    import torch
+
+    def timed(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return float(np.median(ms))
+
+    nb = 1 << 31
+    src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = timed(lambda: dst.copy_(src))
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    gemm_ms = timed(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2 * nb / (copy_ms * 1e-3) / 1e9, 1),
+            "gemm_bf16_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "note": "2 GiB device copy (read + write bytes) and bf16 8192^3 torch.matmul, medians of 10"}
 
 
 def cpu_baseline(name, min_seconds=10.0, max_tokens=8):
@@ -296,6 +346,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    ceil = measured_ceilings() if args.ceilings else None
     cpu = cpu_baseline(args.workload) if args.cpu_baseline else None
     from synth import workloads as W
     wl = W.WORKLOADS[args.workload]
@@ -312,6 +363,8 @@ def main():
                    "touched_experts_mean": head["touched_experts_mean"]},
         "hbm_gbs": round(head["hbm_gbs"], 1),
         "roofline": head.get("roofline"),
+        "ms_per_step_percentiles": head.get("ms_per_step_percentiles"),
+        "measured_ceilings": ceil,
         "cpu_baseline": cpu,
         "phases_ms": {k: round(v, 5) for k, v in head["phases_ms_per_pass"].items()},
         "workloads": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
