@@ -189,9 +189,11 @@ struct MqDense {
 
 typedef __bf16 mq_bf16x8 __attribute__((ext_vector_type(8)));
 
-template <int NF, int MF, bool A2>
+// XL: the activation planes come from LDS (xl: hi plane of the one token over
+// [k0, k1), the lo plane after it) instead of global memory.
+template <int NF, int MF, bool A2, bool XL>
 __device__ __forceinline__ void mq_dense_chunk(const MqDense &d, int row0, int k0, int k1, int t0, int ks,
-                                               int lane) {
+                                               int lane, const uint16_t *xl) {
     typedef const __attribute__((address_space(1))) mq_u32x4 *gvec;
     typedef const __attribute__((address_space(1))) char *gbyte;
     const int r16 = lane & 15, q4 = lane >> 4;
@@ -228,8 +230,14 @@ __device__ __forceinline__ void mq_dense_chunk(const MqDense &d, int row0, int k
         for (int nf = 0; nf < NF; ++nf) b[s][nf] = *(gvec)(wb + wo[nf]);
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
-            a[s][m] = *(gvec)(xb + xo[m]);
-            if (A2) l[s][m] = *(gvec)(lb + xo[m]);
+            if (XL) {
+                const uint16_t *xp = xl + (k - k0) + 8 * q4;
+                a[s][m] = *(const mq_u32x4 *)xp;
+                if (A2) l[s][m] = *(const mq_u32x4 *)(xp + (k1 - k0));
+            } else {
+                a[s][m] = *(gvec)(xb + xo[m]);
+                if (A2) l[s][m] = *(gvec)(lb + xo[m]);
+            }
         }
     };
     auto mma = [&](int s) {
@@ -302,14 +310,145 @@ __device__ __forceinline__ void mq_dense_wg(const MqDense &d, int wg, int wv, in
     for (int t0 = 0; t0 < d.T; t0 += 64) {
         const int nt = d.T - t0;
         if (nt > 48)
-            mq_dense_chunk<NF, 4, A2>(d, row0, k0, k1, t0, ks, lane);
+            mq_dense_chunk<NF, 4, A2, false>(d, row0, k0, k1, t0, ks, lane, nullptr);
         else if (nt > 32)
-            mq_dense_chunk<NF, 3, A2>(d, row0, k0, k1, t0, ks, lane);
+            mq_dense_chunk<NF, 3, A2, false>(d, row0, k0, k1, t0, ks, lane, nullptr);
         else if (nt > 16)
-            mq_dense_chunk<NF, 2, A2>(d, row0, k0, k1, t0, ks, lane);
+            mq_dense_chunk<NF, 2, A2, false>(d, row0, k0, k1, t0, ks, lane, nullptr);
         else
-            mq_dense_chunk<NF, 1, A2>(d, row0, k0, k1, t0, ks, lane);
+            mq_dense_chunk<NF, 1, A2, false>(d, row0, k0, k1, t0, ks, lane, nullptr);
     }
+}
+
+// Shared rows of a one-token down launch: h = silu(sum_s g[s][k]) * sum_s u[s][k]
+// (splits added in order, 16 loads in flight) over the work-group's k range, as
+// two bf16 planes in LDS (hi = bf16(h), lo = bf16(h - hi)) -- the arithmetic of the
+// digit preparation launch's shared rows -- then the dense rows read them there.
+__device__ __forceinline__ void mq_dense_wg_prep(const MqDense &d, const MqDownPrep &pp, int wg, int wv,
+                                                 int lane, uint16_t *hl) {
+    const int rblocks = d.rows / (64 * 2);
+    const int rb = wg % rblocks, ks = wg / rblocks;
+    const int k0 = ks * d.kps, k1 = min(d.K, k0 + d.kps);
+    if (k0 >= k1) return;
+    const int n = k1 - k0, tid = threadIdx.x;
+    for (int k = tid; k < n; k += 256) {
+        float g = 0.0f, u = 0.0f;
+        for (int sp0 = 0; sp0 < pp.snsplit; sp0 += 16) {
+            float gv[16], uv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t so = (int64_t)min(sp0 + j, pp.snsplit - 1) * pp.sstride + k0 + k;
+                gv[j] = pp.sg[so];
+                uv[j] = pp.su[so];
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (sp0 + j < pp.snsplit) {
+                    g += gv[j];
+                    u += uv[j];
+                }
+        }
+        const float h = g / (1.0f + expf(-g)) * u;
+        const uint16_t hb = mq_f32_to_bf16(h);
+        hl[k] = hb;
+        hl[n + k] = mq_f32_to_bf16(h - mq_bf16_to_f32(hb));
+    }
+    __syncthreads();
+    mq_dense_chunk<2, 1, true, true>(d, rb * 128 + wv * 32, k0, k1, 0, ks, lane, hl);
+}
+
+// The slot row `row` of a one-token down launch: h = silu(sum_s g[s][row]) *
+// sum_s u[s][row] (splits in order), its power-of-two scale, digits and group sums,
+// laid out as one row of the digit preparation's output (xr: [group][digit] 16-byte
+// vectors, xs: [block][quad][plane][4] bf16), the same arithmetic.  Thread i takes
+// elements 8 i .. 8 i + 7 (half a group; the two halves are joined by a lane swap).
+__device__ __forceinline__ void mq_row_prep_lds(const MqDownPrep &pp, int row, mq_u32x4 *xr, uint16_t *xs,
+                                                float *rsc, float *wmax, int tid) {
+    const int G = pp.len / 16;
+    const int e0 = 8 * tid;
+    const bool on = e0 < pp.len;
+    float v[8];
+    {
+        float gs[8], us[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { gs[i] = 0.0f; us[i] = 0.0f; }
+        for (int sp = 0; sp < pp.nsplit; sp += 4) {
+            float4 a[4][2], b[4][2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t off = (int64_t)min(sp + j, pp.nsplit - 1) * pp.split_stride + (int64_t)row * pp.len +
+                                    min(e0, pp.len - 8);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    a[j][i] = ((const float4 *)(pp.g + off))[i];
+                    b[j][i] = ((const float4 *)(pp.u + off))[i];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (sp + j < pp.nsplit) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        gs[4 * i] += a[j][i].x; gs[4 * i + 1] += a[j][i].y;
+                        gs[4 * i + 2] += a[j][i].z; gs[4 * i + 3] += a[j][i].w;
+                        us[4 * i] += b[j][i].x; us[4 * i + 1] += b[j][i].y;
+                        us[4 * i + 2] += b[j][i].z; us[4 * i + 3] += b[j][i].w;
+                    }
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = on ? gs[i] / (1.0f + expf(-gs[i])) * us[i] : 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = mq_wave_max(amax);
+    if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    int ex = 0;
+    if (amax > 0.0f) frexpf(amax, &ex);
+    const float inv_s = amax > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
+    if (tid == 0) *rsc = amax > 0.0f ? ldexpf(1.0f, ex - 14) : 1.0f;
+    // this half group's bytes of the digit dwords: dword s4 holds the digits of the
+    // elements 4 b + s4 of the group, so elements 0..7 fill bytes 0, 1 and elements
+    // 8..15 bytes 2, 3 of every dword
+    const int half = tid & 1, g = tid >> 1;
+    uint32_t hp[4], lp[4];
+    int sum = 0;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        uint32_t h = 0, l = 0;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int x = (int)rintf(v[4 * b + s4] * inv_s);
+            sum += x;
+            const int dh = (x + 128) >> 8;
+            const int dl = x - (dh << 8);
+            h |= ((uint32_t)(dh & 0xFF)) << (8 * (2 * half + b));
+            l |= ((uint32_t)(dl & 0xFF)) << (8 * (2 * half + b));
+        }
+        hp[s4] = h;
+        lp[s4] = l;
+    }
+    mq_u32x4 hi, lo;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        hi[s4] = hp[s4] | (uint32_t)__shfl_xor((int)hp[s4], 1, 64);
+        lo[s4] = lp[s4] | (uint32_t)__shfl_xor((int)lp[s4], 1, 64);
+    }
+    sum += __shfl_xor(sum, 1, 64);
+    if (on && half == 0 && g < G) {
+        xr[2 * g] = hi;
+        xr[2 * g + 1] = lo;
+        const float fs = (float)sum;                           // exact: |sum| <= 2^18
+        const uint16_t bh = mq_f32_to_bf16(fs);
+        const uint16_t bl = mq_f32_to_bf16(fs - mq_bf16_to_f32(bh));
+        const int blk = g >> 4, j = g & 15;
+        xs[blk * 32 + (j >> 2) * 8 + (j & 3)] = bh;
+        xs[blk * 32 + (j >> 2) * 8 + 4 + (j & 3)] = bl;
+    }
+    __syncthreads();
 }
 
 // Rows per work-group of the dense path and its k-split: about 256 work-groups.
@@ -402,12 +541,16 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
                                                 const float *__restrict__ xscale, float *__restrict__ out0,
                                                 float *__restrict__ out1, int out_ld, int64_t split_stride,
                                                 int q2_grid, const MqDense dn, const MqRoute rt,
-                                                int route_on) {
+                                                int route_on, const MqDownPrep pp, int prep_on) {
     __shared__ __attribute__((aligned(16))) mq_u32x4 sW[4][384];           // weight slices, one per wave
     static_assert(sizeof(MqRouteLds) <= sizeof(sW), "routing LDS fits the weight slices");
     __shared__ __attribute__((aligned(16))) mq_u32x4 sA[2][DM_AITEMS];     // activation operands
     __shared__ int s_row[16];
     __shared__ float s_sc[16];
+    // one-token down launch: the unit's activation row prepared here
+    __shared__ __attribute__((aligned(16))) mq_u32x4 s_xr[2 * MQ_DOWN_PREP_MAX_LEN / 16];
+    __shared__ __attribute__((aligned(16))) uint16_t s_xs[MQ_DOWN_PREP_MAX_LEN / 256 * 32];
+    __shared__ float s_rsc, s_wmax[4];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, q4 = lane >> 4;
@@ -415,6 +558,8 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
         // appended work-groups: the shared expert's dense rows
         if (GU)
             mq_dense_wg<4, false>(dn, (int)blockIdx.x - q2_grid, wv, lane);
+        else if (prep_on)
+            mq_dense_wg_prep(dn, pp, (int)blockIdx.x - q2_grid, wv, lane, (uint16_t *)&sW[0][0]);
         else
             mq_dense_wg<2, true>(dn, (int)blockIdx.x - q2_grid, wv, lane);
         return;
@@ -444,11 +589,13 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
                                             (int64_t)tile * tile_bytes);
     mq_bcol wb;
     mq_bcol_load(tb + (int64_t)c0 * 336, lane, wb);      // weights first: needs only the unit
+    const bool lrow = !GU && prep_on;                    // activations from the row prepared here
+    if (lrow) mq_row_prep_lds(pp, p0, s_xr, s_xs, &s_rsc, s_wmax, tid);
     float scv = 0.0f;                                    // row scale, to LDS in the loop
     if (tid < 16) {
         const int ar = tid < nt ? (GU ? urv : p0 + tid) : zrow;
         s_row[tid] = ar;
-        scv = xscale[ar];
+        scv = lrow ? (tid < nt ? s_rsc : 1.0f) : xscale[ar];
     }
     __syncthreads();
     // this thread's three activation items, one per LDS slot so that a wave's
@@ -460,6 +607,7 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
     // against the LDS counter and make every LDS wait in the column wait for it
     typedef const __attribute__((address_space(1))) mq_u32x4 *gvec;
     gvec asrc[3];
+    const mq_u32x4 *lsrc[3];                             // (row prepared here) LDS source, null: zero
     int aslot[3], astep[3];
 #pragma unroll
     for (int n = 0; n < 3; ++n) {
@@ -468,18 +616,24 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
             const int l = it & 63, d = (it >> 6) & 1, kk = it >> 7;
             const int tk = l & 15, g = 4 * kk + (l >> 4);
             asrc[n] = (gvec)(xdig + (int64_t)s_row[tk] * G * 2 + g * 2 + d);
+            lsrc[n] = tk < nt ? s_xr + g * 2 + d : nullptr;
             aslot[n] = it;
             astep[n] = 32;
         } else {
             const int l = it - 512;
             asrc[n] = (gvec)((const mq_u32x4 *)(xsum + (int64_t)s_row[l & 15] * G) + (l >> 4));
+            lsrc[n] = (l & 15) < nt ? (const mq_u32x4 *)s_xs + (l >> 4) : nullptr;
             aslot[n] = it;
             astep[n] = 4;
         }
     }
+    const mq_u32x4 z4 = {0u, 0u, 0u, 0u};
+    auto aload = [&](int n, int c) {
+        return lrow ? (lsrc[n] ? lsrc[n][c * astep[n]] : z4) : asrc[n][c * astep[n]];
+    };
     mq_u32x4 ab[3];
 #pragma unroll
-    for (int n = 0; n < 3; ++n) ab[n] = asrc[n][c0 * astep[n]];
+    for (int n = 0; n < 3; ++n) ab[n] = aload(n, c0);
 
     mq_f32x4 tot[4];
 #pragma unroll
@@ -496,7 +650,7 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
         if (c + 1 < c1) {
             mq_bcol_load(tb + (int64_t)(c + 1) * 336, lane, wb);
 #pragma unroll
-            for (int n = 0; n < 3; ++n) ab[n] = asrc[n][(c + 1) * astep[n]];
+            for (int n = 0; n < 3; ++n) ab[n] = aload(n, c + 1);
         }
         __syncthreads();
         mq_acol a;
@@ -552,7 +706,8 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
                      int kblocks, const int4 *units, int max_units, const int32_t *urow, int zrow,
                      int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
-                     int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route, hipStream_t st) {
+                     int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route,
+                     const MqDownPrep *prep, hipStream_t st) {
     if (tiles % 4) return MOE_Q2_EUNSUPPORTED;
     if (gu && !urow) return MOE_Q2_EINVAL;
     if (route && (!gu || route->T < 1 || route->T > MQ_TOPK_BUCKET_MAX_T || route->E > MQ_ROUTE_MAX_E ||
@@ -560,6 +715,11 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
         return MOE_Q2_EINVAL;
     const MqRoute rt = route ? *route : MqRoute{};
     const int route_on = route ? 1 : 0;
+    if (prep && (gu || prep->len > MQ_DOWN_PREP_MAX_LEN || prep->len != kblocks * MQ_QK || prep->nsplit < 1 ||
+                 (dense && (dense->T != 1 || !prep->sg || prep->snsplit < 1))))
+        return MOE_Q2_EINVAL;
+    const MqDownPrep pp = prep ? *prep : MqDownPrep{};
+    const int prep_on = prep ? 1 : 0;
     int nsplit = 1, cps = kblocks;
     mq_dec_split(max_units, tiles, kblocks, gu ? MQ_DEC_SPLIT_GU : MQ_DEC_SPLIT_D, &nsplit, &cps);
     const int64_t q2_grid = (int64_t)max_units * nsplit * (tiles / 4);
@@ -580,6 +740,8 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
         dn.out_ld = dense->out_ld;
         dn.split_stride = dense->split_stride;
         mq_dense_split(dense->rows, dense->K, nf, &dn.nsplit, &dn.kps);
+        // (the in-launch shared SwiGLU holds 2 x kps bf16 in the weight-slice LDS)
+        if (prep && 4 * dn.kps > (int)sizeof(mq_u32x4) * 4 * 384) return MOE_Q2_EUNSUPPORTED;
         if (dn.nsplit != dense->nsplit) return MOE_Q2_EINVAL;       // workspace sized for another split
         dgrid = (int64_t)(dense->rows / (64 * nf)) * dn.nsplit;
         dn.grid = (int)dgrid;
@@ -591,12 +753,12 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
         hipLaunchKernelGGL(k_q2_mma<true>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
                            expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units, urow, zrow,
                            trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
-                           split_stride, (int)q2_grid, dn, rt, route_on);
+                           split_stride, (int)q2_grid, dn, rt, route_on, pp, prep_on);
     else
         hipLaunchKernelGGL(k_q2_mma<false>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
                            expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units, urow, zrow,
                            trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
-                           split_stride, (int)q2_grid, dn, rt, route_on);
+                           split_stride, (int)q2_grid, dn, rt, route_on, pp, prep_on);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

@@ -108,6 +108,20 @@ struct MqRoute {
     int32_t *urow;
     int zrow;
 };
+// One-token batches: the down launch prepares its own activations instead of reading
+// the digit preparation launch's output -- the SwiGLU of the gate/up split partials
+// of its unit's slot row (digits, group sums, scale: the same arithmetic) and, for
+// the appended shared rows, the shared SwiGLU of the dense partials over the
+// work-group's k range (two bf16 planes).  len <= MQ_DOWN_PREP_MAX_LEN.
+#define MQ_DOWN_PREP_MAX_LEN 2048
+struct MqDownPrep {
+    const float *g, *u;        // routed gate/up split partials [nsplit][rows][len]
+    int nsplit, len;
+    int64_t split_stride;
+    const float *sg, *su;      // shared dense partials [snsplit][1][Is] (or null)
+    int snsplit;
+    int64_t sstride;
+};
 // units: max_units records, those past the last unit with slot count 0; urow (gate/up):
 // the [max_units][16] row table of the bucketing; down reads the rows of its slots.
 // route (gate/up only, optional): route in the launch instead of reading units/urow.
@@ -115,7 +129,8 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
                      int kblocks, const int4 *units, int max_units, const int32_t *urow, int zrow,
                      int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
-                     int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route, hipStream_t st);
+                     int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route,
+                     const MqDownPrep *prep, hipStream_t st);
 int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
                         int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                         int max_units, const int32_t *perm, int topk, const void *xdig,

@@ -455,14 +455,23 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
                                                      w.dec_units, urow, T, S, xq,
                                                      (const uint32_t *)xg, xs, gp, up, I, gstride,
                                                      w.fused ? &dgu : nullptr, route_in_gu ? &rt : nullptr,
-                                                     st));
-        MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_swiglu_digits(gp, up, w.dsplit_gu, gstride, S, I, I, hq,
-                                                                (uint32_t *)hg, hsc, w.fused ? &shs : nullptr,
-                                                                st));
+                                                     nullptr, st));
+        // one token (shared expert fused): the down launch prepares its own activations
+        const bool prep_in_down = T == 1 && w.fused && I <= MQ_DOWN_PREP_MAX_LEN;
+        MqDownPrep dp = {};
+        if (prep_in_down) {
+            dp = MqDownPrep{gp, up, w.dsplit_gu, (int)I, gstride, shs.g, shs.u, shs.nsplit, shs.split_stride};
+            MQ_PHASE(MOE_Q2_PH_PREP_H, MOE_Q2_OK);
+        } else {
+            MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_swiglu_digits(gp, up, w.dsplit_gu, gstride, S, I, I, hq,
+                                                                    (uint32_t *)hg, hsc, w.fused ? &shs : nullptr,
+                                                                    st));
+        }
         MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_mma(0, experts_q2, ebytes, 2 * mat_gu, H / 64, I / MQ_QK,
                                                   units, w.dec_units, nullptr, S, S, hq,
                                                   (const uint32_t *)hg, hsc, y, nullptr, H, ystride,
-                                                  w.fused ? &dd : nullptr, nullptr, st));
+                                                  w.fused ? &dd : nullptr, nullptr, prep_in_down ? &dp : nullptr,
+                                                  st));
     }
     const int ysplit = (prefill || valu) ? 1 : w.dsplit_d;
     const int64_t ystride = (int64_t)(T * K + 1) * H;
