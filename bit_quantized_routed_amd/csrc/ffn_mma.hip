@@ -118,9 +118,11 @@ struct mq_acol { mq_i32x4 hi[4], lo[4]; mq_s16x4 sh, sl; };
 
 // One 64-row block column from the wave's LDS slice into the 4 N fragments:
 // integer products of both activation digits on the i8 matrix cores, the min
-// term on the bf16 matrix cores, and the per-block fold with d and dmin.
+// term on the bf16 matrix cores, and the per-block fold with d and dmin -- of all
+// 4 of each lane's token rows, or (one = true, a wave-uniform flag: a unit of one
+// slot) only of the first, the others being padding whose sums are never stored.
 __device__ __forceinline__ void mq_mma_column(const uint32_t *__restrict__ my, int r16, int q4,
-                                              const mq_acol &a, mq_f32x4 (&tot)[4]) {
+                                              const mq_acol &a, mq_f32x4 (&tot)[4], bool one) {
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) {
         const uint32_t *blk = my + (16 * nf + r16) * MQ_BLOCK_DWORDS;
@@ -140,10 +142,13 @@ __device__ __forceinline__ void mq_mma_column(const uint32_t *__restrict__ my, i
         const uint32_t dd = blk[20];
         const float d = mq_h2f((uint16_t)(dd & 0xFFFFu));
         const float dmin = mq_h2f((uint16_t)(dd >> 16));
+        tot[nf][0] = fmaf(d, (float)((ih[0] << 8) + il[0]), fmaf(-dmin, am[0], tot[nf][0]));
+        if (!one) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float qv = (float)((ih[i] << 8) + il[i]);
-            tot[nf][i] = fmaf(d, qv, fmaf(-dmin, am[i], tot[nf][i]));
+            for (int i = 1; i < 4; ++i) {
+                const float qv = (float)((ih[i] << 8) + il[i]);
+                tot[nf][i] = fmaf(d, qv, fmaf(-dmin, am[i], tot[nf][i]));
+            }
         }
     }
 }
@@ -639,6 +644,7 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) tot[nf] = (mq_f32x4){0.f, 0.f, 0.f, 0.f};
     const uint32_t *myd = (const uint32_t *)sW[wv];
+    const bool one = __builtin_amdgcn_readfirstlane(nt) == 1;
     int buf = 0;
     for (int c = c0; c < c1; ++c) {
         if (tid < 16) s_sc[tid] = scv;
@@ -662,7 +668,7 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
         const mq_u32x4 sv = sA[buf][512 + lane];
         a.sh = __builtin_bit_cast(mq_s16x4, (uint2){sv[0], sv[1]});
         a.sl = __builtin_bit_cast(mq_s16x4, (uint2){sv[2], sv[3]});
-        mq_mma_column(myd, r16, q4, a, tot);
+        mq_mma_column(myd, r16, q4, a, tot, one);
         buf ^= 1;
     }
     // D layout: lane l, element i -> token 4*(l/16) + i, row slot 16*nf + l%16
