@@ -826,11 +826,22 @@ int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit,
 // two 16-row fragments (SWIGLU: the gate fragment 16*(w%2).. and the up fragment
 // 32 + 16*(w%2)..  of the same rows; PLAIN: fragments 2*(w%2), 2*(w%2)+1), times
 // all MF token fragments.  Per block column, the 4 tiles' weights (21 KB) and the
-// unit's activation digits + group sums (576 B per token) are staged in LDS, so a
-// token's activations are read once per 256 rows; the next block column is
-// prefetched into registers during the compute.
-#define PF_TS 148   // LDS token stride in dwords: 576 B of data + 16 B pad (conflict-free reads)
-
+// unit's activation digits + group sums (576 B per token) are staged in LDS by
+// direct global-to-LDS loads (16 bytes per lane, 1 KB per wave instruction), so a
+// token's activations are read from memory once per 256 rows and no registers hold
+// the staged data; the next column is loaded while the current one is multiplied.
+// Within a column a wave expands its two fragments' q*sc operands once and then
+// takes one token fragment at a time (four integer chains, the min term, the fold),
+// so the accumulators of a single fragment are live: with the staging registers gone
+// this leaves room for 5 token fragments, units of up to 80 slots (at about 64 slots
+// per expert, 64-slot units would give half the experts a second pass over their
+// weights for a few tokens).
+//
+// LDS layout of one buffer: weights = the 4 tiles' column pieces in global order;
+// activations = [token][32 16-byte digit words] with word w of token t at position
+// w ^ (t & 15), then [token][4 sum words] with word q at q ^ ((t & 15) >> 2); the
+// XOR swizzles keep the 16 lanes that read one word of 16 different tokens on
+// distinct banks.
 template <bool SWIGLU, int MF>
 __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ experts,
                                                    int64_t expert_bytes, int64_t mat_off, int rows,
@@ -842,14 +853,19 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                                                    const float *__restrict__ xscale,
                                                    float *__restrict__ out) {
     constexpr int NTOK = 16 * MF;
-    constexpr int NPB = (4 * 336 + 511) / 512;          // weight pieces per thread
-    constexpr int NPD = NTOK * 32 / 512;                // digit pieces per thread
-    static_assert(NTOK * 32 % 512 == 0 && NTOK * 4 <= 512, "piece split");
-    // sB is padded to whole pieces so that no store is predicated
-    // double-buffered: column b + 1 is stored while column b is multiplied
-    __shared__ __attribute__((aligned(16))) uint32_t sB[2][4 * NPB * 512];
-    __shared__ __attribute__((aligned(16))) uint32_t sA[2][NTOK * PF_TS];
-    __shared__ int arow_s[NTOK];
+    constexpr int NWJ = 4 * 336 / 64;                   // weight loads (1 KB each)
+    constexpr int NDJ = NTOK / 2;                       // digit loads (2 tokens each)
+    constexpr int NSJ = NTOK * 4 / 64;                  // sum loads (16 tokens each)
+    constexpr int NJ = NDJ + NSJ + NWJ;
+    constexpr int JPW = (NJ + 7) / 8;                   // loads per wave (at most)
+    constexpr int SUMS = NTOK * 128;                    // dword offset of the sum words
+    static_assert(4 * 336 % 64 == 0 && NTOK % 16 == 0, "load split");
+    // one LDS array for all staging (weights, activations, token rows)
+    constexpr int SB_SZ = NWJ * 256, SA_SZ = NTOK * 144, SA_OFF = 2 * SB_SZ;
+    __shared__ __attribute__((aligned(16))) uint32_t smem[2 * SB_SZ + 2 * SA_SZ + NTOK];
+    int *arow_s = (int *)(smem + 2 * SB_SZ + 2 * SA_SZ);
+    typedef __attribute__((address_space(1))) void gvoid;
+    typedef __attribute__((address_space(3))) void lvoid;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, q4 = lane >> 4;
@@ -858,9 +874,10 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     const int nslot1 = SWIGLU ? 32 + 16 * hw : 32 * hw + 16;
     const int stiles = rows / (SWIGLU ? 32 : 64) / 4;
     const int U = units_hdr[0];
-    const int G = kblocks * 16;
     const int64_t tile_bytes = (int64_t)kblocks * 64 * MQ_BLOCK_BYTES;
     const mq_i32x4 zi = {0, 0, 0, 0};
+    const int sw = r16;                                  // digit word swizzle of this lane's token
+    const int ssw = 4 * (q4 ^ (r16 >> 2));               // sum word position (dwords)
 
     for (int wu = blockIdx.x; wu < U * stiles; wu += gridDim.x) {
         const int u = wu / stiles, st = wu - u * stiles;
@@ -875,34 +892,47 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
         }
         __syncthreads();
         const uint8_t *tb = experts + (int64_t)e * expert_bytes + mat_off + (int64_t)(4 * st) * tile_bytes;
-        // this thread's activation rows: digit pieces j = tid + 512 n (token j / 32, 16-byte
-        // word j % 32), sum piece tid (token tid / 4, word tid % 4) for tid < NTOK * 4
-        const bool has_sum = tid < NTOK * 4;             // whole waves
-        // per-thread 32-bit byte offsets from uniform bases (scalar base + vector
-        // offset addressing: the column step only moves the scalar base)
-        typedef const __attribute__((address_space(1))) mq_u32x4 *gvec;
-        typedef const __attribute__((address_space(1))) char *gbyte;
-        uint32_t wo[NPB], dofs[NPD];
+        // load j = wv + 8 n of a column: digits of tokens 2j, 2j + 1 (j < NDJ), sums of
+        // tokens 16 (j - NDJ) .. +15, or 1 KB of the 4 tiles' weight pieces; each lane's
+        // byte offset from the column's base is fixed for the work item
+        uint32_t voff[JPW];
 #pragma unroll
-        for (int n = 0; n < NPB; ++n) {
-            const int j = min(tid + 512 * n, 4 * 336 - 1);
-            const int tl = j / 336, w = j - tl * 336;
-            wo[n] = (uint32_t)(tl * tile_bytes + w * 16);
+        for (int n = 0; n < JPW; ++n) {
+            const int j = wv + 8 * n;
+            uint32_t o = 0;
+            if (j < NDJ) {
+                const int t = 2 * j + (lane >> 5), w = (lane & 31) ^ (t & 15);
+                o = (uint32_t)((arow_s[t] * kblocks * 32 + w) * 16);
+            } else if (j < NDJ + NSJ) {
+                const int q = 64 * (j - NDJ) + lane, t = q >> 2, w = (q & 3) ^ ((t & 15) >> 2);
+                o = (uint32_t)((arow_s[t] * kblocks * 16 + 4 * w) * 4);
+            } else if (j < NJ) {
+                const int p = 64 * (j - NDJ - NSJ) + lane, tl = p / 336, w = p - tl * 336;
+                o = (uint32_t)(tl * tile_bytes + w * 16);
+            }
+            voff[n] = o;
         }
+        // column b into buffer buf; digit and sum loads only for the first mfc token
+        // fragments (the rest are never read)
+        auto dma = [&](int b, int buf, int mfc) {
+            const char *db = (const char *)xdig + (int64_t)b * 512;
+            const char *sb = (const char *)xsum + (int64_t)b * 64;
+            const char *wb = (const char *)tb + (int64_t)b * 5376;
 #pragma unroll
-        for (int n = 0; n < NPD; ++n)
-            dofs[n] = (uint32_t)((arow_s[(tid + 512 * n) >> 5] * G * 2 + ((tid + 512 * n) & 31)) * 16);
-        const uint32_t so = (uint32_t)((arow_s[min(tid >> 2, NTOK - 1)] * kblocks * 16 + (tid & 3) * 4) * 4);
-        mq_u32x4 pb[NPB], pd[NPD], ps;
-        auto load = [&](int b) {
-            const gbyte wb = (gbyte)(tb + (int64_t)b * 5376);
-            const gbyte db = (gbyte)(xdig + (int64_t)b * 32);
-            const gbyte sb = (gbyte)(xsum + (int64_t)b * 16);
-#pragma unroll
-            for (int n = 0; n < NPB; ++n) pb[n] = *(gvec)(wb + wo[n]);
-#pragma unroll
-            for (int n = 0; n < NPD; ++n) pd[n] = *(gvec)(db + dofs[n]);
-            ps = *(gvec)(sb + so);
+            for (int n = 0; n < JPW; ++n) {
+                const int j = wv + 8 * n;
+                if (j < NDJ) {
+                    if (j < 8 * mfc)
+                        __builtin_amdgcn_global_load_lds((gvoid *)(db + voff[n]), (lvoid *)(smem + SA_OFF + buf * SA_SZ + 256 * j), 16, 0, 0);
+                } else if (j < NDJ + NSJ) {
+                    if (j - NDJ < mfc)
+                        __builtin_amdgcn_global_load_lds((gvoid *)(sb + voff[n]),
+                                                         (lvoid *)(smem + SA_OFF + buf * SA_SZ + SUMS + 256 * (j - NDJ)), 16, 0, 0);
+                } else if (j < NJ) {
+                    __builtin_amdgcn_global_load_lds((gvoid *)(wb + voff[n]),
+                                                     (lvoid *)(smem + buf * SB_SZ + 256 * (j - NDJ - NSJ)), 16, 0, 0);
+                }
+            }
         };
         // MFC token fragments carry tokens (the rest of MF are skipped): one copy of the
         // column loop per count, so no fragment test sits in the loop
@@ -911,54 +941,48 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
             mq_f32x4 tot[MFC][2];
 #pragma unroll
             for (int m = 0; m < MFC; ++m) { tot[m][0] = (mq_f32x4){0.f, 0.f, 0.f, 0.f}; tot[m][1] = tot[m][0]; }
-            auto store = [&](int buf) {
-#pragma unroll
-                for (int n = 0; n < NPB; ++n) *(mq_u32x4 *)(sB[buf] + 4 * (tid + 512 * n)) = pb[n];
-#pragma unroll
-                for (int n = 0; n < NPD; ++n) {
-                    const int j = tid + 512 * n;
-                    *(mq_u32x4 *)(sA[buf] + (j >> 5) * PF_TS + 4 * (j & 31)) = pd[n];
-                }
-                if (has_sum) *(mq_u32x4 *)(sA[buf] + (tid >> 2) * PF_TS + 128 + 4 * (tid & 3)) = ps;
-            };
-            // One barrier per column: the buffer written in step b (column b + 1) was
+            // One barrier per column: the buffer loaded during step b (column b + 1) was
             // last read in step b - 1, which every wave finished before that step's
-            // barrier.  Loads past the last column repeat it (in bounds, stored into
-            // the idle buffer and never read), so no load or store is conditional.
-            load(0);
-            store(0);
-            load(min(1, kblocks - 1));
+            // barrier; each wave waits for its own loads before the barrier.
+            dma(0, 0, MFC);
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             for (int b = 0; b < kblocks; ++b) {
                 const int cur = b & 1;
-                const uint32_t *blk0 = sB[cur] + (tw * 64 + nslot0 + r16) * MQ_BLOCK_DWORDS;
-                const uint32_t *blk1 = sB[cur] + (tw * 64 + nslot1 + r16) * MQ_BLOCK_DWORDS;
-                const uint32_t *sAc = sA[cur];
-                mq_i32x4 hi[MFC][2], lo[MFC][2];
+                if (b + 1 < kblocks) dma(b + 1, cur ^ 1, MFC);
+                const uint32_t *blk0 = smem + cur * SB_SZ + (tw * 64 + nslot0 + r16) * MQ_BLOCK_DWORDS;
+                const uint32_t *blk1 = smem + cur * SB_SZ + (tw * 64 + nslot1 + r16) * MQ_BLOCK_DWORDS;
+                const uint32_t *sAc = smem + SA_OFF + cur * SA_SZ;
+                // both fragments' q*sc operands of the column, expanded once and kept
+                // across the token fragments
+                mq_i32x4 b0[4], b1[4];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int g = 4 * kk + q4;
-                    const mq_i32x4 b0 = mq_codes_x_scale(blk0[4 + g], __builtin_amdgcn_ubfe(blk0[kk], 8 * q4, 4));
-                    const mq_i32x4 b1 = mq_codes_x_scale(blk1[4 + g], __builtin_amdgcn_ubfe(blk1[kk], 8 * q4, 4));
-#pragma unroll
-                    for (int m = 0; m < MFC; ++m) {
-                        const uint32_t *ap = sAc + (16 * m + r16) * PF_TS + 8 * g;
-                        const mq_i32x4 ah = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)ap);
-                        const mq_i32x4 al = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(ap + 4));
-                        // the first step of each chain starts from zero (no accumulator to clear)
-                        hi[m][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b0, kk ? hi[m][0] : zi, 0, 0, 0);
-                        lo[m][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b0, kk ? lo[m][0] : zi, 0, 0, 0);
-                        hi[m][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b1, kk ? hi[m][1] : zi, 0, 0, 0);
-                        lo[m][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b1, kk ? lo[m][1] : zi, 0, 0, 0);
-                    }
+                    b0[kk] = mq_codes_x_scale(blk0[4 + g], __builtin_amdgcn_ubfe(blk0[kk], 8 * q4, 4));
+                    b1[kk] = mq_codes_x_scale(blk1[4 + g], __builtin_amdgcn_ubfe(blk1[kk], 8 * q4, 4));
                 }
                 const mq_s16x4 bm0 = mq_mins_bf16(blk0[q4]), bm1 = mq_mins_bf16(blk1[q4]);
                 const uint32_t dd0 = blk0[20], dd1 = blk1[20];
                 const float d0 = mq_h2f((uint16_t)(dd0 & 0xFFFFu)), m0 = mq_h2f((uint16_t)(dd0 >> 16));
                 const float d1 = mq_h2f((uint16_t)(dd1 & 0xFFFFu)), m1 = mq_h2f((uint16_t)(dd1 >> 16));
+                // one token fragment at a time: its four integer chains, the min term, the fold
 #pragma unroll
                 for (int m = 0; m < MFC; ++m) {
-                    const mq_u32x4 xv = *(const mq_u32x4 *)(sAc + (16 * m + r16) * PF_TS + 128 + 4 * q4);
+                    const uint32_t *ap = sAc + (16 * m + r16) * 128;
+                    mq_i32x4 hi0, lo0, hi1, lo1;
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const int g = 4 * kk + q4;
+                        const mq_i32x4 ah = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(ap + 4 * ((2 * g) ^ sw)));
+                        const mq_i32x4 al = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(ap + 4 * ((2 * g + 1) ^ sw)));
+                        // the first step of each chain starts from zero (no accumulator to clear)
+                        hi0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b0[kk], kk ? hi0 : zi, 0, 0, 0);
+                        lo0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b0[kk], kk ? lo0 : zi, 0, 0, 0);
+                        hi1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b1[kk], kk ? hi1 : zi, 0, 0, 0);
+                        lo1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b1[kk], kk ? lo1 : zi, 0, 0, 0);
+                    }
+                    const mq_u32x4 xv = *(const mq_u32x4 *)(sAc + SUMS + (16 * m + r16) * 16 + ssw);
                     const mq_s16x4 xh = __builtin_bit_cast(mq_s16x4, (uint2){xv[0], xv[1]});
                     const mq_s16x4 xl = __builtin_bit_cast(mq_s16x4, (uint2){xv[2], xv[3]});
                     const mq_f32x4 zf = {0.f, 0.f, 0.f, 0.f};
@@ -968,14 +992,11 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                     a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, bm1, a1, 0, 0, 0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        tot[m][0][i] = fmaf(d0, (float)((hi[m][0][i] << 8) + lo[m][0][i]),
-                                            fmaf(-m0, a0[i], tot[m][0][i]));
-                        tot[m][1][i] = fmaf(d1, (float)((hi[m][1][i] << 8) + lo[m][1][i]),
-                                            fmaf(-m1, a1[i], tot[m][1][i]));
+                        tot[m][0][i] = fmaf(d0, (float)((hi0[i] << 8) + lo0[i]), fmaf(-m0, a0[i], tot[m][0][i]));
+                        tot[m][1][i] = fmaf(d1, (float)((hi1[i] << 8) + lo1[i]), fmaf(-m1, a1[i], tot[m][1][i]));
                     }
                 }
-                store(cur ^ 1);
-                load(min(b + 2, kblocks - 1));
+                __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
             }
             // outputs: lane holds tokens 16m + 4*q4 + i of row slots (nslot0|nslot1) + r16
@@ -1000,13 +1021,15 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
             }
         };
         const int mfa = (nt + 15) >> 4;                  // 1..MF, uniform
-        static_assert(MF == 4, "one loop copy per fragment count 1..4");
-        if (mfa >= 4) run(std::integral_constant<int, 4>{});
+        static_assert(MF == 5, "one loop copy per fragment count 1..5");
+        if (mfa >= 5) run(std::integral_constant<int, 5>{});
+        else if (mfa == 4) run(std::integral_constant<int, 4>{});
         else if (mfa == 3) run(std::integral_constant<int, 3>{});
         else if (mfa == 2) run(std::integral_constant<int, 2>{});
         else run(std::integral_constant<int, 1>{});
     }
 }
+
 
 int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
                         int rows, int kblocks, const int32_t *units_hdr, const int4 *units,

@@ -6,7 +6,7 @@
 #define FD_TCH 4        // slots per work unit of the vector-ALU decode kernel
 #define MMA_TCH 16      // slots per work unit of the matrix-core decode kernel
 #define MQ_TOPK_BUCKET_MAX_T 4   // largest batch whose bucketing runs in the top-K launch
-#define PF_MF 4         // token fragments per unit of the prefill kernel
+#define PF_MF 5         // token fragments per unit of the prefill kernel
 #define PF_TCH (16 * PF_MF)
 
 int mq_launch_router(const void *x, int bf16, const float *wr, const float *bias, int T, int H,
