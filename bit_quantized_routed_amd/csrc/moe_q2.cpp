@@ -133,7 +133,7 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
         w.sp = take(c, (pgu > pd ? pgu : pd) * 4);
         w.shi = take(c, (size_t)T * Is * 2);
         w.slo = take(c, (size_t)T * Is * 2);
-        w.ysh = take(c, (size_t)T * H * 4);
+        if (w.split_d > 1) w.ysh = take(c, (size_t)T * H * 4);
     }
     w.total = c;
     return w;
@@ -348,8 +348,12 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         if ((rc = mq_launch_gemm_bf16(shi, slo, Is, shared_w + (size_t)2 * Is * H, Is, T, H, Is,
                                       w.split_d, P, sst)))
             return rc;
-        ysh = (float *)(ws + w.ysh);
-        if ((rc = mq_launch_sum_partials(P, w.split_d, (int64_t)T * H, ysh, sst))) return rc;
+        if (w.split_d == 1) {
+            ysh = P;                                     // one split: the product is the sum
+        } else {
+            ysh = (float *)(ws + w.ysh);
+            if ((rc = mq_launch_sum_partials(P, w.split_d, (int64_t)T * H, ysh, sst))) return rc;
+        }
     }
     if ((rc = mark_on(MOE_Q2_PH_SHARED, 1, sst))) return rc;
     if (side) {
