@@ -837,11 +837,12 @@ int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit,
 // per expert, 64-slot units would give half the experts a second pass over their
 // weights for a few tokens).
 //
-// LDS layout of one buffer: weights = the 4 tiles' column pieces in global order;
-// activations = [token][32 16-byte digit words] with word w of token t at position
+// LDS layout: the two activation buffers, then the two weight buffers (a fragment's
+// activation offset, at most 32 KB, is then a constant of the read instruction).
+// Activations = [token][32 16-byte digit words] with word w of token t at position
 // w ^ (t & 15), then [token][4 sum words] with word q at q ^ ((t & 15) >> 2); the
 // XOR swizzles keep the 16 lanes that read one word of 16 different tokens on
-// distinct banks.
+// distinct banks.  Weights = the 4 tiles' column pieces in global order.
 template <bool SWIGLU, int MF>
 __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ experts,
                                                    int64_t expert_bytes, int64_t mat_off, int rows,
@@ -861,7 +862,7 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     constexpr int SUMS = NTOK * 128;                    // dword offset of the sum words
     static_assert(4 * 336 % 64 == 0 && NTOK % 16 == 0, "load split");
     // one LDS array for all staging (weights, activations, token rows)
-    constexpr int SB_SZ = NWJ * 256, SA_SZ = NTOK * 144, SA_OFF = 2 * SB_SZ;
+    constexpr int SB_SZ = NWJ * 256, SA_SZ = NTOK * 144, SB_OFF = 2 * SA_SZ;
     __shared__ __attribute__((aligned(16))) uint32_t smem[2 * SB_SZ + 2 * SA_SZ + NTOK];
     int *arow_s = (int *)(smem + 2 * SB_SZ + 2 * SA_SZ);
     typedef __attribute__((address_space(1))) void gvoid;
@@ -878,6 +879,13 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     const mq_i32x4 zi = {0, 0, 0, 0};
     const int sw = r16;                                  // digit word swizzle of this lane's token
     const int ssw = 4 * (q4 ^ (r16 >> 2));               // sum word position (dwords)
+    // this lane's digit words of MFMA step kk (d = 0 hi, 1 lo) in its token's row of a
+    // buffer, in dwords; fragment m adds 16 * 128 m (a constant of the LDS read)
+    int xo[4][2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int d = 0; d < 2; ++d) xo[kk][d] = r16 * 128 + 4 * ((2 * (4 * kk + q4) + d) ^ sw);
 
     for (int wu = blockIdx.x; wu < U * stiles; wu += gridDim.x) {
         const int u = wu / stiles, st = wu - u * stiles;
@@ -923,14 +931,14 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                 const int j = wv + 8 * n;
                 if (j < NDJ) {
                     if (j < 8 * mfc)
-                        __builtin_amdgcn_global_load_lds((gvoid *)(db + voff[n]), (lvoid *)(smem + SA_OFF + buf * SA_SZ + 256 * j), 16, 0, 0);
+                        __builtin_amdgcn_global_load_lds((gvoid *)(db + voff[n]), (lvoid *)(smem + buf * SA_SZ + 256 * j), 16, 0, 0);
                 } else if (j < NDJ + NSJ) {
                     if (j - NDJ < mfc)
                         __builtin_amdgcn_global_load_lds((gvoid *)(sb + voff[n]),
-                                                         (lvoid *)(smem + SA_OFF + buf * SA_SZ + SUMS + 256 * (j - NDJ)), 16, 0, 0);
+                                                         (lvoid *)(smem + buf * SA_SZ + SUMS + 256 * (j - NDJ)), 16, 0, 0);
                 } else if (j < NJ) {
                     __builtin_amdgcn_global_load_lds((gvoid *)(wb + voff[n]),
-                                                     (lvoid *)(smem + buf * SB_SZ + 256 * (j - NDJ - NSJ)), 16, 0, 0);
+                                                     (lvoid *)(smem + SB_OFF + buf * SB_SZ + 256 * (j - NDJ - NSJ)), 16, 0, 0);
                 }
             }
         };
@@ -950,9 +958,9 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
             for (int b = 0; b < kblocks; ++b) {
                 const int cur = b & 1;
                 if (b + 1 < kblocks) dma(b + 1, cur ^ 1, MFC);
-                const uint32_t *blk0 = smem + cur * SB_SZ + (tw * 64 + nslot0 + r16) * MQ_BLOCK_DWORDS;
-                const uint32_t *blk1 = smem + cur * SB_SZ + (tw * 64 + nslot1 + r16) * MQ_BLOCK_DWORDS;
-                const uint32_t *sAc = smem + SA_OFF + cur * SA_SZ;
+                const uint32_t *blk0 = smem + SB_OFF + cur * SB_SZ + (tw * 64 + nslot0 + r16) * MQ_BLOCK_DWORDS;
+                const uint32_t *blk1 = smem + SB_OFF + cur * SB_SZ + (tw * 64 + nslot1 + r16) * MQ_BLOCK_DWORDS;
+                const uint32_t *sAc = smem + cur * SA_SZ;
                 // both fragments' q*sc operands of the column, expanded once and kept
                 // across the token fragments
                 mq_i32x4 b0[4], b1[4];
@@ -969,13 +977,11 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                 // one token fragment at a time: its four integer chains, the min term, the fold
 #pragma unroll
                 for (int m = 0; m < MFC; ++m) {
-                    const uint32_t *ap = sAc + (16 * m + r16) * 128;
                     mq_i32x4 hi0, lo0, hi1, lo1;
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
-                        const int g = 4 * kk + q4;
-                        const mq_i32x4 ah = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(ap + 4 * ((2 * g) ^ sw)));
-                        const mq_i32x4 al = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(ap + 4 * ((2 * g + 1) ^ sw)));
+                        const mq_i32x4 ah = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(sAc + xo[kk][0] + 2048 * m));
+                        const mq_i32x4 al = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(sAc + xo[kk][1] + 2048 * m));
                         // the first step of each chain starts from zero (no accumulator to clear)
                         hi0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b0[kk], kk ? hi0 : zi, 0, 0, 0);
                         lo0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b0[kk], kk ? lo0 : zi, 0, 0, 0);
