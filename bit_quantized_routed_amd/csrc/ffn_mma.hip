@@ -863,8 +863,7 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     static_assert(4 * 336 % 64 == 0 && NTOK % 16 == 0, "load split");
     // one LDS array for all staging (weights, activations, token rows)
     constexpr int SB_SZ = NWJ * 256, SA_SZ = NTOK * 144, SB_OFF = 2 * SA_SZ;
-    __shared__ __attribute__((aligned(16))) uint32_t smem[2 * SB_SZ + 2 * SA_SZ + NTOK];
-    int *arow_s = (int *)(smem + 2 * SB_SZ + 2 * SA_SZ);
+    __shared__ __attribute__((aligned(16))) uint32_t smem[2 * SB_SZ + 2 * SA_SZ + 2 * NTOK];
     typedef __attribute__((address_space(1))) void gvoid;
     typedef __attribute__((address_space(3))) void lvoid;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -887,61 +886,86 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
 #pragma unroll
         for (int d = 0; d < 2; ++d) xo[kk][d] = r16 * 128 + 4 * ((2 * (4 * kk + q4) + d) ^ sw);
 
-    for (int wu = blockIdx.x; wu < U * stiles; wu += gridDim.x) {
-        const int u = wu / stiles, st = wu - u * stiles;
-        const int4 un = units[u];
-        const int e = un.x, p0 = un.y, nt = un.z;
-        __syncthreads();
-        // token rows of the unit; slots past nt repeat the last token (their sums are
-        // computed and never stored)
-        for (int i = tid; i < NTOK; i += 512) {
-            const int slot = p0 + min(i, nt - 1);
-            arow_s[i] = SWIGLU ? perm[slot] / topk : slot;
-        }
-        __syncthreads();
-        const uint8_t *tb = experts + (int64_t)e * expert_bytes + mat_off + (int64_t)(4 * st) * tile_bytes;
-        // load j = wv + 8 n of a column: digits of tokens 2j, 2j + 1 (j < NDJ), sums of
-        // tokens 16 (j - NDJ) .. +15, or 1 KB of the 4 tiles' weight pieces; each lane's
-        // byte offset from the column's base is fixed for the work item
-        uint32_t voff[JPW];
+    // Work items blockIdx.x, + gridDim.x, ...  While an item runs, the next one's token
+    // rows are loaded (into the other half of arow_b) and, in its last column, the next
+    // item's first column is staged, so consecutive items run back to back.
+    const int nitems = U * stiles;
+    int wu = blockIdx.x;
+    if (wu >= nitems) return;
+    int *arow_b = (int *)(smem + 2 * SB_SZ + 2 * SA_SZ);   // [2][NTOK]
+    // token row of slot i of a unit; slots past its count repeat the last token (their
+    // sums are computed and never stored)
+    auto token_row = [&](const int4 &v, int i) {
+        const int slot = v.y + min(i, v.z - 1);
+        return SWIGLU ? perm[slot] / topk : slot;
+    };
+    int4 un = units[wu / stiles];
+    if (tid < NTOK) arow_b[tid] = token_row(un, tid);
+    __syncthreads();
+    // load j = wv + 8 n of a column: digits of tokens 2j, 2j + 1 (j < NDJ), sums of
+    // tokens 16 (j - NDJ) .. +15, or 1 KB of the 4 tiles' weight pieces; each lane's
+    // byte offset from the column's base is fixed for the work item
+    uint32_t voff[JPW];
+    auto set_voff = [&](const int *arow) {
 #pragma unroll
         for (int n = 0; n < JPW; ++n) {
             const int j = wv + 8 * n;
             uint32_t o = 0;
             if (j < NDJ) {
                 const int t = 2 * j + (lane >> 5), w = (lane & 31) ^ (t & 15);
-                o = (uint32_t)((arow_s[t] * kblocks * 32 + w) * 16);
+                o = (uint32_t)((arow[t] * kblocks * 32 + w) * 16);
             } else if (j < NDJ + NSJ) {
                 const int q = 64 * (j - NDJ) + lane, t = q >> 2, w = (q & 3) ^ ((t & 15) >> 2);
-                o = (uint32_t)((arow_s[t] * kblocks * 16 + 4 * w) * 4);
+                o = (uint32_t)((arow[t] * kblocks * 16 + 4 * w) * 4);
             } else if (j < NJ) {
                 const int p = 64 * (j - NDJ - NSJ) + lane, tl = p / 336, w = p - tl * 336;
                 o = (uint32_t)(tl * tile_bytes + w * 16);
             }
             voff[n] = o;
         }
-        // column b into buffer buf; digit and sum loads only for the first mfc token
-        // fragments (the rest are never read)
-        auto dma = [&](int b, int buf, int mfc) {
-            const char *db = (const char *)xdig + (int64_t)b * 512;
-            const char *sb = (const char *)xsum + (int64_t)b * 64;
-            const char *wb = (const char *)tb + (int64_t)b * 5376;
+    };
+    // column b of the item at tbase into buffer buf; digit and sum loads only for the
+    // first mfc token fragments (the rest are never read)
+    auto dma = [&](int b, int buf, int mfc, const uint8_t *tbase) {
+        const char *db = (const char *)xdig + (int64_t)b * 512;
+        const char *sb = (const char *)xsum + (int64_t)b * 64;
+        const char *wb = (const char *)tbase + (int64_t)b * 5376;
 #pragma unroll
-            for (int n = 0; n < JPW; ++n) {
-                const int j = wv + 8 * n;
-                if (j < NDJ) {
-                    if (j < 8 * mfc)
-                        __builtin_amdgcn_global_load_lds((gvoid *)(db + voff[n]), (lvoid *)(smem + buf * SA_SZ + 256 * j), 16, 0, 0);
-                } else if (j < NDJ + NSJ) {
-                    if (j - NDJ < mfc)
-                        __builtin_amdgcn_global_load_lds((gvoid *)(sb + voff[n]),
-                                                         (lvoid *)(smem + buf * SA_SZ + SUMS + 256 * (j - NDJ)), 16, 0, 0);
-                } else if (j < NJ) {
-                    __builtin_amdgcn_global_load_lds((gvoid *)(wb + voff[n]),
-                                                     (lvoid *)(smem + SB_OFF + buf * SB_SZ + 256 * (j - NDJ - NSJ)), 16, 0, 0);
-                }
+        for (int n = 0; n < JPW; ++n) {
+            const int j = wv + 8 * n;
+            if (j < NDJ) {
+                if (j < 8 * mfc)
+                    __builtin_amdgcn_global_load_lds((gvoid *)(db + voff[n]), (lvoid *)(smem + buf * SA_SZ + 256 * j), 16, 0, 0);
+            } else if (j < NDJ + NSJ) {
+                if (j - NDJ < mfc)
+                    __builtin_amdgcn_global_load_lds((gvoid *)(sb + voff[n]),
+                                                     (lvoid *)(smem + buf * SA_SZ + SUMS + 256 * (j - NDJ)), 16, 0, 0);
+            } else if (j < NJ) {
+                __builtin_amdgcn_global_load_lds((gvoid *)(wb + voff[n]),
+                                                 (lvoid *)(smem + SB_OFF + buf * SB_SZ + 256 * (j - NDJ - NSJ)), 16, 0, 0);
             }
-        };
+        }
+    };
+    bool pre = false;                                    // the item's first column is staged
+    int bpar = 0;                                        // buffer of the item's first column
+    for (int k = 0; wu < nitems; wu += gridDim.x, ++k) {
+        const int u = wu / stiles, st = wu - u * stiles;
+        const int e = un.x, p0 = un.y, nt = un.z;
+        const int *arow_s = arow_b + (k & 1) * NTOK;
+        int *arow_n = arow_b + ((k + 1) & 1) * NTOK;
+        const uint8_t *tb = experts + (int64_t)e * expert_bytes + mat_off + (int64_t)(4 * st) * tile_bytes;
+        // the next item; from 3 columns on, its rows are written in column kblocks - 2
+        // (every wave is past the previous item's outputs, which read that half, once
+        // column 0's barrier is behind it) and its first column staged in the last one
+        const int wn = wu + gridDim.x;
+        const bool has_next = wn < nitems;
+        const int4 unn = has_next ? units[wn / stiles] : make_int4(0, 0, 1, 0);
+        const int stn = wn - (wn / stiles) * stiles;
+        const uint8_t *tbn = experts + (int64_t)unn.x * expert_bytes + mat_off + (int64_t)(4 * stn) * tile_bytes;
+        const int mfcn = (unn.z + 15) >> 4;
+        const bool chain = has_next && kblocks >= 3;
+        const int nrow = has_next && tid < NTOK ? token_row(unn, tid) : 0;
+        if (!pre) set_voff(arow_s);
         // MFC token fragments carry tokens (the rest of MF are skipped): one copy of the
         // column loop per count, so no fragment test sits in the loop
         auto run = [&](auto mfc_tag) {
@@ -949,15 +973,23 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
             mq_f32x4 tot[MFC][2];
 #pragma unroll
             for (int m = 0; m < MFC; ++m) { tot[m][0] = (mq_f32x4){0.f, 0.f, 0.f, 0.f}; tot[m][1] = tot[m][0]; }
-            // One barrier per column: the buffer loaded during step b (column b + 1) was
-            // last read in step b - 1, which every wave finished before that step's
-            // barrier; each wave waits for its own loads before the barrier.
-            dma(0, 0, MFC);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+            // One barrier per column: the buffer loaded during step b (column b + 1, or the
+            // next item's first column) was last read in step b - 1, which every wave
+            // finished before that step's barrier; each wave waits for its own loads
+            // before the barrier.
+            if (!pre) {
+                dma(0, bpar, MFC, tb);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
             for (int b = 0; b < kblocks; ++b) {
-                const int cur = b & 1;
-                if (b + 1 < kblocks) dma(b + 1, cur ^ 1, MFC);
+                const int cur = (b + bpar) & 1;
+                if (b + 1 < kblocks) dma(b + 1, cur ^ 1, MFC, tb);
+                if (chain && b == kblocks - 2 && tid < NTOK) arow_n[tid] = nrow;
+                if (chain && b == kblocks - 1) {
+                    set_voff(arow_n);                    // this item's loads are all issued
+                    dma(0, cur ^ 1, mfcn, tbn);
+                }
                 const uint32_t *blk0 = smem + SB_OFF + cur * SB_SZ + (tw * 64 + nslot0 + r16) * MQ_BLOCK_DWORDS;
                 const uint32_t *blk1 = smem + SB_OFF + cur * SB_SZ + (tw * 64 + nslot1 + r16) * MQ_BLOCK_DWORDS;
                 const uint32_t *sAc = smem + cur * SA_SZ;
@@ -1033,6 +1065,13 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
         else if (mfa == 3) run(std::integral_constant<int, 3>{});
         else if (mfa == 2) run(std::integral_constant<int, 2>{});
         else run(std::integral_constant<int, 1>{});
+        if (has_next && !chain) {                        // short items: the next rows here
+            if (tid < NTOK) arow_n[tid] = nrow;
+            __syncthreads();
+        }
+        pre = chain;
+        bpar = (bpar + kblocks) & 1;
+        un = unn;
     }
 }
 
