@@ -4,8 +4,10 @@ and bf16 inputs, with and without a shared expert, Zipf-biased routing, token co
 on both sides of every launch-shape switch (routing inside the decode gate/up launch
 up to 4 tokens and E <= 256, with its one-token shortcut; per-expert router up to 8;
 decode kernels below 256 tokens; prefill kernels and the chunked bucketing from
-256, also with E > 256), and an empty batch.  Every token's routing and the bucketing are checked; the
-outputs of every token outside the near-tie window are compared with the oracle."""
+256, also with E > 256; with more work items than work-groups and 3 or more block
+columns, so that each item's successor is staged during it, and with units of 80 and
+48 slots), and an empty batch.  Every token's routing and the bucketing are checked;
+the outputs of every token outside the near-tie window are compared with the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -31,6 +33,7 @@ CASES = [
     ("e33_k4_t1_f32", 17,   1,  256,  33, 4, 256, 256, "f32",  0.05, False),
     ("e16_k16_t1",    18,   1,  256,  16, 16, 256, 256, "bf16", 0.05, False),
     ("e300_k8_t260",  19, 260,  256, 300, 8, 256, 256, "bf16", 0.05, True),
+    ("e64_k8_t1024",  20, 1024, 1536, 64, 8, 768, 256, "bf16", 0.05, False),
 ]
 
 
