@@ -13,10 +13,10 @@
 // done on v_mfma_f32_16x16x16_bf16 with B = m_j (exact) and A = A_j split into
 // two bf16 planes.  Each block then folds d and dmin into an fp32 accumulator.
 //
-// MFMA roles: M = the unit's tokens (16), N = 16 weight rows, K = the reduction
-// dimension.  Operand byte order inside a lane's 16-byte K slice follows the
-// code dword: byte b of dword s is weight 4b + s of the group (the activation
-// digits are stored in the same order).
+// MFMA roles: M = 16 of the unit's tokens (one fragment), N = 16 weight rows,
+// K = the reduction dimension.  Operand byte order inside a lane's 16-byte K slice
+// follows the code dword: byte b of dword s is weight 4b + s of the group (the
+// activation digits are stored in the same order).
 //
 // The decode kernel (k_q2_mma) and the prefill kernel (k_q2_mma_pf) differ in
 // how they tile tokens and stage operands; both are described at their
@@ -28,35 +28,6 @@
 
 typedef int32_t mq_i32x4 __attribute__((ext_vector_type(4)));
 typedef short mq_s16x4 __attribute__((ext_vector_type(4)));
-
-struct mq_pf6v { mq_u32x4 a, b, c, d, e, f; };
-
-__device__ __forceinline__ void mq_ld6(const mq_u32x4 *__restrict__ src, int n16, int tid, mq_pf6v &pf) {
-    pf.a = src[min(tid, n16 - 1)];
-    pf.b = src[min(tid + 256, n16 - 1)];
-    pf.c = src[min(tid + 512, n16 - 1)];
-    pf.d = src[min(tid + 768, n16 - 1)];
-    pf.e = src[min(tid + 1024, n16 - 1)];
-    pf.f = src[min(tid + 1280, n16 - 1)];
-}
-
-__device__ __forceinline__ void mq_st6(mq_u32x4 *__restrict__ dst, int n16, int tid, const mq_pf6v &pf) {
-    if (n16 == 4 * 336) {
-        dst[tid] = pf.a;
-        dst[tid + 256] = pf.b;
-        dst[tid + 512] = pf.c;
-        dst[tid + 768] = pf.d;
-        dst[tid + 1024] = pf.e;
-        if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) dst[tid + 1280] = pf.f;
-        return;
-    }
-    if (tid < n16) dst[tid] = pf.a;
-    if (tid + 256 < n16) dst[tid + 256] = pf.b;
-    if (tid + 512 < n16) dst[tid + 512] = pf.c;
-    if (tid + 768 < n16) dst[tid + 768] = pf.d;
-    if (tid + 1024 < n16) dst[tid + 1024] = pf.e;
-    if (tid + 1280 < n16) dst[tid + 1280] = pf.f;
-}
 
 // q*sc for the 16 weights of one group: dword s holds weights s, s+4, s+8, s+12.
 // Every byte product is at most 3 * 15, so one packed 16-bit multiply (the scale
