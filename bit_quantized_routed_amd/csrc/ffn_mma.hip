@@ -1054,7 +1054,7 @@ int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, i
                         hipStream_t st) {
     const int stiles = rows / (swiglu ? 32 : 64) / 4;
     int64_t want = (int64_t)max_units * stiles;
-    int64_t cap = (int64_t)n_cu * 2;
+    int64_t cap = (int64_t)n_cu;       // one persistent work-group per compute unit (LDS-bound)
     const int grid = (int)(want < cap ? want : cap);
     if (grid <= 0) return MOE_Q2_OK;
     if (swiglu)
