@@ -18,13 +18,20 @@
 
 typedef __bf16 mq_bf16x8 __attribute__((ext_vector_type(8)));
 
-template <int MF, int NF, int WM, int WN, int BK, bool A2>
+// SWI (one split, N = 2 Is: B rows 0..Is-1 gate, Is..2Is-1 up): each wave's NF
+// fragments hold 8 NF gate columns and the same 8 NF up columns, so the epilogue
+// writes h = silu(gate) * up as bf16 planes Hhi (and Hlo = bf16(h - hi) if given),
+// [M][Is], with the arithmetic of k_swiglu_partials at one split.
+template <int MF, int NF, int WM, int WN, int BK, bool A2, bool SWI>
 __global__ void __launch_bounds__(256) k_gemm_bf16(const uint16_t *__restrict__ A,
                                                    const uint16_t *__restrict__ Alo, int lda,
                                                    const uint16_t *__restrict__ B, int ldb, int M,
                                                    int N, int K, int k_per_split,
-                                                   float *__restrict__ P) {
+                                                   float *__restrict__ P, uint16_t *__restrict__ Hhi,
+                                                   uint16_t *__restrict__ Hlo) {
     constexpr int BM = 16 * MF * WM, BN = 16 * NF * WN;
+    static_assert(!SWI || NF % 2 == 0, "gate and up fragments in pairs");
+    constexpr int HN = 8 * NF;                       // (SWI) gate columns per wave
     constexpr int NPL = A2 ? 2 : 1;
     constexpr int AS = BK + 8;                       // padded LDS row (bf16 elements)
     constexpr int CPR = BK / 8;                      // 16-byte chunks per tile row
@@ -36,6 +43,15 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(const uint16_t *__restrict__ 
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv / WN, wn = wv % WN;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int Is = N / 2, g0 = blockIdx.x * (BN / 2);      // (SWI) first gate column
+    // B row of LDS row r: plain n0 + r; SWI: wave w's rows are its HN gate rows, then
+    // the same HN up rows (a negative value: past the matrix)
+    auto brow = [&](int r) {
+        if (!SWI) return n0 + r < N ? n0 + r : -1;
+        const int w = r / (2 * HN), q = r - w * 2 * HN, h = q / HN, o = q - h * HN;
+        const int g = g0 + w * HN + o;
+        return g < Is ? h * Is + g : -1;
+    };
     const int split = blockIdx.z;
     const int k0 = split * k_per_split;
     const int k1 = min(K, k0 + k_per_split);
@@ -65,7 +81,8 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(const uint16_t *__restrict__ 
             rb[n] = (mq_u32x4){0u, 0u, 0u, 0u};
             if (c < BN * CPR) {
                 const int r = c / CPR, q = c - r * CPR;
-                if (n0 + r < N) rb[n] = *(const mq_u32x4 *)(B + (int64_t)(n0 + r) * ldb + k + 8 * q);
+                const int br = brow(r);
+                if (br >= 0) rb[n] = *(const mq_u32x4 *)(B + (int64_t)br * ldb + k + 8 * q);
             }
         }
     };
@@ -110,6 +127,25 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(const uint16_t *__restrict__ 
                 }
             }
         }
+    }
+    if (SWI) {
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+            for (int j = 0; j < NF / 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = m0 + (wm * MF + i) * 16 + 4 * (lane >> 4) + e;
+                    const int g = g0 + wn * HN + j * 16 + (lane & 15);
+                    if (m < M && g < Is) {
+                        const float a = acc[i][j][e], c = acc[i][j + NF / 2][e];
+                        const float h = a / (1.0f + expf(-a)) * c;
+                        const uint16_t hb = mq_f32_to_bf16(h);
+                        Hhi[(int64_t)m * Is + g] = hb;
+                        if (Hlo) Hlo[(int64_t)m * Is + g] = mq_f32_to_bf16(h - mq_bf16_to_f32(hb));
+                    }
+                }
+        return;
     }
     float *Pout = P + (int64_t)split * M * N;
 #pragma unroll
@@ -176,10 +212,10 @@ int mq_launch_gemm_bf16(const uint16_t *A, const uint16_t *Alo, int lda, const u
     kps = (kps + bk - 1) / bk * bk;
     const bool two = Alo != nullptr;
 #define MQ_GEMM(MF, NF, WM, WN, BK, A2)                                                        \
-    hipLaunchKernelGGL((k_gemm_bf16<MF, NF, WM, WN, BK, A2>),                                  \
+    hipLaunchKernelGGL((k_gemm_bf16<MF, NF, WM, WN, BK, A2, false>),                           \
                        dim3((N + 16 * NF * WN - 1) / (16 * NF * WN),                            \
                             (M + 16 * MF * WM - 1) / (16 * MF * WM), nsplit),                  \
-                       dim3(256), 0, st, A, Alo, lda, B, ldb, M, N, K, kps, P)
+                       dim3(256), 0, st, A, Alo, lda, B, ldb, M, N, K, kps, P, nullptr, nullptr)
     if (M <= 16) {
         if (two) MQ_GEMM(1, 1, 1, 4, 256, true); else MQ_GEMM(1, 1, 1, 4, 256, false);
     } else if (M <= 32) {
@@ -190,6 +226,21 @@ int mq_launch_gemm_bf16(const uint16_t *A, const uint16_t *Alo, int lda, const u
         if (two) MQ_GEMM(4, 4, 2, 2, 64, true); else MQ_GEMM(4, 4, 2, 2, 64, false);
     }
 #undef MQ_GEMM
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}
+
+int mq_launch_gemm_bf16_swiglu(const uint16_t *A, const uint16_t *Alo, int lda, const uint16_t *B, int ldb,
+                               int M, int Is, int K, uint16_t *hi, uint16_t *lo, hipStream_t st) {
+    if (M <= 64 || K % 64) return MOE_Q2_EUNSUPPORTED;
+    constexpr int MF = 4, NF = 4, WM = 2, WN = 2;
+    const dim3 grid((Is + 8 * NF * WN - 1) / (8 * NF * WN), (M + 16 * MF * WM - 1) / (16 * MF * WM), 1);
+    if (Alo)
+        hipLaunchKernelGGL((k_gemm_bf16<MF, NF, WM, WN, 64, true, true>), grid, dim3(256), 0, st, A, Alo, lda,
+                           B, ldb, M, 2 * Is, K, K, nullptr, hi, lo);
+    else
+        hipLaunchKernelGGL((k_gemm_bf16<MF, NF, WM, WN, 64, false, true>), grid, dim3(256), 0, st, A, Alo,
+                           lda, B, ldb, M, 2 * Is, K, K, nullptr, hi, lo);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

@@ -48,6 +48,10 @@ int mq_launch_split_bf16(const float *x, int64_t n, uint16_t *hi, uint16_t *lo, 
 int mq_gemm_splits(int M, int N, int K, int n_cu);
 int mq_launch_gemm_bf16(const uint16_t *A, const uint16_t *Alo, int lda, const uint16_t *B, int ldb,
                         int M, int N, int K, int nsplit, float *P, hipStream_t st);
+// One split, more than 64 rows: the gate/up product with the SwiGLU in its epilogue
+// (h as bf16 planes [M][Is]; lo optional), no partial sums.
+int mq_launch_gemm_bf16_swiglu(const uint16_t *A, const uint16_t *Alo, int lda, const uint16_t *B, int ldb,
+                               int M, int Is, int K, uint16_t *hi, uint16_t *lo, hipStream_t st);
 int mq_launch_swiglu_partials(const float *P, int nsplit, int M, int Is, uint16_t *hi, uint16_t *lo,
                               hipStream_t st);
 int mq_launch_sum_partials(const float *P, int nsplit, int64_t MN, float *out, hipStream_t st);

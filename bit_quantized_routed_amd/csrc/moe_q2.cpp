@@ -342,9 +342,14 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         }
         float *P = (float *)(ws + w.sp);
         uint16_t *shi = (uint16_t *)(ws + w.shi), *slo = (uint16_t *)(ws + w.slo);
-        if ((rc = mq_launch_gemm_bf16(xa, xa_lo, H, shared_w, H, T, 2 * Is, H, w.split_gu, P, sst)))
-            return rc;
-        if ((rc = mq_launch_swiglu_partials(P, w.split_gu, T, Is, shi, slo, sst))) return rc;
+        if (w.split_gu == 1 && T > 64) {                // SwiGLU in the product's epilogue
+            if ((rc = mq_launch_gemm_bf16_swiglu(xa, xa_lo, H, shared_w, H, T, Is, H, shi, slo, sst)))
+                return rc;
+        } else {
+            if ((rc = mq_launch_gemm_bf16(xa, xa_lo, H, shared_w, H, T, 2 * Is, H, w.split_gu, P, sst)))
+                return rc;
+            if ((rc = mq_launch_swiglu_partials(P, w.split_gu, T, Is, shi, slo, sst))) return rc;
+        }
         if ((rc = mq_launch_gemm_bf16(shi, slo, Is, shared_w + (size_t)2 * Is * H, Is, T, H, Is,
                                       w.split_d, P, sst)))
             return rc;
