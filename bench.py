@@ -334,7 +334,7 @@ def cpu_baseline(name, min_seconds=10.0, max_tokens=8):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus,
+        print("bench.py: the layer runs on one GPU; --gpus %d is not supported" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch
