@@ -11,9 +11,10 @@ weights from HBM rather than from the 256 MB last-level cache.
 
 Steps are timed as HIP graph replays by default (one captured graph holds one
 pass over the rotated layers, or one step; exactly K steps are replayed), which
-removes the host-side launch cost of the ~15 kernels of a decode step; the dominant routed kernel's duration comes from HIP events in a
-separate eager loop of the same K steps, which is also reported
-(eager_ms_per_step).  --graph 0 times the eager loop only.
+removes the host-side launch cost of the ~15 kernels of a decode step; the dominant
+routed kernel's duration comes from HIP events that its own launch records (start and
+end of the kernel's dispatch) in a separate eager loop of the same K steps, which is
+also reported (eager_ms_per_step).  --graph 0 times the eager loop only.
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -218,7 +219,7 @@ def run_workload(name, steps, warmup, rotate, graph=True):
         "hbm_gbs": bytes_per_pass * passes / (ms_per_step * 1e-3) / 1e9,
         "phases_ms_per_pass": phase_ms,
         "ms_per_step_percentiles": pct,
-        "phases_note": "separate instrumented pass; each phase includes ~4 us of event overhead",
+        "phases_note": "separate instrumented pass; gate_up and down are the kernels' own start-to-end times, the other phases are bracketed by events (~4 us of overhead each)",
     }
     # dominant kernel roofline (duration from the timed region's events); on the
     # matrix-core decode path with a bf16 layer input the routed launches also

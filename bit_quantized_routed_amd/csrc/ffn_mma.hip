@@ -22,12 +22,31 @@
 // how they tile tokens and stage operands; both are described at their
 // definitions below.
 #include "common.h"
+#include <hip/hip_ext.h>
 #include <type_traits>
 #include "kernels.h"
 #include "topk_dev.h"
 
 typedef int32_t mq_i32x4 __attribute__((ext_vector_type(4)));
 typedef short mq_s16x4 __attribute__((ext_vector_type(4)));
+
+// A launch whose start and end, when timing events are given, are recorded by the
+// kernel's own dispatch (hipExtLaunchKernelGGL), so their difference is the kernel's
+// duration with no extra packets around it; without events a plain launch.
+#define MQ_LAUNCH_TIMED(ev0, ev1, kernel, grid, block, shm, stream, ...)                       \
+    do {                                                                                       \
+        if ((ev0) || (ev1))                                                                    \
+            hipExtLaunchKernelGGL(kernel, grid, block, shm, stream, ev0, ev1, 0, __VA_ARGS__); \
+        else                                                                                   \
+            hipLaunchKernelGGL(kernel, grid, block, shm, stream, __VA_ARGS__);                 \
+    } while (0)
+
+// Nothing to launch: the timing events still get recorded (an empty interval).
+static int mq_mark_empty(hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
+    if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return MOE_Q2_EHIP;
+    if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return MOE_Q2_EHIP;
+    return MOE_Q2_OK;
+}
 
 // q*sc for the 16 weights of one group: dword s holds weights s, s+4, s+8, s+12.
 // Every byte product is at most 3 * 15, so one packed 16-bit multiply (the scale
@@ -684,7 +703,7 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
                      int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
                      int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route,
-                     const MqDownPrep *prep, hipStream_t st) {
+                     const MqDownPrep *prep, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     if (tiles % 4) return MOE_Q2_EUNSUPPORTED;
     if (gu && !urow) return MOE_Q2_EINVAL;
     if (route && (!gu || route->T < 1 || route->T > MQ_TOPK_BUCKET_MAX_T || route->E > MQ_ROUTE_MAX_E ||
@@ -724,18 +743,18 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
         dn.grid = (int)dgrid;
     }
     const int64_t grid = q2_grid + dgrid;
-    if (grid <= 0) return MOE_Q2_OK;
+    if (grid <= 0) return mq_mark_empty(ev0, ev1, st);
     if (grid > 0x7fffffff) return MOE_Q2_EUNSUPPORTED;
     if (gu)
-        hipLaunchKernelGGL(k_q2_mma<true>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
-                           expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units, urow, zrow,
-                           trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
-                           split_stride, (int)q2_grid, dn, rt, route_on, pp, prep_on);
+        MQ_LAUNCH_TIMED(ev0, ev1, k_q2_mma<true>, dim3((unsigned)grid), dim3(256), 0, st,
+                        (const uint8_t *)experts, expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units,
+                        urow, zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
+                        split_stride, (int)q2_grid, dn, rt, route_on, pp, prep_on);
     else
-        hipLaunchKernelGGL(k_q2_mma<false>, dim3((unsigned)grid), dim3(256), 0, st, (const uint8_t *)experts,
-                           expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units, urow, zrow,
-                           trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
-                           split_stride, (int)q2_grid, dn, rt, route_on, pp, prep_on);
+        MQ_LAUNCH_TIMED(ev0, ev1, k_q2_mma<false>, dim3((unsigned)grid), dim3(256), 0, st,
+                        (const uint8_t *)experts, expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units,
+                        urow, zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
+                        split_stride, (int)q2_grid, dn, rt, route_on, pp, prep_on);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
@@ -1051,20 +1070,20 @@ int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, i
                         int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                         int max_units, const int32_t *perm, int topk, const void *xdig,
                         const uint32_t *xsum, const float *xscale, float *out, int n_cu,
-                        hipStream_t st) {
+                        hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     const int stiles = rows / (swiglu ? 32 : 64) / 4;
     int64_t want = (int64_t)max_units * stiles;
     int64_t cap = (int64_t)n_cu;       // one persistent work-group per compute unit (LDS-bound)
     const int grid = (int)(want < cap ? want : cap);
-    if (grid <= 0) return MOE_Q2_OK;
+    if (grid <= 0) return mq_mark_empty(ev0, ev1, st);
     if (swiglu)
-        hipLaunchKernelGGL((k_q2_mma_pf<true, PF_MF>), dim3(grid), dim3(512), 0, st,
-                           (const uint8_t *)experts, expert_bytes, mat_off, rows, kblocks, units_hdr,
-                           units, perm, topk, (const mq_u32x4 *)xdig, xsum, xscale, out);
+        MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma_pf<true, PF_MF>), dim3(grid), dim3(512), 0, st,
+                        (const uint8_t *)experts, expert_bytes, mat_off, rows, kblocks, units_hdr, units,
+                        perm, topk, (const mq_u32x4 *)xdig, xsum, xscale, out);
     else
-        hipLaunchKernelGGL((k_q2_mma_pf<false, PF_MF>), dim3(grid), dim3(512), 0, st,
-                           (const uint8_t *)experts, expert_bytes, mat_off, rows, kblocks, units_hdr,
-                           units, perm, topk, (const mq_u32x4 *)xdig, xsum, xscale, out);
+        MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma_pf<false, PF_MF>), dim3(grid), dim3(512), 0, st,
+                        (const uint8_t *)experts, expert_bytes, mat_off, rows, kblocks, units_hdr, units,
+                        perm, topk, (const mq_u32x4 *)xdig, xsum, xscale, out);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

@@ -126,6 +126,9 @@ struct MqDownPrep {
     int snsplit;
     int64_t sstride;
 };
+// ev0 / ev1 (optional, both or neither): timing events recorded by the kernel's own
+// dispatch (start and end of the kernel; both recorded on the stream when nothing is
+// launched).
 // units: max_units records, those past the last unit with slot count 0; urow (gate/up):
 // the [max_units][16] row table of the bucketing; down reads the rows of its slots.
 // route (gate/up only, optional): route in the launch instead of reading units/urow.
@@ -134,9 +137,10 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
                      int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
                      int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route,
-                     const MqDownPrep *prep, hipStream_t st);
+                     const MqDownPrep *prep, hipStream_t st, hipEvent_t ev0 = nullptr,
+                     hipEvent_t ev1 = nullptr);
 int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
                         int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                         int max_units, const int32_t *perm, int topk, const void *xdig,
                         const uint32_t *xsum, const float *xscale, float *out, int n_cu,
-                        hipStream_t st);
+                        hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);

@@ -266,6 +266,8 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         if ((rc = (call))) return rc;                                                      \
         if ((rc = mark(ph, 1))) return rc;                                                 \
     } while (0)
+    // the routed-expert kernels take their phase's events into the launch itself
+    auto evk = [&](int phase, int end) -> hipEvent_t { return ev ? ev[2 * phase + end] : nullptr; };
     char *ws = (char *)workspace;
     float *logits = (float *)(ws + w.logits);
     int32_t *idx = (int32_t *)(ws + w.idx);
@@ -431,13 +433,15 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_dec(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr,
                                                   units, w.max_units, perm, K, hq, hg, hsc, y, ncu, st));
     } else if (prefill) {
-        MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma_pf(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr,
-                                                        units, w.max_units, perm, K, xq, (const uint32_t *)xg,
-                                                        xs, h, ncu, st));
+        if ((rc = mq_launch_q2_mma_pf(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr, units, w.max_units,
+                                      perm, K, xq, (const uint32_t *)xg, xs, h, ncu, st,
+                                      evk(MOE_Q2_PH_GATE_UP, 0), evk(MOE_Q2_PH_GATE_UP, 1))))
+            return rc;
         MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_digits(h, 0, T * K, I, I, hq, (uint32_t *)hg, hsc, st));
-        MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_mma_pf(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK,
-                                                     units_hdr, units, w.max_units, perm, K, hq,
-                                                     (const uint32_t *)hg, hsc, y, ncu, st));
+        if ((rc = mq_launch_q2_mma_pf(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr, units,
+                                      w.max_units, perm, K, hq, (const uint32_t *)hg, hsc, y, ncu, st,
+                                      evk(MOE_Q2_PH_DOWN, 0), evk(MOE_Q2_PH_DOWN, 1))))
+            return rc;
     } else {
         // split partial sums: gate and up [dsplit_gu][S + 1][I], y [dsplit_d][S + 1][H]
         const int S = T * K;
@@ -460,11 +464,11 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
             dd = MqDenseSpec{shared_w + (size_t)2 * Is * H, shi, slo, ysh, ysh, T, H, Is, H, H, w.fsplit_d,
                              ysh_stride};
         }
-        MQ_PHASE(MOE_Q2_PH_GATE_UP, mq_launch_q2_mma(1, experts_q2, ebytes, 0, I / 32, H / MQ_QK, units,
-                                                     w.dec_units, urow, T, S, xq,
-                                                     (const uint32_t *)xg, xs, gp, up, I, gstride,
-                                                     w.fused ? &dgu : nullptr, route_in_gu ? &rt : nullptr,
-                                                     nullptr, st));
+        if ((rc = mq_launch_q2_mma(1, experts_q2, ebytes, 0, I / 32, H / MQ_QK, units, w.dec_units, urow, T, S,
+                                   xq, (const uint32_t *)xg, xs, gp, up, I, gstride, w.fused ? &dgu : nullptr,
+                                   route_in_gu ? &rt : nullptr, nullptr, st, evk(MOE_Q2_PH_GATE_UP, 0),
+                                   evk(MOE_Q2_PH_GATE_UP, 1))))
+            return rc;
         // one token (shared expert fused): the down launch prepares its own activations
         const bool prep_in_down = T == 1 && w.fused && I <= MQ_DOWN_PREP_MAX_LEN;
         MqDownPrep dp = {};
@@ -476,11 +480,11 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
                                                                     (uint32_t *)hg, hsc, w.fused ? &shs : nullptr,
                                                                     st));
         }
-        MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_mma(0, experts_q2, ebytes, 2 * mat_gu, H / 64, I / MQ_QK,
-                                                  units, w.dec_units, nullptr, S, S, hq,
-                                                  (const uint32_t *)hg, hsc, y, nullptr, H, ystride,
-                                                  w.fused ? &dd : nullptr, nullptr, prep_in_down ? &dp : nullptr,
-                                                  st));
+        if ((rc = mq_launch_q2_mma(0, experts_q2, ebytes, 2 * mat_gu, H / 64, I / MQ_QK, units, w.dec_units,
+                                   nullptr, S, S, hq, (const uint32_t *)hg, hsc, y, nullptr, H, ystride,
+                                   w.fused ? &dd : nullptr, nullptr, prep_in_down ? &dp : nullptr, st,
+                                   evk(MOE_Q2_PH_DOWN, 0), evk(MOE_Q2_PH_DOWN, 1))))
+            return rc;
     }
     const int ysplit = (prefill || valu) ? 1 : w.dsplit_d;
     const int64_t ystride = (int64_t)(T * K + 1) * H;
