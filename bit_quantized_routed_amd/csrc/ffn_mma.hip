@@ -32,20 +32,30 @@ typedef short mq_s16x4 __attribute__((ext_vector_type(4)));
 
 // A launch whose start and end, when timing events are given, are recorded by the
 // kernel's own dispatch (hipExtLaunchKernelGGL), so their difference is the kernel's
-// duration with no extra packets around it; without events a plain launch.
+// duration with no extra packets around it; without events a plain launch.  Under
+// stream capture the events are recorded around a plain launch instead.
+static bool mq_capturing(hipStream_t st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
 #define MQ_LAUNCH_TIMED(ev0, ev1, kernel, grid, block, shm, stream, ...)                       \
     do {                                                                                       \
-        if ((ev0) || (ev1))                                                                    \
+        if (((ev0) || (ev1)) && !mq_capturing(stream)) {                                       \
             hipExtLaunchKernelGGL(kernel, grid, block, shm, stream, ev0, ev1, 0, __VA_ARGS__); \
-        else                                                                                   \
+        } else {                                                                               \
+            hipError_t e_ = (ev0) ? hipEventRecord(ev0, stream) : hipSuccess;                \
+            if (e_ != hipSuccess) return mq_fail_hip(e_);                                      \
             hipLaunchKernelGGL(kernel, grid, block, shm, stream, __VA_ARGS__);                 \
+            e_ = (ev1) ? hipEventRecord(ev1, stream) : hipSuccess;                             \
+            if (e_ != hipSuccess) return mq_fail_hip(e_);                                      \
+        }                                                                                      \
     } while (0)
 
 // Nothing to launch: the timing events still get recorded (an empty interval).
 static int mq_mark_empty(hipEvent_t ev0, hipEvent_t ev1, hipStream_t st) {
-    if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return MOE_Q2_EHIP;
-    if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return MOE_Q2_EHIP;
-    return MOE_Q2_OK;
+    hipError_t e = ev0 ? hipEventRecord(ev0, st) : hipSuccess;
+    if (e == hipSuccess && ev1) e = hipEventRecord(ev1, st);
+    return e == hipSuccess ? MOE_Q2_OK : mq_fail_hip(e);
 }
 
 // q*sc for the 16 weights of one group: dword s holds weights s, s+4, s+8, s+12.
