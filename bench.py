@@ -161,49 +161,55 @@ def run_workload(name, steps, warmup, rotate, graph=True):
     pct = None
     launch = "eager"
     if graph:
-        # G consecutive steps per captured graph (one pass over the rotated layers
-        # when that divides the step count, else one step), replayed steps / G times:
-        # exactly `steps` steps, with one host launch per G steps
-        G = L if (not stack and steps % L == 0) else 1
-        n_graphs = 1 if (stack or G == L) else L
-        graphs = []
+        # One captured graph holds one pass over the rotated layers (L consecutive
+        # steps; the whole stack for the residual stack, which is one step), plus one
+        # graph of the first steps % L steps: full passes are replayed steps // L times,
+        # then the remainder once -- exactly `steps` steps for any step count, one host
+        # launch per pass.
+        G = 1 if stack else L
+        n_full, rem = steps // G, steps % G
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
-            for i in range(max(G, n_graphs)):
+            for i in range(G):
                 step(i)
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        for j in range(n_graphs):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(G):
-                    step(j + i)
-            graphs.append(g)
-        n_rep = steps // G
+        full = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(full):
+            for i in range(G):
+                step(i)
+        part = None
+        if rem:
+            part = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(part):
+                for i in range(rem):
+                    step(i)
         for r in range(max(1, warmup // G)):
-            graphs[r % n_graphs].replay()
+            full.replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        for r in range(n_rep):
-            graphs[r % n_graphs].replay()
+        for r in range(n_full):
+            full.replay()
+        if part is not None:
+            part.replay()
         torch.cuda.synchronize()
         t2 = time.perf_counter()
-        ms_per_step = (t2 - t1) * 1e3 / (n_rep * G)
-        launch = "hip_graph x%d steps" % G
-        # spread of the step time: a separate pass of event-bracketed replays
-        n_pct = max(10, min(60, n_rep))
+        ms_per_step = (t2 - t1) * 1e3 / steps
+        launch = "hip_graph, %d step(s) per replay" % G
+        # spread of the step time: a separate pass of event-bracketed full replays
+        n_pct = max(10, min(60, max(n_full, 1)))
         pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n_pct)]
         for r in range(n_pct):
             pev[r][0].record()
-            graphs[r % n_graphs].replay()
+            full.replay()
             pev[r][1].record()
         torch.cuda.synchronize()
         per_step = [a.elapsed_time(b) / G for a, b in pev]
         pct = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
                "p90": float(np.percentile(per_step, 90)), "replays": n_pct}
-        del graphs
+        del full, part
     touched = [int((c > 0).sum().item()) for c in counts]
     d_mean = float(np.mean(touched))
     passes = L if stack else 1
@@ -254,7 +260,18 @@ def run_workload(name, steps, warmup, rotate, graph=True):
                            "traffic": None if tr is None else tr.get("bytes_per_launch"),
                            "algorithmic_bytes_per_launch": kbytes,
                            "avg_launch_ms": dom_avg}
-    del layers, ws
+    # one more untimed forward of layer 0 with its routing traced, kept for the parity
+    # check against the oracle's outputs of the CPU baseline (first tokens only)
+    npar = min(T, 8)
+    x0 = dw.activations(wl)
+    o0 = x0.clone() if wl.rmsnorm else torch.zeros((T, wl.hidden), dtype=torch.float32, device="cuda")
+    ti = torch.full((T, K), -1, dtype=torch.int32, device="cuda")
+    mq.forward(x0, layers[0].router_w, layers[0].experts, layers[0].shared_w, K, o0, shape, T,
+               router_b=layers[0].router_b, workspace=ws, trace={"topk_idx": ti})
+    torch.cuda.synchronize()
+    res["_gpu_first_tokens"] = {"out": o0[:npar].cpu().numpy().astype(np.float64),
+                                "idx": ti[:npar].cpu().numpy()}
+    del layers, ws, x0, o0
     torch.cuda.empty_cache()
     return res
 
@@ -299,11 +316,26 @@ def measured_ceilings():
             "note": "2 GiB device copy (read + write bytes) and bf16 8192^3 torch.matmul, medians of 10"}
 
 
-def cpu_baseline(name, min_seconds=10.0, max_tokens=8):
-    """The oracle, untuned, on the host cores for a bounded sample of the workload:
-    the layer for its first tokens, one at a time, until at least min_seconds of
-    oracle time (or max_tokens tokens); each token's routed experts are encoded to
-    Q2 bytes beforehand, untimed (input preparation)."""
+# How the oracle is timed per workload: tokens per oracle call, runs per token
+# (median), the minimum oracle time of the headline sample, and the layer count a
+# one-layer time is scaled by (the residual stack: one layer timed, x40, labelled).
+CPU_PROTOCOL = {
+    "tiny": dict(tokens_per_call=4, max_calls=1, runs=3),
+    "decode1": dict(tokens_per_call=1, max_calls=8, runs=1, min_seconds=10.0),
+    "decode32_zipf": dict(tokens_per_call=1, max_calls=1, runs=3),
+    "prefill2048": dict(tokens_per_call=1, max_calls=1, runs=1),
+    "stack40_t64_zipf": dict(tokens_per_call=1, max_calls=1, runs=1, scale_layers=40),
+}
+
+
+def cpu_baseline(name, gpu=None):
+    """The oracle, untuned, on the host cores for a bounded sample of the workload
+    (CPU_PROTOCOL): the layer (for the residual stack: RMSNorm, layer 0, residual add)
+    on the workload's first tokens, the routed experts of each call encoded to Q2 bytes
+    beforehand, untimed (input preparation); tokens/s from the summed per-call medians.
+    With `gpu` (the GPU's outputs and routing of the same first tokens of layer 0),
+    also a parity summary: per-token infinity-norm relative error, near-tie tokens,
+    routing-set mismatches outside the near-tie window."""
     from oracle import moe
     from tests.oracle_inputs import HostLayer
     from synth import workloads as W
@@ -313,23 +345,49 @@ def cpu_baseline(name, min_seconds=10.0, max_tokens=8):
     except Exception:
         thr = 1
     wl = W.WORKLOADS[name]
+    pr = CPU_PROTOCOL.get(name, dict(tokens_per_call=1, max_calls=1, runs=1))
+    tpc, runs, scale = pr["tokens_per_call"], pr["runs"], pr.get("scale_layers", 1)
+    n_max = tpc * pr["max_calls"]
     hl = HostLayer(wl, 0)
-    xh, _ = W.activations(wl, tokens=max_tokens)
-    idx, _, _, _ = moe.route(xh, hl.router_w, hl.router_b, wl.topk)
-    total, n = 0.0, 0
-    while n < max_tokens and total < min_seconds:
-        for e in idx[n]:
+    x_all, _ = W.activations(wl, tokens=max(n_max, wl.tokens))
+    xin = moe.rmsnorm_bf16(x_all, wl.rms_eps) if wl.rmsnorm else x_all
+    idx, _, logits, margin = moe.route(xin, hl.router_w, hl.router_b, wl.topk)
+    total, n, refs = 0.0, 0, []
+    while n < n_max and total < pr.get("min_seconds", 0.0) or n == 0:
+        rows = slice(n, n + tpc)
+        for e in np.unique(idx[rows]):
             hl.expert_bytes(int(e))          # untimed: input preparation
-        t = time.perf_counter()
-        moe.layer(xh[n:n + 1], hl.router_w, hl.router_b, hl.expert_bytes, hl.shared, wl.topk, wl.hidden,
-                  wl.inter)
-        total += time.perf_counter() - t
-        n += 1
-    return {"value": round(n / total, 4), "unit": "tokens/s", "cores": int(thr),
-            "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": "first %d token(s) of layer 0 of %s, one layer call each (routing, "
-                      "dequantisation of the token's %d experts, fp64 FFNs, shared expert, combine); "
-                      "%.2f s of oracle time" % (n, name, wl.topk, total)}
+        times = []
+        for _ in range(runs):
+            t = time.perf_counter()
+            if wl.rmsnorm:
+                ref, _ = moe.stack(x_all[rows], [hl.oracle_layer()], wl.topk, wl.hidden, wl.inter, wl.rms_eps)
+            else:
+                ref, _ = moe.layer(x_all[rows], hl.router_w, hl.router_b, hl.expert_bytes, hl.shared, wl.topk,
+                                   wl.hidden, wl.inter)
+            times.append(time.perf_counter() - t)
+        total += float(np.median(times))
+        refs.append(ref)
+        n += tpc
+    res = {"value": round(n / (total * scale), 4), "unit": "tokens/s" if scale == 1 else "tokens/s per %d-layer step" % scale,
+           "cores": int(thr), "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+           "sample": "first %d token(s) of layer 0 of %s, %d token(s) per oracle call, median of %d run(s) per "
+                     "call (routing, dequantisation of the touched experts, fp64 FFNs, shared expert, combine%s); "
+                     "%.2f s of oracle time%s" % (n, name, tpc, runs, ", RMSNorm and residual" if wl.rmsnorm else "",
+                                                  total, ("; one layer timed, x%d layers: extrapolated" % scale)
+                                                  if scale > 1 else "")}
+    if gpu is not None:
+        ref = np.concatenate(refs)[:len(gpu["out"])]
+        m = min(len(ref), len(gpu["out"]))
+        near = margin[:m] < 1e-4
+        mism = sum(1 for t in range(m) if not near[t] and set(gpu["idx"][t].tolist()) != set(idx[t].tolist()))
+        num = np.abs(gpu["out"][:m] - ref[:m]).max(axis=1)
+        den = np.abs(ref[:m]).max(axis=1)
+        err = (num / den)[~near]
+        res["parity"] = {"tokens_compared": int((~near).sum()), "near_tie_excluded": int(near.sum()),
+                         "routing_mismatches": int(mism), "max_rel_err": float(err.max()) if err.size else None,
+                         "what": "GPU layer 0 outputs of the same first tokens against the oracle's"}
+    return res
 
 
 def main():
@@ -361,14 +419,24 @@ def main():
                 "note": "the same layer every step (its 211 MB largely held by the 256 MB MALL); "
                         "labelled warm, not the headline"}
     ceil = measured_ceilings() if args.ceilings else None
-    cpu = cpu_baseline(args.workload) if args.cpu_baseline else None
+    cpu = None
+    if args.cpu_baseline:
+        cpu = cpu_baseline(args.workload, head.pop("_gpu_first_tokens", None))
+        for k, v in extras.items():
+            v["cpu_baseline"] = cpu_baseline(k, v.pop("_gpu_first_tokens", None))
+    head.pop("_gpu_first_tokens", None)
+    for v in extras.values():
+        v.pop("_gpu_first_tokens", None)
     from synth import workloads as W
     wl = W.WORKLOADS[args.workload]
     line = {
         "metric": METRIC, "value": round(head["tokens_per_s"], 2), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(head["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "i8mfma+fp32", "data": "synthetic",
+        "dtype_note": "routed experts: exact int8 q*sc codes x int8 digits of 15-bit activations on the "
+                      "integer matrix cores (int32 sums per block), d/dmin folded in fp32; bf16 shared expert "
+                      "on bf16 MFMA with fp32 accumulation; fp32 router; fp32 output",
         "config": {"workload": args.workload, "tokens": wl.tokens, "hidden": wl.hidden,
                    "n_experts": wl.n_experts, "topk": wl.topk, "inter": wl.inter,
                    "shared_inter": wl.shared_inter, "weights": "q2 routed (84 B/256), bf16 shared, fp32 router",
@@ -382,6 +450,7 @@ def main():
         "warm": warm,
         "cpu_baseline": cpu,
         "phases_ms": {k: round(v, 5) for k, v in head["phases_ms_per_pass"].items()},
+        "parity": (cpu or {}).get("parity"),
         "workloads": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                           for kk, vv in v.items() if kk != "touched_experts_per_layer"}
                       for k, v in extras.items()},

@@ -18,8 +18,8 @@ PREFILL_MIN_TOKENS = 256
 BLOCK_BYTES = 84
 
 EXPORTS = ["moe_q2_block_bytes", "moe_q2_expert_bytes", "moe_q2_workspace_size",
-           "moe_q2_forward", "moe_q2_quantize", "moe_q2_pack_expert", "moe_q2_synth_normal",
-           "moe_q2_status_string", "moe_q2_last_hip_error"]
+           "moe_q2_describe", "moe_q2_forward", "moe_q2_quantize", "moe_q2_pack_expert",
+           "moe_q2_synth_normal", "moe_q2_status_string", "moe_q2_last_hip_error"]
 
 
 class Shape(ctypes.Structure):
@@ -27,6 +27,14 @@ class Shape(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("rms_eps", ctypes.c_float)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("routed_kernel", ctypes.c_int32),
+                ("shared_fused", ctypes.c_int32), ("side_branch", ctypes.c_int32),
+                ("split_gate_up", ctypes.c_int32), ("split_down", ctypes.c_int32),
+                ("router_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class Trace(ctypes.Structure):
@@ -66,11 +74,13 @@ def _lib():
         lib.moe_q2_expert_bytes.argtypes = [ctypes.POINTER(Shape)]
         lib.moe_q2_workspace_size.restype = ctypes.c_int
         lib.moe_q2_workspace_size.argtypes = [ctypes.POINTER(Shape), i32, i32, ctypes.POINTER(sz)]
+        lib.moe_q2_describe.restype = ctypes.c_int
+        lib.moe_q2_describe.argtypes = [ctypes.POINTER(Shape), i32, i32, ctypes.POINTER(Plan)]
         lib.moe_q2_forward.restype = ctypes.c_int
         lib.moe_q2_forward.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.POINTER(Shape), i32, vp,
                                        vp, sz, ctypes.POINTER(Trace), vp]
         lib.moe_q2_quantize.restype = ctypes.c_int
-        lib.moe_q2_quantize.argtypes = [vp, i64, vp, vp]
+        lib.moe_q2_quantize.argtypes = [vp, i64, i64, vp, vp]
         lib.moe_q2_pack_expert.restype = ctypes.c_int
         lib.moe_q2_pack_expert.argtypes = [vp, vp, vp, i32, i32, vp, vp]
         lib.moe_q2_synth_normal.restype = ctypes.c_int
@@ -124,6 +134,16 @@ def workspace_size(shape, n_tokens, topk):
     return int(n.value)
 
 
+def describe(shape, n_tokens, topk):
+    """moe_q2_describe as a dict: path, routed kernel, fused shared expert, use of the
+    internal stream, reduction splits, workspace bytes."""
+    p = Plan()
+    rc = _lib().moe_q2_describe(ctypes.byref(shape), n_tokens, topk, ctypes.byref(p))
+    if rc:
+        raise MoeQ2Error(rc, "moe_q2_describe")
+    return {f: getattr(p, f) for f, _ in Plan._fields_ if f != "reserved"}
+
+
 def forward(x, router_w, experts_q2, shared_w, topk, out, shape, n_tokens, router_b=None,
             workspace=None, trace=None, stream=None, check=True):
     """moe_q2_forward on torch device tensors (raw pointers are passed through).
@@ -145,8 +165,9 @@ def forward(x, router_w, experts_q2, shared_w, topk, out, shape, n_tokens, route
     return rc
 
 
-def quantize(w, n_blocks, blocks_out, stream=None):
-    rc = _lib().moe_q2_quantize(_ptr(w), n_blocks, _ptr(blocks_out), _stream(stream))
+def quantize(w, rows, k, blocks_out, stream=None):
+    """moe_q2_quantize: row-major fp32 [rows, k] -> rows * k / 256 Q2 blocks."""
+    rc = _lib().moe_q2_quantize(_ptr(w), rows, k, _ptr(blocks_out), _stream(stream))
     if rc:
         raise MoeQ2Error(rc, "moe_q2_quantize")
 

@@ -549,6 +549,7 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
                                                 int route_on, const MqDownPrep pp, int prep_on) {
     __shared__ __attribute__((aligned(16))) mq_u32x4 sW[4][384];           // weight slices, one per wave
     static_assert(sizeof(MqRouteLds) <= sizeof(sW), "routing LDS fits the weight slices");
+    static_assert(MQ_DOWN_PREP_SHARED_BYTES <= sizeof(sW), "shared SwiGLU planes fit the weight slices");
     __shared__ __attribute__((aligned(16))) mq_u32x4 sA[2][DM_AITEMS];     // activation operands
     __shared__ int s_row[16];
     __shared__ float s_sc[16];
@@ -747,7 +748,8 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
         dn.split_stride = dense->split_stride;
         mq_dense_split(dense->rows, dense->K, nf, &dn.nsplit, &dn.kps);
         // (the in-launch shared SwiGLU holds 2 x kps bf16 in the weight-slice LDS)
-        if (prep && 4 * dn.kps > (int)sizeof(mq_u32x4) * 4 * 384) return MOE_Q2_EUNSUPPORTED;
+        // (the host decides the in-launch preparation against the same limit before enqueuing)
+        if (prep && 4 * dn.kps > MQ_DOWN_PREP_SHARED_BYTES) return MOE_Q2_EUNSUPPORTED;
         if (dn.nsplit != dense->nsplit) return MOE_Q2_EINVAL;       // workspace sized for another split
         dgrid = (int64_t)(dense->rows / (64 * nf)) * dn.nsplit;
         dn.grid = (int)dgrid;

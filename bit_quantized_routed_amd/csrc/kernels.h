@@ -118,6 +118,7 @@ struct MqRoute {
 // the appended shared rows, the shared SwiGLU of the dense partials over the
 // work-group's k range (two bf16 planes).  len <= MQ_DOWN_PREP_MAX_LEN.
 #define MQ_DOWN_PREP_MAX_LEN 2048
+#define MQ_DOWN_PREP_SHARED_BYTES (4 * 384 * 16)   // LDS of the shared SwiGLU planes (the weight slices)
 struct MqDownPrep {
     const float *g, *u;        // routed gate/up split partials [nsplit][rows][len]
     int nsplit, len;

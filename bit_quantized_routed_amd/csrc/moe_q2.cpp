@@ -54,7 +54,7 @@ struct Workspace {
     bool prefill = false, valu = false;
     int dec_units = 0, dsplit_gu = 1, dsplit_d = 1;
     // shared expert fused into the matrix-core decode launches (bf16 layer input)
-    bool fused = false;
+    bool fused = false, prep_in_down = false;
     int fsplit_gu = 1, fsplit_d = 1;
     size_t fgu = 0, fd = 0;
 };
@@ -120,6 +120,9 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
         int kps = 0;
         mq_dense_split((int)(2 * Is), (int)H, 4, &w.fsplit_gu, &kps);
         mq_dense_split((int)H, (int)Is, 2, &w.fsplit_d, &kps);
+        // one token: the down launch prepares its own activations when its LDS holds
+        // the shared SwiGLU planes of a work-group's k range (2 x kps bf16)
+        w.prep_in_down = T == 1 && I <= MQ_DOWN_PREP_MAX_LEN && 4 * (size_t)kps <= MQ_DOWN_PREP_SHARED_BYTES;
         w.fgu = take(c, (size_t)w.fsplit_gu * T * 2 * Is * 4);
         w.fd = take(c, (size_t)w.fsplit_d * T * H * 4);
         w.shi = take(c, (size_t)T * Is * 2);
@@ -157,6 +160,19 @@ static const int KNOWN_FLAGS = MOE_Q2_PATH_DECODE | MOE_Q2_PATH_PREFILL | MOE_Q2
                                MOE_Q2_RESIDUAL_ADD | MOE_Q2_DECODE_VALU | MOE_Q2_SERIAL;
 
 namespace {
+// Joins the concurrent branch back into the calling stream when a call returns
+// after the fork without having joined it (an enqueue failed): the caller's stream
+// then still depends on everything the call put on the internal stream, so a
+// captured graph stays connected and no work is left running unobserved.
+struct SideJoin {
+    hipEvent_t join = nullptr;
+    hipStream_t st = nullptr, sst = nullptr;
+    bool pending = false;
+    ~SideJoin() {
+        if (pending && hipEventRecord(join, sst) == hipSuccess) (void)hipStreamWaitEvent(st, join, 0);
+    }
+};
+
 // The concurrent branch (activation preparation + shared expert): one internal
 // stream and fork / prep / join events per device, created on first use and kept
 // for the process.  `mu`
@@ -202,8 +218,14 @@ SideBranch *side_branch() {
 static int check_common(const moe_q2_shape *s, int32_t n_tokens, int32_t topk) {
     if (!s) return MOE_Q2_EINVAL;
     if (!shape_ok(s)) return MOE_Q2_EUNSUPPORTED;
-    if (n_tokens < 0 || n_tokens > (1 << 20)) return MOE_Q2_EINVAL;
+    if (n_tokens < 0) return MOE_Q2_EINVAL;
     if (topk < 1 || topk > 16 || topk > s->n_experts) return MOE_Q2_EINVAL;
+    // the token grid of the combine and the 32-bit byte offsets of the activation
+    // rows (layer input: T + 1 rows of 2 H bytes; intermediate: T K + 1 rows of 2 I)
+    const int64_t T = n_tokens;
+    if (T > MOE_Q2_MAX_TOKENS) return MOE_Q2_EUNSUPPORTED;
+    if ((T + 1) * 2 * s->hidden > INT32_MAX || (T * topk + 1) * 2 * s->inter > INT32_MAX)
+        return MOE_Q2_EUNSUPPORTED;
     if (s->flags & ~KNOWN_FLAGS) return MOE_Q2_EINVAL;
     if ((s->flags & MOE_Q2_PATH_DECODE) && (s->flags & MOE_Q2_PATH_PREFILL)) return MOE_Q2_EINVAL;
     if (!(s->flags & MOE_Q2_PRE_RMSNORM) && s->act_dtype != MOE_Q2_F32 && s->act_dtype != MOE_Q2_BF16)
@@ -219,6 +241,24 @@ extern "C" int moe_q2_workspace_size(const moe_q2_shape *s, int32_t n_tokens, in
     const int rc = check_common(s, n_tokens, topk);
     if (rc) return rc;
     *bytes = carve(s, n_tokens, topk).total;
+    return MOE_Q2_OK;
+}
+
+extern "C" int moe_q2_describe(const moe_q2_shape *s, int32_t n_tokens, int32_t topk, moe_q2_plan *plan) {
+    if (!plan) return MOE_Q2_EINVAL;
+    const int rc = check_common(s, n_tokens, topk);
+    if (rc) return rc;
+    const Workspace w = carve(s, n_tokens, topk);
+    moe_q2_plan p = {};
+    p.path = w.prefill ? MOE_Q2_PATH_PREFILL : MOE_Q2_PATH_DECODE;
+    p.routed_kernel = w.prefill ? 2 : (w.valu ? 1 : 0);
+    p.shared_fused = w.fused ? 1 : 0;
+    p.side_branch = (!(s->flags & MOE_Q2_SERIAL) && !w.fused) ? 1 : 0;
+    p.split_gate_up = w.prefill || w.valu ? 1 : w.dsplit_gu;
+    p.split_down = w.prefill || w.valu ? 1 : w.dsplit_d;
+    p.router_splits = w.rsplit;
+    p.workspace_bytes = w.total;
+    *plan = p;
     return MOE_Q2_OK;
 }
 
@@ -305,6 +345,7 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     int64_t ysh_stride = 0;
     SideBranch *side = nullptr;
     std::unique_lock<std::mutex> side_lock;
+    SideJoin side_join;                  // declared after the lock: runs before the unlock
     hipStream_t sst = st;
     if (!(s->flags & MOE_Q2_SERIAL) && !w.fused) {
         side = side_branch();
@@ -314,6 +355,10 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
             if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
             if (e != hipSuccess) return mq_fail_hip(e);
             sst = side->s;
+            side_join.join = side->join;
+            side_join.st = st;
+            side_join.sst = sst;
+            side_join.pending = true;
         }
     }
     uint32_t *xq = (uint32_t *)(ws + w.xq);
@@ -470,7 +515,7 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
                                    evk(MOE_Q2_PH_GATE_UP, 1))))
             return rc;
         // one token (shared expert fused): the down launch prepares its own activations
-        const bool prep_in_down = T == 1 && w.fused && I <= MQ_DOWN_PREP_MAX_LEN;
+        const bool prep_in_down = w.prep_in_down;
         MqDownPrep dp = {};
         if (prep_in_down) {
             dp = MqDownPrep{gp, up, w.dsplit_gu, (int)I, gstride, shs.g, shs.u, shs.nsplit, shs.split_stride};
@@ -491,6 +536,7 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     if (side) {
         const hipError_t e = hipStreamWaitEvent(st, side->join, 0);
         if (e != hipSuccess) return mq_fail_hip(e);
+        side_join.pending = false;
     }
     MQ_PHASE(MOE_Q2_PH_COMBINE, mq_launch_combine(y, ysplit, ystride, inv, gate, ysh, ysh_split, ysh_stride, T,
                                                   H, K, accum ? 1 : 0, out, st));

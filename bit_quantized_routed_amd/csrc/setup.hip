@@ -110,9 +110,11 @@ extern "C" int moe_q2_synth_normal(uint64_t seed, uint64_t stream_id, uint64_t s
     return MOE_Q2_OK;
 }
 
-extern "C" int moe_q2_quantize(const float *w, int64_t n_blocks, void *blocks_out, void *stream) {
-    if (n_blocks < 0 || (n_blocks > 0 && (w == nullptr || blocks_out == nullptr)))
-        return MOE_Q2_EINVAL;
+extern "C" int moe_q2_quantize(const float *w, int64_t rows, int64_t k, void *blocks_out, void *stream) {
+    if (rows < 0 || k < 0 || k % MQ_QK) return MOE_Q2_EINVAL;
+    if (k > 0 && rows > INT64_MAX / k) return MOE_Q2_EINVAL;
+    const int64_t n_blocks = rows * (k / MQ_QK);
+    if (n_blocks > 0 && (w == nullptr || blocks_out == nullptr)) return MOE_Q2_EINVAL;
     if (((uintptr_t)w & 15) != 0) return MOE_Q2_EINVAL;
     if (n_blocks == 0) return MOE_Q2_OK;
     const int64_t wgs = (n_blocks + 3) / 4;

@@ -50,7 +50,8 @@ class DeviceLayer:
         for e in range(E):
             for m in range(3):
                 _normal(wl, W.expert_stream(layer, e, m), H * I, wl.expert_sigma, F32, out=tmp)
-                quantize(tmp, H * I // 256, rm[m * mat_bytes:(m + 1) * mat_bytes])
+                rows, k = (I, H) if m < 2 else (H, I)
+                quantize(tmp, rows, k, rm[m * mat_bytes:(m + 1) * mat_bytes])
             pack_expert(rm[:mat_bytes], rm[mat_bytes:2 * mat_bytes], rm[2 * mat_bytes:], H, I,
                         self.experts[e * ebytes:(e + 1) * ebytes])
         del rm
@@ -75,6 +76,13 @@ def activations(wl, tokens=None):
     if wl.act == "bf16":
         return _normal(wl, sid, n, 1.0, BF16).view(T, wl.hidden)
     return _normal(wl, sid, n, 1.0, F32).view(T, wl.hidden)
+
+
+def layer_residual(wl, layer, tokens=None):
+    """The standalone residual-stream input of one stack layer [T, H] fp32 (the
+    device twin of synth.workloads.layer_residual)."""
+    T = wl.tokens if tokens is None else tokens
+    return _normal(wl, W.stream_id(layer, W.TENSOR_H_LAYER), T * wl.hidden, 1.0, F32).view(T, wl.hidden)
 
 
 def workspace(shape, tokens, topk):

@@ -40,11 +40,13 @@
  *     moe_q2_forward forks it onto an internal stream with an event recorded on
  *     `stream` and joins it back with events before the routed experts and the
  *     combine, so the caller sees ordinary stream-ordered semantics (and the
- *     fork/join is legal under graph capture).  The internal stream and its
- *     three events are created by the first call on a device and kept until
- *     the process ends; calls from several host threads on one device enqueue
- *     one at a time.  MOE_Q2_SERIAL keeps every launch on `stream` and touches
- *     no internal state;
+ *     fork/join is legal under graph capture; a call that fails after the fork
+ *     still joins the branch into `stream` before it returns).  The internal
+ *     stream and its three events are the library's only state: created by the
+ *     first such call on a device, kept until the process ends; calls from
+ *     several host threads on one device enqueue one at a time.  The one-token
+ *     and micro-batch decode path with a bf16 layer input never uses them, and
+ *     MOE_Q2_SERIAL keeps every launch on `stream` and touches no internal state;
  *   - arguments are validated before anything is enqueued; a non-zero status
  *     means nothing was enqueued (except MOE_Q2_EHIP, raised when a launch
  *     fails, after which earlier launches of the same call may have run);
@@ -84,6 +86,12 @@ enum {
     MOE_Q2_SERIAL = 32         /* run every launch on `stream` (no internal stream) */
 };
 #define MOE_Q2_PREFILL_MIN_TOKENS 256
+/* Token envelope of one call.  n_tokens <= MOE_Q2_MAX_TOKENS, and the activation
+ * rows the routed kernels address with 32-bit byte offsets must stay below 2^31 bytes:
+ * (n_tokens + 1) * 2 * hidden <= INT32_MAX and (n_tokens * topk + 1) * 2 * inter <=
+ * INT32_MAX.  Larger batches are rejected with MOE_Q2_EUNSUPPORTED before anything
+ * is enqueued; the caller splits them into several calls (tokens are independent). */
+#define MOE_Q2_MAX_TOKENS 65535
 
 typedef struct {
     int32_t hidden;        /* H: multiple of 256, <= 16384 */
@@ -139,6 +147,23 @@ size_t moe_q2_expert_bytes(const moe_q2_shape *s);
 int moe_q2_workspace_size(const moe_q2_shape *s, int32_t n_tokens, int32_t topk,
                           size_t *bytes);
 
+/* How moe_q2_forward runs a shape (host only, nothing is enqueued): the path and
+ * routed kernels it picks, whether the shared expert rides in the routed launches,
+ * whether the concurrent branch uses the internal stream, and the reduction splits.
+ * Returns MOE_Q2_OK and fills *plan, or the status moe_q2_workspace_size returns. */
+typedef struct {
+    int32_t path;            /* MOE_Q2_PATH_DECODE or MOE_Q2_PATH_PREFILL */
+    int32_t routed_kernel;   /* 0 matrix-core decode, 1 vector-ALU decode, 2 matrix-core prefill */
+    int32_t shared_fused;    /* 1: shared-expert rows appended to the routed decode launches */
+    int32_t side_branch;     /* 1: activation preparation and shared expert on the internal stream */
+    int32_t split_gate_up;   /* reduction splits of the routed gate/up and down launches */
+    int32_t split_down;
+    int32_t router_splits;   /* split-K partial logits of the router */
+    int32_t reserved;
+    size_t  workspace_bytes;
+} moe_q2_plan;
+int moe_q2_describe(const moe_q2_shape *s, int32_t n_tokens, int32_t topk, moe_q2_plan *plan);
+
 /* One MoE layer for n_tokens tokens.
  *   x          device [T, H], act_dtype (fp32 under PRE_RMSNORM); 16-byte aligned
  *   router_w   device [E, H] fp32 row-major
@@ -160,15 +185,16 @@ int moe_q2_forward(const void *x, const float *router_w, const void *experts_q2,
                    void *workspace, size_t workspace_bytes, const moe_q2_trace *trace,
                    void *stream);
 
-/* Quantize n_blocks * 256 fp32 weights (device, contiguous; every 256 consecutive
- * values form one block) into n_blocks 84-byte blocks (device) with the coverage
- * round-to-nearest rule, all steps in IEEE fp32:
+/* Quantize a row-major fp32 matrix w [rows, k] (device, 16-byte aligned; k a multiple
+ * of 256, so every row is k / 256 blocks along its reduction dimension) into
+ * rows * k / 256 84-byte blocks (device, row-major: block b of row r at index
+ * r * k / 256 + b) with the coverage round-to-nearest rule, all steps in IEEE fp32:
  *   lo_j = min(0, min x), hi_j = max x per group; dmin = least fp16 >= max_j(0-lo_j)/15;
  *   m_j = ceil((0-lo_j)/dmin); o_j = dmin*m_j; s_j = (hi_j+o_j)/3;
  *   d = least fp16 >= max_j s_j/15; sc_j = ceil(s_j/d); q = clamp(rint((x+o_j)/(d*sc_j)),0,3).
  * Setup helper, not part of the layer.  Blocks whose scale would overflow fp16 are
  * written with d = dmin = +inf. */
-int moe_q2_quantize(const float *w, int64_t n_blocks, void *blocks_out, void *stream);
+int moe_q2_quantize(const float *w, int64_t rows, int64_t k, void *blocks_out, void *stream);
 
 /* Pack one routed expert from row-major Q2 matrices (device): gate [I rows x H/256
  * blocks], up [I x H/256], down [H x I/256] -> out (device, moe_q2_expert_bytes bytes)

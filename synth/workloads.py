@@ -10,6 +10,8 @@ Stream id (64-bit): bits 32..47 = layer + 1 (0 for the activations), low 32 bits
     1            activations x (or the initial residual stream h_0)
     2            router weights [E, H]
     3            router-bias permutation keys [E]
+    4            a standalone residual-stream input of this layer [T, H] (fp32), for
+                 checking each layer of a stack on its own input
     8, 9, 10     shared expert gate [Is, H], up [Is, H], down [H, Is]
     16 + 3e + m  routed expert e, matrix m (0 gate [I, H], 1 up [I, H], 2 down [H, I])
 """
@@ -26,6 +28,7 @@ from .philox import philox4x32_10
 TENSOR_X = 1
 TENSOR_ROUTER_W = 2
 TENSOR_ROUTER_PERM = 3
+TENSOR_H_LAYER = 4
 TENSOR_SHARED = 8
 TENSOR_EXPERT = 16
 
@@ -114,6 +117,13 @@ def activations(wl, tokens=None, start_token=0):
         bits = gen.f32_to_bf16_bits(v)
         return gen.bf16_bits_to_f32(bits), bits
     return v, None
+
+
+def layer_residual(wl, layer, tokens=None):
+    """A residual-stream input of one layer of a stack [T, H]: fp32 N(0,1) draws of
+    the layer's own stream (not bf16-rounded: RMSNorm sees a full fp32 stream)."""
+    T = wl.tokens if tokens is None else tokens
+    return _normal(wl, stream_id(layer, TENSOR_H_LAYER), T * wl.hidden, 1.0).reshape(T, wl.hidden)
 
 
 def router_weights(wl, layer=0):

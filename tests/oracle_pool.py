@@ -53,3 +53,33 @@ class ExpertPool:
     def close(self):
         self._pool.close()
         self._pool.join()
+
+
+def layer_outputs(pool, name, jobs, topk, hidden, inter):
+    """Oracle outputs of several layers of workload `name` for given token rows.
+
+    jobs: list of (layer, host_layer, x_rows).  The routed FFNs of every job are
+    evaluated in one parallel map (each (layer, expert) once, on the rows routed to
+    it), then each layer is assembled by the oracle's own moe.layer from those
+    results.  Returns a list of (out [n, H] fp64, routing dict)."""
+    tasks, where = [], {}
+    for l, hl, x in jobs:
+        idx, _, _, _ = moe.route(x, hl.router_w, hl.router_b, topk)
+        for e in np.unique(idx):
+            toks, _ = np.nonzero(idx == e)           # the rows moe.layer hands to the FFN
+            where[(l, int(e))] = len(tasks)
+            tasks.append((name, l, int(e), np.asarray(x, np.float64)[toks]))
+    print("  [oracle pool] %d expert FFNs over %d layer job(s)" % (len(tasks), len(jobs)), flush=True)
+    ys = pool._pool.map(_expert_ffn, tasks, chunksize=1)
+    out = []
+    for l, hl, x in jobs:
+        def lookup(items, l=l):
+            res = []
+            for e, rows in items:
+                i = where[(l, int(e))]
+                assert np.array_equal(tasks[i][3], np.asarray(rows, np.float64))
+                res.append(ys[i])
+            return res
+        out.append(moe.layer(x, hl.router_w, hl.router_b, None, hl.shared, topk, hidden, inter,
+                             ffn_map=lookup))
+    return out

@@ -62,6 +62,27 @@ def test_workspace_size_rejects(lib, kw, status):
     assert _ws_status(s, 32, 8)[0] == status
 
 
+@pytest.mark.parametrize("H,I,K,T,ok", [
+    (7168, 2048, 8, 65535, True),            # the largest token count: 65535 * 8 * 2 * 2048 < 2^31
+    (7168, 2048, 8, 65536, False),           # above MOE_Q2_MAX_TOKENS
+    (7168, 2048, 16, 32767, True),           # (T K + 1) 2 I = 2147422208 <= INT32_MAX
+    (7168, 2048, 16, 32768, False),          # (T K + 1) 2 I > INT32_MAX
+    (16384, 16384, 16, 4095, True),          # (4095 * 16 + 1) * 32768 < 2^31
+    (16384, 16384, 16, 4096, False),
+    (16384, 256, 1, 65534, True),            # (T + 1) 2 H = 65535 * 32768 < 2^31
+])
+def test_token_envelope(lib, H, I, K, T, ok):
+    """The token envelope: the combine's token grid and the 32-bit byte offsets of
+    the activation rows (header: MOE_Q2_MAX_TOKENS and the two row-byte limits)."""
+    s = mq.make_shape(H, I, 256, 0)
+    rc, _ = _ws_status(s, T, K)
+    assert rc == (mq.OK if ok else mq.EUNSUPPORTED)
+    if ok:
+        assert (T + 1) * 2 * H <= 2**31 - 1 and (T * K + 1) * 2 * I <= 2**31 - 1
+    if not ok:                        # rejected before any HIP call (fake pointers never used)
+        assert _fwd(s, T=T, K=K, wsb=1 << 60) == mq.EUNSUPPORTED
+
+
 def test_workspace_size_values(lib):
     s = mq.make_shape(7168, 2048, 256, 2048)
     rc, n1 = _ws_status(s, 1, 8)
@@ -107,10 +128,13 @@ def test_forward_validation(lib):
 
 
 def test_setup_helpers_validation(lib):
-    assert lib.moe_q2_quantize(None, 0, None, None) == mq.OK
-    assert lib.moe_q2_quantize(A + 4, 1, 2 * A, None) == mq.EINVAL
-    assert lib.moe_q2_quantize(None, 1, 2 * A, None) == mq.EINVAL
-    assert lib.moe_q2_quantize(A, -1, 2 * A, None) == mq.EINVAL
+    assert lib.moe_q2_quantize(None, 0, 256, None, None) == mq.OK
+    assert lib.moe_q2_quantize(None, 5, 0, None, None) == mq.OK
+    assert lib.moe_q2_quantize(A + 4, 1, 256, 2 * A, None) == mq.EINVAL
+    assert lib.moe_q2_quantize(None, 1, 256, 2 * A, None) == mq.EINVAL
+    assert lib.moe_q2_quantize(A, -1, 256, 2 * A, None) == mq.EINVAL
+    assert lib.moe_q2_quantize(A, 2, 100, 2 * A, None) == mq.EINVAL     # k not a multiple of 256
+    assert lib.moe_q2_quantize(A, 1 << 62, 1024, 2 * A, None) == mq.EINVAL   # rows * k overflows
     assert lib.moe_q2_synth_normal(0, 0, 0, 0, 1.0, mq.F32, None, None) == mq.OK
     assert lib.moe_q2_synth_normal(0, 0, 0, 10, 1.0, 5, A, None) == mq.EINVAL
     assert lib.moe_q2_synth_normal(0, 0, 0, 10, 1.0, mq.F32, None, None) == mq.EINVAL

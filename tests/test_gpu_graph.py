@@ -10,14 +10,25 @@ from tests.gpu_util import need_gpu
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["decode1", "decode32_zipf", "tiny_stack"])
-def test_graph_replays_equal_eager(name):
+# The fused decode path (one stream) and the paths whose concurrent branch is forked
+# onto the internal stream inside the capture (prefill kernels with a shared expert,
+# the vector-ALU decode kernel, an fp32 layer input).
+GRAPH_CASES = [("decode1", ""), ("decode32_zipf", ""), ("tiny_stack", ""),
+               ("decode32_zipf", "PATH_PREFILL"), ("decode32_zipf", "DECODE_VALU"), ("tiny", "")]
+
+
+@pytest.mark.parametrize("name,flag", GRAPH_CASES)
+def test_graph_replays_equal_eager(name, flag):
     mq = need_gpu()
     from bit_quantized_routed_amd import workload as dw
     wl = W.WORKLOADS[name]
     dl = dw.DeviceLayer(wl)
     T, K = wl.tokens, wl.topk
-    shape = dl.shape(0)                  # PRE_RMSNORM for the residual-stack shape
+    shape = dl.shape(getattr(mq, flag) if flag else 0)      # PRE_RMSNORM for the stack shape
+    plan = mq.describe(shape, T, K)
+    assert plan["side_branch"] == (0 if plan["shared_fused"] else 1), plan
+    if flag or name == "tiny":
+        assert plan["side_branch"] == 1
     ws = dw.workspace(shape, T, K)
     x = dw.activations(wl)
     out_e = torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")

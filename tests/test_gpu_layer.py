@@ -1,4 +1,6 @@
 """GPU parity of the whole layer against the oracle (HIP path through the C ABI)."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -47,7 +49,25 @@ def test_tiny_layer(kernel):
     assert err <= TOL_DECODE
 
 
-def _full_check(name, sample=None, flags=0):
+@functools.lru_cache(maxsize=4)
+def _pooled_ref(name, toks):
+    """Oracle outputs of the given tokens of layer 0 (experts evaluated in parallel;
+    cached, several tests compare different kernels against the same tokens)."""
+    from tests.oracle_pool import ExpertPool, layer_outputs
+    wl = W.WORKLOADS[name]
+    xh, _ = W.activations(wl)
+    pool = ExpertPool()
+    try:
+        (ref, _), = layer_outputs(pool, name, [(0, host_layer(name), xh[list(toks)])], wl.topk, wl.hidden,
+                                  wl.inter)
+    finally:
+        pool.close()
+    return ref
+
+
+def _full_check(name, sample=None, flags=0, pooled=False):
+    """The layer at full size: every token's routing and the bucketing, and the
+    outputs of the sampled tokens (all by default) against the oracle."""
     mq = need_gpu()
     from bit_quantized_routed_amd import workload as dw
     wl = W.WORKLOADS[name]
@@ -62,10 +82,14 @@ def _full_check(name, sample=None, flags=0):
     excluded, rep = check_routing(tr, route, wl.n_experts, wl.topk)
     toks = np.arange(wl.tokens) if sample is None else np.asarray(sample)
     toks = toks[~excluded[toks]]
-    ref, _ = moe.layer(xh[toks], hl.router_w, hl.router_b, hl.expert_bytes, hl.shared, wl.topk,
-                       wl.hidden, wl.inter)
+    if pooled:
+        ref = _pooled_ref(name, tuple(int(t) for t in toks))
+    else:
+        ref, _ = moe.layer(xh[toks], hl.router_w, hl.router_b, hl.expert_bytes, hl.shared, wl.topk,
+                           wl.hidden, wl.inter)
     err = rel_err(out[toks], ref)
-    print(name, rep, "tokens", toks.tolist(), "rel_err", err)
+    print(name, rep, "tokens compared", toks.size, "rel_err", err)
+    assert toks.size >= (wl.tokens if sample is None else len(sample)) - 2
     assert err <= TOL_DECODE
     return err
 
@@ -77,24 +101,36 @@ def test_decode1_layer(kernel):
     _full_check("decode1", flags=flags)
 
 
-def test_shared_branch_concurrent_equals_serial():
-    """The shared expert forked onto the internal stream gives the same bits as the
-    all-on-one-stream order, over several back-to-back calls."""
+# (workload, flags) pairs whose activation preparation and shared expert run on the
+# internal concurrent stream: the prefill kernels with a shared expert, the vector-ALU
+# decode kernel, an fp32 layer input
+SIDE_BRANCH = [("decode32_zipf", "PATH_PREFILL"), ("decode32_zipf", "DECODE_VALU"), ("tiny", "")]
+
+
+@pytest.mark.parametrize("name,flag", SIDE_BRANCH)
+def test_shared_branch_concurrent_equals_serial(name, flag):
+    """The concurrent branch forked onto the internal stream gives the same bits as
+    the all-on-one-stream order, over several back-to-back calls (the plan confirms
+    that the branch is in use, so the comparison is not between two identical paths)."""
     mq = need_gpu()
     from bit_quantized_routed_amd import workload as dw
-    wl = W.WORKLOADS["decode32_zipf"]
+    wl = W.WORKLOADS[name]
+    f = getattr(mq, flag) if flag else 0
     dl = dw.DeviceLayer(wl)
+    plan = mq.describe(dl.shape(f), wl.tokens, wl.topk)
+    assert plan["side_branch"] == 1 and plan["shared_fused"] == 0, plan
+    assert mq.describe(dl.shape(f | mq.SERIAL), wl.tokens, wl.topk)["side_branch"] == 0
     x = dw.activations(wl)
-    ser, _ = _run(mq, dl, x, wl.tokens, flags=mq.SERIAL)
+    ser, _ = _run(mq, dl, x, wl.tokens, flags=f | mq.SERIAL)
     for _ in range(3):
-        con, _ = _run(mq, dl, x, wl.tokens, flags=0)
+        con, _ = _run(mq, dl, x, wl.tokens, flags=f)
         assert np.array_equal(con, ser)
 
 
 @pytest.mark.parametrize("kernel", ["mma", "valu"])
-def test_decode32_zipf_layer_sampled(kernel):
+def test_decode32_zipf_layer_all_tokens(kernel):
     import bit_quantized_routed_amd as mq
-    _full_check("decode32_zipf", sample=[0, 17], flags=mq.DECODE_VALU if kernel == "valu" else 0)
+    _full_check("decode32_zipf", flags=mq.DECODE_VALU if kernel == "valu" else 0, pooled=True)
 
 
 @pytest.mark.parametrize("T", [2, 3, 4, 5, 8, 9])
@@ -123,10 +159,10 @@ def test_small_batches(T):
 
 
 def test_decode32_forced_prefill_kernels():
-    """The prefill kernels on a decode-sized batch (PATH_PREFILL), all 32 tokens sampled
-    through the oracle: covers partial token fragments and buckets of 1..18 slots."""
+    """The prefill kernels on a decode-sized batch (PATH_PREFILL), all 32 tokens through
+    the oracle: covers partial token fragments and buckets of 1..18 slots."""
     import bit_quantized_routed_amd as mq
-    _full_check("decode32_zipf", sample=[1, 9, 30], flags=mq.PATH_PREFILL)
+    _full_check("decode32_zipf", flags=mq.PATH_PREFILL, pooled=True)
 
 
 def test_tiny_forced_prefill_kernels():

@@ -30,7 +30,7 @@ def _dev_quant(mq, w_np):
     w = torch.from_numpy(np.ascontiguousarray(w_np, dtype=np.float32)).cuda()
     nb = w.numel() // 256
     out = torch.empty(nb * 84, dtype=torch.uint8, device="cuda")
-    mq.quantize(w, nb, out)
+    mq.quantize(w, nb, 256, out)
     return out.cpu().numpy().reshape(nb, 84)
 
 

@@ -20,7 +20,7 @@ from tests.oracle_inputs import HostLayer
 pytestmark = pytest.mark.gpu
 
 TOL_DECODE = 2e-3
-TOL_PREFILL = 1e-2
+TOL_PREFILL = 2e-3          # the exact-integer prefill kernels (observed ~3e-4)
 
 #        name         seed  T    H    E   K   I    Is   act     router sigma  zipf
 CASES = [

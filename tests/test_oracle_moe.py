@@ -244,3 +244,95 @@ def test_stack_with_zero_down_is_identity_and_one_layer_matches():
     want = h0 + moe.layer(moe.rmsnorm_bf16(h0, 1e-6), L.router_w, None, L.expert_bytes,
                           None, wl.topk, H, I)[0]
     assert np.array_equal(h, want)
+
+
+# ----------------------------------------------------------------- stack composition, closed form
+def _onehot_signed_q2(rows, cols, entries):
+    """Q2 bytes [rows * cols/256, 84] of a matrix whose row r holds at most one nonzero
+    W[r, c] = v, entries = {r: (c, v)}.  A positive v is d * sc * q with sc = q = 1,
+    d = v (fp16-exact) and no min; a negative v uses the subtracted min: m_j = 1,
+    dmin = -v, and every other weight of the group gets q = 1 with d * sc = -v, so
+    it decodes to 0 and the chosen one (q = 0) to v."""
+    raw = np.zeros((rows, cols // 256, 84), dtype=np.uint8)
+    for r, (c, v) in entries.items():
+        blk = raw[r, c // 256]
+        i = c % 256
+        j = i // 16
+        mag = np.float16(abs(v))
+        assert float(mag) == abs(v)
+        if v > 0:
+            blk[j] = 1                                    # sc_j = 1, m_j = 0
+            blk[16 + i // 4] |= 1 << (2 * (i % 4))        # q_i = 1
+            blk[80:82] = np.frombuffer(mag.tobytes(), dtype=np.uint8)
+        else:
+            blk[j] = 1 | (1 << 4)                         # sc_j = 1, m_j = 1
+            for ii in range(16 * j, 16 * j + 16):
+                if ii != i:
+                    blk[16 + ii // 4] |= 1 << (2 * (ii % 4))
+            blk[80:82] = np.frombuffer(mag.tobytes(), dtype=np.uint8)
+            blk[82:84] = np.frombuffer(mag.tobytes(), dtype=np.uint8)
+    return raw.reshape(-1, 84)
+
+
+def test_stack_composition_closed_form():
+    """Two layers, E = 2, K = 1, H = 256, I = 512, worked by hand.
+
+    h_0 rows are +-4 (constant magnitude, so RMSNorm gives exactly the signs in
+    bf16).  The router reads coordinate 0 of the layer input: logits (x_0, -x_0), so
+    expert 0 is chosen when x_0 = +1 and expert 1 when x_0 = -1, with gate 1.
+    Gate rows read x_0 times +-64 so that silu sees +64 and returns exactly 64
+    (e^-64 vanishes next to 1 in fp64); up row j reads x_j times s_u, down row k
+    reads h_k times s_d for k in a chosen set, else 0.  So an expert adds
+    s_d * 64 * s_u * x_k to coordinate k of the residual stream:
+      layer 1, expert 0: s_u = 1/8, s_d = -1 on F1 = {0, 3, 7, 100, 200} -> -8 x_k,
+        which flips the sign of h on F1 (4 - 8 = -4) and keeps |h| = 4;
+      layer 1, expert 1: down all zero;
+      layer 2, expert 1: gate -64, s_u = 1/4, s_d = 1/2 on F2 = {1, 5, 100, 255} -> +8 x_k;
+      layer 2, expert 0: s_u = 1/8, s_d = 1 on every k -> +8 x_k.
+    Token A (x_0 = +1): layer 1 takes expert 0 and flips coordinate 0, so layer 2 sees
+    x_0 = -1 and takes expert 1: h_2 = s' (4 + 8 [k in F2]), s' = s with F1 flipped.
+    Token B (x_0 = -1): layer 1 takes expert 1 (no change), layer 2 expert 1 again:
+    h_2 = s (4 + 8 [k in F2]).
+    Each stage is exact in fp64, so the comparison is exact.  This fails if the
+    router or the experts read h instead of RMSNorm(h) (inputs of +-4: a 16x larger
+    expert output), if the residual add is dropped or applied to the normalised input,
+    or if RMSNorm is taken once from h_0 (layer 2 would pick expert 0 for token A)."""
+    H, I = 256, 512
+    rng = np.random.default_rng(11)
+    F1, F2 = [0, 3, 7, 100, 200], [1, 5, 100, 255]
+    zero_lo = np.zeros((H * I // 256, 84), np.uint8)
+
+    def expert(gate_v, s_u, down):
+        g = _onehot_signed_q2(I, H, {j: (0, gate_v) for j in range(I)})
+        u = _onehot_signed_q2(I, H, {j: (j, s_u) for j in range(H)})
+        d = _onehot_signed_q2(H, I, down) if down else zero_lo
+        return (g, u, d)
+
+    l1 = {0: expert(64.0, 0.125, {k: (k, -1.0) for k in F1}), 1: expert(-64.0, 0.125, {})}
+    l2 = {0: expert(64.0, 0.125, {k: (k, 1.0) for k in range(H)}),
+          1: expert(-64.0, 0.25, {k: (k, 0.5) for k in F2})}
+    Wr = np.zeros((2, H))
+    Wr[0, 0], Wr[1, 0] = 1.0, -1.0
+    layers = [dict(router_w=Wr, router_b=None, expert_bytes=l1.__getitem__, shared=None),
+              dict(router_w=Wr, router_b=None, expert_bytes=l2.__getitem__, shared=None)]
+    s = np.where(rng.standard_normal((3, H)) >= 0, 1.0, -1.0)
+    s[0, 0], s[1, 0], s[2, 0] = 1.0, -1.0, 1.0
+    h, routings = moe.stack(4.0 * s, layers, 1, H, I, 1e-6)
+
+    f2 = np.zeros(H)
+    f2[F2] = 1.0
+    want = np.empty_like(s)
+    for t in range(3):
+        sp = s[t].copy()
+        if s[t, 0] > 0:
+            sp[F1] = -sp[F1]                      # layer 1, expert 0 flips F1
+        want[t] = sp * (4.0 + 8.0 * f2)           # layer 2, expert 1 adds 8 x_k on F2
+    assert routings[0]["idx"][:, 0].tolist() == [0, 1, 0]
+    assert routings[1]["idx"][:, 0].tolist() == [1, 1, 1]
+    assert np.all(routings[0]["g"] == 1.0) and np.all(routings[1]["g"] == 1.0)
+    assert np.array_equal(h, want)
+    # one layer alone: h_0 with the sign of F1 flipped for token 0
+    h1, _ = moe.stack(4.0 * s[:1], layers[:1], 1, H, I, 1e-6)
+    w1 = 4.0 * s[0].copy()
+    w1[F1] = -w1[F1]
+    assert np.array_equal(h1[0], w1)
