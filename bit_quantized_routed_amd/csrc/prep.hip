@@ -85,27 +85,45 @@ __global__ void __launch_bounds__(256) k_prep_act(const void *__restrict__ src, 
 }
 
 // x_bf16[t] = bf16(h[t] / sqrt(mean(h[t]^2) + eps)), one work-group per row.
+// The bf16 rounding of each element is a decision on the exact quotient, so the
+// sum of squares, the mean, the square root and the quotient are taken in fp64
+// (rounding errors ~1e-16, far inside a bf16 half-ulp of 2^-9) and the quotient
+// is rounded once, to nearest even, straight to bf16: an fp32 intermediate would
+// round twice, and fp32 arithmetic moves ~1e-7 of the elements across a bf16
+// rounding boundary.
+__device__ __forceinline__ uint16_t mq_f64_to_bf16(double y) {
+    // bf16 keeps 8 significant bits: spacing 2^(e-8) for |y| in [2^(e-1), 2^e),
+    // 2^-133 below the smallest normal; y / spacing is exact, rint rounds it to
+    // nearest even, and the rounded value is exact in fp32, whose top half is bf16
+    int e = 0;
+    (void)frexp(y, &e);
+    e = e < -125 ? -125 : e;
+    const double ulp = ldexp(1.0, e - 8);
+    const float f = (float)(rint(y / ulp) * ulp);
+    return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
 __global__ void __launch_bounds__(256) k_rmsnorm_bf16(const float *__restrict__ h, int H, float eps,
                                                       uint16_t *__restrict__ x) {
     const int t = blockIdx.x;
     const float4 *hr = (const float4 *)(h + (int64_t)t * H);
-    float ss = 0.0f;
+    double ss = 0.0;
     for (int c = threadIdx.x; c < H / 4; c += 256) {
         const float4 v = hr[c];
-        ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss);
-        ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
+        ss = fma((double)v.x, (double)v.x, ss); ss = fma((double)v.y, (double)v.y, ss);
+        ss = fma((double)v.z, (double)v.z, ss); ss = fma((double)v.w, (double)v.w, ss);
     }
-    ss = mq_wave_sum(ss);
-    __shared__ float part[4];
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, MQ_WAVE);
+    __shared__ double part[4];
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-    const float r = 1.0f / sqrtf(tot / (float)H + eps);
+    const double tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const double rs = sqrt(tot / (double)H + (double)eps);
     uint2 *xr = (uint2 *)(x + (int64_t)t * H);
     for (int c = threadIdx.x; c < H / 4; c += 256) {
         const float4 v = hr[c];
-        xr[c] = make_uint2((uint32_t)mq_f32_to_bf16(v.x * r) | ((uint32_t)mq_f32_to_bf16(v.y * r) << 16),
-                           (uint32_t)mq_f32_to_bf16(v.z * r) | ((uint32_t)mq_f32_to_bf16(v.w * r) << 16));
+        xr[c] = make_uint2((uint32_t)mq_f64_to_bf16(v.x / rs) | ((uint32_t)mq_f64_to_bf16(v.y / rs) << 16),
+                           (uint32_t)mq_f64_to_bf16(v.z / rs) | ((uint32_t)mq_f64_to_bf16(v.w / rs) << 16));
     }
 }
 

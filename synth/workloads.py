@@ -69,7 +69,7 @@ class Workload:
     zipf: bool = False
     layers: int = 1
     rmsnorm: bool = False
-    rms_eps: float = 1e-6
+    rms_eps: float = float(np.float32(1e-6))     # the fp32 value the library receives
 
     @property
     def blocks_per_expert(self):

@@ -70,7 +70,11 @@ def layer_outputs(pool, name, jobs, topk, hidden, inter):
             where[(l, int(e))] = len(tasks)
             tasks.append((name, l, int(e), np.asarray(x, np.float64)[toks]))
     print("  [oracle pool] %d expert FFNs over %d layer job(s)" % (len(tasks), len(jobs)), flush=True)
-    ys = pool._pool.map(_expert_ffn, tasks, chunksize=1)
+    ys = []
+    for i, y in enumerate(pool._pool.imap(_expert_ffn, tasks, chunksize=1)):
+        ys.append(y)
+        if (i + 1) % 64 == 0 or i + 1 == len(tasks):
+            print("  [oracle pool] %d / %d expert FFNs done" % (i + 1, len(tasks)), flush=True)
     out = []
     for l, hl, x in jobs:
         def lookup(items, l=l):

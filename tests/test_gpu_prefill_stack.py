@@ -200,10 +200,17 @@ def test_stack40_every_layer():
     assert max(errs) <= TOL
 
 
+# Bound of the chained drift report: each layer's own error is ~2e-4 (the per-layer
+# test), but a 1e-4 difference of the residual streams moves some RMSNorm outputs
+# across a bf16 rounding boundary (one bf16 ulp, 2^-8 relative, of that element of the
+# next layer's input), which the next layers carry on; 3 chained layers measured 1.9e-3.
+DRIFT_TOL = 5e-3
+
+
 def test_stack40_first_layers_chained():
     """Drift report: the first 3 layers chained free-running from h_0 on both sides
     (the per-layer check above is the parity test); at least 2 of the 4 tokens stay
-    outside the widening near-tie window and are compared."""
+    outside the widening near-tie window and are compared, within DRIFT_TOL."""
     mq = need_gpu()
     from bit_quantized_routed_amd import workload as dw
     from tests.oracle_pool import ExpertPool
@@ -231,4 +238,4 @@ def test_stack40_first_layers_chained():
     err, excl = _compare_stack(wl, h_gpu, traces, ref, routings, toks)
     print("stack40 first", n_layers, "layers chained, tokens", toks.tolist(), "excluded", excl, "rel_err", err)
     assert len(toks) - excl >= 2
-    assert err <= TOL
+    assert err <= DRIFT_TOL
