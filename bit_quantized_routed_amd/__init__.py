@@ -18,7 +18,8 @@ PREFILL_MIN_TOKENS = 256
 BLOCK_BYTES = 84
 
 EXPORTS = ["moe_q2_block_bytes", "moe_q2_expert_bytes", "moe_q2_workspace_size",
-           "moe_q2_describe", "moe_q2_forward", "moe_q2_quantize", "moe_q2_pack_expert",
+           "moe_q2_describe", "moe_q2_forward", "moe_q2_forward_noalloc", "moe_q2_quantize",
+           "moe_q2_pack_expert",
            "moe_q2_synth_normal", "moe_q2_status_string", "moe_q2_last_hip_error"]
 
 
@@ -79,6 +80,9 @@ def _lib():
         lib.moe_q2_forward.restype = ctypes.c_int
         lib.moe_q2_forward.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.POINTER(Shape), i32, vp,
                                        vp, sz, ctypes.POINTER(Trace), vp]
+        lib.moe_q2_forward_noalloc.restype = ctypes.c_int
+        lib.moe_q2_forward_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.POINTER(Shape), i32, vp,
+                                               ctypes.POINTER(Trace), vp]
         lib.moe_q2_quantize.restype = ctypes.c_int
         lib.moe_q2_quantize.argtypes = [vp, i64, i64, vp, vp]
         lib.moe_q2_pack_expert.restype = ctypes.c_int
@@ -162,6 +166,27 @@ def forward(x, router_w, experts_q2, shared_w, topk, out, shape, n_tokens, route
                                _stream(stream))
     if rc and check:
         raise MoeQ2Error(rc, "moe_q2_forward")
+    return rc
+
+
+NOALLOC_MAX_BYTES = 128 << 20
+
+
+def forward_noalloc(x, router_w, experts_q2, shared_w, topk, out, shape, n_tokens, router_b=None,
+                    trace=None, stream=None, check=True):
+    """moe_q2_forward_noalloc: the layer on the library's fixed per-device workspace
+    (no workspace argument, nothing allocated; batches whose workspace exceeds
+    NOALLOC_MAX_BYTES are refused)."""
+    tr = None
+    if trace:
+        ev = trace.get("events")
+        tr = Trace(*[_ptr(trace.get(k)) for k in ("topk_idx", "topk_w", "counts", "offsets", "perm")],
+                   ev.array_ptr() if ev is not None else None)
+    rc = _lib().moe_q2_forward_noalloc(_ptr(x), _ptr(router_w), _ptr(experts_q2), _ptr(shared_w), topk,
+                                       _ptr(out), ctypes.byref(shape), n_tokens, _ptr(router_b),
+                                       ctypes.byref(tr) if tr else None, _stream(stream))
+    if rc and check:
+        raise MoeQ2Error(rc, "moe_q2_forward_noalloc")
     return rc
 
 

@@ -267,12 +267,10 @@ static bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
     return pa < pb + nb && pb < pa + na;
 }
 
-extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *experts_q2,
-                              const uint16_t *shared_w, int32_t topk, float *out,
-                              const moe_q2_shape *s, int32_t n_tokens, const float *router_b,
-                              void *workspace, size_t workspace_bytes, const moe_q2_trace *trace,
-                              void *stream) {
-    int rc = check_common(s, n_tokens, topk);
+// Argument checks of a forward call that need no workspace (no HIP call).
+static int check_forward(const void *x, const float *router_w, const void *experts_q2, const uint16_t *shared_w,
+                         int32_t topk, const float *out, const moe_q2_shape *s, int32_t n_tokens) {
+    const int rc = check_common(s, n_tokens, topk);
     if (rc) return rc;
     if (!x || !router_w || !experts_q2 || !out) return MOE_Q2_EINVAL;
     if ((s->shared_inter > 0) != (shared_w != nullptr)) return MOE_Q2_EINVAL;
@@ -281,11 +279,24 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
         return MOE_Q2_EINVAL;
     const bool rms = (s->flags & MOE_Q2_PRE_RMSNORM) != 0;
     const bool accum = (s->flags & MOE_Q2_RESIDUAL_ADD) != 0;
-    const int T = n_tokens, K = topk, H = s->hidden, I = s->inter, E = s->n_experts;
-    const size_t xbytes = (size_t)T * H * ((rms || s->act_dtype == MOE_Q2_F32) ? 4 : 2);
-    if (ranges_overlap(x, xbytes, out, (size_t)T * H * 4)) {
+    const size_t xbytes = (size_t)n_tokens * s->hidden * ((rms || s->act_dtype == MOE_Q2_F32) ? 4 : 2);
+    if (ranges_overlap(x, xbytes, out, (size_t)n_tokens * s->hidden * 4)) {
         if (!(x == (const void *)out && rms && accum)) return MOE_Q2_EINVAL;
     }
+    return MOE_Q2_OK;
+}
+
+// The layer on a caller's workspace.  serial: keep every launch on `stream` (no
+// internal stream), whatever the flags say.
+static int forward_impl(const void *x, const float *router_w, const void *experts_q2, const uint16_t *shared_w,
+                        int32_t topk, float *out, const moe_q2_shape *s, int32_t n_tokens,
+                        const float *router_b, void *workspace, size_t workspace_bytes,
+                        const moe_q2_trace *trace, void *stream, bool serial) {
+    int rc = check_forward(x, router_w, experts_q2, shared_w, topk, out, s, n_tokens);
+    if (rc) return rc;
+    const bool rms = (s->flags & MOE_Q2_PRE_RMSNORM) != 0;
+    const bool accum = (s->flags & MOE_Q2_RESIDUAL_ADD) != 0;
+    const int T = n_tokens, K = topk, H = s->hidden, I = s->inter, E = s->n_experts;
     if (T == 0) return MOE_Q2_OK;
     const Workspace w = carve(s, T, K);
     if (!workspace || workspace_bytes < w.total) return MOE_Q2_EWORKSPACE;
@@ -347,7 +358,7 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     std::unique_lock<std::mutex> side_lock;
     SideJoin side_join;                  // declared after the lock: runs before the unlock
     hipStream_t sst = st;
-    if (!(s->flags & MOE_Q2_SERIAL) && !w.fused) {
+    if (!serial && !(s->flags & MOE_Q2_SERIAL) && !w.fused) {
         side = side_branch();
         if (side) {
             side_lock = std::unique_lock<std::mutex>(side->mu);
@@ -545,4 +556,64 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
     }
     return MOE_Q2_OK;
 #undef MQ_PHASE
+}
+
+extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *experts_q2,
+                              const uint16_t *shared_w, int32_t topk, float *out,
+                              const moe_q2_shape *s, int32_t n_tokens, const float *router_b,
+                              void *workspace, size_t workspace_bytes, const moe_q2_trace *trace,
+                              void *stream) {
+    return forward_impl(x, router_w, experts_q2, shared_w, topk, out, s, n_tokens, router_b, workspace,
+                        workspace_bytes, trace, stream, false);
+}
+
+// ------------------------------------------------------------------ no-allocation entry point
+// The workspace of moe_q2_forward_noalloc: one fixed array per device, part of the
+// library's device code object (allocated when the module is loaded on a device and
+// held until the process ends).  In host code `scratch` only names the symbol; its
+// device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[MOE_Q2_NOALLOC_MAX_BYTES];
+
+namespace {
+struct ScratchAddr {
+    void *ptr = nullptr;
+    bool ready = false;
+};
+ScratchAddr g_scratch[64];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, looked up once per device (with that
+// device current) and kept.
+int scratch_address(void **p) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return mq_fail_hip(e);
+    if (dev < 0 || dev >= 64) return MOE_Q2_EUNSUPPORTED;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    ScratchAddr &a = g_scratch[dev];
+    if (!a.ready) {
+        void *q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return mq_fail_hip(e);
+        if (!q || ((uintptr_t)q & 255)) return MOE_Q2_EHIP;
+        a.ptr = q;
+        a.ready = true;
+    }
+    *p = a.ptr;
+    return MOE_Q2_OK;
+}
+}  // namespace
+
+extern "C" int moe_q2_forward_noalloc(const void *x, const float *router_w, const void *experts_q2,
+                                      const uint16_t *shared_w, int32_t topk, float *out,
+                                      const moe_q2_shape *s, int32_t n_tokens, const float *router_b,
+                                      const moe_q2_trace *trace, void *stream) {
+    int rc = check_forward(x, router_w, experts_q2, shared_w, topk, out, s, n_tokens);
+    if (rc) return rc;
+    if (n_tokens == 0) return MOE_Q2_OK;
+    if (carve(s, n_tokens, topk).total > (size_t)MOE_Q2_NOALLOC_MAX_BYTES) return MOE_Q2_EUNSUPPORTED;
+    void *ws = nullptr;
+    if ((rc = scratch_address(&ws))) return rc;
+    return forward_impl(x, router_w, experts_q2, shared_w, topk, out, s, n_tokens, router_b, ws,
+                        (size_t)MOE_Q2_NOALLOC_MAX_BYTES, trace, stream, true);
 }

@@ -185,6 +185,26 @@ int moe_q2_forward(const void *x, const float *router_w, const void *experts_q2,
                    void *workspace, size_t workspace_bytes, const moe_q2_trace *trace,
                    void *stream);
 
+/* moe_q2_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer, the same kernels and results, without the workspace arguments.  The
+ * workspace is a fixed array of MOE_Q2_NOALLOC_MAX_BYTES per device inside the
+ * library's device code (allocated when the library's code is loaded on a device,
+ * held until the process ends; its address is looked up once per device).  A call
+ * whose moe_q2_workspace_size exceeds it returns MOE_Q2_EUNSUPPORTED before anything
+ * is enqueued (128 MiB holds decode batches up to about 150 tokens of the
+ * DeepSeek-class shape: hidden 7168, 256 experts, top-8, intermediate 2048).
+ * Every launch stays on `stream` (as under MOE_Q2_SERIAL: no internal stream is
+ * created) and no memory is allocated or freed.  All calls on one device share the
+ * array and it keeps the last call's contents: calls that overlap in time on one
+ * device (several streams or host threads) race and must be ordered by the caller;
+ * no call needs any of it to start at zero. */
+#define MOE_Q2_NOALLOC_MAX_BYTES (128u << 20)
+int moe_q2_forward_noalloc(const void *x, const float *router_w, const void *experts_q2,
+                           const uint16_t *shared_w, int32_t topk, float *out,
+                           const moe_q2_shape *s, int32_t n_tokens, const float *router_b,
+                           const moe_q2_trace *trace, void *stream);
+
 /* Quantize a row-major fp32 matrix w [rows, k] (device, 16-byte aligned; k a multiple
  * of 256, so every row is k / 256 blocks along its reduction dimension) into
  * rows * k / 256 84-byte blocks (device, row-major: block b of row r at index

@@ -140,3 +140,16 @@ def test_setup_helpers_validation(lib):
     assert lib.moe_q2_synth_normal(0, 0, 0, 10, 1.0, mq.F32, None, None) == mq.EINVAL
     assert lib.moe_q2_pack_expert(A, A, A, 100, 256, A, None) == mq.EUNSUPPORTED
     assert lib.moe_q2_pack_expert(None, A, A, 256, 256, A, None) == mq.EINVAL
+
+
+def test_noalloc_validation(lib):
+    """moe_q2_forward_noalloc validates like moe_q2_forward and refuses a batch whose
+    workspace exceeds its fixed per-device array, all before any HIP call."""
+    f = lib.moe_q2_forward_noalloc
+    s = mq.make_shape(7168, 2048, 256, 2048)
+    assert f(A, 2 * A, 3 * A, 5 * A, 8, 8 * A, ctypes.byref(s), 0, None, None, None) == mq.OK
+    assert f(None, 2 * A, 3 * A, 5 * A, 8, 8 * A, ctypes.byref(s), 4, None, None, None) == mq.EINVAL
+    assert f(A, 2 * A, 3 * A, None, 8, 8 * A, ctypes.byref(s), 4, None, None, None) == mq.EINVAL
+    assert mq.workspace_size(s, 255, 8) > mq.NOALLOC_MAX_BYTES
+    assert f(A, 2 * A, 3 * A, 5 * A, 8, 64 * A, ctypes.byref(s), 255, None, None, None) == mq.EUNSUPPORTED
+    assert mq.workspace_size(s, 96, 8) <= mq.NOALLOC_MAX_BYTES      # the verification micro-batch fits
