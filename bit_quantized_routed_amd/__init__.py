@@ -14,12 +14,15 @@ LIB_PATH = os.path.join(HERE, "libmoe_q2.so")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_PREFILL, PRE_RMSNORM, RESIDUAL_ADD, DECODE_VALU, SERIAL = 0, 1, 2, 4, 8, 16, 32
+BATCH_INVARIANT, ACT_Q8, GU_Q4, DOWN_Q4 = 64, 128, 256, 512
 PREFILL_MIN_TOKENS = 256
+MAX_TOKENS = 65535
 BLOCK_BYTES = 84
+Q4_BLOCK_BYTES = 148
 
 EXPORTS = ["moe_q2_block_bytes", "moe_q2_expert_bytes", "moe_q2_workspace_size",
            "moe_q2_describe", "moe_q2_forward", "moe_q2_forward_noalloc", "moe_q2_quantize",
-           "moe_q2_pack_expert",
+           "moe_q2_quantize_q4", "moe_q2_q4_block_bytes", "moe_q2_pack_expert",
            "moe_q2_synth_normal", "moe_q2_status_string", "moe_q2_last_hip_error"]
 
 
@@ -85,8 +88,12 @@ def _lib():
                                                ctypes.POINTER(Trace), vp]
         lib.moe_q2_quantize.restype = ctypes.c_int
         lib.moe_q2_quantize.argtypes = [vp, i64, i64, vp, vp]
+        lib.moe_q2_quantize_q4.restype = ctypes.c_int
+        lib.moe_q2_quantize_q4.argtypes = [vp, i64, i64, vp, vp]
+        lib.moe_q2_q4_block_bytes.restype = sz
+        lib.moe_q2_q4_block_bytes.argtypes = []
         lib.moe_q2_pack_expert.restype = ctypes.c_int
-        lib.moe_q2_pack_expert.argtypes = [vp, vp, vp, i32, i32, vp, vp]
+        lib.moe_q2_pack_expert.argtypes = [vp, vp, vp, ctypes.POINTER(Shape), vp, vp]
         lib.moe_q2_synth_normal.restype = ctypes.c_int
         lib.moe_q2_synth_normal.argtypes = [u64, u64, u64, i64, ctypes.c_float, i32, vp, vp]
         lib.moe_q2_status_string.restype = ctypes.c_char_p
@@ -197,8 +204,17 @@ def quantize(w, rows, k, blocks_out, stream=None):
         raise MoeQ2Error(rc, "moe_q2_quantize")
 
 
-def pack_expert(gate, up, down, hidden, inter, out, stream=None):
-    rc = _lib().moe_q2_pack_expert(_ptr(gate), _ptr(up), _ptr(down), hidden, inter, _ptr(out),
+def quantize_q4(w, rows, k, blocks_out, stream=None):
+    """moe_q2_quantize_q4: row-major fp32 [rows, k] -> rows * k / 256 Q4 sibling blocks."""
+    rc = _lib().moe_q2_quantize_q4(_ptr(w), rows, k, _ptr(blocks_out), _stream(stream))
+    if rc:
+        raise MoeQ2Error(rc, "moe_q2_quantize_q4")
+
+
+def pack_expert(gate, up, down, shape, out, stream=None):
+    """moe_q2_pack_expert: row-major gate, up, down block matrices (formats from the
+    shape's flags) -> the expert's tiled layout."""
+    rc = _lib().moe_q2_pack_expert(_ptr(gate), _ptr(up), _ptr(down), ctypes.byref(shape), _ptr(out),
                                    _stream(stream))
     if rc:
         raise MoeQ2Error(rc, "moe_q2_pack_expert")

@@ -12,6 +12,10 @@
 #define MQ_BLOCK_BYTES 84
 #define MQ_BLOCK_DWORDS 21
 #define MQ_WAVE 64
+// Block dwords of the two weight codecs: the 2-bit block (84 bytes) and its 4-bit
+// sibling (148 bytes).
+#define MQ_BD2 21
+#define MQ_BD4 37
 
 typedef _Float16 mq_half2 __attribute__((ext_vector_type(2)));
 typedef short mq_bf16x2_raw __attribute__((ext_vector_type(2)));

@@ -18,6 +18,15 @@
 // follows the code dword: byte b of dword s is weight 4b + s of the group (the
 // activation digits are stored in the same order).
 //
+// Two weight codecs share the arithmetic (the block's dwords: scale/min bytes 0..3,
+// codes, d|dmin last): the 2-bit block of 21 dwords (q in 0..3, sc_j 4 bits, one code
+// dword per group) and its 4-bit sibling of 37 dwords (q in 0..15, sc_j 3 bits so
+// that q*sc <= 105 stays an int8; two code dwords per group: byte b of the first
+// holds elements 4b (low nibble) and 4b + 1, of the second 4b + 2 and 4b + 3, so the
+// expanded operands keep the byte order above).  Two activation formats: two int8
+// digits of 15-bit values (ND = 2) or one int8 digit (Q8, ND = 1), in which case the
+// hi chains are absent.
+//
 // The decode kernel (k_q2_mma) and the prefill kernel (k_q2_mma_pf) differ in
 // how they tile tokens and stage operands; both are described at their
 // definitions below.
@@ -25,6 +34,7 @@
 #include <hip/hip_ext.h>
 #include <type_traits>
 #include "kernels.h"
+#include "prep_rows.h"
 #include "topk_dev.h"
 
 typedef int32_t mq_i32x4 __attribute__((ext_vector_type(4)));
@@ -78,6 +88,28 @@ __device__ __forceinline__ mq_i32x4 mq_codes_x_scale(uint32_t cw, uint32_t sc) {
     return b;
 }
 
+// q*sc of the 4-bit codec: code dwords c0 (elements 4b, 4b + 1 in byte b) and c1
+// (4b + 2, 4b + 3); every byte product is at most 15 * 7.
+__device__ __forceinline__ mq_i32x4 mq_codes4_x_scale(uint32_t c0, uint32_t c1, uint32_t sc) {
+    const uint16_t s = (uint16_t)sc;
+    mq_i32x4 b;
+    b[0] = mq_mul_bytes(c0 & 0x0F0F0F0Fu, s);
+    b[1] = mq_mul_bytes((c0 >> 4) & 0x0F0F0F0Fu, s);
+    b[2] = mq_mul_bytes(c1 & 0x0F0F0F0Fu, s);
+    b[3] = mq_mul_bytes((c1 >> 4) & 0x0F0F0F0Fu, s);
+    return b;
+}
+
+// q*sc operand of group g (g = 4 kk + q4) of the block at `blk` (BD dwords).
+template <int BD>
+__device__ __forceinline__ mq_i32x4 mq_group_operand(const uint32_t *blk, int g, int kk, int q4) {
+    if constexpr (BD == MQ_BD2) {
+        return mq_codes_x_scale(blk[4 + g], __builtin_amdgcn_ubfe(blk[kk], 8 * q4, 4));
+    } else {
+        return mq_codes4_x_scale(blk[4 + 2 * g], blk[5 + 2 * g], __builtin_amdgcn_ubfe(blk[kk], 8 * q4, 3));
+    }
+}
+
 // m_j of 4 consecutive groups (one scale dword) as 4 bf16 (exact small integers).
 __device__ __forceinline__ mq_s16x4 mq_mins_bf16(uint32_t swd) {
     const uint32_t m = (swd >> 4) & 0x0F0F0F0Fu;
@@ -87,66 +119,66 @@ __device__ __forceinline__ mq_s16x4 mq_mins_bf16(uint32_t swd) {
     return r;
 }
 
-// One block column of a 64-row tile is 64 * 84 = 5376 contiguous bytes = 336 uint4;
-// a wave moves it with 6 16-byte loads per lane.  The sixth load of lanes 16..63
-// repeats the last uint4 and lands in padding (the LDS slice holds 384 uint4), so
+// One block column of a 64-row tile is 64 * 4 * BD contiguous bytes = 16 BD uint4
+// (2-bit: 5376 bytes, 336 uint4; 4-bit: 9472 bytes, 592 uint4); a wave moves it with
+// NLD = ceil(BD / 4) 16-byte loads per lane.  The last load of the lanes past the end
+// repeats the last uint4 and lands in padding (the LDS slice holds 64 NLD uint4), so
 // no load or store is predicated.
-struct mq_bcol { mq_u32x4 a, b, c, d, e, f; };
+template <int BD>
+struct mq_bcol {
+    static constexpr int NLD = (BD + 3) / 4, N = 16 * BD;
+    mq_u32x4 v[NLD];
+};
 
-__device__ __forceinline__ void mq_bcol_load(const mq_u32x4 *__restrict__ src, int lane, mq_bcol &v) {
-    v.a = src[lane];
-    v.b = src[lane + 64];
-    v.c = src[lane + 128];
-    v.d = src[lane + 192];
-    v.e = src[lane + 256];
-    v.f = src[min(lane + 320, 335)];
+template <int BD>
+__device__ __forceinline__ void mq_bcol_load(const mq_u32x4 *__restrict__ src, int lane, mq_bcol<BD> &c) {
+    constexpr int NLD = mq_bcol<BD>::NLD;
+#pragma unroll
+    for (int i = 0; i < NLD - 1; ++i) c.v[i] = src[lane + 64 * i];
+    c.v[NLD - 1] = src[min(lane + 64 * (NLD - 1), mq_bcol<BD>::N - 1)];
 }
 
-__device__ __forceinline__ void mq_bcol_store(mq_u32x4 *__restrict__ dst, int lane, const mq_bcol &v) {
-    dst[lane] = v.a;
-    dst[lane + 64] = v.b;
-    dst[lane + 128] = v.c;
-    dst[lane + 192] = v.d;
-    dst[lane + 256] = v.e;
-    dst[lane + 320] = v.f;
+template <int BD>
+__device__ __forceinline__ void mq_bcol_store(mq_u32x4 *__restrict__ dst, int lane, const mq_bcol<BD> &c) {
+#pragma unroll
+    for (int i = 0; i < mq_bcol<BD>::NLD; ++i) dst[lane + 64 * i] = c.v[i];
 }
 
 // Activation operands of one block column for one MFMA lane (token l % 16, group
-// quad q4 = l / 16): digits of groups 4kk + q4 (hi, lo) and the two bf16 planes of
-// the group sums 4q4 .. 4q4+3.
+// quad q4 = l / 16): digits of groups 4kk + q4 (hi, lo; lo only for one digit) and
+// the two bf16 planes of the group sums 4q4 .. 4q4+3.
 struct mq_acol { mq_i32x4 hi[4], lo[4]; mq_s16x4 sh, sl; };
 
 // One 64-row block column from the wave's LDS slice into the 4 N fragments:
-// integer products of both activation digits on the i8 matrix cores, the min
+// integer products of the activation digits on the i8 matrix cores, the min
 // term on the bf16 matrix cores, and the per-block fold with d and dmin -- of all
 // 4 of each lane's token rows, or (one = true, a wave-uniform flag: a unit of one
 // slot) only of the first, the others being padding whose sums are never stored.
+template <int ND, int BD>
 __device__ __forceinline__ void mq_mma_column(const uint32_t *__restrict__ my, int r16, int q4,
                                               const mq_acol &a, mq_f32x4 (&tot)[4], bool one) {
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) {
-        const uint32_t *blk = my + (16 * nf + r16) * MQ_BLOCK_DWORDS;
+        const uint32_t *blk = my + (16 * nf + r16) * BD;
         mq_i32x4 ih = {0, 0, 0, 0}, il = {0, 0, 0, 0};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const uint32_t cw = blk[4 + 4 * kk + q4];
-            const uint32_t sc = __builtin_amdgcn_ubfe(blk[kk], 8 * q4, 4);
-            const mq_i32x4 b = mq_codes_x_scale(cw, sc);
-            ih = __builtin_amdgcn_mfma_i32_16x16x64_i8(a.hi[kk], b, ih, 0, 0, 0);
+            const mq_i32x4 b = mq_group_operand<BD>(blk, 4 * kk + q4, kk, q4);
+            if (ND == 2) ih = __builtin_amdgcn_mfma_i32_16x16x64_i8(a.hi[kk], b, ih, 0, 0, 0);
             il = __builtin_amdgcn_mfma_i32_16x16x64_i8(a.lo[kk], b, il, 0, 0, 0);
         }
         const mq_s16x4 bm = mq_mins_bf16(blk[q4]);
         mq_f32x4 am = {0.f, 0.f, 0.f, 0.f};
         am = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.sh, bm, am, 0, 0, 0);
         am = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.sl, bm, am, 0, 0, 0);
-        const uint32_t dd = blk[20];
+        const uint32_t dd = blk[BD - 1];
         const float d = mq_h2f((uint16_t)(dd & 0xFFFFu));
         const float dmin = mq_h2f((uint16_t)(dd >> 16));
-        tot[nf][0] = fmaf(d, (float)((ih[0] << 8) + il[0]), fmaf(-dmin, am[0], tot[nf][0]));
+        tot[nf][0] = fmaf(d, (float)(ND == 2 ? (ih[0] << 8) + il[0] : il[0]), fmaf(-dmin, am[0], tot[nf][0]));
         if (!one) {
 #pragma unroll
             for (int i = 1; i < 4; ++i) {
-                const float qv = (float)((ih[i] << 8) + il[i]);
+                const float qv = (float)(ND == 2 ? (ih[i] << 8) + il[i] : il[i]);
                 tot[nf][i] = fmaf(d, qv, fmaf(-dmin, am[i], tot[nf][i]));
             }
         }
@@ -170,7 +202,7 @@ __device__ __forceinline__ void mq_mma_column(const uint32_t *__restrict__ my, i
 //   down: out0[s][slot][row]
 // Padding tokens (beyond the unit's count) read the all-zero activation row zrow
 // and write to the discard row trash_row.
-#define DM_AITEMS 576          // 512 digit vectors + 64 sum vectors per column
+#define DM_AITEMS(ND) (256 * (ND) + 64)   // digit vectors + 64 sum vectors per column
 
 // ------------------------------------------------------------------ dense rows
 // The shared expert's bf16 rows for up to 255 tokens, in the same launch as the
@@ -367,6 +399,7 @@ __device__ __forceinline__ void mq_dense_wg_prep(const MqDense &d, const MqDownP
 // laid out as one row of the digit preparation's output (xr: [group][digit] 16-byte
 // vectors, xs: [block][quad][plane][4] bf16), the same arithmetic.  Thread i takes
 // elements 8 i .. 8 i + 7 (half a group; the two halves are joined by a lane swap).
+template <int ND>
 __device__ __forceinline__ void mq_row_prep_lds(const MqDownPrep &pp, int row, mq_u32x4 *xr, uint16_t *xs,
                                                 float *rsc, float *wmax, int tid) {
     const int G = pp.len / 16;
@@ -413,8 +446,8 @@ __device__ __forceinline__ void mq_row_prep_lds(const MqDownPrep &pp, int row, m
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     int ex = 0;
     if (amax > 0.0f) frexpf(amax, &ex);
-    const float inv_s = amax > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
-    if (tid == 0) *rsc = amax > 0.0f ? ldexpf(1.0f, ex - 14) : 1.0f;
+    const float inv_s = amax > 0.0f ? ldexpf(1.0f, MQ_ACT_BITS(ND) - ex) : 1.0f;
+    if (tid == 0) *rsc = amax > 0.0f ? ldexpf(1.0f, ex - MQ_ACT_BITS(ND)) : 1.0f;
     // this half group's bytes of the digit dwords: dword s4 holds the digits of the
     // elements 4 b + s4 of the group, so elements 0..7 fill bytes 0, 1 and elements
     // 8..15 bytes 2, 3 of every dword
@@ -426,9 +459,9 @@ __device__ __forceinline__ void mq_row_prep_lds(const MqDownPrep &pp, int row, m
         uint32_t h = 0, l = 0;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            const int x = (int)rintf(v[4 * b + s4] * inv_s);
+            const int x = mq_quant_act<ND>(v[4 * b + s4] * 1.0f, inv_s);
             sum += x;
-            const int dh = (x + 128) >> 8;
+            const int dh = ND == 2 ? (x + 128) >> 8 : 0;
             const int dl = x - (dh << 8);
             h |= ((uint32_t)(dh & 0xFF)) << (8 * (2 * half + b));
             l |= ((uint32_t)(dl & 0xFF)) << (8 * (2 * half + b));
@@ -444,8 +477,12 @@ __device__ __forceinline__ void mq_row_prep_lds(const MqDownPrep &pp, int row, m
     }
     sum += __shfl_xor(sum, 1, 64);
     if (on && half == 0 && g < G) {
-        xr[2 * g] = hi;
-        xr[2 * g + 1] = lo;
+        if (ND == 2) {
+            xr[2 * g] = hi;
+            xr[2 * g + 1] = lo;
+        } else {
+            xr[g] = lo;
+        }
         const float fs = (float)sum;                           // exact: |sum| <= 2^18
         const uint16_t bh = mq_f32_to_bf16(fs);
         const uint16_t bl = mq_f32_to_bf16(fs - mq_bf16_to_f32(bh));
@@ -536,7 +573,7 @@ __device__ __forceinline__ int4 mq_route_unit(const MqRoute &rt, int u, MqRouteL
     return un;
 }
 
-template <bool GU>
+template <bool GU, int ND, int BD>
 __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ experts, int64_t expert_bytes,
                                                 int64_t mat_off, int tiles, int kblocks, int nsplit,
                                                 int cps, const int4 *__restrict__ units,
@@ -546,15 +583,17 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
                                                 const float *__restrict__ xscale, float *__restrict__ out0,
                                                 float *__restrict__ out1, int out_ld, int64_t split_stride,
                                                 int q2_grid, const MqDense dn, const MqRoute rt,
-                                                int route_on, const MqDownPrep pp, int prep_on) {
-    __shared__ __attribute__((aligned(16))) mq_u32x4 sW[4][384];           // weight slices, one per wave
+                                                int route_on, const MqDownPrep pp, int prep_on,
+                                                const int32_t *__restrict__ eslot) {
+    constexpr int NLD = mq_bcol<BD>::NLD, NA = DM_AITEMS(ND), NIT = (NA + 255) / 256;
+    __shared__ __attribute__((aligned(16))) mq_u32x4 sW[4][64 * NLD];      // weight slices, one per wave
     static_assert(sizeof(MqRouteLds) <= sizeof(sW), "routing LDS fits the weight slices");
     static_assert(MQ_DOWN_PREP_SHARED_BYTES <= sizeof(sW), "shared SwiGLU planes fit the weight slices");
-    __shared__ __attribute__((aligned(16))) mq_u32x4 sA[2][DM_AITEMS];     // activation operands
+    __shared__ __attribute__((aligned(16))) mq_u32x4 sA[2][NA];            // activation operands
     __shared__ int s_row[16];
     __shared__ float s_sc[16];
     // one-token down launch: the unit's activation row prepared here
-    __shared__ __attribute__((aligned(16))) mq_u32x4 s_xr[2 * MQ_DOWN_PREP_MAX_LEN / 16];
+    __shared__ __attribute__((aligned(16))) mq_u32x4 s_xr[ND * MQ_DOWN_PREP_MAX_LEN / 16];
     __shared__ __attribute__((aligned(16))) uint16_t s_xs[MQ_DOWN_PREP_MAX_LEN / 256 * 32];
     __shared__ float s_rsc, s_wmax[4];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -586,17 +625,18 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
         un = units[u];
         urv = GU && tid < 16 ? urow[(int64_t)u * 16 + tid] : 0;
     }
-    const int e = un.x, p0 = un.y, nt = un.z;
+    const int p0 = un.y, nt = un.z;
     if (nt == 0) return;                                 // past the last unit
+    const int e = eslot ? eslot[un.x] : un.x;            // the expert's slot in a cache arena
     const int tile = 4 * tg + wv;
     const int G = kblocks * 16;
-    const int64_t tile_bytes = (int64_t)kblocks * 64 * MQ_BLOCK_BYTES;
+    const int64_t tile_bytes = (int64_t)kblocks * 64 * BD * 4;
     const mq_u32x4 *tb = (const mq_u32x4 *)(experts + (int64_t)e * expert_bytes + mat_off +
                                             (int64_t)tile * tile_bytes);
-    mq_bcol wb;
-    mq_bcol_load(tb + (int64_t)c0 * 336, lane, wb);      // weights first: needs only the unit
+    mq_bcol<BD> wb;
+    mq_bcol_load<BD>(tb + (int64_t)c0 * (16 * BD), lane, wb);   // weights first: needs only the unit
     const bool lrow = !GU && prep_on;                    // activations from the row prepared here
-    if (lrow) mq_row_prep_lds(pp, p0, s_xr, s_xs, &s_rsc, s_wmax, tid);
+    if (lrow) mq_row_prep_lds<ND>(pp, p0, s_xr, s_xs, &s_rsc, s_wmax, tid);
     float scv = 0.0f;                                    // row scale, to LDS in the loop
     if (tid < 16) {
         const int ar = tid < nt ? (GU ? urv : p0 + tid) : zrow;
@@ -604,29 +644,29 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
         scv = lrow ? (tid < nt ? s_rsc : 1.0f) : xscale[ar];
     }
     __syncthreads();
-    // this thread's three activation items, one per LDS slot so that a wave's
+    // this thread's activation items (NIT), one per LDS slot so that a wave's
     // stores are lane-contiguous (the last ones clamped: duplicate writes of
-    // identical data).  Slot i < 512 = (kk * 2 + digit) * 64 + lane holds the digit
+    // identical data).  Slot i < 256 ND = (kk * ND + digit) * 64 + lane holds the digit
     // vector of MFMA step kk for lane (token l % 16, group 4 kk + l / 16); slot
-    // 512 + l the group-sum vector of lane l (token l % 16, quad l / 16).
+    // 256 ND + l the group-sum vector of lane l (token l % 16, quad l / 16).
     // global address space stated explicitly: a generic (flat) load would also count
     // against the LDS counter and make every LDS wait in the column wait for it
     typedef const __attribute__((address_space(1))) mq_u32x4 *gvec;
-    gvec asrc[3];
-    const mq_u32x4 *lsrc[3];                             // (row prepared here) LDS source, null: zero
-    int aslot[3], astep[3];
+    gvec asrc[NIT];
+    const mq_u32x4 *lsrc[NIT];                           // (row prepared here) LDS source, null: zero
+    int aslot[NIT], astep[NIT];
 #pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        const int it = min(tid + 256 * n, DM_AITEMS - 1);
-        if (it < 512) {
-            const int l = it & 63, d = (it >> 6) & 1, kk = it >> 7;
+    for (int n = 0; n < NIT; ++n) {
+        const int it = min(tid + 256 * n, NA - 1);
+        if (it < 256 * ND) {
+            const int l = it & 63, d = (it >> 6) % ND, kk = it / (64 * ND);
             const int tk = l & 15, g = 4 * kk + (l >> 4);
-            asrc[n] = (gvec)(xdig + (int64_t)s_row[tk] * G * 2 + g * 2 + d);
-            lsrc[n] = tk < nt ? s_xr + g * 2 + d : nullptr;
+            asrc[n] = (gvec)(xdig + (int64_t)s_row[tk] * G * ND + g * ND + d);
+            lsrc[n] = tk < nt ? s_xr + g * ND + d : nullptr;
             aslot[n] = it;
-            astep[n] = 32;
+            astep[n] = 16 * ND;
         } else {
-            const int l = it - 512;
+            const int l = it - 256 * ND;
             asrc[n] = (gvec)((const mq_u32x4 *)(xsum + (int64_t)s_row[l & 15] * G) + (l >> 4));
             lsrc[n] = (l & 15) < nt ? (const mq_u32x4 *)s_xs + (l >> 4) : nullptr;
             aslot[n] = it;
@@ -637,9 +677,9 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
     auto aload = [&](int n, int c) {
         return lrow ? (lsrc[n] ? lsrc[n][c * astep[n]] : z4) : asrc[n][c * astep[n]];
     };
-    mq_u32x4 ab[3];
+    mq_u32x4 ab[NIT];
 #pragma unroll
-    for (int n = 0; n < 3; ++n) ab[n] = aload(n, c0);
+    for (int n = 0; n < NIT; ++n) ab[n] = aload(n, c0);
 
     mq_f32x4 tot[4];
 #pragma unroll
@@ -649,27 +689,27 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
     int buf = 0;
     for (int c = c0; c < c1; ++c) {
         if (tid < 16) s_sc[tid] = scv;
-        mq_bcol_store(sW[wv], lane, wb);
+        mq_bcol_store<BD>(sW[wv], lane, wb);
 #pragma unroll
-        for (int n = 0; n < 3; ++n) sA[buf][aslot[n]] = ab[n];
+        for (int n = 0; n < NIT; ++n) sA[buf][aslot[n]] = ab[n];
         // the registers are free again: the next column's loads go out before the
         // barrier, so its latency overlaps the wait for the other waves
         if (c + 1 < c1) {
-            mq_bcol_load(tb + (int64_t)(c + 1) * 336, lane, wb);
+            mq_bcol_load<BD>(tb + (int64_t)(c + 1) * (16 * BD), lane, wb);
 #pragma unroll
-            for (int n = 0; n < 3; ++n) ab[n] = aload(n, c + 1);
+            for (int n = 0; n < NIT; ++n) ab[n] = aload(n, c + 1);
         }
         __syncthreads();
         mq_acol a;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            a.hi[kk] = __builtin_bit_cast(mq_i32x4, sA[buf][(kk * 2) * 64 + lane]);
-            a.lo[kk] = __builtin_bit_cast(mq_i32x4, sA[buf][(kk * 2 + 1) * 64 + lane]);
+            if (ND == 2) a.hi[kk] = __builtin_bit_cast(mq_i32x4, sA[buf][(kk * 2) * 64 + lane]);
+            a.lo[kk] = __builtin_bit_cast(mq_i32x4, sA[buf][(kk * ND + ND - 1) * 64 + lane]);
         }
-        const mq_u32x4 sv = sA[buf][512 + lane];
+        const mq_u32x4 sv = sA[buf][256 * ND + lane];
         a.sh = __builtin_bit_cast(mq_s16x4, (uint2){sv[0], sv[1]});
         a.sl = __builtin_bit_cast(mq_s16x4, (uint2){sv[2], sv[3]});
-        mq_mma_column(myd, r16, q4, a, tot, one);
+        mq_mma_column<ND, BD>(myd, r16, q4, a, tot, one);
         buf ^= 1;
     }
     // D layout: lane l, element i -> token 4*(l/16) + i, row slot 16*nf + l%16
@@ -709,13 +749,14 @@ void mq_dec_split(int max_units, int tiles, int kblocks, int max_split, int *nsp
     *nsplit = (kblocks + c - 1) / c;
 }
 
-int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t mat_off, int tiles,
-                     int kblocks, const int4 *units, int max_units, const int32_t *urow, int zrow,
-                     int trash_row, const void *xdig,
+int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t expert_bytes, int64_t mat_off,
+                     int tiles, int kblocks, const int4 *units, int max_units, int split_units,
+                     const int32_t *urow, int zrow, int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
                      int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route,
                      const MqDownPrep *prep, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     if (tiles % 4) return MOE_Q2_EUNSUPPORTED;
+    if ((fmt.nd != 1 && fmt.nd != 2) || (fmt.bd != MQ_BD2 && fmt.bd != MQ_BD4)) return MOE_Q2_EINVAL;
     if (gu && !urow) return MOE_Q2_EINVAL;
     if (route && (!gu || route->T < 1 || route->T > MQ_TOPK_BUCKET_MAX_T || route->E > MQ_ROUTE_MAX_E ||
                   route->K > 16 || route->K < 1))
@@ -728,7 +769,7 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
     const MqDownPrep pp = prep ? *prep : MqDownPrep{};
     const int prep_on = prep ? 1 : 0;
     int nsplit = 1, cps = kblocks;
-    mq_dec_split(max_units, tiles, kblocks, gu ? MQ_DEC_SPLIT_GU : MQ_DEC_SPLIT_D, &nsplit, &cps);
+    mq_dec_split(split_units, tiles, kblocks, gu ? MQ_DEC_SPLIT_GU : MQ_DEC_SPLIT_D, &nsplit, &cps);
     const int64_t q2_grid = (int64_t)max_units * nsplit * (tiles / 4);
     MqDense dn = {};
     int64_t dgrid = 0;
@@ -757,54 +798,63 @@ int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t 
     const int64_t grid = q2_grid + dgrid;
     if (grid <= 0) return mq_mark_empty(ev0, ev1, st);
     if (grid > 0x7fffffff) return MOE_Q2_EUNSUPPORTED;
-    if (gu)
-        MQ_LAUNCH_TIMED(ev0, ev1, k_q2_mma<true>, dim3((unsigned)grid), dim3(256), 0, st,
-                        (const uint8_t *)experts, expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units,
-                        urow, zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
-                        split_stride, (int)q2_grid, dn, rt, route_on, pp, prep_on);
-    else
-        MQ_LAUNCH_TIMED(ev0, ev1, k_q2_mma<false>, dim3((unsigned)grid), dim3(256), 0, st,
-                        (const uint8_t *)experts, expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units,
-                        urow, zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld,
-                        split_stride, (int)q2_grid, dn, rt, route_on, pp, prep_on);
+#define MQ_Q2_MMA_LAUNCH(GUV, NDV, BDV)                                                                  \
+    MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma<GUV, NDV, BDV>), dim3((unsigned)grid), dim3(256), 0, st,          \
+                    (const uint8_t *)experts, expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units, urow, \
+                    zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld, split_stride,  \
+                    (int)q2_grid, dn, rt, route_on, pp, prep_on, fmt.eslot)
+    const int sel = (gu ? 4 : 0) + (fmt.nd == 2 ? 2 : 0) + (fmt.bd == MQ_BD4 ? 1 : 0);
+    switch (sel) {
+    case 0: MQ_Q2_MMA_LAUNCH(false, 1, MQ_BD2); break;
+    case 1: MQ_Q2_MMA_LAUNCH(false, 1, MQ_BD4); break;
+    case 2: MQ_Q2_MMA_LAUNCH(false, 2, MQ_BD2); break;
+    case 3: MQ_Q2_MMA_LAUNCH(false, 2, MQ_BD4); break;
+    case 4: MQ_Q2_MMA_LAUNCH(true, 1, MQ_BD2); break;
+    case 5: MQ_Q2_MMA_LAUNCH(true, 1, MQ_BD4); break;
+    case 6: MQ_Q2_MMA_LAUNCH(true, 2, MQ_BD2); break;
+    default: MQ_Q2_MMA_LAUNCH(true, 2, MQ_BD4); break;
+    }
+#undef MQ_Q2_MMA_LAUNCH
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
 
 // ------------------------------------------------------------------ activation digits
 // (row preparation in prep_rows.h)
-#include "prep_rows.h"
 
 
-template <int SRC>
+template <int SRC, int ND>
 __global__ void __launch_bounds__(256) k_prep_digits(const void *__restrict__ src,
                                                      const void *__restrict__ src2, int nsplit,
                                                      int64_t split_stride, int nrows, int len,
                                                      int64_t src_ld, mq_u32x4 *__restrict__ xdig,
                                                      uint32_t *__restrict__ xsum,
                                                      float *__restrict__ scale, const MqSharedRows sh) {
-    mq_prep_digits_wg<SRC>(src, src2, nsplit, split_stride, nrows, len, src_ld, xdig, xsum, scale, sh,
-                           (int)blockIdx.x);
+    mq_prep_digits_wg<SRC, ND>(src, src2, nsplit, split_stride, nrows, len, src_ld, xdig, xsum, scale, sh,
+                               (int)blockIdx.x);
 }
 
 int mq_launch_prep_digits(const void *src, int src_bf16, int nrows, int len, int64_t src_ld,
-                          void *xdig, uint32_t *xsum, float *scale, hipStream_t st) {
+                          void *xdig, uint32_t *xsum, float *scale, int nd, hipStream_t st) {
     if (nrows <= 0) return MOE_Q2_OK;
     if (len / 16 > 256 * PD_NG) return MOE_Q2_EUNSUPPORTED;
     dim3 grid(nrows + 1);                        // nrows rows + the zero row
-    if (src_bf16)
-        hipLaunchKernelGGL(k_prep_digits<1>, grid, dim3(256), 0, st, src, nullptr, 1, (int64_t)0, nrows, len,
-                           src_ld, (mq_u32x4 *)xdig, xsum, scale, MqSharedRows{});
-    else
-        hipLaunchKernelGGL(k_prep_digits<0>, grid, dim3(256), 0, st, src, nullptr, 1, (int64_t)0, nrows, len,
-                           src_ld, (mq_u32x4 *)xdig, xsum, scale, MqSharedRows{});
+#define MQ_PREP_LAUNCH(SRCV, NDV)                                                                         \
+    hipLaunchKernelGGL((k_prep_digits<SRCV, NDV>), grid, dim3(256), 0, st, src, nullptr, 1, (int64_t)0, nrows, \
+                       len, src_ld, (mq_u32x4 *)xdig, xsum, scale, MqSharedRows{})
+    if (src_bf16) {
+        if (nd == 2) MQ_PREP_LAUNCH(1, 2); else MQ_PREP_LAUNCH(1, 1);
+    } else {
+        if (nd == 2) MQ_PREP_LAUNCH(0, 2); else MQ_PREP_LAUNCH(0, 1);
+    }
+#undef MQ_PREP_LAUNCH
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
 
 int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit, int64_t split_stride,
                                  int nrows, int len, int64_t src_ld, void *xdig, uint32_t *xsum,
-                                 float *scale, const MqSharedSwiglu *shared, hipStream_t st) {
+                                 float *scale, const MqSharedSwiglu *shared, int nd, hipStream_t st) {
     if (nrows <= 0) return MOE_Q2_OK;
     if (len / 16 > 256 * PD_NG) return MOE_Q2_EUNSUPPORTED;
     MqSharedRows sh = {};
@@ -814,9 +864,14 @@ int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit,
                           shared->lo};
         extra = shared->T * ((shared->Is + 255) / 256);
     }
-    hipLaunchKernelGGL(k_prep_digits<2>, dim3(nrows + 1 + extra), dim3(256), 0, st, (const void *)gate,
-                       (const void *)up, nsplit, split_stride, nrows, len, src_ld, (mq_u32x4 *)xdig, xsum,
-                       scale, sh);
+    if (nd == 2)
+        hipLaunchKernelGGL((k_prep_digits<2, 2>), dim3(nrows + 1 + extra), dim3(256), 0, st, (const void *)gate,
+                           (const void *)up, nsplit, split_stride, nrows, len, src_ld, (mq_u32x4 *)xdig, xsum,
+                           scale, sh);
+    else
+        hipLaunchKernelGGL((k_prep_digits<2, 1>), dim3(nrows + 1 + extra), dim3(256), 0, st, (const void *)gate,
+                           (const void *)up, nsplit, split_stride, nrows, len, src_ld, (mq_u32x4 *)xdig, xsum,
+                           scale, sh);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
@@ -845,7 +900,7 @@ int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit,
 // w ^ (t & 15), then [token][4 sum words] with word q at q ^ ((t & 15) >> 2); the
 // XOR swizzles keep the 16 lanes that read one word of 16 different tokens on
 // distinct banks.  Weights = the 4 tiles' column pieces in global order.
-template <bool SWIGLU, int MF>
+template <bool SWIGLU, int MF, int ND>
 __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ experts,
                                                    int64_t expert_bytes, int64_t mat_off, int rows,
                                                    int kblocks, const int32_t *__restrict__ units_hdr,
@@ -854,17 +909,19 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                                                    const mq_u32x4 *__restrict__ xdig,
                                                    const uint32_t *__restrict__ xsum,
                                                    const float *__restrict__ xscale,
-                                                   float *__restrict__ out) {
+                                                   float *__restrict__ out, const int32_t *__restrict__ eslot) {
     constexpr int NTOK = 16 * MF;
+    constexpr int WPT = 16 * ND;                        // 16-byte digit words per token and column
+    constexpr int TPL = 64 / WPT;                       // tokens per 1 KB digit load
     constexpr int NWJ = 4 * 336 / 64;                   // weight loads (1 KB each)
-    constexpr int NDJ = NTOK / 2;                       // digit loads (2 tokens each)
+    constexpr int NDJ = NTOK / TPL;                     // digit loads
     constexpr int NSJ = NTOK * 4 / 64;                  // sum loads (16 tokens each)
     constexpr int NJ = NDJ + NSJ + NWJ;
     constexpr int JPW = (NJ + 7) / 8;                   // loads per wave (at most)
-    constexpr int SUMS = NTOK * 128;                    // dword offset of the sum words
+    constexpr int SUMS = NTOK * 4 * WPT;                // dword offset of the sum words
     static_assert(4 * 336 % 64 == 0 && NTOK % 16 == 0, "load split");
     // one LDS array for all staging (weights, activations, token rows)
-    constexpr int SB_SZ = NWJ * 256, SA_SZ = NTOK * 144, SB_OFF = 2 * SA_SZ;
+    constexpr int SB_SZ = NWJ * 256, SA_SZ = NTOK * (4 * WPT + 16), SB_OFF = 2 * SA_SZ;
     __shared__ __attribute__((aligned(16))) uint32_t smem[2 * SB_SZ + 2 * SA_SZ + 2 * NTOK];
     typedef __attribute__((address_space(1))) void gvoid;
     typedef __attribute__((address_space(3))) void lvoid;
@@ -880,13 +937,14 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     const mq_i32x4 zi = {0, 0, 0, 0};
     const int sw = r16;                                  // digit word swizzle of this lane's token
     const int ssw = 4 * (q4 ^ (r16 >> 2));               // sum word position (dwords)
-    // this lane's digit words of MFMA step kk (d = 0 hi, 1 lo) in its token's row of a
-    // buffer, in dwords; fragment m adds 16 * 128 m (a constant of the LDS read)
-    int xo[4][2];
+    // this lane's digit words of MFMA step kk (d = 0 hi, 1 lo; the one digit of Q8 at
+    // d = 0) in its token's row of a buffer, in dwords; fragment m adds 16 * 4 WPT m
+    // (a constant of the LDS read)
+    int xo[4][ND];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int d = 0; d < 2; ++d) xo[kk][d] = r16 * 128 + 4 * ((2 * (4 * kk + q4) + d) ^ sw);
+        for (int d = 0; d < ND; ++d) xo[kk][d] = r16 * 4 * WPT + 4 * ((ND * (4 * kk + q4) + d) ^ sw);
 
     // Work items blockIdx.x, + gridDim.x, ...  While an item runs, the next one's token
     // rows are loaded (into the other half of arow_b) and, in its last column, the next
@@ -904,7 +962,7 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     int4 un = units[wu / stiles];
     if (tid < NTOK) arow_b[tid] = token_row(un, tid);
     __syncthreads();
-    // load j = wv + 8 n of a column: digits of tokens 2j, 2j + 1 (j < NDJ), sums of
+    // load j = wv + 8 n of a column: digits of tokens TPL j .. TPL j + TPL - 1 (j < NDJ), sums of
     // tokens 16 (j - NDJ) .. +15, or 1 KB of the 4 tiles' weight pieces; each lane's
     // byte offset from the column's base is fixed for the work item
     uint32_t voff[JPW];
@@ -914,8 +972,8 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
             const int j = wv + 8 * n;
             uint32_t o = 0;
             if (j < NDJ) {
-                const int t = 2 * j + (lane >> 5), w = (lane & 31) ^ (t & 15);
-                o = (uint32_t)((arow[t] * kblocks * 32 + w) * 16);
+                const int t = TPL * j + lane / WPT, w = (lane % WPT) ^ (t & 15);
+                o = (uint32_t)((arow[t] * kblocks * WPT + w) * 16);
             } else if (j < NDJ + NSJ) {
                 const int q = 64 * (j - NDJ) + lane, t = q >> 2, w = (q & 3) ^ ((t & 15) >> 2);
                 o = (uint32_t)((arow[t] * kblocks * 16 + 4 * w) * 4);
@@ -929,14 +987,14 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     // column b of the item at tbase into buffer buf; digit and sum loads only for the
     // first mfc token fragments (the rest are never read)
     auto dma = [&](int b, int buf, int mfc, const uint8_t *tbase) {
-        const char *db = (const char *)xdig + (int64_t)b * 512;
+        const char *db = (const char *)xdig + (int64_t)b * (16 * WPT);
         const char *sb = (const char *)xsum + (int64_t)b * 64;
         const char *wb = (const char *)tbase + (int64_t)b * 5376;
 #pragma unroll
         for (int n = 0; n < JPW; ++n) {
             const int j = wv + 8 * n;
             if (j < NDJ) {
-                if (j < 8 * mfc)
+                if (j < (16 / TPL) * mfc)
                     __builtin_amdgcn_global_load_lds((gvoid *)(db + voff[n]), (lvoid *)(smem + buf * SA_SZ + 256 * j), 16, 0, 0);
             } else if (j < NDJ + NSJ) {
                 if (j - NDJ < mfc)
@@ -955,7 +1013,8 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
         const int e = un.x, p0 = un.y, nt = un.z;
         const int *arow_s = arow_b + (k & 1) * NTOK;
         int *arow_n = arow_b + ((k + 1) & 1) * NTOK;
-        const uint8_t *tb = experts + (int64_t)e * expert_bytes + mat_off + (int64_t)(4 * st) * tile_bytes;
+        const uint8_t *tb = experts + (int64_t)(eslot ? eslot[e] : e) * expert_bytes + mat_off +
+                            (int64_t)(4 * st) * tile_bytes;
         // the next item; from 3 columns on, its rows are written in column kblocks - 2
         // (every wave is past the previous item's outputs, which read that half, once
         // column 0's barrier is behind it) and its first column staged in the last one
@@ -963,7 +1022,8 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
         const bool has_next = wn < nitems;
         const int4 unn = has_next ? units[wn / stiles] : make_int4(0, 0, 1, 0);
         const int stn = wn - (wn / stiles) * stiles;
-        const uint8_t *tbn = experts + (int64_t)unn.x * expert_bytes + mat_off + (int64_t)(4 * stn) * tile_bytes;
+        const uint8_t *tbn = experts + (int64_t)(eslot && has_next ? eslot[unn.x] : unn.x) * expert_bytes + mat_off +
+                             (int64_t)(4 * stn) * tile_bytes;
         const int mfcn = (unn.z + 15) >> 4;
         const bool chain = has_next && kblocks >= 3;
         const int nrow = has_next && tid < NTOK ? token_row(unn, tid) : 0;
@@ -1011,16 +1071,23 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                 // one token fragment at a time: its four integer chains, the min term, the fold
 #pragma unroll
                 for (int m = 0; m < MFC; ++m) {
-                    mq_i32x4 hi0, lo0, hi1, lo1;
+                    mq_i32x4 hi0 = zi, lo0, hi1 = zi, lo1;
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
-                        const mq_i32x4 ah = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(sAc + xo[kk][0] + 2048 * m));
-                        const mq_i32x4 al = __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(sAc + xo[kk][1] + 2048 * m));
+                        const mq_i32x4 al = __builtin_bit_cast(
+                            mq_i32x4, *(const mq_u32x4 *)(sAc + xo[kk][ND - 1] + 16 * 4 * WPT * m));
                         // the first step of each chain starts from zero (no accumulator to clear)
-                        hi0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b0[kk], kk ? hi0 : zi, 0, 0, 0);
-                        lo0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b0[kk], kk ? lo0 : zi, 0, 0, 0);
-                        hi1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b1[kk], kk ? hi1 : zi, 0, 0, 0);
-                        lo1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b1[kk], kk ? lo1 : zi, 0, 0, 0);
+                        if (ND == 2) {
+                            const mq_i32x4 ah = __builtin_bit_cast(
+                                mq_i32x4, *(const mq_u32x4 *)(sAc + xo[kk][0] + 16 * 4 * WPT * m));
+                            hi0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b0[kk], kk ? hi0 : zi, 0, 0, 0);
+                            lo0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b0[kk], kk ? lo0 : zi, 0, 0, 0);
+                            hi1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b1[kk], kk ? hi1 : zi, 0, 0, 0);
+                            lo1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b1[kk], kk ? lo1 : zi, 0, 0, 0);
+                        } else {
+                            lo0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b0[kk], kk ? lo0 : zi, 0, 0, 0);
+                            lo1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b1[kk], kk ? lo1 : zi, 0, 0, 0);
+                        }
                     }
                     const mq_u32x4 xv = *(const mq_u32x4 *)(sAc + SUMS + (16 * m + r16) * 16 + ssw);
                     const mq_s16x4 xh = __builtin_bit_cast(mq_s16x4, (uint2){xv[0], xv[1]});
@@ -1032,8 +1099,10 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                     a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, bm1, a1, 0, 0, 0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        tot[m][0][i] = fmaf(d0, (float)((hi0[i] << 8) + lo0[i]), fmaf(-m0, a0[i], tot[m][0][i]));
-                        tot[m][1][i] = fmaf(d1, (float)((hi1[i] << 8) + lo1[i]), fmaf(-m1, a1[i], tot[m][1][i]));
+                        const int v0 = ND == 2 ? (hi0[i] << 8) + lo0[i] : lo0[i];
+                        const int v1 = ND == 2 ? (hi1[i] << 8) + lo1[i] : lo1[i];
+                        tot[m][0][i] = fmaf(d0, (float)v0, fmaf(-m0, a0[i], tot[m][0][i]));
+                        tot[m][1][i] = fmaf(d1, (float)v1, fmaf(-m1, a1[i], tot[m][1][i]));
                     }
                 }
                 __builtin_amdgcn_s_waitcnt(0);
@@ -1078,24 +1147,27 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
 }
 
 
-int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
-                        int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
+int mq_launch_q2_mma_pf(int swiglu, const MqFormat &fmt, const void *experts, int64_t expert_bytes,
+                        int64_t mat_off, int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                         int max_units, const int32_t *perm, int topk, const void *xdig,
                         const uint32_t *xsum, const float *xscale, float *out, int n_cu,
                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    if ((fmt.nd != 1 && fmt.nd != 2) || fmt.bd != MQ_BD2) return MOE_Q2_EINVAL;
     const int stiles = rows / (swiglu ? 32 : 64) / 4;
     int64_t want = (int64_t)max_units * stiles;
     int64_t cap = (int64_t)n_cu;       // one persistent work-group per compute unit (LDS-bound)
     const int grid = (int)(want < cap ? want : cap);
     if (grid <= 0) return mq_mark_empty(ev0, ev1, st);
-    if (swiglu)
-        MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma_pf<true, PF_MF>), dim3(grid), dim3(512), 0, st,
-                        (const uint8_t *)experts, expert_bytes, mat_off, rows, kblocks, units_hdr, units,
-                        perm, topk, (const mq_u32x4 *)xdig, xsum, xscale, out);
-    else
-        MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma_pf<false, PF_MF>), dim3(grid), dim3(512), 0, st,
-                        (const uint8_t *)experts, expert_bytes, mat_off, rows, kblocks, units_hdr, units,
-                        perm, topk, (const mq_u32x4 *)xdig, xsum, xscale, out);
+#define MQ_PF_LAUNCH(SW, NDV)                                                                           \
+    MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma_pf<SW, PF_MF, NDV>), dim3(grid), dim3(512), 0, st,               \
+                    (const uint8_t *)experts, expert_bytes, mat_off, rows, kblocks, units_hdr, units, perm, \
+                    topk, (const mq_u32x4 *)xdig, xsum, xscale, out, fmt.eslot)
+    if (swiglu) {
+        if (fmt.nd == 2) MQ_PF_LAUNCH(true, 2); else MQ_PF_LAUNCH(true, 1);
+    } else {
+        if (fmt.nd == 2) MQ_PF_LAUNCH(false, 2); else MQ_PF_LAUNCH(false, 1);
+    }
+#undef MQ_PF_LAUNCH
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

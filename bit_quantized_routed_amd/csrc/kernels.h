@@ -15,7 +15,9 @@ int mq_launch_topk(const float *logits, int nsplit, const float *bias, int T, in
                    int32_t *idx, float *gate, int32_t *trace_idx, float *trace_w, hipStream_t st);
 int mq_router_splits(int T, int H, int E);
 int mq_launch_router_mma(const uint16_t *x, const float *wr, int T, int H, int E, int nsplit,
-                         float *P, hipStream_t st);
+                         float *P, int tiles, hipStream_t st);
+// Split count of the router for a batch-invariant call: a function of H alone.
+int mq_router_splits_fixed(int H);
 int mq_launch_bucket(const int32_t *idx, int T, int K, int E, int unit_tokens, int32_t *counts,
                      int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *units_hdr,
                      int4 *units, int fill_units, int32_t *urow, int zrow, hipStream_t st);
@@ -56,10 +58,13 @@ int mq_launch_swiglu_partials(const float *P, int nsplit, int M, int Is, uint16_
                               hipStream_t st);
 int mq_launch_sum_partials(const float *P, int nsplit, int64_t MN, float *out, hipStream_t st);
 // Router (bf16 layer input) and the layer input's activation digits in one launch.
+// tiles: force the MFMA split-K tiles (no one-work-group-per-expert router for few
+// tokens), so that every batch size takes the same per-token summation order.
 int mq_launch_router_prep(const uint16_t *x, const float *wr, int T, int H, int E, int nsplit, float *P,
-                          void *xdig, uint32_t *xsum, float *xscale, hipStream_t st);
+                          void *xdig, uint32_t *xsum, float *xscale, int nd, int tiles, hipStream_t st);
+// nd: activation digits (2: 15-bit, 1: Q8)
 int mq_launch_prep_digits(const void *src, int src_bf16, int nrows, int len, int64_t src_ld,
-                          void *xdig, uint32_t *xsum, float *scale, hipStream_t st);
+                          void *xdig, uint32_t *xsum, float *scale, int nd, hipStream_t st);
 // Optional shared-expert rows of the same launch: SwiGLU of the dense split partials
 // g/u [nsplit][T][Is] into two bf16 planes hi/lo [T][Is].
 struct MqSharedSwiglu {
@@ -71,7 +76,7 @@ struct MqSharedSwiglu {
 };
 int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit, int64_t split_stride,
                                  int nrows, int len, int64_t src_ld, void *xdig, uint32_t *xsum,
-                                 float *scale, const MqSharedSwiglu *shared, hipStream_t st);
+                                 float *scale, const MqSharedSwiglu *shared, int nd, hipStream_t st);
 // Decode kernel: split count along the reduction (shared by the workspace sizing).
 // Gate/up splits are summed by the intermediate preparation, down splits by the
 // combine; a split is taken only while the launch stays within about 768 resident
@@ -133,15 +138,24 @@ struct MqDownPrep {
 // units: max_units records, those past the last unit with slot count 0; urow (gate/up):
 // the [max_units][16] row table of the bucketing; down reads the rows of its slots.
 // route (gate/up only, optional): route in the launch instead of reading units/urow.
-int mq_launch_q2_mma(int gu, const void *experts, int64_t expert_bytes, int64_t mat_off, int tiles,
-                     int kblocks, const int4 *units, int max_units, const int32_t *urow, int zrow,
-                     int trash_row, const void *xdig,
+// Format of one routed launch: activation digits (2: 15-bit, 1: Q8), weight block
+// dwords (21: 2-bit codec, 37: 4-bit sibling) and the optional expert -> slot table
+// of an expert cache (null: expert e at experts + e * expert_bytes).
+struct MqFormat {
+    int nd, bd;
+    const int32_t *eslot;
+};
+// split_units: the unit count the k-split policy is computed for (max_units, or a
+// fixed count when the split must not depend on the batch).
+int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t expert_bytes, int64_t mat_off,
+                     int tiles, int kblocks, const int4 *units, int max_units, int split_units,
+                     const int32_t *urow, int zrow, int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
                      int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route,
                      const MqDownPrep *prep, hipStream_t st, hipEvent_t ev0 = nullptr,
                      hipEvent_t ev1 = nullptr);
-int mq_launch_q2_mma_pf(int swiglu, const void *experts, int64_t expert_bytes, int64_t mat_off,
-                        int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
+int mq_launch_q2_mma_pf(int swiglu, const MqFormat &fmt, const void *experts, int64_t expert_bytes,
+                        int64_t mat_off, int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                         int max_units, const int32_t *perm, int topk, const void *xdig,
                         const uint32_t *xsum, const float *xscale, float *out, int n_cu,
                         hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);

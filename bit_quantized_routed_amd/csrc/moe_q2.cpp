@@ -30,6 +30,12 @@ extern "C" const char *moe_q2_status_string(int status) {
 
 extern "C" size_t moe_q2_block_bytes(void) { return MQ_BLOCK_BYTES; }
 
+extern "C" size_t moe_q2_q4_block_bytes(void) { return 4 * MQ_BD4; }
+
+// Block bytes of the gate/up and of the down matrices of a shape's routed experts.
+static size_t gu_block_bytes(const moe_q2_shape *s) { return s->flags & MOE_Q2_GU_Q4 ? 4 * MQ_BD4 : 4 * MQ_BD2; }
+static size_t down_block_bytes(const moe_q2_shape *s) { return s->flags & MOE_Q2_DOWN_Q4 ? 4 * MQ_BD4 : 4 * MQ_BD2; }
+
 static bool shape_ok(const moe_q2_shape *s) {
     if (!s) return false;
     if (s->hidden <= 0 || s->hidden % 256 || s->hidden > 16384) return false;
@@ -41,7 +47,8 @@ static bool shape_ok(const moe_q2_shape *s) {
 
 extern "C" size_t moe_q2_expert_bytes(const moe_q2_shape *s) {
     if (!shape_ok(s)) return 0;
-    return (size_t)3 * s->hidden * s->inter / MQ_QK * MQ_BLOCK_BYTES;
+    const size_t blocks = (size_t)s->hidden * s->inter / MQ_QK;
+    return 2 * blocks * gu_block_bytes(s) + blocks * down_block_bytes(s);
 }
 
 namespace {
@@ -50,6 +57,9 @@ struct Workspace {
     size_t logits, idx, gate, counts, offsets, perm, inv, units_hdr, units, urow = 0, bchunk = 0, xbf, xq, xg, xs, h,
         hq, hg, hs, y, xlo, sp, shi, slo, ysh;
     int max_units = 0, split_gu = 1, split_d = 1, rsplit = 1;
+    int nd = 2;                 // activation digits: 2 (15-bit) or 1 (Q8)
+    bool bi = false;            // batch-invariant: splits and router fixed by the shape
+    int split_units = 0;        // unit count the decode k-split policy is computed for
     // routed path and, for the matrix-core decode kernels, their reduction splits
     bool prefill = false, valu = false;
     int dec_units = 0, dsplit_gu = 1, dsplit_d = 1;
@@ -77,16 +87,24 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     size_t c = 0;
     // work units: at most ceil(S / tch) + min(E, S) for either kernel's unit size
     w.max_units = units_bound(S, E, FD_TCH);
-    w.prefill = (s->flags & MOE_Q2_PATH_PREFILL) ||
-                (!(s->flags & MOE_Q2_PATH_DECODE) && T >= MOE_Q2_PREFILL_MIN_TOKENS);
+    w.bi = (s->flags & MOE_Q2_BATCH_INVARIANT) != 0;
+    w.nd = (s->flags & MOE_Q2_ACT_Q8) ? 1 : 2;
+    const bool q4 = (s->flags & (MOE_Q2_GU_Q4 | MOE_Q2_DOWN_Q4)) != 0;
+    // the prefill kernels take the 2-bit codec only; a batch-invariant call keeps one
+    // set of kernels for every batch size
+    w.prefill = !w.bi && !q4 &&
+                ((s->flags & MOE_Q2_PATH_PREFILL) ||
+                 (!(s->flags & MOE_Q2_PATH_DECODE) && T >= MOE_Q2_PREFILL_MIN_TOKENS));
     w.valu = !w.prefill && (s->flags & MOE_Q2_DECODE_VALU) != 0;
     int cps = 0;
     if (!w.prefill && !w.valu) {
         w.dec_units = units_bound(S, E, MMA_TCH);
-        mq_dec_split(w.dec_units, (int)(I / 32), (int)(H / MQ_QK), MQ_DEC_SPLIT_GU, &w.dsplit_gu, &cps);
-        mq_dec_split(w.dec_units, (int)(H / 64), (int)(I / MQ_QK), MQ_DEC_SPLIT_D, &w.dsplit_d, &cps);
+        // batch-invariant: the splits of a one-token batch, whatever the batch
+        w.split_units = w.bi ? units_bound((size_t)K, E, MMA_TCH) : w.dec_units;
+        mq_dec_split(w.split_units, (int)(I / 32), (int)(H / MQ_QK), MQ_DEC_SPLIT_GU, &w.dsplit_gu, &cps);
+        mq_dec_split(w.split_units, (int)(H / 64), (int)(I / MQ_QK), MQ_DEC_SPLIT_D, &w.dsplit_d, &cps);
     }
-    w.rsplit = mq_router_splits(T, (int)H, (int)E);
+    w.rsplit = w.bi ? mq_router_splits_fixed((int)H) : mq_router_splits(T, (int)H, (int)E);
     w.logits = take(c, (size_t)w.rsplit * T * E * 4);
     w.idx = take(c, S * 4);
     w.gate = take(c, S * 4);
@@ -102,13 +120,13 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     // activation buffers hold one extra row: the all-zero row that padding tokens
     // of the decode kernels read; h and y one extra row that absorbs their writes
     w.xbf = take(c, (size_t)T * H * 2);
-    w.xq = take(c, (size_t)(T + 1) * H * 2);    // fp16 pairs, or the two int8 digits
+    w.xq = take(c, (size_t)(T + 1) * H * w.nd);  // fp16 pairs, or the int8 digits
     w.xg = take(c, (size_t)(T + 1) * (H / 16) * 8);
     w.xs = take(c, (size_t)(T + 1) * 4);
     // h: the intermediate (S + 1 rows), or for the matrix-core decode kernels the
     // gate and up split partial sums; y: the routed outputs, or their split partials
     w.h = take(c, (w.prefill || w.valu ? 1 : 2 * (size_t)w.dsplit_gu) * (S + 1) * I * 4);
-    w.hq = take(c, (S + 1) * I * 2);
+    w.hq = take(c, (S + 1) * I * w.nd);
     w.hg = take(c, (S + 1) * (I / 16) * 8);
     w.hs = take(c, (S + 1) * 4);
     w.y = take(c, (size_t)w.dsplit_d * (S + 1) * H * 4);
@@ -157,7 +175,8 @@ int device_cus() {
 }  // namespace
 
 static const int KNOWN_FLAGS = MOE_Q2_PATH_DECODE | MOE_Q2_PATH_PREFILL | MOE_Q2_PRE_RMSNORM |
-                               MOE_Q2_RESIDUAL_ADD | MOE_Q2_DECODE_VALU | MOE_Q2_SERIAL;
+                               MOE_Q2_RESIDUAL_ADD | MOE_Q2_DECODE_VALU | MOE_Q2_SERIAL |
+                               MOE_Q2_BATCH_INVARIANT | MOE_Q2_ACT_Q8 | MOE_Q2_GU_Q4 | MOE_Q2_DOWN_Q4;
 
 namespace {
 // Joins the concurrent branch back into the calling stream when a call returns
@@ -232,6 +251,15 @@ static int check_common(const moe_q2_shape *s, int32_t n_tokens, int32_t topk) {
         return MOE_Q2_EINVAL;
     if ((s->flags & MOE_Q2_PRE_RMSNORM) && !(s->rms_eps >= 0.0f && s->rms_eps < 1e30f))
         return MOE_Q2_EINVAL;
+    // combinations of the options
+    const int f = s->flags;
+    const bool bi = f & MOE_Q2_BATCH_INVARIANT, q8 = f & MOE_Q2_ACT_Q8;
+    const bool q4 = f & (MOE_Q2_GU_Q4 | MOE_Q2_DOWN_Q4), valu = f & MOE_Q2_DECODE_VALU;
+    if (bi && (f & MOE_Q2_PATH_PREFILL)) return MOE_Q2_EINVAL;     // one kernel set for every batch
+    if (valu && (bi || q8 || q4)) return MOE_Q2_EUNSUPPORTED;       // the vector-ALU kernel: 2-bit, 15-bit
+    if (q4 && (f & MOE_Q2_PATH_PREFILL)) return MOE_Q2_EUNSUPPORTED;  // prefill kernels: 2-bit only
+    const bool in_bf16 = (f & MOE_Q2_PRE_RMSNORM) || s->act_dtype == MOE_Q2_BF16;
+    if (bi && s->shared_inter > 0 && !in_bf16) return MOE_Q2_EUNSUPPORTED;   // shared expert on split GEMMs
     return MOE_Q2_OK;
 }
 
@@ -288,10 +316,12 @@ static int check_forward(const void *x, const float *router_w, const void *exper
 
 // The layer on a caller's workspace.  serial: keep every launch on `stream` (no
 // internal stream), whatever the flags say.
+// eslot: nullable expert -> slot table of an expert cache (experts_q2 is then the
+// cache's slot arena).
 static int forward_impl(const void *x, const float *router_w, const void *experts_q2, const uint16_t *shared_w,
                         int32_t topk, float *out, const moe_q2_shape *s, int32_t n_tokens,
                         const float *router_b, void *workspace, size_t workspace_bytes,
-                        const moe_q2_trace *trace, void *stream, bool serial) {
+                        const moe_q2_trace *trace, void *stream, bool serial, const int32_t *eslot) {
     int rc = check_forward(x, router_w, experts_q2, shared_w, topk, out, s, n_tokens);
     if (rc) return rc;
     const bool rms = (s->flags & MOE_Q2_PRE_RMSNORM) != 0;
@@ -381,7 +411,7 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
     if (valu)
         rc = mq_launch_prep(xin, xin_bf16, T, H, H, xq, xg, xs, sst);
     else if (!prep_in_router)
-        rc = mq_launch_prep_digits(xin, xin_bf16, T, H, H, xq, (uint32_t *)xg, xs, sst);
+        rc = mq_launch_prep_digits(xin, xin_bf16, T, H, H, xq, (uint32_t *)xg, xs, w.nd, sst);
     if (rc) return rc;
     if ((rc = mark_on(MOE_Q2_PH_PREP_X, 1, sst))) return rc;
     if (side) {
@@ -430,11 +460,11 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
     if (xin_bf16 && prep_in_router) {
         nsplit = w.rsplit;
         MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router_prep((const uint16_t *)xin, router_w, T, H, E, nsplit,
-                                                         logits, xq, (uint32_t *)xg, xs, st));
+                                                         logits, xq, (uint32_t *)xg, xs, w.nd, w.bi ? 1 : 0, st));
     } else if (xin_bf16) {
         nsplit = w.rsplit;
         MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router_mma((const uint16_t *)xin, router_w, T, H, E, nsplit,
-                                                        logits, st));
+                                                        logits, w.bi ? 1 : 0, st));
     } else {
         MQ_PHASE(MOE_Q2_PH_ROUTER, mq_launch_router(xin, 0, router_w, nullptr, T, H, E, logits, st));
     }
@@ -476,7 +506,9 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
     // routed experts
     const int ncu = device_cus();
     const int64_t ebytes = (int64_t)moe_q2_expert_bytes(s);
-    const int64_t mat_gu = (int64_t)I * (H / MQ_QK) * MQ_BLOCK_BYTES;
+    const int64_t mat_gu = (int64_t)I * (H / MQ_QK) * (int64_t)gu_block_bytes(s);   // bytes of gate (or up)
+    const MqFormat fgu = {w.nd, (s->flags & MOE_Q2_GU_Q4) ? MQ_BD4 : MQ_BD2, eslot};
+    const MqFormat fdn = {w.nd, (s->flags & MOE_Q2_DOWN_Q4) ? MQ_BD4 : MQ_BD2, eslot};
     float *h = (float *)(ws + w.h);
     float *y = (float *)(ws + w.y);
     uint32_t *hq = (uint32_t *)(ws + w.hq);
@@ -489,12 +521,12 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
         MQ_PHASE(MOE_Q2_PH_DOWN, mq_launch_q2_dec(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr,
                                                   units, w.max_units, perm, K, hq, hg, hsc, y, ncu, st));
     } else if (prefill) {
-        if ((rc = mq_launch_q2_mma_pf(1, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr, units, w.max_units,
+        if ((rc = mq_launch_q2_mma_pf(1, fgu, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr, units, w.max_units,
                                       perm, K, xq, (const uint32_t *)xg, xs, h, ncu, st,
                                       evk(MOE_Q2_PH_GATE_UP, 0), evk(MOE_Q2_PH_GATE_UP, 1))))
             return rc;
-        MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_digits(h, 0, T * K, I, I, hq, (uint32_t *)hg, hsc, st));
-        if ((rc = mq_launch_q2_mma_pf(0, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr, units,
+        MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_digits(h, 0, T * K, I, I, hq, (uint32_t *)hg, hsc, w.nd, st));
+        if ((rc = mq_launch_q2_mma_pf(0, fdn, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr, units,
                                       w.max_units, perm, K, hq, (const uint32_t *)hg, hsc, y, ncu, st,
                                       evk(MOE_Q2_PH_DOWN, 0), evk(MOE_Q2_PH_DOWN, 1))))
             return rc;
@@ -520,7 +552,8 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
             dd = MqDenseSpec{shared_w + (size_t)2 * Is * H, shi, slo, ysh, ysh, T, H, Is, H, H, w.fsplit_d,
                              ysh_stride};
         }
-        if ((rc = mq_launch_q2_mma(1, experts_q2, ebytes, 0, I / 32, H / MQ_QK, units, w.dec_units, urow, T, S,
+        if ((rc = mq_launch_q2_mma(1, fgu, experts_q2, ebytes, 0, I / 32, H / MQ_QK, units, w.dec_units,
+                                   w.split_units, urow, T, S,
                                    xq, (const uint32_t *)xg, xs, gp, up, I, gstride, w.fused ? &dgu : nullptr,
                                    route_in_gu ? &rt : nullptr, nullptr, st, evk(MOE_Q2_PH_GATE_UP, 0),
                                    evk(MOE_Q2_PH_GATE_UP, 1))))
@@ -534,10 +567,10 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
         } else {
             MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_swiglu_digits(gp, up, w.dsplit_gu, gstride, S, I, I, hq,
                                                                     (uint32_t *)hg, hsc, w.fused ? &shs : nullptr,
-                                                                    st));
+                                                                    w.nd, st));
         }
-        if ((rc = mq_launch_q2_mma(0, experts_q2, ebytes, 2 * mat_gu, H / 64, I / MQ_QK, units, w.dec_units,
-                                   nullptr, S, S, hq, (const uint32_t *)hg, hsc, y, nullptr, H, ystride,
+        if ((rc = mq_launch_q2_mma(0, fdn, experts_q2, ebytes, 2 * mat_gu, H / 64, I / MQ_QK, units,
+                                   w.dec_units, w.split_units, nullptr, S, S, hq, (const uint32_t *)hg, hsc, y, nullptr, H, ystride,
                                    w.fused ? &dd : nullptr, nullptr, prep_in_down ? &dp : nullptr, st,
                                    evk(MOE_Q2_PH_DOWN, 0), evk(MOE_Q2_PH_DOWN, 1))))
             return rc;
@@ -564,7 +597,7 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
                               void *workspace, size_t workspace_bytes, const moe_q2_trace *trace,
                               void *stream) {
     return forward_impl(x, router_w, experts_q2, shared_w, topk, out, s, n_tokens, router_b, workspace,
-                        workspace_bytes, trace, stream, false);
+                        workspace_bytes, trace, stream, false, nullptr);
 }
 
 // ------------------------------------------------------------------ no-allocation entry point
@@ -615,5 +648,5 @@ extern "C" int moe_q2_forward_noalloc(const void *x, const float *router_w, cons
     void *ws = nullptr;
     if ((rc = scratch_address(&ws))) return rc;
     return forward_impl(x, router_w, experts_q2, shared_w, topk, out, s, n_tokens, router_b, ws,
-                        (size_t)MOE_Q2_NOALLOC_MAX_BYTES, trace, stream, true);
+                        (size_t)MOE_Q2_NOALLOC_MAX_BYTES, trace, stream, true, nullptr);
 }

@@ -4,8 +4,13 @@
 #include "common.h"
 
 
-// Per row: s = 2^(e - 14) with max|x| in (2^(e-1), 2^e] (1 for an all-zero row);
-// a = rint(x / s) (|a| <= 2^14), hi = floor((a + 128) / 256), lo = a - 256 hi.
+// Two activation formats (ND = digits per element):
+//  ND = 2 (15-bit, the default): s = 2^(e - 14) with max|x| in [2^(e-1), 2^e) (1 for
+//   an all-zero row); a = rint(x / s) (|a| <= 2^14), hi = floor((a + 128) / 256),
+//   lo = a - 256 hi: two int8 digits, a = 256 hi + lo exactly.
+//  ND = 1 (Q8): s = 2^(e - 7); a = clamp(rint(x / s), -127, 127), one int8 digit.
+// Both scales are powers of two, so x / s is exact and the rounding is a function of
+// x alone (the oracle's Q8 mode takes the same decision).
 // xdig[row][group][digit] = 16 bytes, byte b of dword s = digit of element 4b + s;
 // xsum[row][block][quad][plane][4] = bf16 planes of A_j = sum of the group's a for
 // the groups j = 4 quad .. 4 quad + 3 (hi plane bf16(A_j), lo plane bf16(A_j - hi)):
@@ -29,7 +34,43 @@ struct MqSharedRows {
     uint16_t *hi, *lo;
 };
 
-template <int SRC>
+// Exponent offset of the row scale: 2^(e - MQ_ACT_BITS(ND)).
+#define MQ_ACT_BITS(ND) ((ND) == 2 ? 14 : 7)
+
+// The digits of 16 quantised elements a[0..15] of one group: ND 16-byte vectors.
+template <int ND>
+__device__ __forceinline__ void mq_group_digits(const int (&a)[16], mq_u32x4 *out) {
+    mq_u32x4 hi, lo;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        uint32_t h = 0, l = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int x = a[4 * b + s4];
+            const int dh = ND == 2 ? (x + 128) >> 8 : 0;
+            const int dl = x - (dh << 8);
+            h |= ((uint32_t)(dh & 0xFF)) << (8 * b);
+            l |= ((uint32_t)(dl & 0xFF)) << (8 * b);
+        }
+        hi[s4] = h;
+        lo[s4] = l;
+    }
+    if (ND == 2) {
+        out[0] = hi;
+        out[1] = lo;
+    } else {
+        out[0] = lo;
+    }
+}
+
+// a = rint(v * inv_s), clamped to the int8 range for the one-digit format.
+template <int ND>
+__device__ __forceinline__ int mq_quant_act(float v, float inv_s) {
+    const int x = (int)rintf(v * inv_s);
+    return ND == 2 ? x : min(127, max(-127, x));
+}
+
+template <int SRC, int ND = 2>
 __device__ __forceinline__ void mq_prep_digits_wg(const void *__restrict__ src, const void *__restrict__ src2,
                                                   int nsplit, int64_t split_stride, int nrows, int len,
                                                   int64_t src_ld, mq_u32x4 *__restrict__ xdig,
@@ -137,9 +178,9 @@ __device__ __forceinline__ void mq_prep_digits_wg(const void *__restrict__ src, 
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     int ex = 0;
     if (amax > 0.0f) frexpf(amax, &ex);
-    const float inv_s = amax > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
-    if (tid == 0) scale[row] = amax > 0.0f ? ldexpf(1.0f, ex - 14) : 1.0f;
-    mq_u32x4 *xr = xdig + (int64_t)row * G * 2;
+    const float inv_s = amax > 0.0f ? ldexpf(1.0f, MQ_ACT_BITS(ND) - ex) : 1.0f;
+    if (tid == 0) scale[row] = amax > 0.0f ? ldexpf(1.0f, ex - MQ_ACT_BITS(ND)) : 1.0f;
+    mq_u32x4 *xr = xdig + (int64_t)row * G * ND;
     uint16_t *sr = (uint16_t *)(xsum + (int64_t)row * G);       // G/16 blocks x 32 bf16
 #pragma unroll
     for (int n = 0; n < PD_NG; ++n) {
@@ -149,26 +190,10 @@ __device__ __forceinline__ void mq_prep_digits_wg(const void *__restrict__ src, 
         int sum = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            a[i] = (int)rintf(v[n][i] * inv_s);
+            a[i] = mq_quant_act<ND>(v[n][i], inv_s);
             sum += a[i];
         }
-        mq_u32x4 hi, lo;
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            uint32_t h = 0, l = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int x = a[4 * b + s4];
-                const int dh = (x + 128) >> 8;
-                const int dl = x - (dh << 8);
-                h |= ((uint32_t)(dh & 0xFF)) << (8 * b);
-                l |= ((uint32_t)(dl & 0xFF)) << (8 * b);
-            }
-            hi[s4] = h;
-            lo[s4] = l;
-        }
-        xr[2 * g] = hi;
-        xr[2 * g + 1] = lo;
+        mq_group_digits<ND>(a, xr + ND * g);
         const float fs = (float)sum;                           // exact: |sum| <= 2^18
         const uint16_t bh = mq_f32_to_bf16(fs);
         const uint16_t bl = mq_f32_to_bf16(fs - mq_bf16_to_f32(bh));

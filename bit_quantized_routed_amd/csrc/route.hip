@@ -206,7 +206,7 @@ __global__ void __launch_bounds__(256) k_router_mma(const uint16_t *__restrict__
 // One launch for the two consumers of the bf16 layer input: the router
 // work-groups (gx * gy * gz of them, flattened) and then one work-group per row of
 // activation digits (T rows + the zero row).
-template <int MF>
+template <int MF, int ND>
 __global__ void __launch_bounds__(256) k_router_prep(const uint16_t *__restrict__ x,
                                                      const float *__restrict__ wr, int T, int H, int E,
                                                      int k_per_split, float *__restrict__ P, int gx, int gy,
@@ -220,30 +220,34 @@ __global__ void __launch_bounds__(256) k_router_prep(const uint16_t *__restrict_
         else
             mq_router_wg<MF>(x, wr, T, H, E, k_per_split, P, b % gx, (b / gx) % gy, b / (gx * gy));
     } else {
-        mq_prep_digits_wg<1>(x, nullptr, 1, 0, T, H, H, xdig, xsum, xscale, MqSharedRows{}, b - nr);
+        mq_prep_digits_wg<1, ND>(x, nullptr, 1, 0, T, H, H, xdig, xsum, xscale, MqSharedRows{}, b - nr);
     }
 }
 
 int mq_launch_router_prep(const uint16_t *x, const float *wr, int T, int H, int E, int nsplit, float *P,
-                          void *xdig, uint32_t *xsum, float *xscale, hipStream_t st) {
+                          void *xdig, uint32_t *xsum, float *xscale, int nd, int tiles, hipStream_t st) {
     if (H / 16 > 256 * PD_NG) return MOE_Q2_EUNSUPPORTED;
     int kps = (H + nsplit - 1) / nsplit;
     kps = (kps + 31) / 32 * 32;
-    const bool small = T <= RT_SMALL_T;
+    const bool small = T <= RT_SMALL_T && !tiles;
     if (small && nsplit != 1) return MOE_Q2_EINVAL;
     const int gx = small ? E : (E + 63) / 64, gz = nsplit;
     const int gy = T <= 16 ? 1 : (T + 63) / 64;
     const int64_t grid = (int64_t)gx * gy * gz + T + 1;
     if (grid > 0x7fffffff) return MOE_Q2_EUNSUPPORTED;
-    if (small)
-        hipLaunchKernelGGL(k_router_prep<0>, dim3((unsigned)grid), dim3(256), 0, st, x, wr, T, H, E, kps, P, gx,
-                           gy, gz, (mq_u32x4 *)xdig, xsum, xscale);
-    else if (T <= 16)
-        hipLaunchKernelGGL(k_router_prep<1>, dim3((unsigned)grid), dim3(256), 0, st, x, wr, T, H, E, kps, P, gx,
-                           gy, gz, (mq_u32x4 *)xdig, xsum, xscale);
-    else
-        hipLaunchKernelGGL(k_router_prep<4>, dim3((unsigned)grid), dim3(256), 0, st, x, wr, T, H, E, kps, P, gx,
-                           gy, gz, (mq_u32x4 *)xdig, xsum, xscale);
+#define MQ_RP_LAUNCH(MFV, NDV)                                                                              \
+    hipLaunchKernelGGL((k_router_prep<MFV, NDV>), dim3((unsigned)grid), dim3(256), 0, st, x, wr, T, H, E, kps, \
+                       P, gx, gy, gz, (mq_u32x4 *)xdig, xsum, xscale)
+    const int mf = small ? 0 : (T <= 16 ? 1 : 4);
+    switch (mf * 2 + (nd == 2 ? 1 : 0)) {
+    case 0: MQ_RP_LAUNCH(0, 1); break;
+    case 1: MQ_RP_LAUNCH(0, 2); break;
+    case 2: MQ_RP_LAUNCH(1, 1); break;
+    case 3: MQ_RP_LAUNCH(1, 2); break;
+    case 8: MQ_RP_LAUNCH(4, 1); break;
+    default: MQ_RP_LAUNCH(4, 2); break;
+    }
+#undef MQ_RP_LAUNCH
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
@@ -257,11 +261,16 @@ int mq_router_splits(int T, int H, int E) {
     return s < 1 ? 1 : s;
 }
 
+int mq_router_splits_fixed(int H) {
+    const int s = H / 448;               // 448-wide k ranges: 16 splits at H = 7168
+    return s < 1 ? 1 : (s > 16 ? 16 : s);
+}
+
 int mq_launch_router_mma(const uint16_t *x, const float *wr, int T, int H, int E, int nsplit,
-                         float *P, hipStream_t st) {
+                         float *P, int tiles, hipStream_t st) {
     int kps = (H + nsplit - 1) / nsplit;
     kps = (kps + 31) / 32 * 32;
-    if (T <= RT_SMALL_T) {
+    if (T <= RT_SMALL_T && !tiles) {
         if (nsplit != 1) return MOE_Q2_EINVAL;
         hipLaunchKernelGGL(k_router_mma<0>, dim3(E), dim3(256), 0, st, x, wr, T, H, E, kps, P);
     } else if (T <= 16)

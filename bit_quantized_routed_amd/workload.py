@@ -11,8 +11,8 @@ import torch
 from synth import workloads as W
 from synth.gen import normal_scale
 
-from . import (BF16, F32, PRE_RMSNORM, make_shape, quantize, synth_normal, workspace_size,
-               pack_expert)
+from . import (BF16, F32, GU_Q4, DOWN_Q4, PRE_RMSNORM, make_shape, quantize, quantize_q4, synth_normal,
+               workspace_size, pack_expert)
 
 
 def _normal(wl, stream_id, n, sigma, dtype, out=None, start=0):
@@ -40,27 +40,38 @@ class DeviceLayer:
             for m in range(3):
                 _normal(wl, W.stream_id(layer, W.TENSOR_SHARED + m), Is * H, wl.shared_sigma, BF16,
                         out=self.shared_w[m * Is * H:(m + 1) * Is * H])
-        ebytes = wl.expert_bytes
+        gu4, dn4 = wl.q4_at(layer)
+        self.codec_flags = (GU_Q4 if gu4 else 0) | (DOWN_Q4 if dn4 else 0)
+        ebytes = wl.expert_bytes_at(layer)
+        self.expert_bytes = ebytes
         self.experts = experts_out if experts_out is not None else \
             torch.empty(E * ebytes, dtype=torch.uint8, device="cuda")
         if tmp is None:
             tmp = torch.empty(H * I, dtype=torch.float32, device="cuda")
-        mat_bytes = ebytes // 3
+        nb = H * I // 256
+        mb = [nb * (148 if gu4 else 84)] * 2 + [nb * (148 if dn4 else 84)]      # bytes per matrix
+        off = [0, mb[0], mb[0] + mb[1], ebytes]
         rm = torch.empty(ebytes, dtype=torch.uint8, device="cuda")     # row-major staging
+        shp = self.shape()
         for e in range(E):
             for m in range(3):
                 _normal(wl, W.expert_stream(layer, e, m), H * I, wl.expert_sigma, F32, out=tmp)
                 rows, k = (I, H) if m < 2 else (H, I)
-                quantize(tmp, rows, k, rm[m * mat_bytes:(m + 1) * mat_bytes])
-            pack_expert(rm[:mat_bytes], rm[mat_bytes:2 * mat_bytes], rm[2 * mat_bytes:], H, I,
+                q4 = gu4 if m < 2 else dn4
+                (quantize_q4 if q4 else quantize)(tmp, rows, k, rm[off[m]:off[m + 1]])
+            pack_expert(rm[off[0]:off[1]], rm[off[1]:off[2]], rm[off[2]:off[3]], shp,
                         self.experts[e * ebytes:(e + 1) * ebytes])
         del rm
 
     def shape(self, flags=0):
+        """The layer's shape descriptor: its activation type, RMSNorm for a residual
+        stack, its weight formats, plus `flags`."""
         wl = self.wl
         act = BF16 if wl.act == "bf16" else F32
         if wl.rmsnorm:
             flags |= PRE_RMSNORM
+        gu4, dn4 = wl.q4_at(self.layer)
+        flags |= (GU_Q4 if gu4 else 0) | (DOWN_Q4 if dn4 else 0)
         return make_shape(wl.hidden, wl.inter, wl.n_experts, wl.shared_inter, act, flags,
                           wl.rms_eps)
 

@@ -22,6 +22,19 @@
  *   w_i = d * sc_j * q_i - dmin * m_j
  * Blocks run along each matrix's reduction dimension.
  *
+ * Q4 sibling block (148 bytes, 256 weights, 4.625 bits/weight; this library's own
+ * higher-precision member of the family, for the per-layer and per-matrix format mixes
+ * of the ds4 README mirror, section "Model Weights": q2 with the last expert layers at
+ * q4; routed gate/up and down at different precisions):
+ *   bytes   0..15  group j: bits 0..2 scale sc_j (0..7; bit 3 reserved, ignored), high nibble min m_j
+ *   bytes  16..143 4-bit codes, group j in bytes 16 + 8j .. 16 + 8j + 7: element 4b + s of
+ *                  the group (b, s in 0..3) in byte 16 + 8j + 4 (s / 2) + b, low nibble for
+ *                  even s, high nibble for odd s
+ *   bytes 144..145 d (fp16)       bytes 146..147 dmin (fp16)
+ *   w_i = d * sc_j * q_i - dmin * m_j,  q_i in 0..15
+ * A routed expert's gate/up and down matrices each take the format its shape's flags
+ * give (MOE_Q2_GU_Q4, MOE_Q2_DOWN_Q4), in the same tiled layout with 148-byte blocks.
+ *
  * Routed expert layout (row tiles, so that a run of block columns of 64 rows is
  * one contiguous span and streams from HBM with plain 16-byte loads):
  *   gate/up: I/32 tiles; tile t = block columns b = 0..H/256-1 of 64 rows, slots
@@ -83,7 +96,27 @@ enum {
     MOE_Q2_RESIDUAL_ADD = 8,   /* out += layer(...) instead of out = layer(...) */
     MOE_Q2_DECODE_VALU = 16,   /* decode path: routed experts on the vector-ALU dot-product
                                   kernel instead of the integer matrix-core kernel */
-    MOE_Q2_SERIAL = 32         /* run every launch on `stream` (no internal stream) */
+    MOE_Q2_SERIAL = 32,        /* run every launch on `stream` (no internal stream) */
+    MOE_Q2_BATCH_INVARIANT = 64,
+                               /* every token's outputs, routing and gates are bit-identical
+                                  whatever the batch it is in (1 .. MOE_Q2_MAX_TOKENS tokens):
+                                  one set of kernels and one summation order per token for every
+                                  batch size (decode kernels, router split and reduction splits
+                                  fixed by the shape; the ds4 README mirror, section "DSpark
+                                  Speculative Decoding", notes that batched verification groups
+                                  floating point differently from one-token decode).  Needs a
+                                  bf16 (or PRE_RMSNORM) layer input when there is a shared
+                                  expert; not with PATH_PREFILL (EINVAL) or DECODE_VALU */
+    MOE_Q2_ACT_Q8 = 128,       /* Q8 activations for the routed experts (ds4 README mirror,
+                                  section "Model Weights": decode uses Q8 activations): per row
+                                  a = clamp(rint(v / s), -127, 127), s = 2^(e - 7) with max|v| in
+                                  [2^(e-1), 2^e), for the layer input and the SwiGLU output; one
+                                  int8 digit instead of the default two (15-bit values).  Router
+                                  and shared expert unchanged.  Not with DECODE_VALU */
+    MOE_Q2_GU_Q4 = 256,        /* routed gate/up matrices in the 4-bit sibling format (below) */
+    MOE_Q2_DOWN_Q4 = 512       /* routed down matrix in the 4-bit sibling format.  Either Q4
+                                  flag runs the decode kernels at every batch size (PATH_PREFILL
+                                  and DECODE_VALU: EUNSUPPORTED) */
 };
 #define MOE_Q2_PREFILL_MIN_TOKENS 256
 /* Token envelope of one call.  n_tokens <= MOE_Q2_MAX_TOKENS, and the activation
@@ -139,7 +172,11 @@ enum {
 /* Bytes of one 84-byte super-block. */
 size_t moe_q2_block_bytes(void);
 
-/* Bytes of one routed expert: 3 * H * I / 256 blocks (gate, up, down). */
+/* Bytes of one Q4 sibling block (148). */
+size_t moe_q2_q4_block_bytes(void);
+
+/* Bytes of one routed expert: gate and up (2 * H * I / 256 blocks) and down (H * I / 256
+ * blocks), each in the format the shape's flags give; 0 for an invalid shape. */
 size_t moe_q2_expert_bytes(const moe_q2_shape *s);
 
 /* Device workspace needed by moe_q2_forward for n_tokens tokens and top-K topk.
@@ -216,11 +253,19 @@ int moe_q2_forward_noalloc(const void *x, const float *router_w, const void *exp
  * written with d = dmin = +inf. */
 int moe_q2_quantize(const float *w, int64_t rows, int64_t k, void *blocks_out, void *stream);
 
-/* Pack one routed expert from row-major Q2 matrices (device): gate [I rows x H/256
- * blocks], up [I x H/256], down [H x I/256] -> out (device, moe_q2_expert_bytes bytes)
- * in the tiled layout above.  Setup helper, not part of the layer. */
-int moe_q2_pack_expert(const void *gate, const void *up, const void *down, int32_t hidden,
-                       int32_t inter, void *out, void *stream);
+/* moe_q2_quantize for the Q4 sibling format: rows * k / 256 148-byte blocks, by the
+ * same coverage rule with 15 code steps and 3-bit group scales (all steps IEEE fp32):
+ *   dmin = least fp16 >= max_j(0-lo_j)/15; m_j = ceil((0-lo_j)/dmin); o_j = dmin*m_j;
+ *   s_j = (hi_j+o_j)/15; d = least fp16 >= max_j s_j/7; sc_j = ceil(s_j/d);
+ *   q = clamp(rint((x+o_j)/(d*sc_j)),0,15).  Setup helper, not part of the layer. */
+int moe_q2_quantize_q4(const float *w, int64_t rows, int64_t k, void *blocks_out, void *stream);
+
+/* Pack one routed expert from row-major block matrices (device): gate [I rows x H/256
+ * blocks], up [I x H/256], down [H x I/256], each in the format s->flags give
+ * (MOE_Q2_GU_Q4 / MOE_Q2_DOWN_Q4) -> out (device, moe_q2_expert_bytes(s) bytes) in the
+ * tiled layout above; 4-byte aligned buffers.  Setup helper, not part of the layer. */
+int moe_q2_pack_expert(const void *gate, const void *up, const void *down, const moe_q2_shape *s,
+                       void *out, void *stream);
 
 /* Seeded synthetic inputs for tests and benchmarks (not part of the layer):
  * value j = float(S(start + j) - 262140) * scale, where S(i) is the sum of the eight

@@ -7,7 +7,9 @@ It shares no code with the HIP library (bit_quantized_routed_amd); the only
 code both sides use is the seeded input generator package `synth`.
 
     q2.decode_blocks / encode_blocks   the Q2 super-block codec
+    q4.decode_blocks / encode_blocks   its 4-bit sibling
+    moe.q8_rows                        Q8 activations of the routed experts
     moe.route / bucket / ffn / layer   the MoE layer
     moe.rmsnorm_bf16 / stack           the residual stack with RMSNorm
 """
-from . import q2, moe  # noqa: F401
+from . import q2, q4, moe  # noqa: F401

@@ -19,12 +19,18 @@ and, for a stack of layers with a residual stream h (fp32) and RMSNorm:
     x_l     = bf16_rne(h_l / sqrt(mean(h_l^2) + eps))
     h_{l+1} = h_l + layer_l(x_l)
 
-Expert weights come from their Q2 bytes through q2.decode_* (fp32 values);
+Expert weights come from their block bytes through q2.decode_* (the 2-bit
+format) or q4.decode_* (its 4-bit sibling), chosen per matrix by the block size;
 every product and sum after that is fp64.
+
+Q8 activation mode (act="q8"; ds4 README mirror, section "Model Weights": decode
+uses Q8 activations): the routed experts' two inputs -- the layer input x and the
+SwiGLU output h -- are replaced by their per-row Q8 values before the products,
+see q8_rows.  Router and shared expert stay at full precision.
 """
 import numpy as np
 
-from . import q2
+from . import q2, q4
 
 
 def _f64(a):
@@ -79,23 +85,50 @@ def silu(a):
         return a / (1.0 + np.exp(-a))
 
 
-def ffn(x, w_gate, w_up, w_down):
-    """SwiGLU FFN on token rows x [n, H]: (silu(x Wg^T) * (x Wu^T)) Wd^T, fp64."""
+def q8_rows(v):
+    """Q8 activations of rows v [n, L] (values as fp64): per row, with max|v| in
+    [2^(e-1), 2^e), s = 2^(e - 7) and a = clamp(rint_even(v / s), -127, 127); returns
+    a * s (exact in fp64).  The scale is a power of two, so v / s is exact and the
+    rounding is a function of v alone; an all-zero row stays zero."""
+    v = _f64(v)
+    amax = np.abs(v).max(axis=1, keepdims=True)
+    _, e = np.frexp(amax)
+    s = np.ldexp(1.0, e - 7)
+    a = np.clip(np.rint(v / s), -127, 127)
+    return np.where(amax > 0, a * s, 0.0)
+
+
+def ffn(x, w_gate, w_up, w_down, act="exact"):
+    """SwiGLU FFN on token rows x [n, H]: (silu(x Wg^T) * (x Wu^T)) Wd^T, fp64.
+    act="q8": x and h replaced by q8_rows of themselves (h rounded to fp32 first,
+    the precision the rounding decision is taken in)."""
     x = _f64(x)
+    if act == "q8":
+        x = q8_rows(x)
     a = x @ _f64(w_gate).T
     c = x @ _f64(w_up).T
     h = silu(a) * c
+    if act == "q8":
+        h = q8_rows(h.astype(np.float32))
     return h @ _f64(w_down).T
 
 
+def decode_matrix(raw, rows, cols):
+    """Block bytes [n, 84] (2-bit format) or [n, 148] (Q4 sibling) -> fp32 [rows, cols]."""
+    raw = np.asarray(raw, np.uint8)
+    codec = {q2.BLOCK_BYTES: q2, q4.BLOCK_BYTES: q4}[raw.shape[-1]]
+    return codec.decode_matrix(raw, rows, cols)
+
+
 def expert_weights(raw_gate, raw_up, raw_down, hidden, inter):
-    """Q2 bytes of one routed expert -> fp32 matrices (gate [I,H], up [I,H], down [H,I])."""
-    return (q2.decode_matrix(raw_gate, inter, hidden),
-            q2.decode_matrix(raw_up, inter, hidden),
-            q2.decode_matrix(raw_down, hidden, inter))
+    """Block bytes of one routed expert -> fp32 matrices (gate [I,H], up [I,H], down [H,I]),
+    each matrix in the format its block size names."""
+    return (decode_matrix(raw_gate, inter, hidden),
+            decode_matrix(raw_up, inter, hidden),
+            decode_matrix(raw_down, hidden, inter))
 
 
-def layer(x, router_w, router_b, expert_bytes, shared, topk, hidden, inter, ffn_map=None):
+def layer(x, router_w, router_b, expert_bytes, shared, topk, hidden, inter, ffn_map=None, act="exact"):
     """One MoE layer in fp64.
 
     x            [T, H] activations (fp32 values, or bf16 values widened)
@@ -103,7 +136,8 @@ def layer(x, router_w, router_b, expert_bytes, shared, topk, hidden, inter, ffn_
     shared       None, or (Wg [Is,H], Wu [Is,H], Wd [H,Is]) full-precision weights
     ffn_map      optional evaluator of the routed FFNs: called with a list of
                  (expert, token rows [n, H]) and returning the list of FFN outputs;
-                 by default each is ffn(rows, *expert_weights(*expert_bytes(e))).
+                 by default each is ffn(rows, *expert_weights(*expert_bytes(e)), act).
+    act          "exact" or "q8": the routed experts' activation mode (see ffn)
     Returns out [T, H] fp64 and the routing dict."""
     x = _f64(x)
     idx, g, logits, margin = route(x, router_w, router_b, topk)
@@ -117,7 +151,7 @@ def layer(x, router_w, router_b, expert_bytes, shared, topk, hidden, inter, ffn_
         toks, ks = np.nonzero(idx == e)
         work.append((int(e), toks, ks))
     if ffn_map is None:
-        ys = [ffn(x[toks], *expert_weights(*expert_bytes(e), hidden, inter)) for e, toks, _ in work]
+        ys = [ffn(x[toks], *expert_weights(*expert_bytes(e), hidden, inter), act=act) for e, toks, _ in work]
     else:
         ys = ffn_map([(e, x[toks]) for e, toks, _ in work])
     for (e, toks, ks), y in zip(work, ys):
@@ -150,14 +184,14 @@ def stack(h0, layers, topk, hidden, inter, eps):
     """Residual stack: h_{l+1} = h_l + layer_l(rmsnorm_bf16(h_l)).
 
     layers: list of dicts with router_w, router_b, expert_bytes, shared and
-    optionally ffn_map (see layer()).
+    optionally ffn_map and act (see layer()).
     Returns the final residual stream [T, H] fp64 and per-layer routings."""
     h = _f64(h0)
     routings = []
     for L in layers:
         x = rmsnorm_bf16(h, eps)
         y, r = layer(x, L["router_w"], L["router_b"], L["expert_bytes"], L["shared"],
-                     topk, hidden, inter, ffn_map=L.get("ffn_map"))
+                     topk, hidden, inter, ffn_map=L.get("ffn_map"), act=L.get("act", "exact"))
         h = h + y
         routings.append(r)
     return h, routings

@@ -136,24 +136,28 @@ def encode_matrix(w):
 
 
 def pack_expert(gate, up, down, hidden, inter):
-    """Row-major Q2 bytes of gate [I rows x H/256], up [I x H/256], down [H x I/256]
-    -> the expert's tiled bytes (1-D uint8)."""
+    """Row-major block bytes of gate [I rows x H/256], up [I x H/256], down [H x I/256]
+    (each [n_blocks, block bytes]: 84 for this module's blocks, 148 for the Q4
+    sibling of oracle.q4) -> the expert's tiled bytes (1-D uint8)."""
     nbh, nbi = hidden // QK, inter // QK
-    g = np.asarray(gate, np.uint8).reshape(inter // 32, 32, nbh, BLOCK_BYTES)
-    u = np.asarray(up, np.uint8).reshape(inter // 32, 32, nbh, BLOCK_BYTES)
-    gu = np.concatenate([g, u], axis=1)                  # [t, slot 64, b, 84]
-    gu = gu.transpose(0, 2, 1, 3)                         # [t, b, slot, 84]
-    d = np.asarray(down, np.uint8).reshape(hidden // 64, 64, nbi, BLOCK_BYTES).transpose(0, 2, 1, 3)
+    gate, up, down = (np.asarray(a, np.uint8) for a in (gate, up, down))
+    bg, bd = gate.shape[-1], down.shape[-1]
+    assert up.shape[-1] == bg
+    g = gate.reshape(inter // 32, 32, nbh, bg)
+    u = up.reshape(inter // 32, 32, nbh, bg)
+    gu = np.concatenate([g, u], axis=1)                  # [t, slot 64, b, bytes]
+    gu = gu.transpose(0, 2, 1, 3)                         # [t, b, slot, bytes]
+    d = down.reshape(hidden // 64, 64, nbi, bd).transpose(0, 2, 1, 3)
     return np.concatenate([gu.reshape(-1), d.reshape(-1)])
 
 
-def unpack_expert(raw, hidden, inter):
+def unpack_expert(raw, hidden, inter, gu_bytes=BLOCK_BYTES, down_bytes=BLOCK_BYTES):
     """Inverse of pack_expert: tiled expert bytes -> row-major (gate, up, down) bytes."""
     nbh, nbi = hidden // QK, inter // QK
     raw = np.asarray(raw, np.uint8).reshape(-1)
-    ngu = 2 * inter * nbh * BLOCK_BYTES
-    gu = raw[:ngu].reshape(inter // 32, nbh, 64, BLOCK_BYTES).transpose(0, 2, 1, 3)
-    gate = gu[:, :32].reshape(inter * nbh, BLOCK_BYTES)
-    up = gu[:, 32:].reshape(inter * nbh, BLOCK_BYTES)
-    d = raw[ngu:].reshape(hidden // 64, nbi, 64, BLOCK_BYTES).transpose(0, 2, 1, 3)
-    return gate, up, d.reshape(hidden * nbi, BLOCK_BYTES)
+    ngu = 2 * inter * nbh * gu_bytes
+    gu = raw[:ngu].reshape(inter // 32, nbh, 64, gu_bytes).transpose(0, 2, 1, 3)
+    gate = gu[:, :32].reshape(inter * nbh, gu_bytes)
+    up = gu[:, 32:].reshape(inter * nbh, gu_bytes)
+    d = raw[ngu:].reshape(hidden // 64, nbi, 64, down_bytes).transpose(0, 2, 1, 3)
+    return gate, up, d.reshape(hidden * nbi, down_bytes)

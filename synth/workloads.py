@@ -70,14 +70,30 @@ class Workload:
     layers: int = 1
     rmsnorm: bool = False
     rms_eps: float = float(np.float32(1e-6))     # the fp32 value the library receives
+    # routed matrices in the 4-bit sibling format: gate/up and/or down, in the layers
+    # from q4_from on (the rest in the 2-bit format)
+    q4_gu: bool = False
+    q4_down: bool = False
+    q4_from: int = 0
 
     @property
     def blocks_per_expert(self):
         return 3 * self.hidden * self.inter // 256
 
+    def q4_at(self, layer):
+        """(gate/up in Q4, down in Q4) for a layer."""
+        on = layer >= self.q4_from
+        return self.q4_gu and on, self.q4_down and on
+
+    def expert_bytes_at(self, layer):
+        gu, dn = self.q4_at(layer)
+        nb = self.hidden * self.inter // 256
+        return 2 * nb * (148 if gu else 84) + nb * (148 if dn else 84)
+
     @property
     def expert_bytes(self):
-        return self.blocks_per_expert * 84
+        """Bytes of one routed expert of layer 0."""
+        return self.expert_bytes_at(0)
 
     def x_stream(self):
         return stream_id(0, TENSOR_X)
@@ -97,6 +113,17 @@ WORKLOADS = {
     # small residual stack for exhaustive checks of RMSNorm + residual over many layers
     "tiny_stack": Workload("tiny_stack", 5, 16, 256, 8, 2, 512, 256, "bf16", 0.05,
                            layers=12, rmsnorm=True),
+    # speculative verification micro-batch: 16 sessions, each checking 5 draft tokens
+    # plus its current one in one batched target pass (T = 16 x 6), Zipf routing
+    "verify96_zipf": Workload("verify96_zipf", 6, 96, H_DS, E_DS, K_DS, I_DS, I_DS, "bf16",
+                              0.02, zipf=True),
+    # the deep stack with its last 6 expert layers in the 4-bit sibling format (layers
+    # 0..33 are those of stack40_t64_zipf: same seed)
+    "stack40_q2q4": Workload("stack40_q2q4", 4, 64, H_DS, E_DS, K_DS, I_DS, I_DS, "bf16", 0.02,
+                             zipf=True, layers=40, rmsnorm=True, q4_gu=True, q4_down=True, q4_from=34),
+    # tiny layers in the 4-bit format: both matrices, and gate/up only (per-matrix mix)
+    "tiny_q4": Workload("tiny_q4", 7, 4, 256, 8, 2, 512, 256, "bf16", 0.05, q4_gu=True, q4_down=True),
+    "tiny_q4gu": Workload("tiny_q4gu", 8, 5, 256, 8, 2, 512, 0, "f32", 0.05, q4_gu=True),
 }
 ORDER = ["tiny", "decode1", "decode32_zipf", "prefill2048", "stack40_t64_zipf"]
 

@@ -4,7 +4,7 @@ import functools
 
 import numpy as np
 
-from oracle import q2
+from oracle import q2, q4
 from synth import workloads as W
 from synth.gen import bf16_bits_to_f32
 
@@ -23,10 +23,13 @@ class HostLayer:
         self._cache = {}
 
     def expert_bytes(self, e):
-        """(gate, up, down) Q2 bytes of routed expert e, quantized on the host."""
+        """(gate, up, down) block bytes of routed expert e (each matrix in its layer's
+        format), quantized on the host by the oracle's encoders."""
         if e not in self._cache:
             wl = self.wl
-            self._cache[e] = tuple(q2.encode_matrix(W.expert_f32(wl, self.layer, e, m))
+            gu4, dn4 = wl.q4_at(self.layer)
+            codecs = (q4 if gu4 else q2, q4 if gu4 else q2, q4 if dn4 else q2)
+            self._cache[e] = tuple(codecs[m].encode_matrix(W.expert_f32(wl, self.layer, e, m))
                                    for m in range(3))
         return self._cache[e]
 

@@ -7,7 +7,7 @@ import os
 
 import numpy as np
 
-from oracle import moe, q2
+from oracle import moe, q2, q4
 from synth import workloads as W
 
 
@@ -21,11 +21,14 @@ def _init_worker():
 
 
 def _expert_ffn(args):
-    name, layer, e, rows = args
+    name, layer, e, rows = args[:4]
+    act = args[4] if len(args) > 4 else "exact"
     wl = W.WORKLOADS[name]
-    raw = [q2.encode_matrix(W.expert_f32(wl, layer, e, m)) for m in range(3)]
+    gu4, dn4 = wl.q4_at(layer)
+    codecs = (q4 if gu4 else q2, q4 if gu4 else q2, q4 if dn4 else q2)
+    raw = [codecs[m].encode_matrix(W.expert_f32(wl, layer, e, m)) for m in range(3)]
     wg, wu, wd = moe.expert_weights(*raw, wl.hidden, wl.inter)
-    return moe.ffn(rows, wg, wu, wd)
+    return moe.ffn(rows, wg, wu, wd, act=act)
 
 
 class ExpertPool:
@@ -44,10 +47,10 @@ class ExpertPool:
                 else:
                     os.environ[k] = v
 
-    def ffn_map(self, name, layer):
+    def ffn_map(self, name, layer, act="exact"):
         def run(items):
             print("  [oracle pool] layer %d: %d expert FFNs" % (layer, len(items)), flush=True)
-            return self._pool.map(_expert_ffn, [(name, layer, e, rows) for e, rows in items], chunksize=1)
+            return self._pool.map(_expert_ffn, [(name, layer, e, rows, act) for e, rows in items], chunksize=1)
         return run
 
     def close(self):
@@ -55,7 +58,7 @@ class ExpertPool:
         self._pool.join()
 
 
-def layer_outputs(pool, name, jobs, topk, hidden, inter):
+def layer_outputs(pool, name, jobs, topk, hidden, inter, act="exact"):
     """Oracle outputs of several layers of workload `name` for given token rows.
 
     jobs: list of (layer, host_layer, x_rows).  The routed FFNs of every job are
@@ -68,7 +71,7 @@ def layer_outputs(pool, name, jobs, topk, hidden, inter):
         for e in np.unique(idx):
             toks, _ = np.nonzero(idx == e)           # the rows moe.layer hands to the FFN
             where[(l, int(e))] = len(tasks)
-            tasks.append((name, l, int(e), np.asarray(x, np.float64)[toks]))
+            tasks.append((name, l, int(e), np.asarray(x, np.float64)[toks], act))
     print("  [oracle pool] %d expert FFNs over %d layer job(s)" % (len(tasks), len(jobs)), flush=True)
     ys = []
     for i, y in enumerate(pool._pool.imap(_expert_ffn, tasks, chunksize=1)):
@@ -85,5 +88,5 @@ def layer_outputs(pool, name, jobs, topk, hidden, inter):
                 res.append(ys[i])
             return res
         out.append(moe.layer(x, hl.router_w, hl.router_b, None, hl.shared, topk, hidden, inter,
-                             ffn_map=lookup))
+                             ffn_map=lookup, act=act))
     return out

@@ -37,8 +37,13 @@ def test_exports_every_declared_function(lib):
 
 def test_constants(lib):
     assert mq.block_bytes() == 84
+    assert lib.moe_q2_q4_block_bytes() == 148 == mq.Q4_BLOCK_BYTES
     s = mq.make_shape(7168, 2048, 256, 2048)
     assert mq.expert_bytes(s) == 14_450_688
+    nb = 7168 * 2048 // 256
+    assert mq.expert_bytes(mq.make_shape(7168, 2048, 256, 2048, flags=mq.GU_Q4)) == 2 * nb * 148 + nb * 84
+    assert mq.expert_bytes(mq.make_shape(7168, 2048, 256, 2048, flags=mq.DOWN_Q4)) == 2 * nb * 84 + nb * 148
+    assert mq.expert_bytes(mq.make_shape(7168, 2048, 256, 2048, flags=mq.GU_Q4 | mq.DOWN_Q4)) == 3 * nb * 148
     for st in (mq.OK, mq.EINVAL, mq.EUNSUPPORTED, mq.EWORKSPACE, mq.EHIP):
         assert lib.moe_q2_status_string(st)
     assert lib.moe_q2_status_string(-99) == b"unknown status"
@@ -53,7 +58,13 @@ def _ws_status(shape, T, K):
     (dict(hidden=7000), mq.EUNSUPPORTED), (dict(inter=2000), mq.EUNSUPPORTED),
     (dict(n_experts=0), mq.EUNSUPPORTED), (dict(n_experts=513), mq.EUNSUPPORTED),
     (dict(shared_inter=100), mq.EUNSUPPORTED), (dict(act_dtype=7), mq.EINVAL),
-    (dict(flags=64), mq.EINVAL), (dict(flags=mq.PATH_DECODE | mq.PATH_PREFILL), mq.EINVAL),
+    (dict(flags=1024), mq.EINVAL), (dict(flags=mq.PATH_DECODE | mq.PATH_PREFILL), mq.EINVAL),
+    (dict(flags=mq.BATCH_INVARIANT | mq.PATH_PREFILL), mq.EINVAL),
+    (dict(flags=mq.BATCH_INVARIANT | mq.DECODE_VALU), mq.EUNSUPPORTED),
+    (dict(flags=mq.ACT_Q8 | mq.DECODE_VALU), mq.EUNSUPPORTED),
+    (dict(flags=mq.GU_Q4 | mq.DECODE_VALU), mq.EUNSUPPORTED),
+    (dict(flags=mq.DOWN_Q4 | mq.PATH_PREFILL), mq.EUNSUPPORTED),
+    (dict(flags=mq.BATCH_INVARIANT, act_dtype=mq.F32), mq.EUNSUPPORTED),   # fp32 input + shared expert
 ])
 def test_workspace_size_rejects(lib, kw, status):
     base = dict(hidden=7168, inter=2048, n_experts=256, shared_inter=2048, act_dtype=mq.BF16, flags=0)
@@ -138,8 +149,13 @@ def test_setup_helpers_validation(lib):
     assert lib.moe_q2_synth_normal(0, 0, 0, 0, 1.0, mq.F32, None, None) == mq.OK
     assert lib.moe_q2_synth_normal(0, 0, 0, 10, 1.0, 5, A, None) == mq.EINVAL
     assert lib.moe_q2_synth_normal(0, 0, 0, 10, 1.0, mq.F32, None, None) == mq.EINVAL
-    assert lib.moe_q2_pack_expert(A, A, A, 100, 256, A, None) == mq.EUNSUPPORTED
-    assert lib.moe_q2_pack_expert(None, A, A, 256, 256, A, None) == mq.EINVAL
+    bad = mq.make_shape(100, 256, 8, 0)
+    ok = mq.make_shape(256, 256, 8, 0)
+    assert lib.moe_q2_pack_expert(A, A, A, ctypes.byref(bad), A, None) == mq.EUNSUPPORTED
+    assert lib.moe_q2_pack_expert(None, A, A, ctypes.byref(ok), A, None) == mq.EINVAL
+    assert lib.moe_q2_pack_expert(A, A, A, None, A, None) == mq.EINVAL
+    assert lib.moe_q2_quantize_q4(A + 4, 1, 256, 2 * A, None) == mq.EINVAL
+    assert lib.moe_q2_quantize_q4(None, 0, 256, None, None) == mq.OK
 
 
 def test_noalloc_validation(lib):
@@ -153,3 +169,22 @@ def test_noalloc_validation(lib):
     assert mq.workspace_size(s, 255, 8) > mq.NOALLOC_MAX_BYTES
     assert f(A, 2 * A, 3 * A, 5 * A, 8, 64 * A, ctypes.byref(s), 255, None, None, None) == mq.EUNSUPPORTED
     assert mq.workspace_size(s, 96, 8) <= mq.NOALLOC_MAX_BYTES      # the verification micro-batch fits
+
+
+def test_plans(lib):
+    """Path choices (moe_q2_describe): batch-invariant calls keep the one-token splits,
+    router split and decode kernels at every batch size; Q4 matrices run the decode
+    kernels at prefill sizes; Q8 activations halve the digit buffers."""
+    s = mq.make_shape(7168, 2048, 256, 2048)
+    one = mq.describe(s, 1, 8)
+    bi = mq.make_shape(7168, 2048, 256, 2048, flags=mq.BATCH_INVARIANT)
+    plans = [mq.describe(bi, T, 8) for T in (1, 5, 32, 96, 255, 2048)]
+    for p in plans:
+        assert p["path"] == mq.PATH_DECODE and p["routed_kernel"] == 0
+        assert (p["split_gate_up"], p["split_down"]) == (one["split_gate_up"], one["split_down"])
+        assert p["router_splits"] == plans[0]["router_splits"] == 16
+    assert mq.describe(s, 2048, 8)["path"] == mq.PATH_PREFILL
+    q4 = mq.make_shape(7168, 2048, 256, 2048, flags=mq.GU_Q4 | mq.DOWN_Q4)
+    assert mq.describe(q4, 2048, 8)["path"] == mq.PATH_DECODE
+    q8 = mq.make_shape(7168, 2048, 256, 2048, flags=mq.ACT_Q8)
+    assert mq.workspace_size(q8, 32, 8) < mq.workspace_size(s, 32, 8)
