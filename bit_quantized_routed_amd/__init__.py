@@ -23,6 +23,7 @@ Q4_BLOCK_BYTES = 148
 EXPORTS = ["moe_q2_block_bytes", "moe_q2_expert_bytes", "moe_q2_workspace_size",
            "moe_q2_describe", "moe_q2_forward", "moe_q2_forward_noalloc", "moe_q2_quantize",
            "moe_q2_quantize_q4", "moe_q2_q4_block_bytes", "moe_q2_pack_expert",
+           "moe_q2_cache_state_bytes", "moe_q2_cache_reset", "moe_q2_forward_cached",
            "moe_q2_synth_normal", "moe_q2_status_string", "moe_q2_last_hip_error"]
 
 
@@ -31,6 +32,15 @@ class Shape(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("rms_eps", ctypes.c_float)]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("slots", ctypes.c_void_p), ("slot_bytes", ctypes.c_int64), ("n_slots", ctypes.c_int32),
+                ("n_keys", ctypes.c_int32), ("state", ctypes.c_void_p)]
+
+
+CACHE_MAX_SLOTS = 2048
+CACHE_HDR = 8
 
 
 class Plan(ctypes.Structure):
@@ -48,7 +58,7 @@ class Trace(ctypes.Structure):
 
 
 PHASES = ["rmsnorm", "router", "topk", "bucket", "prep_x", "gate_up", "prep_h", "down",
-          "shared", "combine"]
+          "shared", "combine", "cache"]
 
 
 class MoeQ2Error(RuntimeError):
@@ -86,6 +96,13 @@ def _lib():
         lib.moe_q2_forward_noalloc.restype = ctypes.c_int
         lib.moe_q2_forward_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.POINTER(Shape), i32, vp,
                                                ctypes.POINTER(Trace), vp]
+        lib.moe_q2_cache_state_bytes.restype = sz
+        lib.moe_q2_cache_state_bytes.argtypes = [i32, i32]
+        lib.moe_q2_cache_reset.restype = ctypes.c_int
+        lib.moe_q2_cache_reset.argtypes = [ctypes.POINTER(Cache), vp]
+        lib.moe_q2_forward_cached.restype = ctypes.c_int
+        lib.moe_q2_forward_cached.argtypes = [vp, vp, vp, i32, ctypes.POINTER(Cache), vp, i32, vp,
+                                              ctypes.POINTER(Shape), i32, vp, vp, sz, ctypes.POINTER(Trace), vp]
         lib.moe_q2_quantize.restype = ctypes.c_int
         lib.moe_q2_quantize.argtypes = [vp, i64, i64, vp, vp]
         lib.moe_q2_quantize_q4.restype = ctypes.c_int
@@ -177,6 +194,45 @@ def forward(x, router_w, experts_q2, shared_w, topk, out, shape, n_tokens, route
 
 
 NOALLOC_MAX_BYTES = 128 << 20
+
+
+def _trace_struct(trace):
+    if not trace:
+        return None
+    ev = trace.get("events")
+    return Trace(*[_ptr(trace.get(k)) for k in ("topk_idx", "topk_w", "counts", "offsets", "perm")],
+                 ev.array_ptr() if ev is not None else None)
+
+
+def cache_state_bytes(n_slots, n_keys):
+    return int(_lib().moe_q2_cache_state_bytes(n_slots, n_keys))
+
+
+def make_cache(slots, slot_bytes, n_slots, n_keys, state):
+    """moe_q2_cache over caller-owned device tensors: `slots` (n_slots * slot_bytes
+    bytes) and `state` (cache_state_bytes(n_slots, n_keys) bytes, int32)."""
+    return Cache(_ptr(slots), slot_bytes, n_slots, n_keys, _ptr(state))
+
+
+def cache_reset(cache, stream=None):
+    rc = _lib().moe_q2_cache_reset(ctypes.byref(cache), _stream(stream))
+    if rc:
+        raise MoeQ2Error(rc, "moe_q2_cache_reset")
+
+
+def forward_cached(x, router_w, host_experts, key_base, cache, shared_w, topk, out, shape, n_tokens,
+                   router_b=None, workspace=None, trace=None, stream=None, check=True):
+    """moe_q2_forward_cached: the routed experts in pinned host memory (`host_experts`,
+    a pinned tensor) behind the HBM expert cache `cache` (make_cache)."""
+    tr = _trace_struct(trace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib().moe_q2_forward_cached(_ptr(x), _ptr(router_w), _ptr(host_experts), key_base, ctypes.byref(cache),
+                                      _ptr(shared_w), topk, _ptr(out), ctypes.byref(shape), n_tokens,
+                                      _ptr(router_b), _ptr(workspace), ws_bytes,
+                                      ctypes.byref(tr) if tr else None, _stream(stream))
+    if rc and check:
+        raise MoeQ2Error(rc, "moe_q2_forward_cached")
+    return rc
 
 
 def forward_noalloc(x, router_w, experts_q2, shared_w, topk, out, shape, n_tokens, router_b=None,

@@ -6,7 +6,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoe_q2.so")
-SOURCES = ["moe_q2.cpp", "setup.hip", "route.hip", "prep.hip", "ffn_dec.hip", "ffn_mma.hip", "combine.hip", "gemm.hip"]
+SOURCES = ["moe_q2.cpp", "setup.hip", "route.hip", "prep.hip", "ffn_dec.hip", "ffn_mma.hip", "combine.hip", "gemm.hip",
+           "cache.hip"]
 
 # Packed fp32 VALU ops are switched off for all device code.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

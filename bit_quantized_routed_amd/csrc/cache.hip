@@ -1,0 +1,178 @@
+// Budgeted HBM cache of routed experts streamed from host memory on misses
+// ("DwarfStar (ds4)" (opensourcealternatives.to), section FAQ: routed experts come
+// from slower storage through an in-memory cache; "DwarfStar 4" (aiany.app),
+// section "What Sets It Apart": configurable expert-cache budgets).  The cache is
+// planned and filled on the device, after the bucketing has counted the slots of
+// every expert, so a cached layer needs no host round trip and stays capturable.
+//
+// Policy (least recently used, ties by index): a touched expert already resident
+// keeps its slot (its stamp becomes the call's clock); the missing experts, in
+// increasing key order, take the slots no touched expert uses, in increasing
+// (stamp, slot index) order -- empty slots (stamp 0) first.
+//
+// State (int32, device): [0] clock, [1] hits, [2] misses (both cumulative),
+// [3] misses of the last call, [4] experts touched by the last call, [5..7] 0,
+// then slot_key[n_slots] (-1: empty), slot_stamp[n_slots], key_slot[n_keys] (-1: absent).
+#include "common.h"
+#include "kernels.h"
+
+#define MQ_CACHE_HDR 8
+#define MQ_CACHE_THREADS 1024
+
+__global__ void __launch_bounds__(256) k_cache_reset(int32_t *__restrict__ state, int n_slots, int n_keys) {
+    const int64_t n = MQ_CACHE_HDR + 2 * (int64_t)n_slots + n_keys;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        int32_t v = 0;
+        if (i >= MQ_CACHE_HDR && i < MQ_CACHE_HDR + n_slots) v = -1;                 // slot_key
+        if (i >= MQ_CACHE_HDR + 2 * (int64_t)n_slots) v = -1;                         // key_slot
+        state[i] = v;
+    }
+}
+
+int mq_launch_cache_reset(int32_t *state, int n_slots, int n_keys, hipStream_t st) {
+    const int64_t n = MQ_CACHE_HDR + 2 * (int64_t)n_slots + n_keys;
+    int64_t grid = (n + 255) / 256;
+    if (grid > 1024) grid = 1024;
+    hipLaunchKernelGGL(k_cache_reset, dim3((unsigned)grid), dim3(256), 0, st, state, n_slots, n_keys);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}
+
+// One work-group.  counts: slots per expert of this call (E <= MQ_CACHE_THREADS);
+// out: eslot[e] (the slot of each touched expert, -1 otherwise), the miss list
+// (expert, slot) in increasing expert order and its length.
+__global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *__restrict__ counts, int E,
+                                                                int key_base, int32_t *__restrict__ state,
+                                                                int n_slots, int n_keys,
+                                                                int32_t *__restrict__ eslot,
+                                                                int2 *__restrict__ misses,
+                                                                int32_t *__restrict__ n_miss) {
+    __shared__ int32_t s_stamp[MOE_Q2_CACHE_MAX_SLOTS], s_key[MOE_Q2_CACHE_MAX_SLOTS];
+    __shared__ int32_t s_miss[MQ_CACHE_THREADS], s_victim[MQ_CACHE_THREADS];
+    __shared__ int32_t s_wsum[MQ_CACHE_THREADS / 64], s_hits;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int32_t *slot_key = state + MQ_CACHE_HDR;
+    int32_t *slot_stamp = slot_key + n_slots;
+    int32_t *key_slot = slot_stamp + n_slots;
+    const int32_t clock = state[0] + 1;
+    for (int s = tid; s < n_slots; s += MQ_CACHE_THREADS) {
+        s_stamp[s] = slot_stamp[s];
+        s_key[s] = slot_key[s];
+    }
+    if (tid == 0) s_hits = 0;
+    s_victim[tid] = -1;
+    __syncthreads();
+    // 1. hits keep their slot (stamped with this call's clock); misses are flagged.
+    // (A state not made by moe_q2_cache_reset with this n_slots could hold a slot out
+    // of range: it is read as a miss, and step 4 keeps every slot index in range, so
+    // such misuse gives wrong results but no access outside the buffers.)
+    int miss = 0;
+    if (tid < E) {
+        int32_t sl = -1;
+        if (counts[tid] > 0) {
+            sl = key_slot[key_base + tid];
+            if (sl >= n_slots) sl = -1;
+            if (sl >= 0) {
+                s_stamp[sl] = clock;
+                atomicAdd(&s_hits, 1);                   // a count: commutative
+            } else {
+                miss = 1;
+            }
+        }
+        eslot[tid] = sl;
+    }
+    // 2. rank of each miss among the misses, in expert order (work-group scan)
+    int r = miss;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int p = __shfl_up(r, o, 64);
+        if (lane >= o) r += p;
+    }
+    if (lane == 63) s_wsum[wv] = r;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wv; ++w) base += s_wsum[w];
+    int nm = 0;
+    for (int w = 0; w < MQ_CACHE_THREADS / 64; ++w) nm += s_wsum[w];
+    s_miss[tid] = miss ? base + r - 1 : -1;
+    // 3. the slots no touched expert uses, ranked by (stamp, slot index); the first
+    // nm of them are the victims, victim i taken by the miss of rank i
+    for (int s = tid; s < n_slots; s += MQ_CACHE_THREADS) {
+        const int32_t st = s_stamp[s];
+        if (st < clock) {
+            int rank = 0;
+            for (int q = 0; q < n_slots; ++q) {
+                const int32_t sq = s_stamp[q];
+                rank += (sq < st || (sq == st && q < s)) ? 1 : 0;
+            }
+            if (rank < nm) s_victim[rank] = s;
+        }
+    }
+    __syncthreads();
+    // 4. evictions (the victims' old keys), then the new keys; all keys distinct
+    if (tid < E && s_miss[tid] >= 0) {
+        const int v = s_victim[s_miss[tid]];
+        const int32_t old = v >= 0 ? s_key[v] : -1;
+        if (old >= 0 && old < n_keys) key_slot[old] = -1;
+    }
+    __syncthreads();
+    if (tid < E && s_miss[tid] >= 0) {
+        const int i = s_miss[tid];
+        const int v = max(s_victim[i], 0);       // always a victim when n_slots >= the touched experts
+        key_slot[key_base + tid] = v;
+        s_key[v] = key_base + tid;
+        s_stamp[v] = clock;
+        eslot[tid] = v;
+        misses[i] = make_int2(tid, v);
+    }
+    __syncthreads();
+    for (int s = tid; s < n_slots; s += MQ_CACHE_THREADS) {
+        slot_stamp[s] = s_stamp[s];
+        slot_key[s] = s_key[s];
+    }
+    if (tid == 0) {
+        state[0] = clock;
+        state[1] += s_hits;
+        state[2] += nm;
+        state[3] = nm;
+        state[4] = s_hits + nm;
+        *n_miss = nm;
+    }
+}
+
+int mq_launch_cache_plan(const int32_t *counts, int E, int key_base, int32_t *state, int n_slots, int n_keys,
+                         int32_t *eslot, int2 *misses, int32_t *n_miss, hipStream_t st) {
+    if (E > MQ_CACHE_THREADS || n_slots > MOE_Q2_CACHE_MAX_SLOTS) return MOE_Q2_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_cache_plan, dim3(1), dim3(MQ_CACHE_THREADS), 0, st, counts, E, key_base, state, n_slots,
+                       n_keys, eslot, misses, n_miss);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}
+
+// The missed experts' bytes from host memory (read over the host link by the
+// work-groups) into their slots: chunks of 4 KiB, miss-major, grid-strided, 16 bytes
+// per thread and step; the miss count is read on the device.
+#define MQ_FILL_CHUNK 4096
+__global__ void __launch_bounds__(256) k_cache_fill(const uint8_t *__restrict__ host, int64_t expert_bytes,
+                                                   uint8_t *__restrict__ slots, int64_t slot_bytes,
+                                                   const int2 *__restrict__ misses,
+                                                   const int32_t *__restrict__ n_miss) {
+    const int64_t cpe = (expert_bytes + MQ_FILL_CHUNK - 1) / MQ_FILL_CHUNK;
+    const int64_t total = (int64_t)(*n_miss) * cpe;
+    for (int64_t c = blockIdx.x; c < total; c += gridDim.x) {
+        const int64_t i = c / cpe, off = (c - i * cpe) * MQ_FILL_CHUNK + 16 * (int64_t)threadIdx.x;
+        if (off < expert_bytes) {
+            const int2 m = misses[i];
+            const mq_u32x4 v = *(const mq_u32x4 *)(host + (int64_t)m.x * expert_bytes + off);
+            *(mq_u32x4 *)(slots + (int64_t)m.y * slot_bytes + off) = v;
+        }
+    }
+}
+
+int mq_launch_cache_fill(const void *host, int64_t expert_bytes, void *slots, int64_t slot_bytes,
+                         const int2 *misses, const int32_t *n_miss, int n_cu, hipStream_t st) {
+    hipLaunchKernelGGL(k_cache_fill, dim3(2 * n_cu), dim3(256), 0, st, (const uint8_t *)host, expert_bytes,
+                       (uint8_t *)slots, slot_bytes, misses, n_miss);
+    MQ_LAUNCH_CHECK();
+    return MOE_Q2_OK;
+}

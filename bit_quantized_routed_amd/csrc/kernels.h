@@ -159,3 +159,10 @@ int mq_launch_q2_mma_pf(int swiglu, const MqFormat &fmt, const void *experts, in
                         int max_units, const int32_t *perm, int topk, const void *xdig,
                         const uint32_t *xsum, const float *xscale, float *out, int n_cu,
                         hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+// Expert cache (cache.hip): state reset, the plan of one call (eslot, miss list) and
+// the copy of the missed experts from host memory into their slots.
+int mq_launch_cache_reset(int32_t *state, int n_slots, int n_keys, hipStream_t st);
+int mq_launch_cache_plan(const int32_t *counts, int E, int key_base, int32_t *state, int n_slots, int n_keys,
+                         int32_t *eslot, int2 *misses, int32_t *n_miss, hipStream_t st);
+int mq_launch_cache_fill(const void *host, int64_t expert_bytes, void *slots, int64_t slot_bytes,
+                         const int2 *misses, const int32_t *n_miss, int n_cu, hipStream_t st);

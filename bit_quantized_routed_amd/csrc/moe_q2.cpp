@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -55,7 +56,7 @@ namespace {
 struct Workspace {
     size_t total = 0;
     size_t logits, idx, gate, counts, offsets, perm, inv, units_hdr, units, urow = 0, bchunk = 0, xbf, xq, xg, xs, h,
-        hq, hg, hs, y, xlo, sp, shi, slo, ysh;
+        hq, hg, hs, y, xlo, sp, shi, slo, ysh, eslot, misses, nmiss;
     int max_units = 0, split_gu = 1, split_d = 1, rsplit = 1;
     int nd = 2;                 // activation digits: 2 (15-bit) or 1 (Q8)
     bool bi = false;            // batch-invariant: splits and router fixed by the shape
@@ -113,6 +114,10 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     w.perm = take(c, S * 4);
     w.inv = take(c, S * 4);
     w.units_hdr = take(c, 16);
+    // expert cache of a call (moe_q2_forward_cached): slot per expert, miss list
+    w.eslot = take(c, E * 4);
+    w.misses = take(c, E * 8);
+    w.nmiss = take(c, 16);
     w.units = take(c, (size_t)w.max_units * 16);
     if (w.dec_units) w.urow = take(c, (size_t)w.dec_units * MMA_TCH * 4);   // row table of the units
     if (T >= MQ_BUCKET_PAR_MIN_T)                   // per-chunk expert counts of the large-batch bucketing
@@ -316,12 +321,19 @@ static int check_forward(const void *x, const float *router_w, const void *exper
 
 // The layer on a caller's workspace.  serial: keep every launch on `stream` (no
 // internal stream), whatever the flags say.
-// eslot: nullable expert -> slot table of an expert cache (experts_q2 is then the
-// cache's slot arena).
+// An expert-cache call: the layer's experts in host memory, its first key, the cache.
+struct CacheCall {
+    const void *host;
+    int key_base;
+    const moe_q2_cache *c;
+};
+
+// cache: nullable; with it, experts_q2 is the host copy and the routed kernels read
+// the cache's slots.
 static int forward_impl(const void *x, const float *router_w, const void *experts_q2, const uint16_t *shared_w,
                         int32_t topk, float *out, const moe_q2_shape *s, int32_t n_tokens,
                         const float *router_b, void *workspace, size_t workspace_bytes,
-                        const moe_q2_trace *trace, void *stream, bool serial, const int32_t *eslot) {
+                        const moe_q2_trace *trace, void *stream, bool serial, const CacheCall *cache) {
     int rc = check_forward(x, router_w, experts_q2, shared_w, topk, out, s, n_tokens);
     if (rc) return rc;
     const bool rms = (s->flags & MOE_Q2_PRE_RMSNORM) != 0;
@@ -471,7 +483,7 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
     // few tokens: the bucketing runs in the top-K launch (its phase then reads zero),
     // or, on the matrix-core decode path, inside the gate/up launch (both phases zero)
     const int tch = valu ? FD_TCH : (prefill ? PF_TCH : MMA_TCH);
-    const bool route_in_gu = !valu && !prefill && nsplit == 1 && T <= MQ_TOPK_BUCKET_MAX_T &&
+    const bool route_in_gu = !cache && !valu && !prefill && nsplit == 1 && T <= MQ_TOPK_BUCKET_MAX_T &&
                              E <= MQ_ROUTE_MAX_E && K <= 16;
     MqRoute rt = {};
     if (route_in_gu) {
@@ -505,9 +517,26 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
     }
     // routed experts
     const int ncu = device_cus();
-    const int64_t ebytes = (int64_t)moe_q2_expert_bytes(s);
+    int64_t ebytes = (int64_t)moe_q2_expert_bytes(s);
+    // expert cache: plan the call from the bucketing's counts, copy the misses from
+    // host memory, then read every routed expert from its slot
+    const int32_t *eslot = nullptr;
+    if (cache) {
+        int32_t *es = (int32_t *)(ws + w.eslot), *nm = (int32_t *)(ws + w.nmiss);
+        int2 *ml = (int2 *)(ws + w.misses);
+        MQ_PHASE(MOE_Q2_PH_CACHE, (rc = mq_launch_cache_plan(counts, E, cache->key_base, cache->c->state,
+                                                             cache->c->n_slots, cache->c->n_keys, es, ml, nm, st))
+                                      ? rc
+                                      : mq_launch_cache_fill(cache->host, ebytes, cache->c->slots,
+                                                             cache->c->slot_bytes, ml, nm, ncu, st));
+        experts_q2 = cache->c->slots;
+        ebytes = cache->c->slot_bytes;
+        eslot = es;
+    } else if ((rc = mark(MOE_Q2_PH_CACHE, 0)) || (rc = mark(MOE_Q2_PH_CACHE, 1))) {
+        return rc;
+    }
     const int64_t mat_gu = (int64_t)I * (H / MQ_QK) * (int64_t)gu_block_bytes(s);   // bytes of gate (or up)
-    const MqFormat fgu = {w.nd, (s->flags & MOE_Q2_GU_Q4) ? MQ_BD4 : MQ_BD2, eslot};
+    const MqFormat fgu = {w.nd, (s->flags & MOE_Q2_GU_Q4) ? MQ_BD4 : MQ_BD2, eslot};   // after the cache plan
     const MqFormat fdn = {w.nd, (s->flags & MOE_Q2_DOWN_Q4) ? MQ_BD4 : MQ_BD2, eslot};
     float *h = (float *)(ws + w.h);
     float *y = (float *)(ws + w.y);
@@ -598,6 +627,54 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
                               void *stream) {
     return forward_impl(x, router_w, experts_q2, shared_w, topk, out, s, n_tokens, router_b, workspace,
                         workspace_bytes, trace, stream, false, nullptr);
+}
+
+// ------------------------------------------------------------------ expert cache
+extern "C" size_t moe_q2_cache_state_bytes(int32_t n_slots, int32_t n_keys) {
+    if (n_slots < 1 || n_slots > MOE_Q2_CACHE_MAX_SLOTS || n_keys < 1 || n_keys > (1 << 28)) return 0;
+    return (size_t)4 * (8 + 2 * (size_t)n_slots + (size_t)n_keys);
+}
+
+static int check_cache(const moe_q2_cache *c) {
+    if (!c || !c->slots || !c->state) return MOE_Q2_EINVAL;
+    if (!moe_q2_cache_state_bytes(c->n_slots, c->n_keys)) return MOE_Q2_EINVAL;
+    if (c->slot_bytes <= 0 || (c->slot_bytes & 15) || ((uintptr_t)c->slots & 15) || ((uintptr_t)c->state & 3))
+        return MOE_Q2_EINVAL;
+    return MOE_Q2_OK;
+}
+
+extern "C" int moe_q2_cache_reset(const moe_q2_cache *cache, void *stream) {
+    const int rc = check_cache(cache);
+    if (rc) return rc;
+    return mq_launch_cache_reset(cache->state, cache->n_slots, cache->n_keys, (hipStream_t)stream);
+}
+
+extern "C" int moe_q2_forward_cached(const void *x, const float *router_w, const void *host_experts,
+                                     int32_t key_base, const moe_q2_cache *cache, const uint16_t *shared_w,
+                                     int32_t topk, float *out, const moe_q2_shape *s, int32_t n_tokens,
+                                     const float *router_b, void *workspace, size_t workspace_bytes,
+                                     const moe_q2_trace *trace, void *stream) {
+    int rc = check_forward(x, router_w, host_experts, shared_w, topk, out, s, n_tokens);
+    if (rc) return rc;
+    if ((rc = check_cache(cache))) return rc;
+    if (s->flags & MOE_Q2_DECODE_VALU) return MOE_Q2_EUNSUPPORTED;
+    const int64_t E = s->n_experts;
+    if (key_base < 0 || key_base + E > cache->n_keys) return MOE_Q2_EINVAL;
+    if (cache->slot_bytes < (int64_t)moe_q2_expert_bytes(s)) return MOE_Q2_EINVAL;
+    const int64_t touched_max = std::min<int64_t>(E, (int64_t)n_tokens * topk);
+    if (cache->n_slots < touched_max) return MOE_Q2_EUNSUPPORTED;
+    if (n_tokens == 0) return MOE_Q2_OK;
+    // the host copy must be pinned memory the device can read (a host query; pageable
+    // memory would fault the kernels that read it)
+    hipPointerAttribute_t pa;
+    if (hipPointerGetAttributes(&pa, host_experts) != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_Q2_EINVAL;
+    }
+    if (pa.type != hipMemoryTypeHost || !pa.devicePointer) return MOE_Q2_EINVAL;
+    const CacheCall cc = {pa.devicePointer, key_base, cache};
+    return forward_impl(x, router_w, host_experts, shared_w, topk, out, s, n_tokens, router_b, workspace,
+                        workspace_bytes, trace, stream, false, &cc);
 }
 
 // ------------------------------------------------------------------ no-allocation entry point

@@ -166,6 +166,7 @@ enum {
     MOE_Q2_PH_DOWN,             /* routed Q2 down projection */
     MOE_Q2_PH_SHARED,           /* shared expert (bf16 MFMA) */
     MOE_Q2_PH_COMBINE,          /* weighted combine (+ residual) */
+    MOE_Q2_PH_CACHE,            /* expert cache: plan and fill of the missed experts */
     MOE_Q2_N_PHASES
 };
 
@@ -221,6 +222,48 @@ int moe_q2_forward(const void *x, const float *router_w, const void *experts_q2,
                    const moe_q2_shape *s, int32_t n_tokens, const float *router_b,
                    void *workspace, size_t workspace_bytes, const moe_q2_trace *trace,
                    void *stream);
+
+/* Budgeted HBM cache of routed experts whose home is host memory ("DwarfStar (ds4)"
+ * (opensourcealternatives.to), section FAQ: routed experts stream from slower storage
+ * through an in-memory cache on misses; "DwarfStar 4" (aiany.app), section "What Sets
+ * It Apart": configurable expert-cache budgets).  The budget is n_slots expert slots of
+ * HBM; a call's touched experts are looked up by key (key_base + expert index, so
+ * several layers can share one cache), the missing ones are copied from host memory
+ * into slots chosen least-recently-used (ties by slot index; empty slots first), and
+ * the routed kernels read every expert from its slot.  Planning and copying run on the
+ * device after the bucketing: no host synchronisation, capturable in a HIP graph.
+ * The caller owns every buffer; calls that share a cache must be ordered on one stream.
+ * state (int32, device): [0] calls, [1] hits, [2] misses (cumulative), [3] misses and
+ * [4] touched experts of the last call, [5..7] 0, then slot_key[n_slots] (-1: empty),
+ * slot_stamp[n_slots] (last call that used the slot), key_slot[n_keys] (-1: absent). */
+#define MOE_Q2_CACHE_MAX_SLOTS 2048
+typedef struct {
+    void    *slots;       /* device, n_slots * slot_bytes, 16-byte aligned: the budget */
+    int64_t  slot_bytes;  /* >= moe_q2_expert_bytes of every layer using the cache, multiple of 16 */
+    int32_t  n_slots;     /* 1 .. MOE_Q2_CACHE_MAX_SLOTS */
+    int32_t  n_keys;      /* valid keys 0 .. n_keys - 1 */
+    int32_t *state;       /* device, moe_q2_cache_state_bytes(n_slots, n_keys) bytes */
+} moe_q2_cache;
+
+/* Bytes of a cache's state; 0 for n_slots or n_keys out of range. */
+size_t moe_q2_cache_state_bytes(int32_t n_slots, int32_t n_keys);
+
+/* Empties the cache (writes its initial state with a kernel on `stream`). */
+int moe_q2_cache_reset(const moe_q2_cache *cache, void *stream);
+
+/* moe_q2_forward with the routed experts in host memory behind `cache`:
+ *   host_experts  the layer's E experts back to back (moe_q2_expert_bytes(s) each, the
+ *                 tiled layout), in pinned host memory (hipHostMalloc, or a pinned torch
+ *                 tensor); checked with hipPointerGetAttributes, EINVAL for other memory
+ *   key_base      the layer's first key: expert e has key key_base + e (key_base >= 0,
+ *                 key_base + E <= n_keys)
+ * Needs n_slots >= min(E, n_tokens * topk) (every touched expert resident at once);
+ * not with MOE_Q2_DECODE_VALU.  The results are those of moe_q2_forward on the same
+ * experts resident in HBM, bit for bit.  The workspace is moe_q2_workspace_size's. */
+int moe_q2_forward_cached(const void *x, const float *router_w, const void *host_experts, int32_t key_base,
+                          const moe_q2_cache *cache, const uint16_t *shared_w, int32_t topk, float *out,
+                          const moe_q2_shape *s, int32_t n_tokens, const float *router_b,
+                          void *workspace, size_t workspace_bytes, const moe_q2_trace *trace, void *stream);
 
 /* moe_q2_forward for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same

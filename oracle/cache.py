@@ -1,0 +1,63 @@
+"""Budgeted expert cache, oracle side: the replacement policy as a plain simulation.
+
+TEST INFRASTRUCTURE: only tests/ may import this module.  It shares no code with
+the HIP library.
+
+The pages stream routed experts from slower storage into an in-memory expert
+cache on misses, with configurable cache budgets ("DwarfStar (ds4)"
+(opensourcealternatives.to), section FAQ; "DwarfStar 4" (aiany.app), section
+"What Sets It Apart"), and name no replacement policy.  The reading taken here is
+least-recently-used over a fixed number of slots, with every tie broken by index:
+
+  state: slot -> key or empty, and slot -> stamp (the number of the call that last
+  used the slot, 0 for an empty slot).  Call c (c = 1, 2, ...) touches a set of keys:
+    1. every touched key already in a slot is a hit: that slot's stamp becomes c;
+    2. the missing keys, in increasing key order, take the slots not used by call c
+       in increasing (stamp, slot index) order -- empty slots first (stamp 0), then
+       the least recently used; a slot's previous key is evicted, the new key and
+       stamp c written.
+  A call may touch at most as many keys as there are slots.
+"""
+
+
+class LRUCache:
+    def __init__(self, n_slots):
+        self.n = n_slots
+        self.key = [-1] * n_slots          # slot -> key (-1: empty)
+        self.stamp = [0] * n_slots         # slot -> last call that used it
+        self.clock = 0
+        self.hits = 0
+        self.misses = 0
+
+    def where(self, k):
+        for s in range(self.n):
+            if self.key[s] == k:
+                return s
+        return -1
+
+    def call(self, keys):
+        """One call touching `keys`; returns (slot of each key as a dict, hits, missed
+        keys in the order they were placed, evicted keys)."""
+        keys = sorted(set(int(k) for k in keys))
+        assert len(keys) <= self.n, "a call touches more keys than the cache has slots"
+        self.clock += 1
+        c = self.clock
+        slot_of, missing = {}, []
+        for k in keys:
+            s = self.where(k)
+            if s >= 0:
+                self.stamp[s] = c
+                slot_of[k] = s
+            else:
+                missing.append(k)
+        free = sorted((self.stamp[s], s) for s in range(self.n) if self.stamp[s] < c)
+        evicted = []
+        for k, (_, s) in zip(missing, free):
+            if self.key[s] >= 0:
+                evicted.append(self.key[s])
+            self.key[s] = k
+            self.stamp[s] = c
+            slot_of[k] = s
+        self.hits += len(keys) - len(missing)
+        self.misses += len(missing)
+        return slot_of, len(keys) - len(missing), missing, evicted

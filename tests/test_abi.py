@@ -188,3 +188,26 @@ def test_plans(lib):
     assert mq.describe(q4, 2048, 8)["path"] == mq.PATH_DECODE
     q8 = mq.make_shape(7168, 2048, 256, 2048, flags=mq.ACT_Q8)
     assert mq.workspace_size(q8, 32, 8) < mq.workspace_size(s, 32, 8)
+
+
+def test_cache_validation(lib):
+    """Expert-cache entry points: state size, and the checks made before any HIP call."""
+    assert mq.cache_state_bytes(128, 256) == 4 * (8 + 2 * 128 + 256)
+    assert mq.cache_state_bytes(0, 256) == 0 and mq.cache_state_bytes(2049, 256) == 0
+    s = mq.make_shape(7168, 2048, 256, 2048)
+    eb = mq.expert_bytes(s)
+    f = lib.moe_q2_forward_cached
+
+    def call(cache, key_base=0, T=32, shape=s):
+        return f(A, 2 * A, 3 * A, key_base, ctypes.byref(cache), 5 * A, 8, 8 * A, ctypes.byref(shape), T,
+                 None, 16 * A, 1 << 40, None, None)
+    good = mq.make_cache(64 * A, eb, 256, 256, 32 * A)
+    assert call(mq.make_cache(64 * A, eb, 128, 256, 32 * A), T=32) == mq.EUNSUPPORTED   # 256 touched > 128 slots
+    assert call(good, key_base=1) == mq.EINVAL                                         # keys beyond n_keys
+    assert call(mq.make_cache(64 * A, eb - 16, 256, 256, 32 * A)) == mq.EINVAL          # slot too small
+    assert call(mq.make_cache(64 * A, eb, 256, 256, None)) == mq.EINVAL                 # no state
+    assert call(mq.make_cache(64 * A, eb, 0, 256, 32 * A)) == mq.EINVAL
+    sv = mq.make_shape(7168, 2048, 256, 2048, flags=mq.DECODE_VALU)
+    assert call(good, shape=sv) == mq.EUNSUPPORTED
+    assert call(good, T=0) == mq.OK                                                     # empty batch
+    assert lib.moe_q2_cache_reset(None, None) == mq.EINVAL

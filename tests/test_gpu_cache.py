@@ -1,0 +1,161 @@
+"""The budgeted HBM expert cache (moe_q2_forward_cached) on the GPU: a layer whose
+routed experts live in pinned host memory gives the same bits as the layer resident
+in HBM, over a sequence of micro-batches with different routing (hits, misses and
+evictions), on the decode and prefill kernels, with one cache shared by two layers,
+and under graph capture; after every call the device's cache state (slot contents,
+stamps, key map, counters) equals the oracle's LRU simulation fed the same touched
+experts."""
+import numpy as np
+import pytest
+import torch
+
+from oracle.cache import LRUCache
+from synth import workloads as W
+from tests.gpu_util import need_gpu, make_trace, trace_np
+
+pytestmark = pytest.mark.gpu
+
+
+class _Cache:
+    def __init__(self, mq, n_slots, n_keys, slot_bytes):
+        self.slots = torch.empty(n_slots * slot_bytes, dtype=torch.uint8, device="cuda")
+        self.state = torch.empty(mq.cache_state_bytes(n_slots, n_keys) // 4, dtype=torch.int32, device="cuda")
+        self.c = mq.make_cache(self.slots, slot_bytes, n_slots, n_keys, self.state)
+        self.n_slots, self.n_keys = n_slots, n_keys
+        mq.cache_reset(self.c)
+
+    def check(self, mq, oracle):
+        st = self.state.cpu().numpy()
+        H, n = mq.CACHE_HDR, self.n_slots
+        key, stamp, key_slot = st[H:H + n], st[H + n:H + 2 * n], st[H + 2 * n:]
+        assert st[0] == oracle.clock and st[1] == oracle.hits and st[2] == oracle.misses
+        assert key.tolist() == oracle.key and stamp.tolist() == oracle.stamp
+        want = np.full(self.n_keys, -1)
+        for s, k in enumerate(oracle.key):
+            if k >= 0:
+                want[k] = s
+        assert np.array_equal(key_slot, want)
+
+
+def _host_copy(dev):
+    host = torch.empty(dev.numel(), dtype=torch.uint8, pin_memory=True)
+    host.copy_(dev)
+    torch.cuda.synchronize()
+    return host
+
+
+def _pair(mq, dl, x, T, cache, host, key_base=0, flags=0):
+    """(resident output, cached output, touched experts) of one batch."""
+    from bit_quantized_routed_amd import workload as dw
+    wl = dl.wl
+    shape = dl.shape(flags)
+    ws = dw.workspace(shape, T, wl.topk)
+    o1 = torch.zeros((T, wl.hidden), dtype=torch.float32, device="cuda")
+    o2 = torch.full((T, wl.hidden), 9.0, dtype=torch.float32, device="cuda")
+    tr = make_trace(T, wl.topk, wl.n_experts)
+    mq.forward(x, dl.router_w, dl.experts, dl.shared_w, wl.topk, o1, shape, T, router_b=dl.router_b,
+               workspace=ws)
+    mq.forward_cached(x, dl.router_w, host, key_base, cache.c, dl.shared_w, wl.topk, o2, shape, T,
+                      router_b=dl.router_b, workspace=ws, trace=tr)
+    torch.cuda.synchronize()
+    touched = np.nonzero(trace_np(tr)["counts"] > 0)[0]
+    return o1.cpu().numpy(), o2.cpu().numpy(), touched
+
+
+def test_cache_decode_sequence_matches_resident_and_lru():
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.WORKLOADS["decode32_zipf"]
+    dl = dw.DeviceLayer(wl)
+    host = _host_copy(dl.experts)
+    T, E = wl.tokens, wl.n_experts
+    cache = _Cache(mq, 128, E, wl.expert_bytes)            # half the layer's experts
+    oracle = LRUCache(128)
+    xs = dw.activations(wl, tokens=4 * T)
+    order = [0, 1, 2, 0, 3, 1, 1]                          # new batches, repeats (hits)
+    for n, b in enumerate(order):
+        x = xs[b * T:(b + 1) * T].contiguous()
+        o1, o2, touched = _pair(mq, dl, x, T, cache, host)
+        _, hits, missing, evicted = oracle.call(touched)
+        print("  [cache] call %d batch %d: touched %d, hits %d, misses %d, evicted %d"
+              % (n, b, len(touched), hits, len(missing), len(evicted)), flush=True)
+        assert np.array_equal(o1, o2), n
+        cache.check(mq, oracle)
+    assert oracle.misses > 128 and oracle.hits > 0            # evictions happened, and hits
+
+
+def test_cache_prefill_and_one_token():
+    """The prefill kernels (300 tokens: all experts touched, the cache holds the whole
+    layer) and a one-token call on the same cache."""
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.Workload("cache_e32_t300", 41, 300, 512, 32, 4, 512, 256, "bf16", 0.05)
+    dl = dw.DeviceLayer(wl)
+    host = _host_copy(dl.experts)
+    cache = _Cache(mq, 32, 32, wl.expert_bytes)
+    oracle = LRUCache(32)
+    x = dw.activations(wl)
+    assert mq.describe(dl.shape(0), 300, wl.topk)["routed_kernel"] == 2
+    for T, xx in ((300, x), (1, x[7:8].contiguous()), (300, x)):
+        o1, o2, touched = _pair(mq, dl, xx, T, cache, host)
+        oracle.call(touched)
+        assert np.array_equal(o1, o2), T
+        cache.check(mq, oracle)
+
+
+def test_cache_shared_by_two_layers():
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.WORKLOADS["tiny_stack"]
+    layers = [dw.DeviceLayer(wl, layer=l) for l in range(2)]
+    hosts = [_host_copy(l.experts) for l in layers]
+    E = wl.n_experts
+    cache = _Cache(mq, 12, 2 * E, wl.expert_bytes)        # 12 slots for 2 x 8 experts
+    oracle = LRUCache(12)
+    h = dw.layer_residual(wl, 0)
+    for step in range(3):
+        for l, (dl, host) in enumerate(zip(layers, hosts)):
+            x = h[4 * step:4 * step + 4].contiguous()
+            o1, o2, touched = _pair(mq, dl, x, 4, cache, host, key_base=l * E, flags=mq.RESIDUAL_ADD)
+            oracle.call(touched + l * E)
+            assert np.array_equal(o1, o2), (step, l)
+            cache.check(mq, oracle)
+
+
+def test_cache_under_graph_capture():
+    """A captured cached forward replays the plan and the fill each time: outputs equal
+    the resident layer's, and the state advances like the oracle's (hits only)."""
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.WORKLOADS["tiny"]
+    dl = dw.DeviceLayer(wl)
+    host = _host_copy(dl.experts)
+    T, E = wl.tokens, wl.n_experts
+    cache = _Cache(mq, 8, E, wl.expert_bytes)
+    oracle = LRUCache(8)
+    shape = dl.shape(0)
+    ws = dw.workspace(shape, T, wl.topk)
+    x = dw.activations(wl)
+    ref, o, touched = _pair(mq, dl, x, T, cache, host)
+    oracle.call(touched)
+    out = torch.zeros((T, wl.hidden), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mq.forward_cached(x, dl.router_w, host, 0, cache.c, dl.shared_w, wl.topk, out, shape, T,
+                          router_b=dl.router_b, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    oracle.call(touched)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mq.forward_cached(x, dl.router_w, host, 0, cache.c, dl.shared_w, wl.topk, out, shape, T,
+                          router_b=dl.router_b, workspace=ws)
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        oracle.call(touched)
+        assert np.array_equal(out.cpu().numpy(), ref), rep
+        cache.check(mq, oracle)
