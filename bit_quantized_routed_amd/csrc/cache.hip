@@ -8,11 +8,14 @@
 // Policy (least recently used, ties by index): a touched expert already resident
 // keeps its slot (its stamp becomes the call's clock); the missing experts, in
 // increasing key order, take the slots no touched expert uses, in increasing
-// (stamp, slot index) order -- empty slots (stamp 0) first.
+// (stamp, slot index) order -- empty slots (stamp 0) first.  Missing experts beyond
+// those slots (a call touching more experts than the budget holds) stay uncached:
+// the routed kernels read them straight from host memory for this call.
 //
 // State (int32, device): [0] clock, [1] hits, [2] misses (both cumulative),
-// [3] misses of the last call, [4] experts touched by the last call, [5..7] 0,
-// then slot_key[n_slots] (-1: empty), slot_stamp[n_slots], key_slot[n_keys] (-1: absent).
+// [3] misses of the last call, [4] experts touched by the last call, [5] misses of
+// the last call left uncached, [6] uncached misses (cumulative), [7] 0, then
+// slot_key[n_slots] (-1: empty), slot_stamp[n_slots], key_slot[n_keys] (-1: absent).
 #include "common.h"
 #include "kernels.h"
 
@@ -39,8 +42,9 @@ int mq_launch_cache_reset(int32_t *state, int n_slots, int n_keys, hipStream_t s
 }
 
 // One work-group.  counts: slots per expert of this call (E <= MQ_CACHE_THREADS);
-// out: eslot[e] (the slot of each touched expert, -1 otherwise), the miss list
-// (expert, slot) in increasing expert order and its length.
+// out: eslot[e] (the slot of each touched expert; -1 for an expert not touched or
+// read from host memory), the list (expert, slot) of the misses to copy, in
+// increasing expert order, and its length.
 __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *__restrict__ counts, int E,
                                                                 int key_base, int32_t *__restrict__ state,
                                                                 int n_slots, int n_keys,
@@ -96,7 +100,8 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
     for (int w = 0; w < MQ_CACHE_THREADS / 64; ++w) nm += s_wsum[w];
     s_miss[tid] = miss ? base + r - 1 : -1;
     // 3. the slots no touched expert uses, ranked by (stamp, slot index); the first
-    // nm of them are the victims, victim i taken by the miss of rank i
+    // nm of them are the victims, victim i taken by the miss of rank i (misses of rank
+    // at or past the number of such slots stay uncached)
     for (int s = tid; s < n_slots; s += MQ_CACHE_THREADS) {
         const int32_t st = s_stamp[s];
         if (st < clock) {
@@ -110,20 +115,26 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
     }
     __syncthreads();
     // 4. evictions (the victims' old keys), then the new keys; all keys distinct
-    if (tid < E && s_miss[tid] >= 0) {
+    const int free_slots = n_slots - s_hits;             // slots no touched expert uses
+    const int nfill = min(nm, free_slots);
+    if (tid < E && s_miss[tid] >= 0 && s_miss[tid] < nfill) {
         const int v = s_victim[s_miss[tid]];
         const int32_t old = v >= 0 ? s_key[v] : -1;
         if (old >= 0 && old < n_keys) key_slot[old] = -1;
     }
     __syncthreads();
-    if (tid < E && s_miss[tid] >= 0) {
+    if (tid < E && s_miss[tid] >= 0 && s_miss[tid] < nfill) {
         const int i = s_miss[tid];
-        const int v = max(s_victim[i], 0);       // always a victim when n_slots >= the touched experts
-        key_slot[key_base + tid] = v;
-        s_key[v] = key_base + tid;
-        s_stamp[v] = clock;
-        eslot[tid] = v;
-        misses[i] = make_int2(tid, v);
+        const int v = s_victim[i];
+        if (v >= 0) {                                    // always, for a state made by the reset
+            key_slot[key_base + tid] = v;
+            s_key[v] = key_base + tid;
+            s_stamp[v] = clock;
+            eslot[tid] = v;
+            misses[i] = make_int2(tid, v);
+        } else {
+            misses[i] = make_int2(tid, -1);              // skipped by the copy
+        }
     }
     __syncthreads();
     for (int s = tid; s < n_slots; s += MQ_CACHE_THREADS) {
@@ -136,7 +147,9 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
         state[2] += nm;
         state[3] = nm;
         state[4] = s_hits + nm;
-        *n_miss = nm;
+        state[5] = nm - nfill;
+        state[6] += nm - nfill;
+        *n_miss = nfill;
     }
 }
 
@@ -161,8 +174,8 @@ __global__ void __launch_bounds__(256) k_cache_fill(const uint8_t *__restrict__ 
     const int64_t total = (int64_t)(*n_miss) * cpe;
     for (int64_t c = blockIdx.x; c < total; c += gridDim.x) {
         const int64_t i = c / cpe, off = (c - i * cpe) * MQ_FILL_CHUNK + 16 * (int64_t)threadIdx.x;
-        if (off < expert_bytes) {
-            const int2 m = misses[i];
+        const int2 m = misses[i];
+        if (off < expert_bytes && m.y >= 0) {
             const mq_u32x4 v = *(const mq_u32x4 *)(host + (int64_t)m.x * expert_bytes + off);
             *(mq_u32x4 *)(slots + (int64_t)m.y * slot_bytes + off) = v;
         }

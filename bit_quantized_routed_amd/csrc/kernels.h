@@ -140,10 +140,14 @@ struct MqDownPrep {
 // route (gate/up only, optional): route in the launch instead of reading units/urow.
 // Format of one routed launch: activation digits (2: 15-bit, 1: Q8), weight block
 // dwords (21: 2-bit codec, 37: 4-bit sibling) and the optional expert -> slot table
-// of an expert cache (null: expert e at experts + e * expert_bytes).
+// of an expert cache (null: expert e at experts + e * expert_bytes; else slot
+// eslot[e] >= 0 at experts + slot * expert_bytes, and eslot[e] < 0 means host
+// memory: host + e * host_bytes).
 struct MqFormat {
     int nd, bd;
     const int32_t *eslot;
+    const void *host;
+    int64_t host_bytes;
 };
 // split_units: the unit count the k-split policy is computed for (max_units, or a
 // fixed count when the split must not depend on the batch).

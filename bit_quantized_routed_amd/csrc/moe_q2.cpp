@@ -536,8 +536,10 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
         return rc;
     }
     const int64_t mat_gu = (int64_t)I * (H / MQ_QK) * (int64_t)gu_block_bytes(s);   // bytes of gate (or up)
-    const MqFormat fgu = {w.nd, (s->flags & MOE_Q2_GU_Q4) ? MQ_BD4 : MQ_BD2, eslot};   // after the cache plan
-    const MqFormat fdn = {w.nd, (s->flags & MOE_Q2_DOWN_Q4) ? MQ_BD4 : MQ_BD2, eslot};
+    const void *hcopy = cache ? cache->host : nullptr;
+    const int64_t hbytes = (int64_t)moe_q2_expert_bytes(s);
+    const MqFormat fgu = {w.nd, (s->flags & MOE_Q2_GU_Q4) ? MQ_BD4 : MQ_BD2, eslot, hcopy, hbytes};
+    const MqFormat fdn = {w.nd, (s->flags & MOE_Q2_DOWN_Q4) ? MQ_BD4 : MQ_BD2, eslot, hcopy, hbytes};
     float *h = (float *)(ws + w.h);
     float *y = (float *)(ws + w.y);
     uint32_t *hq = (uint32_t *)(ws + w.hq);
@@ -661,8 +663,6 @@ extern "C" int moe_q2_forward_cached(const void *x, const float *router_w, const
     const int64_t E = s->n_experts;
     if (key_base < 0 || key_base + E > cache->n_keys) return MOE_Q2_EINVAL;
     if (cache->slot_bytes < (int64_t)moe_q2_expert_bytes(s)) return MOE_Q2_EINVAL;
-    const int64_t touched_max = std::min<int64_t>(E, (int64_t)n_tokens * topk);
-    if (cache->n_slots < touched_max) return MOE_Q2_EUNSUPPORTED;
     if (n_tokens == 0) return MOE_Q2_OK;
     // the host copy must be pinned memory the device can read (a host query; pageable
     // memory would fault the kernels that read it)

@@ -234,8 +234,9 @@ int moe_q2_forward(const void *x, const float *router_w, const void *experts_q2,
  * device after the bucketing: no host synchronisation, capturable in a HIP graph.
  * The caller owns every buffer; calls that share a cache must be ordered on one stream.
  * state (int32, device): [0] calls, [1] hits, [2] misses (cumulative), [3] misses and
- * [4] touched experts of the last call, [5..7] 0, then slot_key[n_slots] (-1: empty),
- * slot_stamp[n_slots] (last call that used the slot), key_slot[n_keys] (-1: absent). */
+ * [4] touched experts of the last call, [5] misses of the last call read from host
+ * memory uncached, [6] such misses (cumulative), [7] 0, then slot_key[n_slots] (-1:
+ * empty), slot_stamp[n_slots] (last call that used the slot), key_slot[n_keys] (-1: absent). */
 #define MOE_Q2_CACHE_MAX_SLOTS 2048
 typedef struct {
     void    *slots;       /* device, n_slots * slot_bytes, 16-byte aligned: the budget */
@@ -257,9 +258,10 @@ int moe_q2_cache_reset(const moe_q2_cache *cache, void *stream);
  *                 tensor); checked with hipPointerGetAttributes, EINVAL for other memory
  *   key_base      the layer's first key: expert e has key key_base + e (key_base >= 0,
  *                 key_base + E <= n_keys)
- * Needs n_slots >= min(E, n_tokens * topk) (every touched expert resident at once);
- * not with MOE_Q2_DECODE_VALU.  The results are those of moe_q2_forward on the same
- * experts resident in HBM, bit for bit.  The workspace is moe_q2_workspace_size's. */
+ * A call that touches more missing experts than the slots its hits leave free caches
+ * the first ones (in key order) and reads the rest straight from host memory for that
+ * call.  Not with MOE_Q2_DECODE_VALU.  The results are those of moe_q2_forward on the
+ * same experts resident in HBM, bit for bit.  The workspace is moe_q2_workspace_size's. */
 int moe_q2_forward_cached(const void *x, const float *router_w, const void *host_experts, int32_t key_base,
                           const moe_q2_cache *cache, const uint16_t *shared_w, int32_t topk, float *out,
                           const moe_q2_shape *s, int32_t n_tokens, const float *router_b,

@@ -15,8 +15,9 @@ least-recently-used over a fixed number of slots, with every tie broken by index
     2. the missing keys, in increasing key order, take the slots not used by call c
        in increasing (stamp, slot index) order -- empty slots first (stamp 0), then
        the least recently used; a slot's previous key is evicted, the new key and
-       stamp c written.
-  A call may touch at most as many keys as there are slots.
+       stamp c written;
+    3. missing keys beyond those slots (a call touching more keys than the budget
+       holds) stay uncached: read from their home for this call only.
 """
 
 
@@ -28,6 +29,7 @@ class LRUCache:
         self.clock = 0
         self.hits = 0
         self.misses = 0
+        self.uncached = 0
 
     def where(self, k):
         for s in range(self.n):
@@ -36,10 +38,9 @@ class LRUCache:
         return -1
 
     def call(self, keys):
-        """One call touching `keys`; returns (slot of each key as a dict, hits, missed
-        keys in the order they were placed, evicted keys)."""
+        """One call touching `keys`; returns (slot of each cached key as a dict, hits,
+        missed keys in increasing order (placed first, then the uncached), evicted keys)."""
         keys = sorted(set(int(k) for k in keys))
-        assert len(keys) <= self.n, "a call touches more keys than the cache has slots"
         self.clock += 1
         c = self.clock
         slot_of, missing = {}, []
@@ -60,4 +61,6 @@ class LRUCache:
             slot_of[k] = s
         self.hits += len(keys) - len(missing)
         self.misses += len(missing)
+        self.uncached += max(0, len(missing) - len(free))
+        self.last_uncached = max(0, len(missing) - len(free))
         return slot_of, len(keys) - len(missing), missing, evicted

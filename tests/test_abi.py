@@ -202,7 +202,7 @@ def test_cache_validation(lib):
         return f(A, 2 * A, 3 * A, key_base, ctypes.byref(cache), 5 * A, 8, 8 * A, ctypes.byref(shape), T,
                  None, 16 * A, 1 << 40, None, None)
     good = mq.make_cache(64 * A, eb, 256, 256, 32 * A)
-    assert call(mq.make_cache(64 * A, eb, 128, 256, 32 * A), T=32) == mq.EUNSUPPORTED   # 256 touched > 128 slots
+    assert call(good) == mq.EINVAL          # host_experts not pinned host memory: refused by the pointer query
     assert call(good, key_base=1) == mq.EINVAL                                         # keys beyond n_keys
     assert call(mq.make_cache(64 * A, eb - 16, 256, 256, 32 * A)) == mq.EINVAL          # slot too small
     assert call(mq.make_cache(64 * A, eb, 256, 256, None)) == mq.EINVAL                 # no state

@@ -29,6 +29,7 @@ class _Cache:
         H, n = mq.CACHE_HDR, self.n_slots
         key, stamp, key_slot = st[H:H + n], st[H + n:H + 2 * n], st[H + 2 * n:]
         assert st[0] == oracle.clock and st[1] == oracle.hits and st[2] == oracle.misses
+        assert st[5] == oracle.last_uncached and st[6] == oracle.uncached
         assert key.tolist() == oracle.key and stamp.tolist() == oracle.stamp
         want = np.full(self.n_keys, -1)
         for s, k in enumerate(oracle.key):
@@ -51,7 +52,8 @@ def _pair(mq, dl, x, T, cache, host, key_base=0, flags=0):
     shape = dl.shape(flags)
     ws = dw.workspace(shape, T, wl.topk)
     o1 = torch.zeros((T, wl.hidden), dtype=torch.float32, device="cuda")
-    o2 = torch.full((T, wl.hidden), 9.0, dtype=torch.float32, device="cuda")
+    # (unwritten outputs would keep 9.0; under RESIDUAL_ADD both start from zero)
+    o2 = torch.full((T, wl.hidden), 0.0 if flags & mq.RESIDUAL_ADD else 9.0, dtype=torch.float32, device="cuda")
     tr = make_trace(T, wl.topk, wl.n_experts)
     mq.forward(x, dl.router_w, dl.experts, dl.shared_w, wl.topk, o1, shape, T, router_b=dl.router_b,
                workspace=ws)
@@ -100,6 +102,28 @@ def test_cache_prefill_and_one_token():
         o1, o2, touched = _pair(mq, dl, xx, T, cache, host)
         oracle.call(touched)
         assert np.array_equal(o1, o2), T
+        cache.check(mq, oracle)
+
+
+def test_cache_smaller_than_a_call():
+    """A budget of 8 slots for calls touching ~60 experts: the first misses in key
+    order are cached, the rest read straight from host memory by the routed kernels;
+    the outputs are still the resident layer's bits."""
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.Workload("cache_e64_t24", 42, 24, 512, 64, 6, 512, 256, "bf16", 0.05, zipf=True)
+    dl = dw.DeviceLayer(wl)
+    host = _host_copy(dl.experts)
+    cache = _Cache(mq, 8, 64, wl.expert_bytes)
+    oracle = LRUCache(8)
+    xs = dw.activations(wl, tokens=48)
+    for b in (0, 1, 0):
+        x = xs[24 * b:24 * (b + 1)].contiguous()
+        o1, o2, touched = _pair(mq, dl, x, 24, cache, host)
+        oracle.call(touched)
+        print("  [cache] small budget: touched %d, uncached %d" % (len(touched), oracle.last_uncached), flush=True)
+        assert oracle.last_uncached > 0
+        assert np.array_equal(o1, o2), b
         cache.check(mq, oracle)
 
 

@@ -48,6 +48,13 @@ def test_invariants_random_calls():
         assert all(c.stamp[slot_of[k]] == c.clock for k in keys)
 
 
-def test_too_many_keys_rejected():
-    with pytest.raises(AssertionError):
-        LRUCache(2).call([1, 2, 3])
+def test_more_keys_than_free_slots_stay_uncached():
+    # 3 slots hold 1, 2, 3; call {2, 4, 5, 6}: 2 hits (slot 1), the two free slots
+    # (0 then 2, both stamp 1) take 4 and 5 in key order, 6 stays uncached.
+    c = LRUCache(3)
+    c.call([1, 2, 3])
+    slot_of, hits, missing, evicted = c.call([2, 4, 5, 6])
+    assert slot_of == {2: 1, 4: 0, 5: 2} and hits == 1 and missing == [4, 5, 6]
+    assert evicted == [1, 3] and c.key == [4, 2, 5] and (c.uncached, c.last_uncached) == (1, 1)
+    c.call([7, 8, 9, 10, 11])                        # all miss: 3 placed, 2 uncached
+    assert c.key == [7, 8, 9] and c.uncached == 3
