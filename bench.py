@@ -32,6 +32,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_INT8_PEAK_TOPS = 5000.0
+PCIE_PEAK_GBS = 64.0            # PCIe 5.0 x16, one direction, nominal
 EXPERT_BYTES_FULL = 14_450_688
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (2-bit experts), decode and prefill"
 
@@ -42,7 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", default="decode1")
-    ap.add_argument("--extra", default="decode32_zipf,prefill2048,stack40_t64_zipf",
+    ap.add_argument("--extra", default="decode32_zipf,prefill2048,stack40_t64_zipf,verify96_zipf:bi,"
+                                       "stack40_q2q4,decode32_zipf:q8,prefill2048:q8,decode32_zipf:cache",
                     help="comma-separated extra workloads reported in the same line ('' for none)")
     ap.add_argument("--rotate", type=int, default=8, help="distinct layers cycled by decode steps")
     ap.add_argument("--cpu-baseline", type=int, default=1)
@@ -87,12 +90,24 @@ def traffic_record(kernel):
     return rec
 
 
-def run_workload(name, steps, warmup, rotate, graph=True):
+# Row options: "name:q8" (Q8 activations), "name:bi" (batch-invariant mode).
+ROW_FLAGS = {"": 0, "q8": 128, "bi": 64}
+
+
+def matrix_bytes(wl, layer):
+    """(gate + up, down) bytes of one routed expert of a layer (formats per layer)."""
+    nb = wl.hidden * wl.inter // 256
+    gu4, dn4 = wl.q4_at(layer)
+    return 2 * nb * (148 if gu4 else 84), nb * (148 if dn4 else 84)
+
+
+def run_workload(spec, steps, warmup, rotate, graph=True):
     import torch
     import bit_quantized_routed_amd as mq
     from bit_quantized_routed_amd import workload as dw
     from synth import workloads as W
 
+    name, _, opt = spec.partition(":")
     wl = W.WORKLOADS[name]
     L = wl.layers if wl.layers > 1 else rotate
     t0 = time.time()
@@ -100,11 +115,12 @@ def run_workload(name, steps, warmup, rotate, graph=True):
     layers = [dw.DeviceLayer(wl, layer=l, tmp=tmp) for l in range(L)]
     del tmp
     torch.cuda.synchronize()
-    log("[bench] %s: %d layer(s) generated in %.1fs" % (name, L, time.time() - t0))
+    log("[bench] %s: %d layer(s) generated in %.1fs" % (spec, L, time.time() - t0))
     T, K, E = wl.tokens, wl.topk, wl.n_experts
-    flags = mq.RESIDUAL_ADD if wl.rmsnorm else 0
-    shape = layers[0].shape(flags)
-    ws = dw.workspace(shape, T, K)
+    flags = (mq.RESIDUAL_ADD if wl.rmsnorm else 0) | ROW_FLAGS[opt]
+    shapes = [layer.shape(flags) for layer in layers]        # per layer: the weight formats
+    shape = shapes[0]
+    ws = torch.empty(max(mq.workspace_size(sh, T, K) for sh in shapes), dtype=torch.uint8, device="cuda")
     x = dw.activations(wl)
     out = x if wl.rmsnorm else torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")
     counts = [torch.zeros(E, dtype=torch.int32, device="cuda") for _ in range(L)]
@@ -115,7 +131,7 @@ def run_workload(name, steps, warmup, rotate, graph=True):
         tr = {"counts": counts[l]}
         if events is not None:
             tr["events"] = events
-        mq.forward(x, layers[l].router_w, layers[l].experts, layers[l].shared_w, K, out, shape, T,
+        mq.forward(x, layers[l].router_w, layers[l].experts, layers[l].shared_w, K, out, shapes[l], T,
                    router_b=layers[l].router_b, workspace=ws, trace=tr)
 
     def step(i, evs=None):
@@ -214,9 +230,14 @@ def run_workload(name, steps, warmup, rotate, graph=True):
     d_mean = float(np.mean(touched))
     passes = L if stack else 1
     tokens_per_step = T * (1 if not stack else 1)
-    bytes_per_pass = layer_bytes(wl, d_mean)
+    mb = [matrix_bytes(wl, l) for l in range(L)]
+    # routed bytes per pass, averaged over the rotated (or stacked) layers
+    routed_gu = float(np.mean([t * m[0] for t, m in zip(touched, mb)]))
+    routed_dn = float(np.mean([t * m[1] for t, m in zip(touched, mb)]))
+    bytes_per_pass = layer_bytes(wl, 0) + routed_gu + routed_dn
     res = {
-        "workload": name, "tokens": T, "layers_in_step": passes, "layers_resident": L,
+        "workload": spec, "tokens": T, "layers_in_step": passes, "layers_resident": L,
+        "flags": flags,
         "ms_per_step": ms_per_step, "eager_ms_per_step": eager_ms, "launch": launch,
         "tokens_per_s": tokens_per_step / (ms_per_step * 1e-3),
         "layer_tokens_per_s": T * passes / (ms_per_step * 1e-3),
@@ -230,25 +251,29 @@ def run_workload(name, steps, warmup, rotate, graph=True):
     # dominant kernel roofline (duration from the timed region's events); on the
     # matrix-core decode path with a bf16 layer input the routed launches also
     # stream the shared expert's gate/up and down rows
-    gu_bytes = d_mean * 2 * (wl.expert_bytes // 3)
-    dn_bytes = d_mean * (wl.expert_bytes // 3)
+    gu_bytes = routed_gu
+    dn_bytes = routed_dn
     if T < 256 and wl.shared_inter and (wl.act == "bf16" or wl.rmsnorm):
         gu_bytes += 2 * wl.shared_inter * wl.hidden * 2
         dn_bytes += wl.shared_inter * wl.hidden * 2
     kbytes = {"gate_up": gu_bytes + T * wl.hidden * 2.5 + T * K * wl.inter * 4,
               "down": dn_bytes + T * K * wl.inter * 2.5 + T * K * wl.hidden * 4,
               "shared": 3 * wl.shared_inter * wl.hidden * 2}.get(dom)
-    prefill = T >= 256
+    prefill = mq.describe(shape, T, K)["path"] == mq.PATH_PREFILL
     if prefill:
-        # useful MACs x 2 against the dense bf16 MFMA peak (the integer path issues two
-        # int8 MACs per useful MAC, i.e. the same fraction of the int8 peak)
+        # useful MACs x 2 against the dense MFMA peak of the arithmetic: the default path
+        # issues two int8 MACs per useful MAC on units twice the bf16 rate (the same
+        # fraction of the bf16 peak as of the int8 peak); Q8 issues one int8 MAC per
+        # useful MAC, against the int8 peak
+        q8 = bool(flags & mq.ACT_Q8)
+        peak = MFMA_INT8_PEAK_TOPS if q8 else MFMA_BF16_PEAK_TFLOPS
         kflops = {"gate_up": T * K * 2 * wl.inter * wl.hidden * 2,
                   "down": T * K * wl.hidden * wl.inter * 2,
                   "shared": T * 3 * wl.shared_inter * wl.hidden * 2}[dom]
         ach = kflops / (dom_avg * 1e-3) / 1e12
         res["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1),
-                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                           "peak": peak, "unit": "TOP/s (int8)" if q8 else "TFLOP/s",
+                           "frac": round(ach / peak, 4), "traffic": None,
                            "algorithmic_flops_per_launch": kflops, "avg_launch_ms": dom_avg}
         res["useful_tflops"] = (T * K * 3 * wl.inter * wl.hidden * 2 +
                                 T * 3 * wl.shared_inter * wl.hidden * 2) / (ms_per_step * 1e-3) / 1e12
@@ -272,6 +297,81 @@ def run_workload(name, steps, warmup, rotate, graph=True):
     res["_gpu_first_tokens"] = {"out": o0[:npar].cpu().numpy().astype(np.float64),
                                 "idx": ti[:npar].cpu().numpy()}
     del layers, ws, x0, o0
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_cached(spec, steps, warmup, budget=0.5, n_batches=64):
+    """A layer whose routed experts live in pinned host memory behind an HBM expert
+    cache of `budget` x E slots (moe_q2_forward_cached), fed a stream of distinct
+    micro-batches (n_batches batches of the workload's token count, cycled), so the
+    routing -- and with it the hits and misses -- changes from step to step as in a
+    serving loop.  Eager timing; the same stream through the resident layer is timed
+    alongside.  Reported: step time, hit rate, misses per step (copied into slots, or
+    read straight from host memory when the free slots run out) and the host-link
+    rate of the bytes brought over per step."""
+    import torch
+    import bit_quantized_routed_amd as mq
+    from bit_quantized_routed_amd import workload as dw
+    from synth import workloads as W
+
+    name = spec.partition(":")[0]
+    wl = W.WORKLOADS[name]
+    T, K, E = wl.tokens, wl.topk, wl.n_experts
+    dl = dw.DeviceLayer(wl)
+    eb = wl.expert_bytes
+    t0 = time.time()
+    host = torch.empty(E * eb, dtype=torch.uint8, pin_memory=True)
+    host.copy_(dl.experts)
+    torch.cuda.synchronize()
+    log("[bench] %s: %.1f GB of experts in pinned host memory (%.1fs)" % (spec, E * eb / 1e9, time.time() - t0))
+    n_slots = int(E * budget)
+    slots = torch.empty(n_slots * eb, dtype=torch.uint8, device="cuda")
+    state = torch.empty(mq.cache_state_bytes(n_slots, E) // 4, dtype=torch.int32, device="cuda")
+    cache = mq.make_cache(slots, eb, n_slots, E, state)
+    mq.cache_reset(cache)
+    shape = dl.shape(0)
+    ws = dw.workspace(shape, T, K)
+    xs = dw.activations(wl, tokens=T * n_batches)
+    out = torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")
+
+    def cached(i):
+        b = i % n_batches
+        mq.forward_cached(xs[b * T:(b + 1) * T], dl.router_w, host, 0, cache, dl.shared_w, K, out, shape, T,
+                          router_b=dl.router_b, workspace=ws)
+
+    def resident(i):
+        b = i % n_batches
+        mq.forward(xs[b * T:(b + 1) * T], dl.router_w, dl.experts, dl.shared_w, K, out, shape, T,
+                   router_b=dl.router_b, workspace=ws)
+
+    def timed(fn, first):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(first, first + steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t1) * 1e3 / steps
+
+    for i in range(warmup):
+        cached(i)
+    st0 = state[:8].cpu().numpy().astype(np.int64)
+    ms = timed(cached, warmup)
+    st1 = state[:8].cpu().numpy().astype(np.int64)
+    for i in range(warmup):
+        resident(i)
+    ms_res = timed(resident, warmup)
+    hits, misses, unc = (st1[1] - st0[1]) / steps, (st1[2] - st0[2]) / steps, (st1[6] - st0[6]) / steps
+    host_bytes = misses * eb            # copied once, or read once by the routed kernels
+    res = {"workload": spec, "tokens": T, "budget_experts": n_slots, "budget_bytes": n_slots * eb,
+           "experts_per_layer": E, "launch": "eager", "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+           "resident_ms_per_step": ms_res, "hit_rate": hits / max(hits + misses, 1e-9),
+           "touched_per_step": hits + misses, "misses_per_step": misses, "uncached_per_step": unc,
+           "host_bytes_per_step": host_bytes, "host_link_gbs": host_bytes / (ms * 1e-3) / 1e9,
+           "host_link_peak_gbs": PCIE_PEAK_GBS,
+           "note": "distinct %d-token batches cycled (%d), experts homed in pinned host memory, %d of %d "
+                   "experts' slots in HBM" % (T, n_batches, n_slots, E)}
+    del dl, host, slots, xs, ws
     torch.cuda.empty_cache()
     return res
 
@@ -403,7 +503,10 @@ def main():
     head = run_workload(args.workload, args.steps, args.warmup, args.rotate, bool(args.graph))
     extras = {}
     for name in [n for n in args.extra.split(",") if n and n != args.workload]:
-        extras[name] = run_workload(name, args.steps, args.warmup, args.rotate, bool(args.graph))
+        if name.endswith(":cache"):
+            extras[name] = run_cached(name, args.steps, args.warmup)
+        else:
+            extras[name] = run_workload(name, args.steps, args.warmup, args.rotate, bool(args.graph))
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -423,7 +526,8 @@ def main():
     if args.cpu_baseline:
         cpu = cpu_baseline(args.workload, head.pop("_gpu_first_tokens", None))
         for k, v in extras.items():
-            v["cpu_baseline"] = cpu_baseline(k, v.pop("_gpu_first_tokens", None))
+            if k in CPU_PROTOCOL:           # the oracle's time does not depend on the row options
+                v["cpu_baseline"] = cpu_baseline(k, v.pop("_gpu_first_tokens", None))
     head.pop("_gpu_first_tokens", None)
     for v in extras.values():
         v.pop("_gpu_first_tokens", None)

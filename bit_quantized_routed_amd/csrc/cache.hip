@@ -42,13 +42,15 @@ int mq_launch_cache_reset(int32_t *state, int n_slots, int n_keys, hipStream_t s
 }
 
 // One work-group.  counts: slots per expert of this call (E <= MQ_CACHE_THREADS);
-// out: eslot[e] (the slot of each touched expert; -1 for an expert not touched or
-// read from host memory), the list (expert, slot) of the misses to copy, in
-// increasing expert order, and its length.
+// out: eptr[e], the address the routed kernels read touched expert e from (its slot
+// in `slots`, or host + e * host_bytes for a miss left uncached), the list (expert,
+// slot) of the misses to copy, in increasing expert order, and its length.
 __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *__restrict__ counts, int E,
                                                                 int key_base, int32_t *__restrict__ state,
                                                                 int n_slots, int n_keys,
-                                                                int32_t *__restrict__ eslot,
+                                                                const uint8_t *slots, int64_t slot_bytes,
+                                                                const uint8_t *host, int64_t host_bytes,
+                                                                uint64_t *__restrict__ eptr,
                                                                 int2 *__restrict__ misses,
                                                                 int32_t *__restrict__ n_miss) {
     __shared__ int32_t s_stamp[MOE_Q2_CACHE_MAX_SLOTS], s_key[MOE_Q2_CACHE_MAX_SLOTS];
@@ -83,7 +85,7 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
                 miss = 1;
             }
         }
-        eslot[tid] = sl;
+        eptr[tid] = (uint64_t)(sl >= 0 ? slots + (int64_t)sl * slot_bytes : host + (int64_t)tid * host_bytes);
     }
     // 2. rank of each miss among the misses, in expert order (work-group scan)
     int r = miss;
@@ -130,7 +132,7 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
             key_slot[key_base + tid] = v;
             s_key[v] = key_base + tid;
             s_stamp[v] = clock;
-            eslot[tid] = v;
+            eptr[tid] = (uint64_t)(slots + (int64_t)v * slot_bytes);
             misses[i] = make_int2(tid, v);
         } else {
             misses[i] = make_int2(tid, -1);              // skipped by the copy
@@ -154,10 +156,12 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
 }
 
 int mq_launch_cache_plan(const int32_t *counts, int E, int key_base, int32_t *state, int n_slots, int n_keys,
-                         int32_t *eslot, int2 *misses, int32_t *n_miss, hipStream_t st) {
+                         const void *slots, int64_t slot_bytes, const void *host, int64_t host_bytes,
+                         uint64_t *eptr, int2 *misses, int32_t *n_miss, hipStream_t st) {
     if (E > MQ_CACHE_THREADS || n_slots > MOE_Q2_CACHE_MAX_SLOTS) return MOE_Q2_EUNSUPPORTED;
     hipLaunchKernelGGL(k_cache_plan, dim3(1), dim3(MQ_CACHE_THREADS), 0, st, counts, E, key_base, state, n_slots,
-                       n_keys, eslot, misses, n_miss);
+                       n_keys, (const uint8_t *)slots, slot_bytes, (const uint8_t *)host, host_bytes, eptr, misses,
+                       n_miss);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

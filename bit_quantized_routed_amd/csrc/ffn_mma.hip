@@ -584,8 +584,7 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
                                                 float *__restrict__ out1, int out_ld, int64_t split_stride,
                                                 int q2_grid, const MqDense dn, const MqRoute rt,
                                                 int route_on, const MqDownPrep pp, int prep_on,
-                                                const int32_t *__restrict__ eslot, const uint8_t *host,
-                                                int64_t host_bytes) {
+                                                const uint64_t *__restrict__ eptr) {
     constexpr int NLD = mq_bcol<BD>::NLD, NA = DM_AITEMS(ND), NIT = (NA + 255) / 256;
     __shared__ __attribute__((aligned(16))) mq_u32x4 sW[4][64 * NLD];      // weight slices, one per wave
     static_assert(sizeof(MqRouteLds) <= sizeof(sW), "routing LDS fits the weight slices");
@@ -628,9 +627,8 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
     }
     const int p0 = un.y, nt = un.z;
     if (nt == 0) return;                                 // past the last unit
-    // the expert's bytes: resident, in a cache slot, or (an uncached miss) in host memory
-    const int sl = eslot ? eslot[un.x] : un.x;
-    const uint8_t *eb = sl >= 0 ? experts + (int64_t)sl * expert_bytes : host + (int64_t)un.x * host_bytes;
+    // the expert's bytes: resident, or where an expert cache's plan put it
+    const uint8_t *eb = eptr ? (const uint8_t *)eptr[un.x] : experts + (int64_t)un.x * expert_bytes;
     const int tile = 4 * tg + wv;
     const int G = kblocks * 16;
     const int64_t tile_bytes = (int64_t)kblocks * 64 * BD * 4;
@@ -804,8 +802,7 @@ int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t e
     MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma<GUV, NDV, BDV>), dim3((unsigned)grid), dim3(256), 0, st,          \
                     (const uint8_t *)experts, expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units, urow, \
                     zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld, split_stride,  \
-                    (int)q2_grid, dn, rt, route_on, pp, prep_on, fmt.eslot, (const uint8_t *)fmt.host,       \
-                    fmt.host_bytes)
+                    (int)q2_grid, dn, rt, route_on, pp, prep_on, fmt.eptr)
     const int sel = (gu ? 4 : 0) + (fmt.nd == 2 ? 2 : 0) + (fmt.bd == MQ_BD4 ? 1 : 0);
     switch (sel) {
     case 0: MQ_Q2_MMA_LAUNCH(false, 1, MQ_BD2); break;
@@ -912,8 +909,7 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                                                    const mq_u32x4 *__restrict__ xdig,
                                                    const uint32_t *__restrict__ xsum,
                                                    const float *__restrict__ xscale,
-                                                   float *__restrict__ out, const int32_t *__restrict__ eslot,
-                                                   const uint8_t *host, int64_t host_bytes) {
+                                                   float *__restrict__ out, const uint64_t *__restrict__ eptr) {
     constexpr int NTOK = 16 * MF;
     constexpr int WPT = 16 * ND;                        // 16-byte digit words per token and column
     constexpr int TPL = 64 / WPT;                       // tokens per 1 KB digit load
@@ -1017,9 +1013,8 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
         const int e = un.x, p0 = un.y, nt = un.z;
         const int *arow_s = arow_b + (k & 1) * NTOK;
         int *arow_n = arow_b + ((k + 1) & 1) * NTOK;
-        const int sl = eslot ? eslot[e] : e;             // resident, cache slot, or host memory
-        const uint8_t *tb = (sl >= 0 ? experts + (int64_t)sl * expert_bytes : host + (int64_t)e * host_bytes) +
-                            mat_off + (int64_t)(4 * st) * tile_bytes;
+        const uint8_t *tb = (eptr ? (const uint8_t *)eptr[e] : experts + (int64_t)e * expert_bytes) + mat_off +
+                            (int64_t)(4 * st) * tile_bytes;
         // the next item; from 3 columns on, its rows are written in column kblocks - 2
         // (every wave is past the previous item's outputs, which read that half, once
         // column 0's barrier is behind it) and its first column staged in the last one
@@ -1027,8 +1022,7 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
         const bool has_next = wn < nitems;
         const int4 unn = has_next ? units[wn / stiles] : make_int4(0, 0, 1, 0);
         const int stn = wn - (wn / stiles) * stiles;
-        const int sln = eslot && has_next ? eslot[unn.x] : unn.x;
-        const uint8_t *tbn = (sln >= 0 ? experts + (int64_t)sln * expert_bytes : host + (int64_t)unn.x * host_bytes) +
+        const uint8_t *tbn = (eptr && has_next ? (const uint8_t *)eptr[unn.x] : experts + (int64_t)unn.x * expert_bytes) +
                              mat_off + (int64_t)(4 * stn) * tile_bytes;
         const int mfcn = (unn.z + 15) >> 4;
         const bool chain = has_next && kblocks >= 3;
@@ -1167,8 +1161,7 @@ int mq_launch_q2_mma_pf(int swiglu, const MqFormat &fmt, const void *experts, in
 #define MQ_PF_LAUNCH(SW, NDV)                                                                           \
     MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma_pf<SW, PF_MF, NDV>), dim3(grid), dim3(512), 0, st,               \
                     (const uint8_t *)experts, expert_bytes, mat_off, rows, kblocks, units_hdr, units, perm, \
-                    topk, (const mq_u32x4 *)xdig, xsum, xscale, out, fmt.eslot, (const uint8_t *)fmt.host, \
-                    fmt.host_bytes)
+                    topk, (const mq_u32x4 *)xdig, xsum, xscale, out, fmt.eptr)
     if (swiglu) {
         if (fmt.nd == 2) MQ_PF_LAUNCH(true, 2); else MQ_PF_LAUNCH(true, 1);
     } else {

@@ -139,15 +139,12 @@ struct MqDownPrep {
 // the [max_units][16] row table of the bucketing; down reads the rows of its slots.
 // route (gate/up only, optional): route in the launch instead of reading units/urow.
 // Format of one routed launch: activation digits (2: 15-bit, 1: Q8), weight block
-// dwords (21: 2-bit codec, 37: 4-bit sibling) and the optional expert -> slot table
-// of an expert cache (null: expert e at experts + e * expert_bytes; else slot
-// eslot[e] >= 0 at experts + slot * expert_bytes, and eslot[e] < 0 means host
-// memory: host + e * host_bytes).
+// dwords (21: 2-bit codec, 37: 4-bit sibling) and the optional table of expert
+// addresses written by an expert cache's plan (null: expert e at
+// experts + e * expert_bytes; else at eptr[e], a cache slot or host memory).
 struct MqFormat {
     int nd, bd;
-    const int32_t *eslot;
-    const void *host;
-    int64_t host_bytes;
+    const uint64_t *eptr;
 };
 // split_units: the unit count the k-split policy is computed for (max_units, or a
 // fixed count when the split must not depend on the batch).
@@ -166,7 +163,10 @@ int mq_launch_q2_mma_pf(int swiglu, const MqFormat &fmt, const void *experts, in
 // Expert cache (cache.hip): state reset, the plan of one call (eslot, miss list) and
 // the copy of the missed experts from host memory into their slots.
 int mq_launch_cache_reset(int32_t *state, int n_slots, int n_keys, hipStream_t st);
+// eptr: the address of every touched expert for the routed kernels (its slot, or
+// host + e * host_bytes for a miss left uncached).
 int mq_launch_cache_plan(const int32_t *counts, int E, int key_base, int32_t *state, int n_slots, int n_keys,
-                         int32_t *eslot, int2 *misses, int32_t *n_miss, hipStream_t st);
+                         const void *slots, int64_t slot_bytes, const void *host, int64_t host_bytes,
+                         uint64_t *eptr, int2 *misses, int32_t *n_miss, hipStream_t st);
 int mq_launch_cache_fill(const void *host, int64_t expert_bytes, void *slots, int64_t slot_bytes,
                          const int2 *misses, const int32_t *n_miss, int n_cu, hipStream_t st);

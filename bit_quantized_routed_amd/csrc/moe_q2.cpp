@@ -115,7 +115,7 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     w.inv = take(c, S * 4);
     w.units_hdr = take(c, 16);
     // expert cache of a call (moe_q2_forward_cached): slot per expert, miss list
-    w.eslot = take(c, E * 4);
+    w.eslot = take(c, E * 8);
     w.misses = take(c, E * 8);
     w.nmiss = take(c, 16);
     w.units = take(c, (size_t)w.max_units * 16);
@@ -517,29 +517,28 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
     }
     // routed experts
     const int ncu = device_cus();
-    int64_t ebytes = (int64_t)moe_q2_expert_bytes(s);
+    const int64_t ebytes = (int64_t)moe_q2_expert_bytes(s);
     // expert cache: plan the call from the bucketing's counts, copy the misses from
     // host memory, then read every routed expert from its slot
-    const int32_t *eslot = nullptr;
+    const uint64_t *eptr = nullptr;
     if (cache) {
-        int32_t *es = (int32_t *)(ws + w.eslot), *nm = (int32_t *)(ws + w.nmiss);
+        uint64_t *ep = (uint64_t *)(ws + w.eslot);
+        int32_t *nm = (int32_t *)(ws + w.nmiss);
         int2 *ml = (int2 *)(ws + w.misses);
         MQ_PHASE(MOE_Q2_PH_CACHE, (rc = mq_launch_cache_plan(counts, E, cache->key_base, cache->c->state,
-                                                             cache->c->n_slots, cache->c->n_keys, es, ml, nm, st))
+                                                             cache->c->n_slots, cache->c->n_keys, cache->c->slots,
+                                                             cache->c->slot_bytes, cache->host, ebytes, ep, ml, nm,
+                                                             st))
                                       ? rc
                                       : mq_launch_cache_fill(cache->host, ebytes, cache->c->slots,
                                                              cache->c->slot_bytes, ml, nm, ncu, st));
-        experts_q2 = cache->c->slots;
-        ebytes = cache->c->slot_bytes;
-        eslot = es;
+        eptr = ep;
     } else if ((rc = mark(MOE_Q2_PH_CACHE, 0)) || (rc = mark(MOE_Q2_PH_CACHE, 1))) {
         return rc;
     }
     const int64_t mat_gu = (int64_t)I * (H / MQ_QK) * (int64_t)gu_block_bytes(s);   // bytes of gate (or up)
-    const void *hcopy = cache ? cache->host : nullptr;
-    const int64_t hbytes = (int64_t)moe_q2_expert_bytes(s);
-    const MqFormat fgu = {w.nd, (s->flags & MOE_Q2_GU_Q4) ? MQ_BD4 : MQ_BD2, eslot, hcopy, hbytes};
-    const MqFormat fdn = {w.nd, (s->flags & MOE_Q2_DOWN_Q4) ? MQ_BD4 : MQ_BD2, eslot, hcopy, hbytes};
+    const MqFormat fgu = {w.nd, (s->flags & MOE_Q2_GU_Q4) ? MQ_BD4 : MQ_BD2, eptr};
+    const MqFormat fdn = {w.nd, (s->flags & MOE_Q2_DOWN_Q4) ? MQ_BD4 : MQ_BD2, eptr};
     float *h = (float *)(ws + w.h);
     float *y = (float *)(ws + w.y);
     uint32_t *hq = (uint32_t *)(ws + w.hq);
