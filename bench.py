@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", default="decode1")
-    ap.add_argument("--extra", default="decode32_zipf,prefill2048,stack40_t64_zipf,verify96_zipf:bi,"
+    ap.add_argument("--extra", default="decode32_zipf,prefill2048,stack40_t64_zipf,verify96_zipf,verify96_zipf:bi,"
                                        "stack40_q2q4,decode32_zipf:q8,prefill2048:q8,decode32_zipf:cache",
                     help="comma-separated extra workloads reported in the same line ('' for none)")
     ap.add_argument("--rotate", type=int, default=8, help="distinct layers cycled by decode steps")
@@ -279,7 +279,7 @@ def run_workload(spec, steps, warmup, rotate, graph=True):
                                 T * 3 * wl.shared_inter * wl.hidden * 2) / (ms_per_step * 1e-3) / 1e12
     elif kbytes is not None and dom_avg > 0:
         ach = kbytes / (dom_avg * 1e-3) / 1e9
-        tr = traffic_record("%s/%s" % (name, dom))
+        tr = traffic_record("%s/%s" % (spec, dom))
         res["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                            "traffic": None if tr is None else tr.get("bytes_per_launch"),
@@ -376,9 +376,9 @@ def run_cached(spec, steps, warmup, budget=0.5, n_batches=64):
     return res
 
 
-def W_layers(name):
+def W_layers(spec):
     from synth import workloads as W
-    return W.WORKLOADS[name].layers
+    return W.WORKLOADS[spec.partition(":")[0]].layers
 
 
 def measured_ceilings():
@@ -524,7 +524,7 @@ def main():
     ceil = measured_ceilings() if args.ceilings else None
     cpu = None
     if args.cpu_baseline:
-        cpu = cpu_baseline(args.workload, head.pop("_gpu_first_tokens", None))
+        cpu = cpu_baseline(args.workload.partition(":")[0], head.pop("_gpu_first_tokens", None))
         for k, v in extras.items():
             if k in CPU_PROTOCOL:           # the oracle's time does not depend on the row options
                 v["cpu_baseline"] = cpu_baseline(k, v.pop("_gpu_first_tokens", None))
@@ -532,7 +532,7 @@ def main():
     for v in extras.values():
         v.pop("_gpu_first_tokens", None)
     from synth import workloads as W
-    wl = W.WORKLOADS[args.workload]
+    wl = W.WORKLOADS[args.workload.partition(":")[0]]
     line = {
         "metric": METRIC, "value": round(head["tokens_per_s"], 2), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
