@@ -16,11 +16,16 @@
 // [3] misses of the last call, [4] experts touched by the last call, [5] misses of
 // the last call left uncached, [6] uncached misses (cumulative), [7] 0, then
 // slot_key[n_slots] (-1: empty), slot_stamp[n_slots], key_slot[n_keys] (-1: absent).
+// The cumulative counters wrap modulo 2^32.  The clock never overflows: once it
+// reaches MQ_CACHE_CLOCK_LIMIT, the next call first renumbers the used slots' stamps
+// 1, 2, ... in their (stamp, slot index) order and restarts the clock at the number
+// of used slots, which keeps every later decision of the policy unchanged.
 #include "common.h"
 #include "kernels.h"
 
 #define MQ_CACHE_HDR 8
 #define MQ_CACHE_THREADS 1024
+#define MQ_CACHE_CLOCK_LIMIT (1 << 30)
 
 __global__ void __launch_bounds__(256) k_cache_reset(int32_t *__restrict__ state, int n_slots, int n_keys) {
     const int64_t n = MQ_CACHE_HDR + 2 * (int64_t)n_slots + n_keys;
@@ -60,7 +65,7 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
     int32_t *slot_key = state + MQ_CACHE_HDR;
     int32_t *slot_stamp = slot_key + n_slots;
     int32_t *key_slot = slot_stamp + n_slots;
-    const int32_t clock = state[0] + 1;
+    int32_t clock0 = state[0];
     for (int s = tid; s < n_slots; s += MQ_CACHE_THREADS) {
         s_stamp[s] = slot_stamp[s];
         s_key[s] = slot_key[s];
@@ -68,6 +73,35 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
     if (tid == 0) s_hits = 0;
     s_victim[tid] = -1;
     __syncthreads();
+    // 0. clock renumbering (see the state layout above); n_slots <= 2 * MQ_CACHE_THREADS
+    if (clock0 >= MQ_CACHE_CLOCK_LIMIT) {
+        int32_t nv[MOE_Q2_CACHE_MAX_SLOTS / MQ_CACHE_THREADS];
+        int used = 0;
+#pragma unroll
+        for (int k = 0; k < MOE_Q2_CACHE_MAX_SLOTS / MQ_CACHE_THREADS; ++k) {
+            const int s = tid + k * MQ_CACHE_THREADS;
+            nv[k] = 0;
+            if (s < n_slots && s_stamp[s] > 0) {
+                const int32_t st = s_stamp[s];
+                int rank = 0;
+                for (int q = 0; q < n_slots; ++q) {
+                    const int32_t sq = s_stamp[q];
+                    rank += (sq > 0 && (sq < st || (sq == st && q < s))) ? 1 : 0;
+                }
+                nv[k] = rank + 1;
+            }
+        }
+        for (int q = 0; q < n_slots; ++q) used += s_stamp[q] > 0 ? 1 : 0;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < MOE_Q2_CACHE_MAX_SLOTS / MQ_CACHE_THREADS; ++k) {
+            const int s = tid + k * MQ_CACHE_THREADS;
+            if (s < n_slots) s_stamp[s] = nv[k];
+        }
+        clock0 = used;
+        __syncthreads();
+    }
+    const int32_t clock = clock0 + 1;
     // 1. hits keep their slot (stamped with this call's clock); misses are flagged.
     // (A state not made by moe_q2_cache_reset with this n_slots could hold a slot out
     // of range: it is read as a miss, and step 4 keeps every slot index in range, so
@@ -144,13 +178,14 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
         slot_key[s] = s_key[s];
     }
     if (tid == 0) {
+        uint32_t *cnt = (uint32_t *)state;               // cumulative counters wrap
         state[0] = clock;
-        state[1] += s_hits;
-        state[2] += nm;
+        cnt[1] += (uint32_t)s_hits;
+        cnt[2] += (uint32_t)nm;
         state[3] = nm;
         state[4] = s_hits + nm;
         state[5] = nm - nfill;
-        state[6] += nm - nfill;
+        cnt[6] += (uint32_t)(nm - nfill);
         *n_miss = nfill;
     }
 }

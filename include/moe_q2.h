@@ -233,10 +233,14 @@ int moe_q2_forward(const void *x, const float *router_w, const void *experts_q2,
  * the routed kernels read every expert from its slot.  Planning and copying run on the
  * device after the bucketing: no host synchronisation, capturable in a HIP graph.
  * The caller owns every buffer; calls that share a cache must be ordered on one stream.
- * state (int32, device): [0] calls, [1] hits, [2] misses (cumulative), [3] misses and
+ * state (int32, device): [0] call clock, [1] hits, [2] misses (cumulative), [3] misses and
  * [4] touched experts of the last call, [5] misses of the last call read from host
  * memory uncached, [6] such misses (cumulative), [7] 0, then slot_key[n_slots] (-1:
- * empty), slot_stamp[n_slots] (last call that used the slot), key_slot[n_keys] (-1: absent). */
+ * empty), slot_stamp[n_slots] (clock of the last call that used the slot, 0: empty),
+ * key_slot[n_keys] (-1: absent).  Cumulative counters wrap modulo 2^32; when the clock
+ * reaches 2^30 the next call renumbers the used slots' stamps 1, 2, ... in their
+ * (stamp, slot index) order and restarts the clock there, so the policy never sees an
+ * overflow and its decisions do not change. */
 #define MOE_Q2_CACHE_MAX_SLOTS 2048
 typedef struct {
     void    *slots;       /* device, n_slots * slot_bytes, 16-byte aligned: the budget */

@@ -183,3 +183,51 @@ def test_cache_under_graph_capture():
         oracle.call(touched)
         assert np.array_equal(out.cpu().numpy(), ref), rep
         cache.check(mq, oracle)
+
+
+def test_cache_clock_renumbering():
+    """When the call clock reaches its limit (2^30, set here from the host), the next
+    call renumbers the used slots' stamps in (stamp, slot) order before it plans: the
+    slot contents, key map, counters and every later eviction stay those of the
+    oracle's policy, whose clock never wraps."""
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.Workload("cache_e32_t6", 43, 6, 512, 32, 4, 512, 0, "bf16", 0.05, zipf=True)
+    dl = dw.DeviceLayer(wl)
+    host = _host_copy(dl.experts)
+    cache = _Cache(mq, 10, 32, wl.expert_bytes)
+    oracle = LRUCache(10)
+    xs = dw.activations(wl, tokens=6 * 8)
+    H, n = mq.CACHE_HDR, cache.n_slots
+
+    def check_order():
+        st = cache.state.cpu().numpy()
+        key, stamp, key_slot = st[H:H + n], st[H + n:H + 2 * n], st[H + 2 * n:]
+        assert key.tolist() == oracle.key
+        assert st[1] == oracle.hits and st[2] == oracle.misses and st[6] == oracle.uncached
+        order_dev = sorted(range(n), key=lambda s: (stamp[s], s))
+        order_ora = sorted(range(n), key=lambda s: (oracle.stamp[s], s))
+        assert order_dev == order_ora
+        assert all((stamp[s] == 0) == (oracle.stamp[s] == 0) for s in range(n))
+        want = np.full(cache.n_keys, -1)
+        for s, k in enumerate(oracle.key):
+            if k >= 0:
+                want[k] = s
+        assert np.array_equal(key_slot, want)
+        return int(st[0])
+
+    for b in range(4):
+        x = xs[6 * b:6 * (b + 1)].contiguous()
+        o1, o2, touched = _pair(mq, dl, x, 6, cache, host)
+        oracle.call(touched)
+        assert np.array_equal(o1, o2), b
+        cache.check(mq, oracle)
+    cache.state[0] = 1 << 30                             # the clock at its limit
+    torch.cuda.synchronize()
+    for b in (4, 0, 5, 6, 1, 7):
+        x = xs[6 * b:6 * (b + 1)].contiguous()
+        o1, o2, touched = _pair(mq, dl, x, 6, cache, host)
+        oracle.call(touched)
+        assert np.array_equal(o1, o2), b
+        clock = check_order()
+        assert clock <= n + 6                            # renumbered, then counting again
