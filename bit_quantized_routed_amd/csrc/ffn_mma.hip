@@ -573,10 +573,10 @@ __device__ __forceinline__ int4 mq_route_unit(const MqRoute &rt, int u, MqRouteL
     return un;
 }
 
-template <bool GU, int ND, int BD>
-__global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ experts, int64_t expert_bytes,
+template <bool GU, int ND, int BD, bool MERGE>
+__global__ void __launch_bounds__(256, MERGE && BD == MQ_BD2 ? 3 : 1) k_q2_mma(const uint8_t *__restrict__ experts, int64_t expert_bytes,
                                                 int64_t mat_off, int tiles, int kblocks, int nsplit,
-                                                int cps, const int4 *__restrict__ units,
+                                                int cps, int seg, const int4 *__restrict__ units,
                                                 const int32_t *__restrict__ urow, int zrow,
                                                 int trash_row, const mq_u32x4 *__restrict__ xdig,
                                                 const uint32_t *__restrict__ xsum,
@@ -684,10 +684,39 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
     mq_f32x4 tot[4];
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) tot[nf] = (mq_f32x4){0.f, 0.f, 0.f, 0.f};
+    // D layout: lane l, element i -> token 4*(l/16) + i, row slot 16*nf + l%16
+    auto store = [&](int kso) {
+        float *o0 = out0 + (int64_t)kso * split_stride;
+        float *o1 = GU ? out1 + (int64_t)kso * split_stride : nullptr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * q4 + i;
+            const float sc = s_sc[t];
+            const int64_t orow = (int64_t)(t < nt ? p0 + t : trash_row) * out_ld;
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf) {
+                const float v = tot[nf][i] * sc;
+                if (GU) {
+                    // slots 0..31: gate rows 32*tile + slot; 32..63: up rows 32*tile + slot - 32
+                    float *o = nf < 2 ? o0 : o1;
+                    o[orow + 32 * tile + 16 * (nf & 1) + r16] = v;
+                } else {
+                    o0[orow + 64 * tile + 16 * nf + r16] = v;
+                }
+            }
+        }
+    };
     const uint32_t *myd = (const uint32_t *)sW[wv];
     const bool one = __builtin_amdgcn_readfirstlane(nt) == 1;
     int buf = 0;
-    for (int c = c0; c < c1; ++c) {
+    // MERGE: one work-group walks the ranges of several splits and stores each split's
+    // sums, started from zero, where its range ends: the same values as one
+    // work-group per split (a separate instantiation: the extra loop level costs
+    // registers)
+    const int sl = MERGE ? seg : c1 - c0;
+    for (int cs = c0; cs < c1; cs += sl) {
+    const int ce = min(c1, cs + sl);
+    for (int c = cs; c < ce; ++c) {
         if (tid < 16) s_sc[tid] = scv;
         mq_bcol_store<BD>(sW[wv], lane, wb);
 #pragma unroll
@@ -712,25 +741,9 @@ __global__ void __launch_bounds__(256) k_q2_mma(const uint8_t *__restrict__ expe
         mq_mma_column<ND, BD>(myd, r16, q4, a, tot, one);
         buf ^= 1;
     }
-    // D layout: lane l, element i -> token 4*(l/16) + i, row slot 16*nf + l%16
-    float *o0 = out0 + (int64_t)ks * split_stride;
-    float *o1 = GU ? out1 + (int64_t)ks * split_stride : nullptr;
+    store(MERGE ? cs / seg : ks);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = 4 * q4 + i;
-        const float sc = s_sc[t];
-        const int64_t orow = (int64_t)(t < nt ? p0 + t : trash_row) * out_ld;
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
-            const float v = tot[nf][i] * sc;
-            if (GU) {
-                // slots 0..31: gate rows 32*tile + slot; 32..63: up rows 32*tile + slot - 32
-                float *o = nf < 2 ? o0 : o1;
-                o[orow + 32 * tile + 16 * (nf & 1) + r16] = v;
-            } else {
-                o0[orow + 64 * tile + 16 * nf + r16] = v;
-            }
-        }
+    for (int nf = 0; nf < 4; ++nf) tot[nf] = (mq_f32x4){0.f, 0.f, 0.f, 0.f};
     }
 }
 
@@ -750,7 +763,7 @@ void mq_dec_split(int max_units, int tiles, int kblocks, int max_split, int *nsp
 }
 
 int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t expert_bytes, int64_t mat_off,
-                     int tiles, int kblocks, const int4 *units, int max_units, int split_units,
+                     int tiles, int kblocks, const int4 *units, int max_units, int split_units, int merge,
                      const int32_t *urow, int zrow, int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
                      int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route,
@@ -770,6 +783,13 @@ int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t e
     const int prep_on = prep ? 1 : 0;
     int nsplit = 1, cps = kblocks;
     mq_dec_split(split_units, tiles, kblocks, gu ? MQ_DEC_SPLIT_GU : MQ_DEC_SPLIT_D, &nsplit, &cps);
+    // merge: one work-group per unit and tile group walks all nsplit ranges and stores
+    // each range's partial sums (the outputs of nsplit work-groups, with fewer of them)
+    const int seg = cps;
+    if (merge) {
+        nsplit = 1;
+        cps = kblocks;
+    }
     const int64_t q2_grid = (int64_t)max_units * nsplit * (tiles / 4);
     MqDense dn = {};
     int64_t dgrid = 0;
@@ -798,11 +818,16 @@ int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t e
     const int64_t grid = q2_grid + dgrid;
     if (grid <= 0) return mq_mark_empty(ev0, ev1, st);
     if (grid > 0x7fffffff) return MOE_Q2_EUNSUPPORTED;
-#define MQ_Q2_MMA_LAUNCH(GUV, NDV, BDV)                                                                  \
-    MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma<GUV, NDV, BDV>), dim3((unsigned)grid), dim3(256), 0, st,          \
-                    (const uint8_t *)experts, expert_bytes, mat_off, tiles, kblocks, nsplit, cps, units, urow, \
+#define MQ_Q2_MMA_LAUNCH1(GUV, NDV, BDV, MV)                                                             \
+    MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma<GUV, NDV, BDV, MV>), dim3((unsigned)grid), dim3(256), 0, st,      \
+                    (const uint8_t *)experts, expert_bytes, mat_off, tiles, kblocks, nsplit, cps, seg, units, urow, \
                     zrow, trash_row, (const mq_u32x4 *)xdig, xsum, xscale, out0, out1, out_ld, split_stride,  \
                     (int)q2_grid, dn, rt, route_on, pp, prep_on, fmt.eptr)
+#define MQ_Q2_MMA_LAUNCH(GUV, NDV, BDV)                                                                  \
+    do {                                                                                                 \
+        if (merge) MQ_Q2_MMA_LAUNCH1(GUV, NDV, BDV, true);                                              \
+        else MQ_Q2_MMA_LAUNCH1(GUV, NDV, BDV, false);                                                    \
+    } while (0)
     const int sel = (gu ? 4 : 0) + (fmt.nd == 2 ? 2 : 0) + (fmt.bd == MQ_BD4 ? 1 : 0);
     switch (sel) {
     case 0: MQ_Q2_MMA_LAUNCH(false, 1, MQ_BD2); break;
@@ -815,6 +840,7 @@ int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t e
     default: MQ_Q2_MMA_LAUNCH(true, 2, MQ_BD4); break;
     }
 #undef MQ_Q2_MMA_LAUNCH
+#undef MQ_Q2_MMA_LAUNCH1
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

@@ -147,9 +147,12 @@ struct MqFormat {
     const uint64_t *eptr;
 };
 // split_units: the unit count the k-split policy is computed for (max_units, or a
-// fixed count when the split must not depend on the batch).
+// fixed count when the split must not depend on the batch).  merge: one work-group
+// walks the k ranges of all splits and stores each range's partials (bit-identical
+// to one work-group per split; for a fixed split on a batch large enough to fill
+// the device without splitting).
 int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t expert_bytes, int64_t mat_off,
-                     int tiles, int kblocks, const int4 *units, int max_units, int split_units,
+                     int tiles, int kblocks, const int4 *units, int max_units, int split_units, int merge,
                      const int32_t *urow, int zrow, int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
                      int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route,
