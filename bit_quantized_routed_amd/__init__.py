@@ -47,7 +47,7 @@ class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("routed_kernel", ctypes.c_int32),
                 ("shared_fused", ctypes.c_int32), ("side_branch", ctypes.c_int32),
                 ("split_gate_up", ctypes.c_int32), ("split_down", ctypes.c_int32),
-                ("router_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("router_splits", ctypes.c_int32), ("merged", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -169,7 +169,7 @@ def describe(shape, n_tokens, topk):
     rc = _lib().moe_q2_describe(ctypes.byref(shape), n_tokens, topk, ctypes.byref(p))
     if rc:
         raise MoeQ2Error(rc, "moe_q2_describe")
-    return {f: getattr(p, f) for f, _ in Plan._fields_ if f != "reserved"}
+    return {f: getattr(p, f) for f, _ in Plan._fields_}
 
 
 def forward(x, router_w, experts_q2, shared_w, topk, out, shape, n_tokens, router_b=None,

@@ -300,6 +300,7 @@ extern "C" int moe_q2_describe(const moe_q2_shape *s, int32_t n_tokens, int32_t 
     p.split_gate_up = w.prefill || w.valu ? 1 : w.dsplit_gu;
     p.split_down = w.prefill || w.valu ? 1 : w.dsplit_d;
     p.router_splits = w.rsplit;
+    p.merged = (w.merge_gu ? 1 : 0) | (w.merge_d ? 2 : 0);
     p.workspace_bytes = w.total;
     *plan = p;
     return MOE_Q2_OK;

@@ -197,7 +197,9 @@ typedef struct {
     int32_t split_gate_up;   /* reduction splits of the routed gate/up and down launches */
     int32_t split_down;
     int32_t router_splits;   /* split-K partial logits of the router */
-    int32_t reserved;
+    int32_t merged;          /* bit 0 / bit 1: the gate/up / down splits are walked by one
+                                work-group each (batch-invariant mode on a batch that fills the
+                                device unsplit; the same partial sums as one work-group per split) */
     size_t  workspace_bytes;
 } moe_q2_plan;
 int moe_q2_describe(const moe_q2_shape *s, int32_t n_tokens, int32_t topk, moe_q2_plan *plan);

@@ -124,6 +124,15 @@ WORKLOADS = {
     # tiny layers in the 4-bit format: both matrices, and gate/up only (per-matrix mix)
     "tiny_q4": Workload("tiny_q4", 7, 4, 256, 8, 2, 512, 256, "bf16", 0.05, q4_gu=True, q4_down=True),
     "tiny_q4gu": Workload("tiny_q4gu", 8, 5, 256, 8, 2, 512, 0, "f32", 0.05, q4_gu=True),
+    # mid-size layers (hidden and intermediate 2048, 64 experts, top-8, 24 tokens, Zipf) for
+    # option combinations: a one-token call splits the reduction, a 24-token call need not
+    "mid_e64": Workload("mid_e64", 51, 24, 2048, 64, 8, 2048, 256, "bf16", 0.05, zipf=True),
+    "mid_e64_q4": Workload("mid_e64_q4", 52, 24, 2048, 64, 8, 2048, 256, "bf16", 0.05, zipf=True,
+                           q4_gu=True, q4_down=True),
+    "mid_e64_q4gu": Workload("mid_e64_q4gu", 53, 24, 2048, 64, 8, 2048, 0, "bf16", 0.05, zipf=True,
+                             q4_gu=True),
+    "mid_e64_q4dn": Workload("mid_e64_q4dn", 54, 24, 2048, 64, 8, 2048, 256, "bf16", 0.05, zipf=True,
+                             q4_down=True),
 }
 ORDER = ["tiny", "decode1", "decode32_zipf", "prefill2048", "stack40_t64_zipf"]
 

@@ -183,6 +183,10 @@ def test_plans(lib):
         assert p["path"] == mq.PATH_DECODE and p["routed_kernel"] == 0
         assert (p["split_gate_up"], p["split_down"]) == (one["split_gate_up"], one["split_down"])
         assert p["router_splits"] == plans[0]["router_splits"] == 16
+    # the fixed splits run merged (one work-group per unit and tile group) from the
+    # batch sizes whose own plan needs no split; never without the batch-invariant flag
+    assert [p["merged"] for p in plans] == [0, 3, 3, 3, 3, 3]
+    assert all(mq.describe(s, T, 8)["merged"] == 0 for T in (1, 5, 32, 96, 255))
     assert mq.describe(s, 2048, 8)["path"] == mq.PATH_PREFILL
     q4 = mq.make_shape(7168, 2048, 256, 2048, flags=mq.GU_Q4 | mq.DOWN_Q4)
     assert mq.describe(q4, 2048, 8)["path"] == mq.PATH_DECODE

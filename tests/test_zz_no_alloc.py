@@ -77,3 +77,15 @@ def test_noalloc_refuses_large_batch_before_enqueue():
     assert rc == mq.EUNSUPPORTED
     torch.cuda.synchronize()
     assert torch.all(out == 5.0)
+
+
+def test_noalloc_with_options():
+    """Batch-invariant 4-bit layer: a 24-token call (merged split work-groups) and then
+    a one-token call (one work-group per split) on the fixed workspace."""
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.WORKLOADS["mid_e64_q4"]
+    dl = dw.DeviceLayer(wl)
+    for T in (24, 1):
+        print("  [noalloc] mid_e64_q4 batch-invariant T =", T, flush=True)
+        _both(mq, dw, dl, wl, T, flags=mq.BATCH_INVARIANT)
