@@ -54,9 +54,12 @@ __global__ void __launch_bounds__(256) k_router_logits(const void *__restrict__ 
 
 // ---------------------------------------------------------------- logits on MFMA
 // bf16 activations x fp32 router weights.  Each weight is split exactly into three
-// bf16 terms w = hi + mid + lo (8 + 8 + 8 significant bits, round-to-nearest at
-// each step), so every product with a bf16 activation is exact in fp32 and the
-// MFMA accumulates in fp32 (v_mfma_f32_16x16x32_bf16, three per fragment pair).
+// bf16 terms w = hi + mid + lo by truncation: hi = the top 8 significant bits of w,
+// mid = the top 8 of r = w - hi, lo = r - mid (both differences exact in fp32; r
+// spans at most the 16 bit positions below hi's, so lo keeps at most 8 significant
+// bits and is a bf16 value), so every product with a bf16 activation is exact in
+// fp32 and the MFMA accumulates in fp32 (v_mfma_f32_16x16x32_bf16, three per
+// fragment pair).  Truncation takes one mask per term.
 // Tile: 64 tokens x 64 experts per work-group, wave w owns experts 16w..16w+15
 // and the 4 token fragments; fragments are loaded straight from global memory.
 // Split-K partial logits go to P[split][T][E] (summed in order by top-K).
@@ -66,13 +69,13 @@ typedef short mq_s16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void mq_split3(const float (&w)[8], mq_s16x8 &hi, mq_s16x8 &mid, mq_s16x8 &lo) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint16_t h = mq_f32_to_bf16(w[i]);
-        const float r1 = w[i] - mq_bf16_to_f32(h);
-        const uint16_t m = mq_f32_to_bf16(r1);
-        const float r2 = r1 - mq_bf16_to_f32(m);
-        hi[i] = (short)h;
-        mid[i] = (short)m;
-        lo[i] = (short)mq_f32_to_bf16(r2);
+        const uint32_t b = __float_as_uint(w[i]);
+        const float r1 = w[i] - __uint_as_float(b & 0xFFFF0000u);
+        const uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
+        const float r2 = r1 - __uint_as_float(m);
+        hi[i] = (short)(b >> 16);
+        mid[i] = (short)(m >> 16);
+        lo[i] = (short)(__float_as_uint(r2) >> 16);
     }
 }
 
