@@ -57,9 +57,11 @@ __global__ void __launch_bounds__(256) k_router_logits(const void *__restrict__ 
 // bf16 terms w = hi + mid + lo by truncation: hi = the top 8 significant bits of w,
 // mid = the top 8 of r = w - hi, lo = r - mid (both differences exact in fp32; r
 // spans at most the 16 bit positions below hi's, so lo keeps at most 8 significant
-// bits and is a bf16 value), so every product with a bf16 activation is exact in
-// fp32 and the MFMA accumulates in fp32 (v_mfma_f32_16x16x32_bf16, three per
-// fragment pair).  Truncation takes one mask per term.
+// bits and is a bf16 value whenever it stays a normal number, i.e. for
+// |w| >= 2^-102; below that what is lost is under 2^-126), so every product with a
+// bf16 activation is exact in fp32 and the MFMA accumulates in fp32
+// (v_mfma_f32_16x16x32_bf16, three per fragment pair).  Truncation takes one mask
+// per term.
 // Tile: 64 tokens x 64 experts per work-group, wave w owns experts 16w..16w+15
 // and the 4 token fragments; fragments are loaded straight from global memory.
 // Split-K partial logits go to P[split][T][E] (summed in order by top-K).
