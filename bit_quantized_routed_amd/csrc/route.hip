@@ -440,7 +440,8 @@ __global__ void __launch_bounds__(256) k_bucket_hist(const int32_t *__restrict__
 }
 
 // (256 threads, so that it finds room on a compute unit next to a concurrent
-// launch; thread i owns experts BKP_EPT * i .. + BKP_EPT - 1)
+// launch; thread i owns the ept = ceil(E / 256) experts ept * i .. ept * i + ept - 1,
+// so that every thread has work for E <= 256 and the scan stays in expert order)
 #define BKP_EPT 4
 __global__ void __launch_bounds__(256) k_bucket_scan(int C, int E, int unit_tokens, int32_t *__restrict__ cnt,
                                                      int32_t *__restrict__ counts_out,
@@ -449,12 +450,13 @@ __global__ void __launch_bounds__(256) k_bucket_scan(int C, int E, int unit_toke
                                                      int4 *__restrict__ units, int fill_units) {
     __shared__ int wsum[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int ept = (E + 255) / 256;
     int cn[BKP_EPT];
 #pragma unroll
     for (int q = 0; q < BKP_EPT; ++q) {               // expert totals, 16 counts at once
-        const int e = BKP_EPT * tid + q;
+        const int e = ept * tid + q;
         int c = 0;
-        if (e < E) {
+        if (q < ept && e < E) {
             const int32_t *row = cnt + (int64_t)e * C;
             for (int k0 = 0; k0 < C; k0 += 16) {
                 int v[16];
@@ -482,8 +484,8 @@ __global__ void __launch_bounds__(256) k_bucket_scan(int C, int E, int unit_toke
     int off = ba + a - tc, u = bb + b - tu;           // exclusive: first slot and unit of the thread
 #pragma unroll
     for (int q = 0; q < BKP_EPT; ++q) {
-        const int e = BKP_EPT * tid + q, c = cn[q];
-        if (e < E) {
+        const int e = ept * tid + q, c = cn[q];
+        if (q < ept && e < E) {
             counts_out[e] = c;
             offsets_out[e] = off;
             for (int k = 0; k < c; k += unit_tokens, ++u)
