@@ -133,7 +133,8 @@ typedef struct {
     int32_t shared_inter;  /* Is: shared expert intermediate, multiple of 256, or 0 = none */
     int32_t act_dtype;     /* MOE_Q2_F32 or MOE_Q2_BF16 (ignored under PRE_RMSNORM: x is fp32) */
     int32_t flags;         /* MOE_Q2_PATH_* | MOE_Q2_PRE_RMSNORM | MOE_Q2_RESIDUAL_ADD |
-                              MOE_Q2_DECODE_VALU | MOE_Q2_SERIAL */
+                              MOE_Q2_DECODE_VALU | MOE_Q2_SERIAL | MOE_Q2_BATCH_INVARIANT |
+                              MOE_Q2_ACT_Q8 | MOE_Q2_GU_Q4 | MOE_Q2_DOWN_Q4 */
     float   rms_eps;       /* used under MOE_Q2_PRE_RMSNORM */
 } moe_q2_shape;
 
@@ -208,7 +209,8 @@ int moe_q2_describe(const moe_q2_shape *s, int32_t n_tokens, int32_t topk, moe_q
  *   x          device [T, H], act_dtype (fp32 under PRE_RMSNORM); 16-byte aligned
  *   router_w   device [E, H] fp32 row-major
  *   experts_q2 device, E experts back to back in the tiled layout above (each
- *              3 * H * I / 256 blocks of 84 bytes); 16-byte aligned
+ *              3 * H * I / 256 blocks: 84 bytes, or 148 for the matrices the Q4 flags
+ *              name; moe_q2_expert_bytes); 16-byte aligned
  *   shared_w   device bf16 gate [Is, H], up [Is, H], down [H, Is] back to back;
  *              NULL iff shared_inter == 0
  *   topk       K, 1 <= K <= min(E, 16)
