@@ -469,8 +469,15 @@ def cpu_baseline(name, gpu=None):
         total += float(np.median(times))
         refs.append(ref)
         n += tpc
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     res = {"value": round(n / (total * scale), 4), "unit": "tokens/s" if scale == 1 else "tokens/s per %d-layer step" % scale,
-           "cores": int(thr), "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+           "cores": int(thr), "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
+           "kind": "oracle",
            "sample": "first %d token(s) of layer 0 of %s, %d token(s) per oracle call, median of %d run(s) per "
                      "call (routing, dequantisation of the touched experts, fp64 FFNs, shared expert, combine%s); "
                      "%.2f s of oracle time%s" % (n, name, tpc, runs, ", RMSNorm and residual" if wl.rmsnorm else "",
