@@ -91,3 +91,47 @@ def test_empty_batch_leaves_output_untouched():
                router_b=dl.router_b, workspace=ws)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+# the same odd shapes under the layer's options: batch invariance, Q8 activations,
+# the 4-bit sibling format for all routed matrices, and all three together (Q8
+# against the oracle's Q8 mode)
+OPT_CASES = ["e100_k6_t5", "e65_k1_t3_f32", "e16_k16_t9", "e300_k8_t40", "e512_k16_t2", "e8_k2_t300",
+             "e16_k16_t1"]
+OPTIONS = {"bi": ("BATCH_INVARIANT",), "q8": ("ACT_Q8",), "q4": (), "bi_q8_q4": ("BATCH_INVARIANT", "ACT_Q8")}
+
+
+@pytest.mark.parametrize("opt", list(OPTIONS))
+@pytest.mark.parametrize("name", OPT_CASES)
+def test_shape_options(name, opt):
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    case = next(c for c in CASES if c[0] == name)
+    _, seed, T, H, E, K, I, Is, act, rs, zipf = case
+    q4 = opt in ("q4", "bi_q8_q4")
+    wl = W.Workload(name + "_" + opt, seed, T, H, E, K, I, Is, act, rs, zipf=zipf, q4_gu=q4, q4_down=q4)
+    dl = dw.DeviceLayer(wl)
+    hl = HostLayer(wl)
+    flags = 0
+    for f in OPTIONS[opt]:
+        flags |= getattr(mq, f)
+    shape = dl.shape(flags)
+    x = dw.activations(wl)
+    ws = dw.workspace(shape, T, K)
+    tr = make_trace(T, K, E)
+    out = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+    mq.forward(x, dl.router_w, dl.experts, dl.shared_w, K, out, shape, T,
+               router_b=dl.router_b, workspace=ws, trace=tr)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().astype(np.float64)
+    tr = trace_np(tr)
+    xh, _ = W.activations(wl)
+    idx, g, logits, margin = moe.route(xh, hl.router_w, hl.router_b, K)
+    excluded, rep = check_routing(tr, {"idx": idx, "g": g, "logits": logits, "margin": margin}, E, K)
+    toks = np.nonzero(~excluded)[0]
+    assert toks.size > 0
+    a = "q8" if "ACT_Q8" in OPTIONS[opt] else "exact"
+    ref, _ = moe.layer(xh[toks], hl.router_w, hl.router_b, hl.expert_bytes, hl.shared, K, H, I, act=a)
+    err = rel_err(out[toks], ref)
+    print(name, opt, rep, "tokens", toks.size, "rel_err", err)
+    assert err <= TOL_DECODE
