@@ -18,12 +18,24 @@ least-recently-used over a fixed number of slots, with every tie broken by index
        stamp c written;
     3. missing keys beyond those slots (a call touching more keys than the budget
        holds) stay uncached: read from their home for this call only.
+
+With frequency admission (admit=True) every key also carries the number of calls
+that touched it (counted at the start of each call, saturating at 2^31 - 1), and in
+step 2 a missing key takes its slot only when the key the slot holds was touched by
+fewer calls than the missing key; otherwise the slot keeps its key and stamp and the
+missing key is read from its home for this call (as in step 3).  Empty slots always
+take their key.  Under a skewed, stationary popularity this keeps the frequently
+used keys resident instead of letting one-off keys evict them.
 """
+
+COUNT_MAX = 2 ** 31 - 1
 
 
 class LRUCache:
-    def __init__(self, n_slots):
+    def __init__(self, n_slots, admit=False):
         self.n = n_slots
+        self.admit = admit
+        self.count = {}                    # key -> calls that touched it
         self.key = [-1] * n_slots          # slot -> key (-1: empty)
         self.stamp = [0] * n_slots         # slot -> last call that used it
         self.clock = 0
@@ -43,6 +55,8 @@ class LRUCache:
         keys = sorted(set(int(k) for k in keys))
         self.clock += 1
         c = self.clock
+        for k in keys:
+            self.count[k] = min(self.count.get(k, 0) + 1, COUNT_MAX)
         slot_of, missing = {}, []
         for k in keys:
             s = self.where(k)
@@ -53,14 +67,19 @@ class LRUCache:
                 missing.append(k)
         free = sorted((self.stamp[s], s) for s in range(self.n) if self.stamp[s] < c)
         evicted = []
+        placed = 0
         for k, (_, s) in zip(missing, free):
-            if self.key[s] >= 0:
-                evicted.append(self.key[s])
+            old = self.key[s]
+            if self.admit and old >= 0 and self.count.get(old, 0) >= self.count[k]:
+                continue                   # not admitted: read from its home this call
+            if old >= 0:
+                evicted.append(old)
             self.key[s] = k
             self.stamp[s] = c
             slot_of[k] = s
+            placed += 1
         self.hits += len(keys) - len(missing)
         self.misses += len(missing)
-        self.uncached += max(0, len(missing) - len(free))
-        self.last_uncached = max(0, len(missing) - len(free))
+        self.uncached += len(missing) - placed
+        self.last_uncached = len(missing) - placed
         return slot_of, len(keys) - len(missing), missing, evicted

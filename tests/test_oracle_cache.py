@@ -58,3 +58,54 @@ def test_more_keys_than_free_slots_stay_uncached():
     assert evicted == [1, 3] and c.key == [4, 2, 5] and (c.uncached, c.last_uncached) == (1, 1)
     c.call([7, 8, 9, 10, 11])                        # all miss: 3 placed, 2 uncached
     assert c.key == [7, 8, 9] and c.uncached == 3
+
+
+def test_frequency_admission_worked_sequence():
+    # 2 slots, admission by touch counts.  Call 1 {0, 1}: empty slots take both ->
+    # [0, 1], counts 0:1 1:1.  Call 2 {0}: hit (count 0:2).  Call 3 {2}: miss; the slots
+    # not used by call 3 by (stamp, index): slot 1 (key 1, stamp 1), slot 0 (stamp 2);
+    # 2 is paired with slot 1, whose key was touched as often (1 >= 1): not admitted,
+    # 2 read from its home, nothing evicted.  Call 4 {2}: 2 now touched twice > 1: it
+    # evicts 1.  Plain LRU evicts 1 already in call 3.
+    c = LRUCache(2, admit=True)
+    c.call([0, 1])
+    c.call([0])
+    slot_of, hits, missing, evicted = c.call([2])
+    assert slot_of == {} and missing == [2] and evicted == [] and c.key == [0, 1]
+    assert (c.uncached, c.last_uncached) == (1, 1) and c.stamp == [2, 1]
+    slot_of, _, _, evicted = c.call([2])
+    assert slot_of == {2: 1} and evicted == [1] and c.key == [0, 2] and c.last_uncached == 0
+    assert c.count == {0: 2, 1: 1, 2: 2}
+    lru = LRUCache(2)
+    lru.call([0, 1])
+    lru.call([0])
+    assert lru.call([2])[3] == [1]
+
+
+def test_frequency_admission_invariants_random_calls():
+    rng = np.random.default_rng(1)
+    c = LRUCache(12, admit=True)
+    touches = {}
+    p = 1.0 / np.arange(1, 41) ** 1.1                  # skewed popularity over 40 keys
+    p /= p.sum()
+    for _ in range(300):
+        keys = rng.choice(40, size=rng.integers(1, 13), replace=False, p=p)
+        for k in keys:
+            touches[int(k)] = touches.get(int(k), 0) + 1
+        before = {k for k in c.key if k >= 0}
+        old_keys = list(c.key)
+        slot_of, hits, missing, evicted = c.call(keys)
+        assert hits == len(set(keys) & before) and len(missing) == len(set(keys) - before)
+        assert c.last_uncached == len(missing) - len(set(missing) & set(slot_of))
+        for s in range(c.n):                               # a key is replaced only by a more touched one
+            if old_keys[s] >= 0 and c.key[s] != old_keys[s]:
+                assert c.count[old_keys[s]] < c.count[c.key[s]]
+                assert old_keys[s] in evicted
+        held = [k for k in c.key if k >= 0]
+        assert len(held) == len(set(held))
+        assert c.count == touches
+    plain = LRUCache(12)
+    rng = np.random.default_rng(1)
+    for _ in range(300):
+        plain.call(rng.choice(40, size=rng.integers(1, 13), replace=False, p=p))
+    assert c.hits > plain.hits                           # the point of the admission rule
