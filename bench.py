@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", default="decode1")
     ap.add_argument("--extra", default="decode32_zipf,prefill2048,stack40_t64_zipf,verify96_zipf,verify96_zipf:bi,"
-                                       "stack40_q2q4,decode32_zipf:q8,prefill2048:q8,decode32_zipf:cache",
+                                       "stack40_q2q4,decode32_zipf:q8,prefill2048:q8,decode32_zipf:cache,"
+                                       "decode32_zipf:cache_admit",
                     help="comma-separated extra workloads reported in the same line ('' for none)")
     ap.add_argument("--rotate", type=int, default=8, help="distinct layers cycled by decode steps")
     ap.add_argument("--cpu-baseline", type=int, default=1)
@@ -315,7 +316,8 @@ def run_cached(spec, steps, warmup, budget=0.5, n_batches=64):
     from bit_quantized_routed_amd import workload as dw
     from synth import workloads as W
 
-    name = spec.partition(":")[0]
+    name, _, opt = spec.partition(":")
+    policy = mq.CACHE_LRU_ADMIT if opt == "cache_admit" else mq.CACHE_LRU
     wl = W.WORKLOADS[name]
     T, K, E = wl.tokens, wl.topk, wl.n_experts
     dl = dw.DeviceLayer(wl)
@@ -328,7 +330,7 @@ def run_cached(spec, steps, warmup, budget=0.5, n_batches=64):
     n_slots = int(E * budget)
     slots = torch.empty(n_slots * eb, dtype=torch.uint8, device="cuda")
     state = torch.empty(mq.cache_state_bytes(n_slots, E) // 4, dtype=torch.int32, device="cuda")
-    cache = mq.make_cache(slots, eb, n_slots, E, state)
+    cache = mq.make_cache(slots, eb, n_slots, E, state, policy=policy)
     mq.cache_reset(cache)
     shape = dl.shape(0)
     ws = dw.workspace(shape, T, K)
@@ -369,6 +371,7 @@ def run_cached(spec, steps, warmup, budget=0.5, n_batches=64):
            "touched_per_step": hits + misses, "misses_per_step": misses, "uncached_per_step": unc,
            "host_bytes_per_step": host_bytes, "host_link_gbs": host_bytes / (ms * 1e-3) / 1e9,
            "host_link_peak_gbs": PCIE_PEAK_GBS,
+           "policy": "lru with frequency admission" if policy == mq.CACHE_LRU_ADMIT else "lru",
            "note": "distinct %d-token batches cycled (%d), experts homed in pinned host memory, %d of %d "
                    "experts' slots in HBM" % (T, n_batches, n_slots, E)}
     del dl, host, slots, xs, ws
@@ -510,7 +513,7 @@ def main():
     head = run_workload(args.workload, args.steps, args.warmup, args.rotate, bool(args.graph))
     extras = {}
     for name in [n for n in args.extra.split(",") if n and n != args.workload]:
-        if name.endswith(":cache"):
+        if name.endswith(":cache") or name.endswith(":cache_admit"):
             extras[name] = run_cached(name, args.steps, args.warmup)
         else:
             extras[name] = run_workload(name, args.steps, args.warmup, args.rotate, bool(args.graph))

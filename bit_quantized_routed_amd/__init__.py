@@ -36,11 +36,13 @@ class Shape(ctypes.Structure):
 
 class Cache(ctypes.Structure):
     _fields_ = [("slots", ctypes.c_void_p), ("slot_bytes", ctypes.c_int64), ("n_slots", ctypes.c_int32),
-                ("n_keys", ctypes.c_int32), ("state", ctypes.c_void_p)]
+                ("n_keys", ctypes.c_int32), ("state", ctypes.c_void_p), ("policy", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 CACHE_MAX_SLOTS = 2048
 CACHE_HDR = 8
+CACHE_LRU, CACHE_LRU_ADMIT = 0, 1
 
 
 class Plan(ctypes.Structure):
@@ -208,10 +210,11 @@ def cache_state_bytes(n_slots, n_keys):
     return int(_lib().moe_q2_cache_state_bytes(n_slots, n_keys))
 
 
-def make_cache(slots, slot_bytes, n_slots, n_keys, state):
+def make_cache(slots, slot_bytes, n_slots, n_keys, state, policy=CACHE_LRU):
     """moe_q2_cache over caller-owned device tensors: `slots` (n_slots * slot_bytes
-    bytes) and `state` (cache_state_bytes(n_slots, n_keys) bytes, int32)."""
-    return Cache(_ptr(slots), slot_bytes, n_slots, n_keys, _ptr(state))
+    bytes) and `state` (cache_state_bytes(n_slots, n_keys) bytes, int32); policy
+    CACHE_LRU or CACHE_LRU_ADMIT (frequency admission)."""
+    return Cache(_ptr(slots), slot_bytes, n_slots, n_keys, _ptr(state), policy, 0)
 
 
 def cache_reset(cache, stream=None):

@@ -12,10 +12,16 @@
 // those slots (a call touching more experts than the budget holds) stay uncached:
 // the routed kernels read them straight from host memory for this call.
 //
+// Frequency admission (policy MOE_Q2_CACHE_LRU_ADMIT): a missing expert takes the slot
+// it is paired with only if the key the slot holds was touched by fewer calls than the
+// missing one (an empty slot always); otherwise the slot keeps its key and stamp and
+// the expert is read from host memory for this call.
+//
 // State (int32, device): [0] clock, [1] hits, [2] misses (both cumulative),
 // [3] misses of the last call, [4] experts touched by the last call, [5] misses of
 // the last call left uncached, [6] uncached misses (cumulative), [7] 0, then
-// slot_key[n_slots] (-1: empty), slot_stamp[n_slots], key_slot[n_keys] (-1: absent).
+// slot_key[n_slots] (-1: empty), slot_stamp[n_slots], key_slot[n_keys] (-1: absent),
+// key_count[n_keys] (calls that touched the key, saturating at 2^31 - 1).
 // The cumulative counters wrap modulo 2^32.  The clock never overflows: once it
 // reaches MQ_CACHE_CLOCK_LIMIT, the next call first renumbers the used slots' stamps
 // 1, 2, ... in their (stamp, slot index) order and restarts the clock at the number
@@ -28,17 +34,18 @@
 #define MQ_CACHE_CLOCK_LIMIT (1 << 30)
 
 __global__ void __launch_bounds__(256) k_cache_reset(int32_t *__restrict__ state, int n_slots, int n_keys) {
-    const int64_t n = MQ_CACHE_HDR + 2 * (int64_t)n_slots + n_keys;
+    const int64_t ks = MQ_CACHE_HDR + 2 * (int64_t)n_slots;                          // key_slot
+    const int64_t n = ks + 2 * (int64_t)n_keys;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         int32_t v = 0;
         if (i >= MQ_CACHE_HDR && i < MQ_CACHE_HDR + n_slots) v = -1;                 // slot_key
-        if (i >= MQ_CACHE_HDR + 2 * (int64_t)n_slots) v = -1;                         // key_slot
-        state[i] = v;
+        if (i >= ks && i < ks + n_keys) v = -1;                                       // key_slot
+        state[i] = v;                                                                 // stamps, counts: 0
     }
 }
 
 int mq_launch_cache_reset(int32_t *state, int n_slots, int n_keys, hipStream_t st) {
-    const int64_t n = MQ_CACHE_HDR + 2 * (int64_t)n_slots + n_keys;
+    const int64_t n = MQ_CACHE_HDR + 2 * (int64_t)n_slots + 2 * (int64_t)n_keys;
     int64_t grid = (n + 255) / 256;
     if (grid > 1024) grid = 1024;
     hipLaunchKernelGGL(k_cache_reset, dim3((unsigned)grid), dim3(256), 0, st, state, n_slots, n_keys);
@@ -57,20 +64,24 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
                                                                 const uint8_t *host, int64_t host_bytes,
                                                                 uint64_t *__restrict__ eptr,
                                                                 int2 *__restrict__ misses,
-                                                                int32_t *__restrict__ n_miss) {
+                                                                int32_t *__restrict__ n_miss, int policy) {
     __shared__ int32_t s_stamp[MOE_Q2_CACHE_MAX_SLOTS], s_key[MOE_Q2_CACHE_MAX_SLOTS];
     __shared__ int32_t s_miss[MQ_CACHE_THREADS], s_victim[MQ_CACHE_THREADS];
-    __shared__ int32_t s_wsum[MQ_CACHE_THREADS / 64], s_hits;
+    __shared__ int32_t s_wsum[MQ_CACHE_THREADS / 64], s_hits, s_placed;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int32_t *slot_key = state + MQ_CACHE_HDR;
     int32_t *slot_stamp = slot_key + n_slots;
     int32_t *key_slot = slot_stamp + n_slots;
+    int32_t *key_count = key_slot + n_keys;
     int32_t clock0 = state[0];
     for (int s = tid; s < n_slots; s += MQ_CACHE_THREADS) {
         s_stamp[s] = slot_stamp[s];
         s_key[s] = slot_key[s];
     }
-    if (tid == 0) s_hits = 0;
+    if (tid == 0) {
+        s_hits = 0;
+        s_placed = 0;
+    }
     s_victim[tid] = -1;
     __syncthreads();
     // 0. clock renumbering (see the state layout above); n_slots <= 2 * MQ_CACHE_THREADS
@@ -107,9 +118,13 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
     // of range: it is read as a miss, and step 4 keeps every slot index in range, so
     // such misuse gives wrong results but no access outside the buffers.)
     int miss = 0;
+    int32_t my_count = 0;                                // touches of this call's key (tid < E)
     if (tid < E) {
         int32_t sl = -1;
         if (counts[tid] > 0) {
+            const int32_t kc = key_count[key_base + tid];
+            my_count = kc < 0x7FFFFFFF ? kc + 1 : kc;    // this call's touch, saturating
+            key_count[key_base + tid] = my_count;        // (only this thread's key)
             sl = key_slot[key_base + tid];
             if (sl >= n_slots) sl = -1;
             if (sl >= 0) {
@@ -150,26 +165,35 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
         }
     }
     __syncthreads();
-    // 4. evictions (the victims' old keys), then the new keys; all keys distinct
+    // 4. admission, evictions (the victims' old keys), then the new keys; all keys
+    // distinct.  A victim's key is not touched by this call, so its count is the one
+    // before the call (step 1 changed only touched keys' counts).
     const int free_slots = n_slots - s_hits;             // slots no touched expert uses
     const int nfill = min(nm, free_slots);
-    if (tid < E && s_miss[tid] >= 0 && s_miss[tid] < nfill) {
-        const int v = s_victim[s_miss[tid]];
+    const bool paired = tid < E && s_miss[tid] >= 0 && s_miss[tid] < nfill;
+    int v = -1;
+    bool place = false;
+    if (paired) {
+        v = s_victim[s_miss[tid]];                       // >= 0 for a state made by the reset
         const int32_t old = v >= 0 ? s_key[v] : -1;
-        if (old >= 0 && old < n_keys) key_slot[old] = -1;
+        const bool known = old >= 0 && old < n_keys;
+        place = v >= 0 && (policy != MOE_Q2_CACHE_LRU_ADMIT || !known || key_count[old] < my_count);
+        if (place) {
+            if (known) key_slot[old] = -1;
+            atomicAdd(&s_placed, 1);                     // a count: commutative
+        }
     }
     __syncthreads();
-    if (tid < E && s_miss[tid] >= 0 && s_miss[tid] < nfill) {
+    if (paired) {
         const int i = s_miss[tid];
-        const int v = s_victim[i];
-        if (v >= 0) {                                    // always, for a state made by the reset
+        if (place) {
             key_slot[key_base + tid] = v;
             s_key[v] = key_base + tid;
             s_stamp[v] = clock;
             eptr[tid] = (uint64_t)(slots + (int64_t)v * slot_bytes);
             misses[i] = make_int2(tid, v);
         } else {
-            misses[i] = make_int2(tid, -1);              // skipped by the copy
+            misses[i] = make_int2(tid, -1);              // not copied: read from host memory
         }
     }
     __syncthreads();
@@ -184,19 +208,19 @@ __global__ void __launch_bounds__(MQ_CACHE_THREADS) k_cache_plan(const int32_t *
         cnt[2] += (uint32_t)nm;
         state[3] = nm;
         state[4] = s_hits + nm;
-        state[5] = nm - nfill;
-        cnt[6] += (uint32_t)(nm - nfill);
-        *n_miss = nfill;
+        state[5] = nm - s_placed;
+        cnt[6] += (uint32_t)(nm - s_placed);
+        *n_miss = nfill;                                 // list length (unplaced entries skipped)
     }
 }
 
 int mq_launch_cache_plan(const int32_t *counts, int E, int key_base, int32_t *state, int n_slots, int n_keys,
                          const void *slots, int64_t slot_bytes, const void *host, int64_t host_bytes,
-                         uint64_t *eptr, int2 *misses, int32_t *n_miss, hipStream_t st) {
+                         uint64_t *eptr, int2 *misses, int32_t *n_miss, int policy, hipStream_t st) {
     if (E > MQ_CACHE_THREADS || n_slots > MOE_Q2_CACHE_MAX_SLOTS) return MOE_Q2_EUNSUPPORTED;
     hipLaunchKernelGGL(k_cache_plan, dim3(1), dim3(MQ_CACHE_THREADS), 0, st, counts, E, key_base, state, n_slots,
                        n_keys, (const uint8_t *)slots, slot_bytes, (const uint8_t *)host, host_bytes, eptr, misses,
-                       n_miss);
+                       n_miss, policy);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }

@@ -170,6 +170,6 @@ int mq_launch_cache_reset(int32_t *state, int n_slots, int n_keys, hipStream_t s
 // host + e * host_bytes for a miss left uncached).
 int mq_launch_cache_plan(const int32_t *counts, int E, int key_base, int32_t *state, int n_slots, int n_keys,
                          const void *slots, int64_t slot_bytes, const void *host, int64_t host_bytes,
-                         uint64_t *eptr, int2 *misses, int32_t *n_miss, hipStream_t st);
+                         uint64_t *eptr, int2 *misses, int32_t *n_miss, int policy, hipStream_t st);
 int mq_launch_cache_fill(const void *host, int64_t expert_bytes, void *slots, int64_t slot_bytes,
                          const int2 *misses, const int32_t *n_miss, int n_cu, hipStream_t st);

@@ -539,7 +539,7 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
         MQ_PHASE(MOE_Q2_PH_CACHE, (rc = mq_launch_cache_plan(counts, E, cache->key_base, cache->c->state,
                                                              cache->c->n_slots, cache->c->n_keys, cache->c->slots,
                                                              cache->c->slot_bytes, cache->host, ebytes, ep, ml, nm,
-                                                             st))
+                                                             cache->c->policy, st))
                                       ? rc
                                       : mq_launch_cache_fill(cache->host, ebytes, cache->c->slots,
                                                              cache->c->slot_bytes, ml, nm, ncu, st));
@@ -644,13 +644,15 @@ extern "C" int moe_q2_forward(const void *x, const float *router_w, const void *
 // ------------------------------------------------------------------ expert cache
 extern "C" size_t moe_q2_cache_state_bytes(int32_t n_slots, int32_t n_keys) {
     if (n_slots < 1 || n_slots > MOE_Q2_CACHE_MAX_SLOTS || n_keys < 1 || n_keys > (1 << 28)) return 0;
-    return (size_t)4 * (8 + 2 * (size_t)n_slots + (size_t)n_keys);
+    return (size_t)4 * (8 + 2 * (size_t)n_slots + 2 * (size_t)n_keys);
 }
 
 static int check_cache(const moe_q2_cache *c) {
     if (!c || !c->slots || !c->state) return MOE_Q2_EINVAL;
     if (!moe_q2_cache_state_bytes(c->n_slots, c->n_keys)) return MOE_Q2_EINVAL;
     if (c->slot_bytes <= 0 || (c->slot_bytes & 15) || ((uintptr_t)c->slots & 15) || ((uintptr_t)c->state & 3))
+        return MOE_Q2_EINVAL;
+    if ((c->policy != MOE_Q2_CACHE_LRU && c->policy != MOE_Q2_CACHE_LRU_ADMIT) || c->reserved != 0)
         return MOE_Q2_EINVAL;
     return MOE_Q2_OK;
 }

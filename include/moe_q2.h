@@ -237,21 +237,31 @@ int moe_q2_forward(const void *x, const float *router_w, const void *experts_q2,
  * the routed kernels read every expert from its slot.  Planning and copying run on the
  * device after the bucketing: no host synchronisation, capturable in a HIP graph.
  * The caller owns every buffer; calls that share a cache must be ordered on one stream.
+ * Policy MOE_Q2_CACHE_LRU: missing experts (in key order) take the slots this call
+ * does not use in least-recently-used order.  MOE_Q2_CACHE_LRU_ADMIT adds frequency
+ * admission: a missing expert takes its slot only if the key the slot holds was touched
+ * by fewer calls (empty slots always); otherwise it is read from host memory for this
+ * call and the slot keeps its key -- frequently used experts stay resident under a
+ * skewed routing.
  * state (int32, device): [0] call clock, [1] hits, [2] misses (cumulative), [3] misses and
  * [4] touched experts of the last call, [5] misses of the last call read from host
  * memory uncached, [6] such misses (cumulative), [7] 0, then slot_key[n_slots] (-1:
  * empty), slot_stamp[n_slots] (clock of the last call that used the slot, 0: empty),
- * key_slot[n_keys] (-1: absent).  Cumulative counters wrap modulo 2^32; when the clock
+ * key_slot[n_keys] (-1: absent), key_count[n_keys] (calls that touched the key,
+ * saturating at 2^31 - 1).  Cumulative counters wrap modulo 2^32; when the clock
  * reaches 2^30 the next call renumbers the used slots' stamps 1, 2, ... in their
  * (stamp, slot index) order and restarts the clock there, so the policy never sees an
  * overflow and its decisions do not change. */
 #define MOE_Q2_CACHE_MAX_SLOTS 2048
+enum { MOE_Q2_CACHE_LRU = 0, MOE_Q2_CACHE_LRU_ADMIT = 1 };
 typedef struct {
     void    *slots;       /* device, n_slots * slot_bytes, 16-byte aligned: the budget */
     int64_t  slot_bytes;  /* >= moe_q2_expert_bytes of every layer using the cache, multiple of 16 */
     int32_t  n_slots;     /* 1 .. MOE_Q2_CACHE_MAX_SLOTS */
     int32_t  n_keys;      /* valid keys 0 .. n_keys - 1 */
     int32_t *state;       /* device, moe_q2_cache_state_bytes(n_slots, n_keys) bytes */
+    int32_t  policy;      /* MOE_Q2_CACHE_LRU or MOE_Q2_CACHE_LRU_ADMIT */
+    int32_t  reserved;    /* 0 */
 } moe_q2_cache;
 
 /* Bytes of a cache's state; 0 for n_slots or n_keys out of range. */

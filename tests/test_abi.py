@@ -196,7 +196,7 @@ def test_plans(lib):
 
 def test_cache_validation(lib):
     """Expert-cache entry points: state size, and the checks made before any HIP call."""
-    assert mq.cache_state_bytes(128, 256) == 4 * (8 + 2 * 128 + 256)
+    assert mq.cache_state_bytes(128, 256) == 4 * (8 + 2 * 128 + 2 * 256)
     assert mq.cache_state_bytes(0, 256) == 0 and mq.cache_state_bytes(2049, 256) == 0
     s = mq.make_shape(7168, 2048, 256, 2048)
     eb = mq.expert_bytes(s)
@@ -211,6 +211,10 @@ def test_cache_validation(lib):
     assert call(mq.make_cache(64 * A, eb - 16, 256, 256, 32 * A)) == mq.EINVAL          # slot too small
     assert call(mq.make_cache(64 * A, eb, 256, 256, None)) == mq.EINVAL                 # no state
     assert call(mq.make_cache(64 * A, eb, 0, 256, 32 * A)) == mq.EINVAL
+    assert call(mq.make_cache(64 * A, eb, 256, 256, 32 * A, policy=2)) == mq.EINVAL       # unknown policy
+    bad = mq.make_cache(64 * A, eb, 256, 256, 32 * A, policy=mq.CACHE_LRU_ADMIT)
+    bad.reserved = 1
+    assert call(bad) == mq.EINVAL
     sv = mq.make_shape(7168, 2048, 256, 2048, flags=mq.DECODE_VALU)
     assert call(good, shape=sv) == mq.EUNSUPPORTED
     assert call(good, T=0) == mq.OK                                                     # empty batch

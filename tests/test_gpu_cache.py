@@ -17,18 +17,20 @@ pytestmark = pytest.mark.gpu
 
 
 class _Cache:
-    def __init__(self, mq, n_slots, n_keys, slot_bytes):
+    def __init__(self, mq, n_slots, n_keys, slot_bytes, policy=0):
         self.slots = torch.empty(n_slots * slot_bytes, dtype=torch.uint8, device="cuda")
         self.state = torch.empty(mq.cache_state_bytes(n_slots, n_keys) // 4, dtype=torch.int32, device="cuda")
-        self.c = mq.make_cache(self.slots, slot_bytes, n_slots, n_keys, self.state)
+        self.c = mq.make_cache(self.slots, slot_bytes, n_slots, n_keys, self.state, policy=policy)
         self.n_slots, self.n_keys = n_slots, n_keys
         mq.cache_reset(self.c)
 
     def check(self, mq, oracle):
         st = self.state.cpu().numpy()
-        H, n = mq.CACHE_HDR, self.n_slots
-        key, stamp, key_slot = st[H:H + n], st[H + n:H + 2 * n], st[H + 2 * n:]
+        H, n, nk = mq.CACHE_HDR, self.n_slots, self.n_keys
+        key, stamp = st[H:H + n], st[H + n:H + 2 * n]
+        key_slot, key_count = st[H + 2 * n:H + 2 * n + nk], st[H + 2 * n + nk:]
         assert st[0] == oracle.clock and st[1] == oracle.hits and st[2] == oracle.misses
+        assert all(key_count[k] == oracle.count.get(k, 0) for k in range(nk))
         assert st[5] == oracle.last_uncached and st[6] == oracle.uncached
         assert key.tolist() == oracle.key and stamp.tolist() == oracle.stamp
         want = np.full(self.n_keys, -1)
@@ -64,15 +66,16 @@ def _pair(mq, dl, x, T, cache, host, key_base=0, flags=0):
     return o1.cpu().numpy(), o2.cpu().numpy(), touched
 
 
-def test_cache_decode_sequence_matches_resident_and_lru():
+@pytest.mark.parametrize("policy", [0, 1], ids=["lru", "lru_admit"])
+def test_cache_decode_sequence_matches_resident_and_lru(policy):
     mq = need_gpu()
     from bit_quantized_routed_amd import workload as dw
     wl = W.WORKLOADS["decode32_zipf"]
     dl = dw.DeviceLayer(wl)
     host = _host_copy(dl.experts)
     T, E = wl.tokens, wl.n_experts
-    cache = _Cache(mq, 128, E, wl.expert_bytes)            # half the layer's experts
-    oracle = LRUCache(128)
+    cache = _Cache(mq, 128, E, wl.expert_bytes, policy=policy)   # half the layer's experts
+    oracle = LRUCache(128, admit=policy == 1)
     xs = dw.activations(wl, tokens=4 * T)
     order = [0, 1, 2, 0, 3, 1, 1]                          # new batches, repeats (hits)
     for n, b in enumerate(order):
@@ -84,6 +87,8 @@ def test_cache_decode_sequence_matches_resident_and_lru():
         assert np.array_equal(o1, o2), n
         cache.check(mq, oracle)
     assert oracle.misses > 128 and oracle.hits > 0            # evictions happened, and hits
+    if policy == 1:
+        assert oracle.uncached > 0                            # misses the admission rule turned away
 
 
 def test_cache_prefill_and_one_token():
@@ -185,7 +190,8 @@ def test_cache_under_graph_capture():
         cache.check(mq, oracle)
 
 
-def test_cache_clock_renumbering():
+@pytest.mark.parametrize("policy", [0, 1], ids=["lru", "lru_admit"])
+def test_cache_clock_renumbering(policy):
     """When the call clock reaches its limit (2^30, set here from the host), the next
     call renumbers the used slots' stamps in (stamp, slot) order before it plans: the
     slot contents, key map, counters and every later eviction stay those of the
@@ -195,15 +201,17 @@ def test_cache_clock_renumbering():
     wl = W.Workload("cache_e32_t6", 43, 6, 512, 32, 4, 512, 0, "bf16", 0.05, zipf=True)
     dl = dw.DeviceLayer(wl)
     host = _host_copy(dl.experts)
-    cache = _Cache(mq, 10, 32, wl.expert_bytes)
-    oracle = LRUCache(10)
+    cache = _Cache(mq, 10, 32, wl.expert_bytes, policy=policy)
+    oracle = LRUCache(10, admit=policy == 1)
     xs = dw.activations(wl, tokens=6 * 8)
     H, n = mq.CACHE_HDR, cache.n_slots
 
     def check_order():
         st = cache.state.cpu().numpy()
-        key, stamp, key_slot = st[H:H + n], st[H + n:H + 2 * n], st[H + 2 * n:]
+        key, stamp = st[H:H + n], st[H + n:H + 2 * n]
+        key_slot, key_count = st[H + 2 * n:H + 2 * n + cache.n_keys], st[H + 2 * n + cache.n_keys:]
         assert key.tolist() == oracle.key
+        assert all(key_count[k] == oracle.count.get(k, 0) for k in range(cache.n_keys))
         assert st[1] == oracle.hits and st[2] == oracle.misses and st[6] == oracle.uncached
         order_dev = sorted(range(n), key=lambda s: (stamp[s], s))
         order_ora = sorted(range(n), key=lambda s: (oracle.stamp[s], s))
