@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", default="decode1")
     ap.add_argument("--extra", default="decode32_zipf,prefill2048,stack40_t64_zipf,verify96_zipf,verify96_zipf:bi,"
-                                       "stack40_q2q4,decode32_zipf:q8,prefill2048:q8,decode32_zipf:cache,"
+                                       "stack40_q2q4,decode32_zipf:q8,prefill2048:q8,prefill2048_q4,decode32_zipf:cache,"
                                        "decode32_zipf:cache_admit",
                     help="comma-separated extra workloads reported in the same line ('' for none)")
     ap.add_argument("--rotate", type=int, default=8, help="distinct layers cycled by decode steps")

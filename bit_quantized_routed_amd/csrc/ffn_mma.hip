@@ -926,7 +926,7 @@ int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit,
 // w ^ (t & 15), then [token][4 sum words] with word q at q ^ ((t & 15) >> 2); the
 // XOR swizzles keep the 16 lanes that read one word of 16 different tokens on
 // distinct banks.  Weights = the 4 tiles' column pieces in global order.
-template <bool SWIGLU, int MF, int ND>
+template <bool SWIGLU, int MF, int ND, int BD>
 __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ experts,
                                                    int64_t expert_bytes, int64_t mat_off, int rows,
                                                    int kblocks, const int32_t *__restrict__ units_hdr,
@@ -939,13 +939,14 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     constexpr int NTOK = 16 * MF;
     constexpr int WPT = 16 * ND;                        // 16-byte digit words per token and column
     constexpr int TPL = 64 / WPT;                       // tokens per 1 KB digit load
-    constexpr int NWJ = 4 * 336 / 64;                   // weight loads (1 KB each)
+    constexpr int CV = 16 * BD;                         // uint4 per tile column (64 rows x BD dwords)
+    constexpr int NWJ = 4 * CV / 64;                    // weight loads (1 KB each): BD
     constexpr int NDJ = NTOK / TPL;                     // digit loads
     constexpr int NSJ = NTOK * 4 / 64;                  // sum loads (16 tokens each)
     constexpr int NJ = NDJ + NSJ + NWJ;
     constexpr int JPW = (NJ + 7) / 8;                   // loads per wave (at most)
     constexpr int SUMS = NTOK * 4 * WPT;                // dword offset of the sum words
-    static_assert(4 * 336 % 64 == 0 && NTOK % 16 == 0, "load split");
+    static_assert(4 * CV % 64 == 0 && NTOK % 16 == 0, "load split");
     // one LDS array for all staging (weights, activations, token rows)
     constexpr int SB_SZ = NWJ * 256, SA_SZ = NTOK * (4 * WPT + 16), SB_OFF = 2 * SA_SZ;
     __shared__ __attribute__((aligned(16))) uint32_t smem[2 * SB_SZ + 2 * SA_SZ + 2 * NTOK];
@@ -959,7 +960,7 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     const int nslot1 = SWIGLU ? 32 + 16 * hw : 32 * hw + 16;
     const int stiles = rows / (SWIGLU ? 32 : 64) / 4;
     const int U = units_hdr[0];
-    const int64_t tile_bytes = (int64_t)kblocks * 64 * MQ_BLOCK_BYTES;
+    const int64_t tile_bytes = (int64_t)kblocks * 64 * 4 * BD;
     const mq_i32x4 zi = {0, 0, 0, 0};
     const int sw = r16;                                  // digit word swizzle of this lane's token
     const int ssw = 4 * (q4 ^ (r16 >> 2));               // sum word position (dwords)
@@ -1004,7 +1005,7 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                 const int q = 64 * (j - NDJ) + lane, t = q >> 2, w = (q & 3) ^ ((t & 15) >> 2);
                 o = (uint32_t)((arow[t] * kblocks * 16 + 4 * w) * 4);
             } else if (j < NJ) {
-                const int p = 64 * (j - NDJ - NSJ) + lane, tl = p / 336, w = p - tl * 336;
+                const int p = 64 * (j - NDJ - NSJ) + lane, tl = p / CV, w = p - tl * CV;
                 o = (uint32_t)(tl * tile_bytes + w * 16);
             }
             voff[n] = o;
@@ -1015,7 +1016,7 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
     auto dma = [&](int b, int buf, int mfc, const uint8_t *tbase) {
         const char *db = (const char *)xdig + (int64_t)b * (16 * WPT);
         const char *sb = (const char *)xsum + (int64_t)b * 64;
-        const char *wb = (const char *)tbase + (int64_t)b * 5376;
+        const char *wb = (const char *)tbase + (int64_t)b * (16 * CV);
 #pragma unroll
         for (int n = 0; n < JPW; ++n) {
             const int j = wv + 8 * n;
@@ -1078,20 +1079,19 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                     set_voff(arow_n);                    // this item's loads are all issued
                     dma(0, cur ^ 1, mfcn, tbn);
                 }
-                const uint32_t *blk0 = smem + SB_OFF + cur * SB_SZ + (tw * 64 + nslot0 + r16) * MQ_BLOCK_DWORDS;
-                const uint32_t *blk1 = smem + SB_OFF + cur * SB_SZ + (tw * 64 + nslot1 + r16) * MQ_BLOCK_DWORDS;
+                const uint32_t *blk0 = smem + SB_OFF + cur * SB_SZ + (tw * 64 + nslot0 + r16) * BD;
+                const uint32_t *blk1 = smem + SB_OFF + cur * SB_SZ + (tw * 64 + nslot1 + r16) * BD;
                 const uint32_t *sAc = smem + cur * SA_SZ;
                 // both fragments' q*sc operands of the column, expanded once and kept
                 // across the token fragments
                 mq_i32x4 b0[4], b1[4];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const int g = 4 * kk + q4;
-                    b0[kk] = mq_codes_x_scale(blk0[4 + g], __builtin_amdgcn_ubfe(blk0[kk], 8 * q4, 4));
-                    b1[kk] = mq_codes_x_scale(blk1[4 + g], __builtin_amdgcn_ubfe(blk1[kk], 8 * q4, 4));
+                    b0[kk] = mq_group_operand<BD>(blk0, 4 * kk + q4, kk, q4);
+                    b1[kk] = mq_group_operand<BD>(blk1, 4 * kk + q4, kk, q4);
                 }
                 const mq_s16x4 bm0 = mq_mins_bf16(blk0[q4]), bm1 = mq_mins_bf16(blk1[q4]);
-                const uint32_t dd0 = blk0[20], dd1 = blk1[20];
+                const uint32_t dd0 = blk0[BD - 1], dd1 = blk1[BD - 1];
                 const float d0 = mq_h2f((uint16_t)(dd0 & 0xFFFFu)), m0 = mq_h2f((uint16_t)(dd0 >> 16));
                 const float d1 = mq_h2f((uint16_t)(dd1 & 0xFFFFu)), m1 = mq_h2f((uint16_t)(dd1 >> 16));
                 // one token fragment at a time: its four integer chains, the min term, the fold
@@ -1156,12 +1156,19 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
             }
         };
         const int mfa = (nt + 15) >> 4;                  // 1..MF, uniform
-        static_assert(MF == 5, "one loop copy per fragment count 1..5");
-        if (mfa >= 5) run(std::integral_constant<int, 5>{});
-        else if (mfa == 4) run(std::integral_constant<int, 4>{});
-        else if (mfa == 3) run(std::integral_constant<int, 3>{});
-        else if (mfa == 2) run(std::integral_constant<int, 2>{});
-        else run(std::integral_constant<int, 1>{});
+        static_assert(MF == 4 || MF == 5, "one loop copy per fragment count 1..MF");
+        if constexpr (MF == 5) {
+            if (mfa >= 5) run(std::integral_constant<int, 5>{});
+            else if (mfa == 4) run(std::integral_constant<int, 4>{});
+            else if (mfa == 3) run(std::integral_constant<int, 3>{});
+            else if (mfa == 2) run(std::integral_constant<int, 2>{});
+            else run(std::integral_constant<int, 1>{});
+        } else {
+            if (mfa >= 4) run(std::integral_constant<int, 4>{});
+            else if (mfa == 3) run(std::integral_constant<int, 3>{});
+            else if (mfa == 2) run(std::integral_constant<int, 2>{});
+            else run(std::integral_constant<int, 1>{});
+        }
         if (has_next && !chain) {                        // short items: the next rows here
             if (tid < NTOK) arow_n[tid] = nrow;
             __syncthreads();
@@ -1176,23 +1183,40 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
 int mq_launch_q2_mma_pf(int swiglu, const MqFormat &fmt, const void *experts, int64_t expert_bytes,
                         int64_t mat_off, int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                         int max_units, const int32_t *perm, int topk, const void *xdig,
-                        const uint32_t *xsum, const float *xscale, float *out, int n_cu,
+                        const uint32_t *xsum, const float *xscale, float *out, int n_cu, int mf,
                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-    if ((fmt.nd != 1 && fmt.nd != 2) || fmt.bd != MQ_BD2) return MOE_Q2_EINVAL;
+    if ((fmt.nd != 1 && fmt.nd != 2) || (fmt.bd != MQ_BD2 && fmt.bd != MQ_BD4)) return MOE_Q2_EINVAL;
+    // fragments per unit (the bucketing's unit size / 16): 5, or 4 where the staging
+    // of 4-bit weights with two-digit activations of 80 tokens would not fit in LDS
+    if (mf != PF_MF && mf != 4) return MOE_Q2_EINVAL;
+    if (mf == PF_MF && fmt.nd == 2 && fmt.bd == MQ_BD4) return MOE_Q2_EINVAL;
     const int stiles = rows / (swiglu ? 32 : 64) / 4;
     int64_t want = (int64_t)max_units * stiles;
     int64_t cap = (int64_t)n_cu;       // one persistent work-group per compute unit (LDS-bound)
     const int grid = (int)(want < cap ? want : cap);
     if (grid <= 0) return mq_mark_empty(ev0, ev1, st);
-#define MQ_PF_LAUNCH(SW, NDV)                                                                           \
-    MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma_pf<SW, PF_MF, NDV>), dim3(grid), dim3(512), 0, st,               \
+#define MQ_PF_LAUNCH(SW, MFV, NDV, BDV)                                                                 \
+    MQ_LAUNCH_TIMED(ev0, ev1, (k_q2_mma_pf<SW, MFV, NDV, BDV>), dim3(grid), dim3(512), 0, st,             \
                     (const uint8_t *)experts, expert_bytes, mat_off, rows, kblocks, units_hdr, units, perm, \
                     topk, (const mq_u32x4 *)xdig, xsum, xscale, out, fmt.eptr)
-    if (swiglu) {
-        if (fmt.nd == 2) MQ_PF_LAUNCH(true, 2); else MQ_PF_LAUNCH(true, 1);
+#define MQ_PF_SW(MFV, NDV, BDV)                                                                         \
+    do {                                                                                                 \
+        if (swiglu) MQ_PF_LAUNCH(true, MFV, NDV, BDV);                                                   \
+        else MQ_PF_LAUNCH(false, MFV, NDV, BDV);                                                         \
+    } while (0)
+    // instantiations: 80-slot units for every format but 4-bit weights with two
+    // digits (64-slot units), and 64-slot units of the 2-bit kernels for a layer
+    // whose other matrix is 4-bit (one bucketing serves both launches)
+    if (mf == PF_MF) {
+        if (fmt.nd == 2) MQ_PF_SW(PF_MF, 2, MQ_BD2);
+        else if (fmt.bd == MQ_BD2) MQ_PF_SW(PF_MF, 1, MQ_BD2);
+        else MQ_PF_SW(PF_MF, 1, MQ_BD4);
     } else {
-        if (fmt.nd == 2) MQ_PF_LAUNCH(false, 2); else MQ_PF_LAUNCH(false, 1);
+        if (fmt.nd != 2) return MOE_Q2_EINVAL;
+        if (fmt.bd == MQ_BD2) MQ_PF_SW(4, 2, MQ_BD2);
+        else MQ_PF_SW(4, 2, MQ_BD4);
     }
+#undef MQ_PF_SW
 #undef MQ_PF_LAUNCH
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;

@@ -6,8 +6,8 @@
 #define FD_TCH 4        // slots per work unit of the vector-ALU decode kernel
 #define MMA_TCH 16      // slots per work unit of the matrix-core decode kernel
 #define MQ_TOPK_BUCKET_MAX_T 4   // largest batch whose bucketing runs in the top-K launch
-#define PF_MF 5         // token fragments per unit of the prefill kernel
-#define PF_TCH (16 * PF_MF)
+#define PF_MF 5         // token fragments per unit of the prefill kernel (4 for a layer
+                        // with a 4-bit matrix and two-digit activations)
 
 int mq_launch_router(const void *x, int bf16, const float *wr, const float *bias, int T, int H,
                      int E, float *logits, hipStream_t st);
@@ -161,7 +161,7 @@ int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t e
 int mq_launch_q2_mma_pf(int swiglu, const MqFormat &fmt, const void *experts, int64_t expert_bytes,
                         int64_t mat_off, int rows, int kblocks, const int32_t *units_hdr, const int4 *units,
                         int max_units, const int32_t *perm, int topk, const void *xdig,
-                        const uint32_t *xsum, const float *xscale, float *out, int n_cu,
+                        const uint32_t *xsum, const float *xscale, float *out, int n_cu, int mf,
                         hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // Expert cache (cache.hip): state reset, the plan of one call (eslot, miss list) and
 // the copy of the missed experts from host memory into their slots.

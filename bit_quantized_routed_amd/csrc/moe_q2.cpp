@@ -63,6 +63,9 @@ struct Workspace {
     int split_units = 0;        // unit count the decode k-split policy is computed for
     // routed path and, for the matrix-core decode kernels, their reduction splits
     bool prefill = false, valu = false;
+    // prefill token fragments per unit (units of 16 pf_mf slots, one bucketing for both
+    // launches): 4 when a 4-bit matrix meets two-digit activations (LDS), else 5
+    int pf_mf = PF_MF;
     int dec_units = 0, dsplit_gu = 1, dsplit_d = 1;
     // batch-invariant on a batch that fills the device unsplit: one work-group walks
     // all of a fixed split's k ranges (same partials, fewer work-groups)
@@ -94,12 +97,12 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     w.bi = (s->flags & MOE_Q2_BATCH_INVARIANT) != 0;
     w.nd = (s->flags & MOE_Q2_ACT_Q8) ? 1 : 2;
     const bool q4 = (s->flags & (MOE_Q2_GU_Q4 | MOE_Q2_DOWN_Q4)) != 0;
-    // the prefill kernels take the 2-bit codec only; a batch-invariant call keeps one
-    // set of kernels for every batch size
-    w.prefill = !w.bi && !q4 &&
+    // a batch-invariant call keeps one set of kernels for every batch size
+    w.prefill = !w.bi &&
                 ((s->flags & MOE_Q2_PATH_PREFILL) ||
                  (!(s->flags & MOE_Q2_PATH_DECODE) && T >= MOE_Q2_PREFILL_MIN_TOKENS));
     w.valu = !w.prefill && (s->flags & MOE_Q2_DECODE_VALU) != 0;
+    if (q4 && w.nd == 2) w.pf_mf = 4;
     int cps = 0;
     if (!w.prefill && !w.valu) {
         w.dec_units = units_bound(S, E, MMA_TCH);
@@ -272,7 +275,6 @@ static int check_common(const moe_q2_shape *s, int32_t n_tokens, int32_t topk) {
     const bool q4 = f & (MOE_Q2_GU_Q4 | MOE_Q2_DOWN_Q4), valu = f & MOE_Q2_DECODE_VALU;
     if (bi && (f & MOE_Q2_PATH_PREFILL)) return MOE_Q2_EINVAL;     // one kernel set for every batch
     if (valu && (bi || q8 || q4)) return MOE_Q2_EUNSUPPORTED;       // the vector-ALU kernel: 2-bit, 15-bit
-    if (q4 && (f & MOE_Q2_PATH_PREFILL)) return MOE_Q2_EUNSUPPORTED;  // prefill kernels: 2-bit only
     const bool in_bf16 = (f & MOE_Q2_PRE_RMSNORM) || s->act_dtype == MOE_Q2_BF16;
     if (bi && s->shared_inter > 0 && !in_bf16) return MOE_Q2_EUNSUPPORTED;   // shared expert on split GEMMs
     return MOE_Q2_OK;
@@ -493,7 +495,7 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
     }
     // few tokens: the bucketing runs in the top-K launch (its phase then reads zero),
     // or, on the matrix-core decode path, inside the gate/up launch (both phases zero)
-    const int tch = valu ? FD_TCH : (prefill ? PF_TCH : MMA_TCH);
+    const int tch = valu ? FD_TCH : (prefill ? 16 * w.pf_mf : MMA_TCH);
     const bool route_in_gu = !cache && !valu && !prefill && nsplit == 1 && T <= MQ_TOPK_BUCKET_MAX_T &&
                              E <= MQ_ROUTE_MAX_E && K <= 16;
     MqRoute rt = {};
@@ -563,12 +565,12 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
                                                   units, w.max_units, perm, K, hq, hg, hsc, y, ncu, st));
     } else if (prefill) {
         if ((rc = mq_launch_q2_mma_pf(1, fgu, experts_q2, ebytes, 0, I, H / MQ_QK, units_hdr, units, w.max_units,
-                                      perm, K, xq, (const uint32_t *)xg, xs, h, ncu, st,
+                                      perm, K, xq, (const uint32_t *)xg, xs, h, ncu, w.pf_mf, st,
                                       evk(MOE_Q2_PH_GATE_UP, 0), evk(MOE_Q2_PH_GATE_UP, 1))))
             return rc;
         MQ_PHASE(MOE_Q2_PH_PREP_H, mq_launch_prep_digits(h, 0, T * K, I, I, hq, (uint32_t *)hg, hsc, w.nd, st));
         if ((rc = mq_launch_q2_mma_pf(0, fdn, experts_q2, ebytes, 2 * mat_gu, H, I / MQ_QK, units_hdr, units,
-                                      w.max_units, perm, K, hq, (const uint32_t *)hg, hsc, y, ncu, st,
+                                      w.max_units, perm, K, hq, (const uint32_t *)hg, hsc, y, ncu, w.pf_mf, st,
                                       evk(MOE_Q2_PH_DOWN, 0), evk(MOE_Q2_PH_DOWN, 1))))
             return rc;
     } else {

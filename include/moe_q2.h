@@ -90,7 +90,8 @@ enum { MOE_Q2_F32 = 0, MOE_Q2_BF16 = 1 };
 enum {
     MOE_Q2_PATH_AUTO = 0,      /* decode kernels below MOE_Q2_PREFILL_MIN_TOKENS tokens, else prefill */
     MOE_Q2_PATH_DECODE = 1,    /* force the decode kernels (up to 16 slots per work unit) */
-    MOE_Q2_PATH_PREFILL = 2,   /* force the prefill kernels (up to 64 slots per work unit) */
+    MOE_Q2_PATH_PREFILL = 2,   /* force the prefill kernels (up to 80 slots per work unit; 64
+                                  when a 4-bit matrix meets the default 15-bit activations) */
     MOE_Q2_PRE_RMSNORM = 4,    /* x is the fp32 residual stream h; the layer input is
                                   bf16(h / sqrt(mean(h^2) + rms_eps)) (unit gain) */
     MOE_Q2_RESIDUAL_ADD = 8,   /* out += layer(...) instead of out = layer(...) */
@@ -115,8 +116,7 @@ enum {
                                   and shared expert unchanged.  Not with DECODE_VALU */
     MOE_Q2_GU_Q4 = 256,        /* routed gate/up matrices in the 4-bit sibling format (below) */
     MOE_Q2_DOWN_Q4 = 512       /* routed down matrix in the 4-bit sibling format.  Either Q4
-                                  flag runs the decode kernels at every batch size (PATH_PREFILL
-                                  and DECODE_VALU: EUNSUPPORTED) */
+                                  flag with DECODE_VALU: EUNSUPPORTED */
 };
 #define MOE_Q2_PREFILL_MIN_TOKENS 256
 /* Token envelope of one call.  n_tokens <= MOE_Q2_MAX_TOKENS, and the activation

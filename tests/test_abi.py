@@ -63,7 +63,6 @@ def _ws_status(shape, T, K):
     (dict(flags=mq.BATCH_INVARIANT | mq.DECODE_VALU), mq.EUNSUPPORTED),
     (dict(flags=mq.ACT_Q8 | mq.DECODE_VALU), mq.EUNSUPPORTED),
     (dict(flags=mq.GU_Q4 | mq.DECODE_VALU), mq.EUNSUPPORTED),
-    (dict(flags=mq.DOWN_Q4 | mq.PATH_PREFILL), mq.EUNSUPPORTED),
     (dict(flags=mq.BATCH_INVARIANT, act_dtype=mq.F32), mq.EUNSUPPORTED),   # fp32 input + shared expert
 ])
 def test_workspace_size_rejects(lib, kw, status):
@@ -189,7 +188,10 @@ def test_plans(lib):
     assert all(mq.describe(s, T, 8)["merged"] == 0 for T in (1, 5, 32, 96, 255))
     assert mq.describe(s, 2048, 8)["path"] == mq.PATH_PREFILL
     q4 = mq.make_shape(7168, 2048, 256, 2048, flags=mq.GU_Q4 | mq.DOWN_Q4)
-    assert mq.describe(q4, 2048, 8)["path"] == mq.PATH_DECODE
+    assert mq.describe(q4, 2048, 8)["path"] == mq.PATH_PREFILL
+    assert mq.describe(q4, 32, 8)["path"] == mq.PATH_DECODE
+    q4pf = mq.make_shape(7168, 2048, 256, 2048, flags=mq.DOWN_Q4 | mq.PATH_PREFILL)
+    assert mq.describe(q4pf, 32, 8)["routed_kernel"] == 2
     q8 = mq.make_shape(7168, 2048, 256, 2048, flags=mq.ACT_Q8)
     assert mq.workspace_size(q8, 32, 8) < mq.workspace_size(s, 32, 8)
 

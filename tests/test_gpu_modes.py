@@ -81,7 +81,7 @@ Q4_CASES = [
     ("q4_t5",        31, 5,   256, 8,  2, 512, 256, "bf16", True, True),
     ("q4dn_t3_f32",  32, 3,   512, 16, 4, 256, 0,   "f32",  False, True),
     ("q4gu_t40",     33, 40,  256, 65, 8, 256, 256, "bf16", True, False),
-    ("q4_t300",      34, 300, 256, 8,  2, 512, 256, "bf16", True, True),   # decode kernels at 300 tokens
+    ("q4_t300",      34, 300, 256, 8,  2, 512, 256, "bf16", True, True),   # prefill kernels at 300 tokens
     ("q4_t1_k16",    35, 1,   256, 16, 16, 256, 256, "bf16", True, True),  # one token, in-launch routing
 ]
 
@@ -99,9 +99,41 @@ def test_q4_formats(case):
     for e in sorted({0, E - 1}):                  # device encoders + packer = the oracle's
         assert np.array_equal(dev[e * eb:(e + 1) * eb], hl.packed_expert(e))
     plan = mq.describe(dl.shape(0), T, K)
-    assert plan["path"] == mq.PATH_DECODE
+    assert plan["path"] == (mq.PATH_PREFILL if T >= mq.PREFILL_MIN_TOKENS else mq.PATH_DECODE)
     out, tr = _layer(mq, dl, dw.activations(wl), T)
     _check(wl, out, tr)
+
+
+Q4_PREFILL_CASES = [
+    # name            seed T    H     E   K  I    Is   act     q4_gu q4_down flags
+    # 64-slot units, several per expert with a ragged last one; more work items than
+    # work-groups; 4 and 3 block columns (chained items)
+    ("q4pf_t600",      36, 600, 1024, 16, 4, 768, 0,   "bf16", True,  True,  ()),
+    # one 4-bit matrix: the 2-bit matrix's launch also on 64-slot units
+    ("q4gupf_t300",    37, 300, 512,  16, 4, 512, 256, "bf16", True,  False, ()),
+    ("q4dnpf_t40",     38, 40,  512,  16, 8, 768, 0,   "f32",  False, True,  ("PATH_PREFILL",)),
+    # Q8 activations: 80-slot units for both formats
+    ("q4pf_q8_t600",   39, 600, 1024, 16, 4, 768, 0,   "bf16", True,  True,  ("ACT_Q8",)),
+    ("q4gupf_q8_t64",  40, 64,  512,  65, 8, 256, 256, "bf16", True,  False, ("ACT_Q8", "PATH_PREFILL")),
+]
+
+
+@pytest.mark.parametrize("case", Q4_PREFILL_CASES, ids=[c[0] for c in Q4_PREFILL_CASES])
+def test_q4_prefill(case):
+    """The prefill kernels on the 4-bit format (both matrices, and either one), with
+    the default two-digit and with Q8 activations, against the oracle."""
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    name, seed, T, H, E, K, I, Is, act, gu, dn, names = case
+    wl = W.Workload(name, seed, T, H, E, K, I, Is, act, 0.05, q4_gu=gu, q4_down=dn)
+    dl = dw.DeviceLayer(wl)
+    f = 0
+    for n in names:
+        f |= getattr(mq, n)
+    assert mq.describe(dl.shape(f), T, K)["routed_kernel"] == 2
+    out, tr = _layer(mq, dl, dw.activations(wl), T, flags=f)
+    q8 = "ACT_Q8" in names
+    _check(wl, out, tr, act="q8" if q8 else "exact", tol=TOL_Q8 if q8 else TOL)
 
 
 def test_tiny_q4_workloads():

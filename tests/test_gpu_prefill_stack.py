@@ -30,14 +30,16 @@ def _bucket_property(tr, E, K):
     assert np.array_equal(tr["perm"], np.argsort(idx, kind="stable"))
 
 
-def test_prefill2048_sampled():
-    """64 tokens of the 2048-token prefill: for every bucket larger than one 80-slot
-    work unit, the token of its last slot (in the unit's second pass) and of its 81st
-    slot (the first of the second unit), tokens 0 and 2047, the rest seeded at random."""
+@pytest.mark.parametrize("name,unit", [("prefill2048", 80), ("prefill2048_q4", 64)])
+def test_prefill2048_sampled(name, unit):
+    """64 tokens of the 2048-token prefill (2-bit layer: 80-slot work units; 4-bit
+    layer: 64-slot units): for every bucket larger than one work unit, the token of
+    its last slot and of the first slot of its second unit, tokens 0 and 2047, the
+    rest seeded at random."""
     mq = need_gpu()
     from bit_quantized_routed_amd import workload as dw
     from tests.oracle_pool import ExpertPool, layer_outputs
-    wl = W.WORKLOADS["prefill2048"]
+    wl = W.WORKLOADS[name]
     dl = dw.DeviceLayer(wl)
     T, K = wl.tokens, wl.topk
     shape = dl.shape()
@@ -59,11 +61,11 @@ def test_prefill2048_sampled():
     excluded, rep = check_routing(trn, route, wl.n_experts, K)
     print("  [prefill] routing and bucketing checked", rep, flush=True)
     off, perm = trn["offsets"], trn["perm"]
-    big = np.nonzero(trn["counts"] > 80)[0]
+    big = np.nonzero(trn["counts"] > unit)[0]
     want = {0, T - 1}
     for e in big:
         want.add(int(perm[off[e + 1] - 1]) // K)
-        want.add(int(perm[off[e] + 80]) // K)
+        want.add(int(perm[off[e] + unit]) // K)
     rng = np.random.default_rng(3)
     for t in rng.permutation(T):
         if len(want) >= 64:
@@ -77,7 +79,7 @@ def test_prefill2048_sampled():
     finally:
         pool.close()
     err = rel_err(o[sample], ref)
-    print("prefill2048", rep, "tokens compared", sample.size, "buckets > 80 slots", big.size,
+    print(name, rep, "tokens compared", sample.size, "buckets > %d slots" % unit, big.size,
           "rel_err", err, "bucket sizes min/max", int(trn["counts"].min()), int(trn["counts"].max()))
     assert sample.size >= 60
     assert err <= TOL
