@@ -130,8 +130,14 @@ struct mq_bcol {
     mq_u32x4 v[NLD];
 };
 
+// The loads name the global address space: a generic (flat) load also counts against
+// the LDS counter, so every LDS wait of the column would wait for this prefetch of
+// the next column too.  (Expert bytes are device memory or pinned host memory, both
+// global.)
 template <int BD>
-__device__ __forceinline__ void mq_bcol_load(const mq_u32x4 *__restrict__ src, int lane, mq_bcol<BD> &c) {
+__device__ __forceinline__ void mq_bcol_load(const mq_u32x4 *__restrict__ src_, int lane, mq_bcol<BD> &c) {
+    typedef const __attribute__((address_space(1))) mq_u32x4 *gvec;
+    const gvec src = (gvec)src_;
     constexpr int NLD = mq_bcol<BD>::NLD;
 #pragma unroll
     for (int i = 0; i < NLD - 1; ++i) c.v[i] = src[lane + 64 * i];
