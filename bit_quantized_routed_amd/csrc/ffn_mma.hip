@@ -112,7 +112,10 @@ __device__ __forceinline__ mq_i32x4 mq_group_operand(const uint32_t *blk, int g,
 
 // m_j of 4 consecutive groups (one scale dword) as 4 bf16 (exact small integers).
 __device__ __forceinline__ mq_s16x4 mq_mins_bf16(uint32_t swd) {
-    const uint32_t m = (swd >> 4) & 0x0F0F0F0Fu;
+    uint32_t m = (swd >> 4) & 0x0F0F0F0Fu;
+    // m kept whole (opaque to the combiner, which would otherwise turn each byte into
+    // its own 4-bit field extract): the byte conversions then read its bytes directly
+    asm("" : "+v"(m));
     mq_s16x4 r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = (short)(__float_as_uint((float)((m >> (8 * i)) & 0xFFu)) >> 16);
