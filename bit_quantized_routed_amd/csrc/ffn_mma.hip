@@ -1103,18 +1103,32 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                 const uint32_t dd0 = blk0[BD - 1], dd1 = blk1[BD - 1];
                 const float d0 = mq_h2f((uint16_t)(dd0 & 0xFFFFu)), m0 = mq_h2f((uint16_t)(dd0 >> 16));
                 const float d1 = mq_h2f((uint16_t)(dd1 & 0xFFFFu)), m1 = mq_h2f((uint16_t)(dd1 >> 16));
-                // one token fragment at a time: its four integer chains, the min term, the fold
+                // one token fragment at a time: its four integer chains, the min term, the
+                // fold; the next fragment's activation operands are read from LDS ahead
+                // (the first PK of the 4 MFMA steps of the next fragment: what the register
+                // budget of two waves per SIMD allows without spills)
+                constexpr int PK = 3;
+                mq_i32x4 xa[2][PK][ND];
+                auto xop = [&](int m, int kk, int d) {
+                    return __builtin_bit_cast(mq_i32x4, *(const mq_u32x4 *)(sAc + xo[kk][d] + 16 * 4 * WPT * m));
+                };
+                auto xread = [&](int m, mq_i32x4 (&x)[PK][ND]) {
+#pragma unroll
+                    for (int kk = 0; kk < PK; ++kk)
+#pragma unroll
+                        for (int d = 0; d < ND; ++d) x[kk][d] = xop(m, kk, d);
+                };
+                xread(0, xa[0]);
 #pragma unroll
                 for (int m = 0; m < MFC; ++m) {
                     mq_i32x4 hi0 = zi, lo0, hi1 = zi, lo1;
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
-                        const mq_i32x4 al = __builtin_bit_cast(
-                            mq_i32x4, *(const mq_u32x4 *)(sAc + xo[kk][ND - 1] + 16 * 4 * WPT * m));
+                        if (kk == PK && m + 1 < MFC) xread(m + 1, xa[(m + 1) & 1]);
+                        const mq_i32x4 al = kk < PK ? xa[m & 1][kk][ND - 1] : xop(m, kk, ND - 1);
                         // the first step of each chain starts from zero (no accumulator to clear)
                         if (ND == 2) {
-                            const mq_i32x4 ah = __builtin_bit_cast(
-                                mq_i32x4, *(const mq_u32x4 *)(sAc + xo[kk][0] + 16 * 4 * WPT * m));
+                            const mq_i32x4 ah = kk < PK ? xa[m & 1][kk][0] : xop(m, kk, 0);
                             hi0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b0[kk], kk ? hi0 : zi, 0, 0, 0);
                             lo0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(al, b0[kk], kk ? lo0 : zi, 0, 0, 0);
                             hi1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah, b1[kk], kk ? hi1 : zi, 0, 0, 0);
