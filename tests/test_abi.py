@@ -172,8 +172,9 @@ def test_noalloc_validation(lib):
 
 def test_plans(lib):
     """Path choices (moe_q2_describe): batch-invariant calls keep the one-token splits,
-    router split and decode kernels at every batch size; Q4 matrices run the decode
-    kernels at prefill sizes; Q8 activations halve the digit buffers."""
+    router split and decode kernels at every batch size; Q4 matrices take the prefill
+    kernels from the same batch size as Q2 (and when forced); Q8 activations halve the
+    digit buffers."""
     s = mq.make_shape(7168, 2048, 256, 2048)
     one = mq.describe(s, 1, 8)
     bi = mq.make_shape(7168, 2048, 256, 2048, flags=mq.BATCH_INVARIANT)
