@@ -91,12 +91,14 @@ def test_cache_decode_sequence_matches_resident_and_lru(policy):
         assert oracle.uncached > 0                            # misses the admission rule turned away
 
 
-def test_cache_prefill_and_one_token():
+@pytest.mark.parametrize("q4", [(False, False), (True, True), (False, True)], ids=["q2", "q4", "q4dn"])
+def test_cache_prefill_and_one_token(q4):
     """The prefill kernels (300 tokens: all experts touched, the cache holds the whole
-    layer) and a one-token call on the same cache."""
+    layer) and a one-token call on the same cache; 2-bit experts, 4-bit experts, and
+    a 4-bit down matrix only (the prefill kernels' 64-slot units)."""
     mq = need_gpu()
     from bit_quantized_routed_amd import workload as dw
-    wl = W.Workload("cache_e32_t300", 41, 300, 512, 32, 4, 512, 256, "bf16", 0.05)
+    wl = W.Workload("cache_e32_t300", 41, 300, 512, 32, 4, 512, 256, "bf16", 0.05, q4_gu=q4[0], q4_down=q4[1])
     dl = dw.DeviceLayer(wl)
     host = _host_copy(dl.experts)
     cache = _Cache(mq, 32, 32, wl.expert_bytes)
