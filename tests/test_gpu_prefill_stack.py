@@ -30,19 +30,22 @@ def _bucket_property(tr, E, K):
     assert np.array_equal(tr["perm"], np.argsort(idx, kind="stable"))
 
 
-@pytest.mark.parametrize("name,unit", [("prefill2048", 80), ("prefill2048_q4", 64)])
-def test_prefill2048_sampled(name, unit):
+@pytest.mark.parametrize("name,unit,act", [("prefill2048", 80, "exact"), ("prefill2048_q4", 64, "exact"),
+                                            ("prefill2048", 80, "q8"), ("prefill2048_q4", 80, "q8")],
+                         ids=["q2", "q4", "q2_act_q8", "q4_act_q8"])
+def test_prefill2048_sampled(name, unit, act):
     """64 tokens of the 2048-token prefill (2-bit layer: 80-slot work units; 4-bit
-    layer: 64-slot units): for every bucket larger than one work unit, the token of
-    its last slot and of the first slot of its second unit, tokens 0 and 2047, the
-    rest seeded at random."""
+    layer: 64-slot units with two-digit activations, 80 with Q8 activations, which are
+    checked against the oracle's Q8 mode): for every bucket larger than one work unit,
+    the token of its last slot and of the first slot of its second unit, tokens 0 and
+    2047, the rest seeded at random."""
     mq = need_gpu()
     from bit_quantized_routed_amd import workload as dw
     from tests.oracle_pool import ExpertPool, layer_outputs
     wl = W.WORKLOADS[name]
     dl = dw.DeviceLayer(wl)
     T, K = wl.tokens, wl.topk
-    shape = dl.shape()
+    shape = dl.shape(mq.ACT_Q8 if act == "q8" else 0)
     assert mq.describe(shape, T, K)["routed_kernel"] == 2
     ws = dw.workspace(shape, T, K)
     tr = make_trace(T, K, wl.n_experts)
@@ -75,11 +78,11 @@ def test_prefill2048_sampled(name, unit):
     sample = sample[~excluded[sample]]
     pool = ExpertPool()
     try:
-        (ref, _), = layer_outputs(pool, wl.name, [(0, hl, xh[sample])], K, wl.hidden, wl.inter)
+        (ref, _), = layer_outputs(pool, wl.name, [(0, hl, xh[sample])], K, wl.hidden, wl.inter, act=act)
     finally:
         pool.close()
     err = rel_err(o[sample], ref)
-    print(name, rep, "tokens compared", sample.size, "buckets > %d slots" % unit, big.size,
+    print(name, act, rep, "tokens compared", sample.size, "buckets > %d slots" % unit, big.size,
           "rel_err", err, "bucket sizes min/max", int(trn["counts"].min()), int(trn["counts"].max()))
     assert sample.size >= 60
     assert err <= TOL
