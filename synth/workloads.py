@@ -125,6 +125,9 @@ WORKLOADS = {
     # same seed: prefill2048's activations, router and routing)
     "prefill2048_q4": Workload("prefill2048_q4", 3, 2048, H_DS, E_DS, K_DS, I_DS, I_DS, "bf16",
                                1.0 / math.sqrt(H_DS), q4_gu=True, q4_down=True),
+    # the one-token decode layer with both routed matrices in the 4-bit format
+    "decode1_q4": Workload("decode1_q4", 1, 1, H_DS, E_DS, K_DS, I_DS, I_DS, "bf16", 0.02,
+                           q4_gu=True, q4_down=True),
     # tiny layers in the 4-bit format: both matrices, and gate/up only (per-matrix mix)
     "tiny_q4": Workload("tiny_q4", 7, 4, 256, 8, 2, 512, 256, "bf16", 0.05, q4_gu=True, q4_down=True),
     "tiny_q4gu": Workload("tiny_q4gu", 8, 5, 256, 8, 2, 512, 0, "f32", 0.05, q4_gu=True),

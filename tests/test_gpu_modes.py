@@ -136,6 +136,23 @@ def test_q4_prefill(case):
     _check(wl, out, tr, act="q8" if q8 else "exact", tol=TOL_Q8 if q8 else TOL)
 
 
+@pytest.mark.parametrize("flag", ["", "ACT_Q8"])
+def test_decode1_q4(flag):
+    """The full-size one-token layer at Q4 (in-launch routing, the down launch's own
+    activation preparation and the shared rows in the routed launches, with 148-byte
+    blocks), default and Q8 activations, against the oracle."""
+    mq = need_gpu()
+    from bit_quantized_routed_amd import workload as dw
+    wl = W.WORKLOADS["decode1_q4"]
+    dl = dw.DeviceLayer(wl)
+    f = getattr(mq, flag) if flag else 0
+    plan = mq.describe(dl.shape(f), 1, wl.topk)
+    assert plan["path"] == mq.PATH_DECODE and plan["shared_fused"] == 1
+    out, tr = _layer(mq, dl, dw.activations(wl), 1, flags=f)
+    q8 = flag == "ACT_Q8"
+    _check(wl, out, tr, act="q8" if q8 else "exact", pooled=True, tol=TOL_Q8 if q8 else TOL)
+
+
 def test_tiny_q4_workloads():
     mq = need_gpu()
     from bit_quantized_routed_amd import workload as dw
