@@ -7,9 +7,10 @@
 #include "kernels.h"
 
 // All loads are issued before the sums (split partials in batches of CB_SB, clamped
-// indices); the sums then run in fixed order.
-#define CB_KMAX 16
+// indices); the sums then run in fixed order.  KMAX: 8 (top-K up to 8) or 16 (the
+// indices past K are clamped to K - 1 and their terms skipped).
 #define CB_SB 8
+template <int CB_KMAX>
 __global__ void __launch_bounds__(256) k_combine(const float *__restrict__ y, int nsplit,
                                                  int64_t split_stride, const int32_t *__restrict__ inv,
                                                  const float *__restrict__ gate,
@@ -80,8 +81,12 @@ int mq_launch_combine(const float *y, int nsplit, int64_t split_stride, const in
     // few tokens: 64-thread work-groups, so that the loads of a row spread over more
     // compute units (the launch is latency- and load-issue-bound there)
     const int nb = T <= 8 ? 64 : 256;
-    hipLaunchKernelGGL(k_combine, dim3((H / 4 + nb - 1) / nb, T), dim3(nb), 0, st, y, nsplit, split_stride,
-                       inv, gate, shared, sh_nsplit, sh_stride, H, K, accumulate, out);
+    if (K <= 8)
+        hipLaunchKernelGGL(k_combine<8>, dim3((H / 4 + nb - 1) / nb, T), dim3(nb), 0, st, y, nsplit,
+                           split_stride, inv, gate, shared, sh_nsplit, sh_stride, H, K, accumulate, out);
+    else
+        hipLaunchKernelGGL(k_combine<16>, dim3((H / 4 + nb - 1) / nb, T), dim3(nb), 0, st, y, nsplit,
+                           split_stride, inv, gate, shared, sh_nsplit, sh_stride, H, K, accumulate, out);
     MQ_LAUNCH_CHECK();
     return MOE_Q2_OK;
 }
