@@ -772,7 +772,8 @@ void mq_dec_split(int max_units, int tiles, int kblocks, int max_split, int *nsp
 }
 
 int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t expert_bytes, int64_t mat_off,
-                     int tiles, int kblocks, const int4 *units, int max_units, int split_units, int merge,
+                     int tiles, int kblocks, const int4 *units, int max_units, int split_units, int max_split,
+                     int merge,
                      const int32_t *urow, int zrow, int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
                      int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route,
@@ -791,7 +792,8 @@ int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t e
     const MqDownPrep pp = prep ? *prep : MqDownPrep{};
     const int prep_on = prep ? 1 : 0;
     int nsplit = 1, cps = kblocks;
-    mq_dec_split(split_units, tiles, kblocks, gu ? MQ_DEC_SPLIT_GU : MQ_DEC_SPLIT_D, &nsplit, &cps);
+    if (max_split < 1) return MOE_Q2_EINVAL;
+    mq_dec_split(split_units, tiles, kblocks, max_split, &nsplit, &cps);
     // merge: one work-group per unit and tile group walks all nsplit ranges and stores
     // each range's partial sums (the outputs of nsplit work-groups, with fewer of them)
     const int seg = cps;

@@ -84,6 +84,11 @@ int mq_launch_prep_swiglu_digits(const float *gate, const float *up, int nsplit,
 // few work-groups are otherwise latency-bound).
 #define MQ_DEC_SPLIT_GU 4
 #define MQ_DEC_SPLIT_D 2
+// Batch-invariant calls keep the splits of a one-token batch at every batch size, so
+// their limits weigh the batched calls (a speculative-verification pass) against the
+// one-token call: gate/up at most 2, down unsplit.
+#define MQ_DEC_SPLIT_GU_BI 2
+#define MQ_DEC_SPLIT_D_BI 1
 void mq_dec_split(int max_units, int tiles, int kblocks, int max_split, int *nsplit, int *cps);
 // zrow: index of the all-zero activation row (written by the digit preparation after
 // the real rows); trash_row: an output row that absorbs padding-token writes; outputs
@@ -147,12 +152,12 @@ struct MqFormat {
     const uint64_t *eptr;
 };
 // split_units: the unit count the k-split policy is computed for (max_units, or a
-// fixed count when the split must not depend on the batch).  merge: one work-group
+// fixed count when the split must not depend on the batch); max_split its limit.  merge: one work-group
 // walks the k ranges of all splits and stores each range's partials (bit-identical
 // to one work-group per split; for a fixed split on a batch large enough to fill
 // the device without splitting).
 int mq_launch_q2_mma(int gu, const MqFormat &fmt, const void *experts, int64_t expert_bytes, int64_t mat_off,
-                     int tiles, int kblocks, const int4 *units, int max_units, int split_units, int merge,
+                     int tiles, int kblocks, const int4 *units, int max_units, int split_units, int max_split, int merge,
                      const int32_t *urow, int zrow, int trash_row, const void *xdig,
                      const uint32_t *xsum, const float *xscale, float *out0, float *out1, int out_ld,
                      int64_t split_stride, const MqDenseSpec *dense, const MqRoute *route,

@@ -66,7 +66,7 @@ struct Workspace {
     // prefill token fragments per unit (units of 16 pf_mf slots, one bucketing for both
     // launches): 4 when a 4-bit matrix meets two-digit activations (LDS), else 5
     int pf_mf = PF_MF;
-    int dec_units = 0, dsplit_gu = 1, dsplit_d = 1;
+    int dec_units = 0, dsplit_gu = 1, dsplit_d = 1, max_split_gu = 1, max_split_d = 1;
     // batch-invariant on a batch that fills the device unsplit: one work-group walks
     // all of a fixed split's k ranges (same partials, fewer work-groups)
     bool merge_gu = false, merge_d = false;
@@ -106,15 +106,18 @@ Workspace carve(const moe_q2_shape *s, int T, int K) {
     int cps = 0;
     if (!w.prefill && !w.valu) {
         w.dec_units = units_bound(S, E, MMA_TCH);
-        // batch-invariant: the splits of a one-token batch, whatever the batch
+        // batch-invariant: the splits of a one-token batch (under the batch-invariant
+        // limits), whatever the batch
         w.split_units = w.bi ? units_bound((size_t)K, E, MMA_TCH) : w.dec_units;
-        mq_dec_split(w.split_units, (int)(I / 32), (int)(H / MQ_QK), MQ_DEC_SPLIT_GU, &w.dsplit_gu, &cps);
-        mq_dec_split(w.split_units, (int)(H / 64), (int)(I / MQ_QK), MQ_DEC_SPLIT_D, &w.dsplit_d, &cps);
+        w.max_split_gu = w.bi ? MQ_DEC_SPLIT_GU_BI : MQ_DEC_SPLIT_GU;
+        w.max_split_d = w.bi ? MQ_DEC_SPLIT_D_BI : MQ_DEC_SPLIT_D;
+        mq_dec_split(w.split_units, (int)(I / 32), (int)(H / MQ_QK), w.max_split_gu, &w.dsplit_gu, &cps);
+        mq_dec_split(w.split_units, (int)(H / 64), (int)(I / MQ_QK), w.max_split_d, &w.dsplit_d, &cps);
         if (w.bi) {
             int own = 1;
-            mq_dec_split(w.dec_units, (int)(I / 32), (int)(H / MQ_QK), MQ_DEC_SPLIT_GU, &own, &cps);
+            mq_dec_split(w.dec_units, (int)(I / 32), (int)(H / MQ_QK), w.max_split_gu, &own, &cps);
             w.merge_gu = own == 1 && w.dsplit_gu > 1;
-            mq_dec_split(w.dec_units, (int)(H / 64), (int)(I / MQ_QK), MQ_DEC_SPLIT_D, &own, &cps);
+            mq_dec_split(w.dec_units, (int)(H / 64), (int)(I / MQ_QK), w.max_split_d, &own, &cps);
             w.merge_d = own == 1 && w.dsplit_d > 1;
         }
     }
@@ -596,7 +599,7 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
                              ysh_stride};
         }
         if ((rc = mq_launch_q2_mma(1, fgu, experts_q2, ebytes, 0, I / 32, H / MQ_QK, units, w.dec_units,
-                                   w.split_units, w.merge_gu ? 1 : 0, urow, T, S,
+                                   w.split_units, w.max_split_gu, w.merge_gu ? 1 : 0, urow, T, S,
                                    xq, (const uint32_t *)xg, xs, gp, up, I, gstride, w.fused ? &dgu : nullptr,
                                    route_in_gu ? &rt : nullptr, nullptr, st, evk(MOE_Q2_PH_GATE_UP, 0),
                                    evk(MOE_Q2_PH_GATE_UP, 1))))
@@ -613,7 +616,7 @@ static int forward_impl(const void *x, const float *router_w, const void *expert
                                                                     w.nd, st));
         }
         if ((rc = mq_launch_q2_mma(0, fdn, experts_q2, ebytes, 2 * mat_gu, H / 64, I / MQ_QK, units,
-                                   w.dec_units, w.split_units, w.merge_d ? 1 : 0, nullptr, S, S, hq, (const uint32_t *)hg, hsc, y, nullptr, H, ystride,
+                                   w.dec_units, w.split_units, w.max_split_d, w.merge_d ? 1 : 0, nullptr, S, S, hq, (const uint32_t *)hg, hsc, y, nullptr, H, ystride,
                                    w.fused ? &dd : nullptr, nullptr, prep_in_down ? &dp : nullptr, st,
                                    evk(MOE_Q2_PH_DOWN, 0), evk(MOE_Q2_PH_DOWN, 1))))
             return rc;

@@ -103,7 +103,8 @@ enum {
                                   whatever the batch it is in (1 .. MOE_Q2_MAX_TOKENS tokens):
                                   one set of kernels and one summation order per token for every
                                   batch size (decode kernels, router split and reduction splits
-                                  fixed by the shape; the ds4 README mirror, section "DSpark
+                                  fixed by the shape: gate/up at most 2 k-splits, down unsplit;
+                                  the ds4 README mirror, section "DSpark
                                   Speculative Decoding", notes that batched verification groups
                                   floating point differently from one-token decode).  Needs a
                                   bf16 (or PRE_RMSNORM) layer input when there is a shared

@@ -171,21 +171,23 @@ def test_noalloc_validation(lib):
 
 
 def test_plans(lib):
-    """Path choices (moe_q2_describe): batch-invariant calls keep the one-token splits,
-    router split and decode kernels at every batch size; Q4 matrices take the prefill
+    """Path choices (moe_q2_describe): batch-invariant calls keep one set of splits
+    (gate/up at most 2, down unsplit: fixed by the shape), the router split and the
+    decode kernels at every batch size; Q4 matrices take the prefill
     kernels from the same batch size as Q2 (and when forced); Q8 activations halve the
     digit buffers."""
     s = mq.make_shape(7168, 2048, 256, 2048)
     one = mq.describe(s, 1, 8)
     bi = mq.make_shape(7168, 2048, 256, 2048, flags=mq.BATCH_INVARIANT)
     plans = [mq.describe(bi, T, 8) for T in (1, 5, 32, 96, 255, 2048)]
+    assert (one["split_gate_up"], one["split_down"]) == (4, 2)
     for p in plans:
         assert p["path"] == mq.PATH_DECODE and p["routed_kernel"] == 0
-        assert (p["split_gate_up"], p["split_down"]) == (one["split_gate_up"], one["split_down"])
+        assert (p["split_gate_up"], p["split_down"]) == (2, 1)
         assert p["router_splits"] == plans[0]["router_splits"] == 16
-    # the fixed splits run merged (one work-group per unit and tile group) from the
-    # batch sizes whose own plan needs no split; never without the batch-invariant flag
-    assert [p["merged"] for p in plans] == [0, 3, 3, 3, 3, 3]
+    # the fixed gate/up splits run merged (one work-group per unit and tile group) from
+    # the batch sizes whose own plan needs no split; never without the batch-invariant flag
+    assert [p["merged"] for p in plans] == [0, 1, 1, 1, 1, 1]
     assert all(mq.describe(s, T, 8)["merged"] == 0 for T in (1, 5, 32, 96, 255))
     assert mq.describe(s, 2048, 8)["path"] == mq.PATH_PREFILL
     q4 = mq.make_shape(7168, 2048, 256, 2048, flags=mq.GU_Q4 | mq.DOWN_Q4)

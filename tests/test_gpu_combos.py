@@ -67,7 +67,7 @@ def test_batch_invariance_with_formats(case, pool):
     flags = _flags(mq, names)
     shape = dl.shape(flags)
     one, batch = mq.describe(shape, 1, K), mq.describe(shape, T, K)
-    assert one["merged"] == 0 and batch["merged"] == 3 and one["split_gate_up"] > 1
+    assert one["merged"] == 0 and batch["merged"] == 1 and one["split_gate_up"] > 1
     assert (one["split_gate_up"], one["split_down"]) == (batch["split_gate_up"], batch["split_down"])
     x = dw.activations(wl)
     out, tr = _run(mq, dl, x, T, flags)
