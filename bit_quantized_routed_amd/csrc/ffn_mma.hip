@@ -36,6 +36,7 @@
 #include "kernels.h"
 #include "prep_rows.h"
 #include "topk_dev.h"
+#include "timeline.h"
 
 typedef int32_t mq_i32x4 __attribute__((ext_vector_type(4)));
 typedef short mq_s16x4 __attribute__((ext_vector_type(4)));
@@ -608,14 +609,18 @@ __global__ void __launch_bounds__(256, MERGE && BD == MQ_BD2 ? 3 : 1) k_q2_mma(c
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, q4 = lane >> 4;
+    MQ_TL(GU, 0, mq_tl_now());
+    MQ_TL(GU, 3, mq_tl_hw());
     if ((int)blockIdx.x >= q2_grid) {
         // appended work-groups: the shared expert's dense rows
+        MQ_TL(GU, 4, 1);
         if (GU)
             mq_dense_wg<4, false>(dn, (int)blockIdx.x - q2_grid, wv, lane);
         else if (prep_on)
             mq_dense_wg_prep(dn, pp, (int)blockIdx.x - q2_grid, wv, lane, (uint16_t *)&sW[0][0]);
         else
             mq_dense_wg<2, true>(dn, (int)blockIdx.x - q2_grid, wv, lane);
+        MQ_TL_END(GU);
         return;
     }
     const int groups = tiles >> 2;
@@ -623,7 +628,11 @@ __global__ void __launch_bounds__(256, MERGE && BD == MQ_BD2 ? 3 : 1) k_q2_mma(c
     const int rest = blockIdx.x / groups;
     const int ks = rest % nsplit, u = rest / nsplit;
     const int c0 = ks * cps, c1 = min(kblocks, c0 + cps);
-    if (c0 >= c1) return;
+    if (c0 >= c1) {
+        MQ_TL(GU, 4, 2);
+        MQ_TL(GU, 2, mq_tl_now());
+        return;
+    }
     // the unit and (gate/up) its row table: routed here, or two independent loads
     // (nothing else waits on global memory before the first activation loads)
     int4 un;
@@ -635,7 +644,11 @@ __global__ void __launch_bounds__(256, MERGE && BD == MQ_BD2 ? 3 : 1) k_q2_mma(c
         urv = GU && tid < 16 ? urow[(int64_t)u * 16 + tid] : 0;
     }
     const int p0 = un.y, nt = un.z;
-    if (nt == 0) return;                                 // past the last unit
+    if (nt == 0) {                                       // past the last unit
+        MQ_TL(GU, 4, 2);
+        MQ_TL(GU, 2, mq_tl_now());
+        return;
+    }
     // the expert's bytes: resident, or where an expert cache's plan put it
     const uint8_t *eb = eptr ? (const uint8_t *)eptr[un.x] : experts + (int64_t)un.x * expert_bytes;
     const int tile = 4 * tg + wv;
@@ -722,6 +735,7 @@ __global__ void __launch_bounds__(256, MERGE && BD == MQ_BD2 ? 3 : 1) k_q2_mma(c
     // sums, started from zero, where its range ends: the same values as one
     // work-group per split (a separate instantiation: the extra loop level costs
     // registers)
+    MQ_TL(GU, 1, mq_tl_now());
     const int sl = MERGE ? seg : c1 - c0;
     for (int cs = c0; cs < c1; cs += sl) {
     const int ce = min(c1, cs + sl);
@@ -754,7 +768,25 @@ __global__ void __launch_bounds__(256, MERGE && BD == MQ_BD2 ? 3 : 1) k_q2_mma(c
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) tot[nf] = (mq_f32x4){0.f, 0.f, 0.f, 0.f};
     }
+    MQ_TL_END(GU);
 }
+
+#ifdef MQ_WG_TIMELINE
+__device__ unsigned long long mq_tl_buf[2][MQ_TL_MAX_WG][MQ_TL_SLOTS];
+
+extern "C" int moe_q2_timeline_read(void *host, size_t bytes) {
+    if (!host || bytes != sizeof(mq_tl_buf)) return MOE_Q2_EINVAL;
+    const hipError_t e = hipMemcpyFromSymbol(host, HIP_SYMBOL(mq_tl_buf), sizeof(mq_tl_buf), 0,
+                                             hipMemcpyDeviceToHost);
+    return e == hipSuccess ? MOE_Q2_OK : mq_fail_hip(e);
+}
+
+extern "C" int moe_q2_timeline_clear(void) {
+    static unsigned long long zero[2][MQ_TL_MAX_WG][MQ_TL_SLOTS];
+    const hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(mq_tl_buf), zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+    return e == hipSuccess ? MOE_Q2_OK : mq_fail_hip(e);
+}
+#endif
 
 // Split count along the reduction for the decode kernel: enough work-groups for
 // one resident round at three per compute unit of a 256-CU device, at most
