@@ -74,9 +74,31 @@ def layer_bytes(wl, touched):
     return b
 
 
+def library_source(text):
+    """A kernel source as libmoe_q2.so compiles it: without the per-work-group timeline
+    marks, which exist only in the timeline build (every line naming one contains
+    "MQ_TL"; the device array and its accessors sit in one "#ifdef MQ_WG_TIMELINE"
+    block; the include of timeline.h)."""
+    out, depth = [], 0
+    for line in text.splitlines(keepends=True):
+        st = line.strip()
+        if depth:
+            if st.startswith("#if"):
+                depth += 1
+            elif st.startswith("#endif"):
+                depth -= 1
+            continue
+        if st == "#ifdef MQ_WG_TIMELINE":
+            depth = 1
+        elif "MQ_TL" not in line and st != '#include "timeline.h"':
+            out.append(line)
+    return "".join(out)
+
+
 def traffic_record(kernel):
     """HBM traffic per launch from committed rocprofv3 counter runs, valid only while
-    the kernel source is unchanged (sha256 recorded with the counters)."""
+    the kernel source, as the library compiles it, is unchanged (sha256 recorded with
+    the counters)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -85,7 +107,7 @@ def traffic_record(kernel):
     if not rec:
         return None
     src = os.path.join(ROOT, rec["source"])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = hashlib.sha256(library_source(open(src).read()).encode()).hexdigest()
     if sha != rec["source_sha256"]:
         return None
     return rec

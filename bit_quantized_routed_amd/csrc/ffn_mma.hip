@@ -628,11 +628,8 @@ __global__ void __launch_bounds__(256, MERGE && BD == MQ_BD2 ? 3 : 1) k_q2_mma(c
     const int rest = blockIdx.x / groups;
     const int ks = rest % nsplit, u = rest / nsplit;
     const int c0 = ks * cps, c1 = min(kblocks, c0 + cps);
-    if (c0 >= c1) {
-        MQ_TL(GU, 4, 2);
-        MQ_TL(GU, 2, mq_tl_now());
-        return;
-    }
+    MQ_TL_NO_WORK(GU, c0 >= c1);
+    if (c0 >= c1) return;
     // the unit and (gate/up) its row table: routed here, or two independent loads
     // (nothing else waits on global memory before the first activation loads)
     int4 un;
@@ -644,11 +641,8 @@ __global__ void __launch_bounds__(256, MERGE && BD == MQ_BD2 ? 3 : 1) k_q2_mma(c
         urv = GU && tid < 16 ? urow[(int64_t)u * 16 + tid] : 0;
     }
     const int p0 = un.y, nt = un.z;
-    if (nt == 0) {                                       // past the last unit
-        MQ_TL(GU, 4, 2);
-        MQ_TL(GU, 2, mq_tl_now());
-        return;
-    }
+    MQ_TL_NO_WORK(GU, nt == 0);
+    if (nt == 0) return;                                 // past the last unit
     // the expert's bytes: resident, or where an expert cache's plan put it
     const uint8_t *eb = eptr ? (const uint8_t *)eptr[un.x] : experts + (int64_t)un.x * expert_bytes;
     const int tile = 4 * tg + wv;
@@ -770,7 +764,6 @@ __global__ void __launch_bounds__(256, MERGE && BD == MQ_BD2 ? 3 : 1) k_q2_mma(c
     }
     MQ_TL_END(GU);
 }
-
 #ifdef MQ_WG_TIMELINE
 __device__ unsigned long long mq_tl_buf[2][MQ_TL_MAX_WG][MQ_TL_SLOTS];
 

@@ -40,7 +40,19 @@ __device__ __forceinline__ unsigned long long mq_tl_hw() {
         __syncthreads();                                                                \
         MQ_TL(kind, 2, mq_tl_now());                                                    \
     } while (0)
+// role and end of a work-group about to leave with no work (cond uniform)
+#define MQ_TL_NO_WORK(kind, cond)                                                        \
+    do {                                                                                \
+        if (cond) {                                                                     \
+            MQ_TL(kind, 4, 2);                                                          \
+            MQ_TL(kind, 2, mq_tl_now());                                                \
+        }                                                                               \
+    } while (0)
 #else
 #define MQ_TL(kind, slot, value) do {} while (0)
 #define MQ_TL_END(kind) do {} while (0)
+#define MQ_TL_NO_WORK(kind, cond) do {} while (0)
 #endif
+// Every line of the kernel sources that names a timeline mark contains "MQ_TL", and the
+// device array and accessors sit in one "#ifdef MQ_WG_TIMELINE" block: without them
+// (and the include of this header) a source reads as the library compiles it.

@@ -1,6 +1,6 @@
 """Host-side behaviour of bench.py (no GPU): more than one GPU is refused with a
 message, and the HBM traffic records are used only while the kernel source they were
-measured on is unchanged."""
+measured on is unchanged as the library compiles it (the timeline build's marks aside)."""
 import json
 import os
 import subprocess
@@ -23,7 +23,8 @@ def test_traffic_records_follow_the_source_hash(tmp_path, monkeypatch):
         recs = json.load(f)
     key = "decode1/gate_up"
     import hashlib
-    cur = hashlib.sha256(open(os.path.join(ROOT, recs[key]["source"]), "rb").read()).hexdigest()
+    text = open(os.path.join(ROOT, recs[key]["source"])).read()
+    cur = hashlib.sha256(bench.library_source(text).encode()).hexdigest()
     got = bench.traffic_record(key)
     if cur == recs[key]["source_sha256"]:                 # counters taken on this source
         assert got is not None and got["bytes_per_launch"] == recs[key]["bytes_per_launch"]
@@ -38,4 +39,9 @@ def test_traffic_records_follow_the_source_hash(tmp_path, monkeypatch):
     (prof / "traffic.json").write_text(json.dumps({key: rec}))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.traffic_record(key) is None
+    # timeline marks added or removed leave the compiled source, and the record, as they were
+    src.write_text(bench.library_source(text).replace("\n}\n", "\n    MQ_TL(GU, 0, 0);\n}\n", 1) +
+                   "#ifdef MQ_WG_TIMELINE\nint x;\n#if 1\n#endif\n#endif\n")
+    assert bench.library_source(src.read_text()) == bench.library_source(text)
+    assert (bench.traffic_record(key) is not None) == (cur == recs[key]["source_sha256"])
     assert bench.traffic_record("no/such") is None
