@@ -9,9 +9,10 @@
 // (s a power of two, |a| <= 2^14) and split into two int8 digits a = 256*hi + lo
 // (lo in [-128, 127]).  The first sum is then exact on v_mfma_i32_16x16x64_i8:
 // B = q*sc (0..45, an int8 built from the code dword with four mask/multiply
-// pairs), A = hi and A = lo digits.  The min term is a 16-long product per block,
-// done on v_mfma_f32_16x16x16_bf16 with B = m_j (exact) and A = A_j split into
-// two bf16 planes.  Each block then folds d and dmin into an fp32 accumulator.
+// pairs), A = hi and A = lo digits.  The min term is a 16-long product per block
+// of m_j (exact in bf16) with A_j split into two bf16 planes, both planes in one
+// K = 32 product on v_mfma_f32_16x16x32_bf16 (the planes as the two halves of K, m_j
+// repeated).  Each block then folds d and dmin into an fp32 accumulator.
 //
 // MFMA roles: M = 16 of the unit's tokens (one fragment), N = 16 weight rows,
 // K = the reduction dimension.  Operand byte order inside a lane's 16-byte K slice
@@ -123,6 +124,20 @@ __device__ __forceinline__ mq_s16x4 mq_mins_bf16(uint32_t swd) {
     return r;
 }
 
+typedef __bf16 mq_bf16x8 __attribute__((ext_vector_type(8)));
+
+// The min-term sums of one block for a lane's token and row: sums = the lane's group
+// sums of 4 groups as two bf16 planes (hi in elements 0..3, lo in 4..7), bm = m_j of
+// the same 4 groups; each m_j meets both planes of its group, all 16 groups over the
+// lanes' K slices, in one K = 32 product.
+__device__ __forceinline__ mq_f32x4 mq_min_term(mq_u32x4 sums, mq_s16x4 bm) {
+    const uint2 b = __builtin_bit_cast(uint2, bm);
+    const mq_u32x4 bb = {b.x, b.y, b.x, b.y};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mq_bf16x8, sums),
+                                                  __builtin_bit_cast(mq_bf16x8, bb),
+                                                  (mq_f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+
 // One block column of a 64-row tile is 64 * 4 * BD contiguous bytes = 16 BD uint4
 // (2-bit: 5376 bytes, 336 uint4; 4-bit: 9472 bytes, 592 uint4); a wave moves it with
 // NLD = ceil(BD / 4) 16-byte loads per lane.  The last load of the lanes past the end
@@ -156,8 +171,9 @@ __device__ __forceinline__ void mq_bcol_store(mq_u32x4 *__restrict__ dst, int la
 
 // Activation operands of one block column for one MFMA lane (token l % 16, group
 // quad q4 = l / 16): digits of groups 4kk + q4 (hi, lo; lo only for one digit) and
-// the two bf16 planes of the group sums 4q4 .. 4q4+3.
-struct mq_acol { mq_i32x4 hi[4], lo[4]; mq_s16x4 sh, sl; };
+// the two bf16 planes of the group sums 4q4 .. 4q4+3 (hi plane in the first two
+// dwords of s, lo plane in the last two).
+struct mq_acol { mq_i32x4 hi[4], lo[4]; mq_u32x4 s; };
 
 // One 64-row block column from the wave's LDS slice into the 4 N fragments:
 // integer products of the activation digits on the i8 matrix cores, the min
@@ -177,10 +193,7 @@ __device__ __forceinline__ void mq_mma_column(const uint32_t *__restrict__ my, i
             if (ND == 2) ih = __builtin_amdgcn_mfma_i32_16x16x64_i8(a.hi[kk], b, ih, 0, 0, 0);
             il = __builtin_amdgcn_mfma_i32_16x16x64_i8(a.lo[kk], b, il, 0, 0, 0);
         }
-        const mq_s16x4 bm = mq_mins_bf16(blk[q4]);
-        mq_f32x4 am = {0.f, 0.f, 0.f, 0.f};
-        am = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.sh, bm, am, 0, 0, 0);
-        am = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.sl, bm, am, 0, 0, 0);
+        const mq_f32x4 am = mq_min_term(a.s, mq_mins_bf16(blk[q4]));
         const uint32_t dd = blk[BD - 1];
         const float d = mq_h2f((uint16_t)(dd & 0xFFFFu));
         const float dmin = mq_h2f((uint16_t)(dd >> 16));
@@ -233,8 +246,6 @@ struct MqDense {
     int T, rows, K, half, nsplit, kps, out_ld, grid;
     int64_t split_stride;
 };
-
-typedef __bf16 mq_bf16x8 __attribute__((ext_vector_type(8)));
 
 // XL: the activation planes come from LDS (xl: hi plane of the one token over
 // [k0, k1), the lo plane after it) instead of global memory.
@@ -752,9 +763,7 @@ __global__ void __launch_bounds__(256, MERGE && BD == MQ_BD2 ? 3 : 1) k_q2_mma(c
             if (ND == 2) a.hi[kk] = __builtin_bit_cast(mq_i32x4, sA[buf][(kk * 2) * 64 + lane]);
             a.lo[kk] = __builtin_bit_cast(mq_i32x4, sA[buf][(kk * ND + ND - 1) * 64 + lane]);
         }
-        const mq_u32x4 sv = sA[buf][256 * ND + lane];
-        a.sh = __builtin_bit_cast(mq_s16x4, (uint2){sv[0], sv[1]});
-        a.sl = __builtin_bit_cast(mq_s16x4, (uint2){sv[2], sv[3]});
+        a.s = sA[buf][256 * ND + lane];
         mq_mma_column<ND, BD>(myd, r16, q4, a, tot, one);
         buf ^= 1;
     }
@@ -1166,13 +1175,7 @@ __global__ void __launch_bounds__(512) k_q2_mma_pf(const uint8_t *__restrict__ e
                         }
                     }
                     const mq_u32x4 xv = *(const mq_u32x4 *)(sAc + SUMS + (16 * m + r16) * 16 + ssw);
-                    const mq_s16x4 xh = __builtin_bit_cast(mq_s16x4, (uint2){xv[0], xv[1]});
-                    const mq_s16x4 xl = __builtin_bit_cast(mq_s16x4, (uint2){xv[2], xv[3]});
-                    const mq_f32x4 zf = {0.f, 0.f, 0.f, 0.f};
-                    mq_f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, bm0, zf, 0, 0, 0);
-                    a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, bm0, a0, 0, 0, 0);
-                    mq_f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, bm1, zf, 0, 0, 0);
-                    a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, bm1, a1, 0, 0, 0);
+                    const mq_f32x4 a0 = mq_min_term(xv, bm0), a1 = mq_min_term(xv, bm1);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int v0 = ND == 2 ? (hi0[i] << 8) + lo0[i] : lo0[i];
