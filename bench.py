@@ -279,9 +279,10 @@ def run_workload(spec, steps, warmup, rotate, graph=True):
     if T < 256 and wl.shared_inter and (wl.act == "bf16" or wl.rmsnorm):
         gu_bytes += 2 * wl.shared_inter * wl.hidden * 2
         dn_bytes += wl.shared_inter * wl.hidden * 2
-    kbytes = {"gate_up": gu_bytes + T * wl.hidden * 2.5 + T * K * wl.inter * 4,
-              "down": dn_bytes + T * K * wl.inter * 2.5 + T * K * wl.hidden * 4,
-              "shared": 3 * wl.shared_inter * wl.hidden * 2}.get(dom)
+    launch_bytes = {"gate_up": gu_bytes + T * wl.hidden * 2.5 + T * K * wl.inter * 4,
+                    "down": dn_bytes + T * K * wl.inter * 2.5 + T * K * wl.hidden * 4,
+                    "shared": 3 * wl.shared_inter * wl.hidden * 2}
+    kbytes = launch_bytes.get(dom)
     prefill = mq.describe(shape, T, K)["path"] == mq.PATH_PREFILL
     if prefill:
         # useful MACs x 2 against the dense MFMA peak of the arithmetic: the default path
@@ -307,6 +308,7 @@ def run_workload(spec, steps, warmup, rotate, graph=True):
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                            "traffic": None if tr is None else tr.get("bytes_per_launch"),
                            "algorithmic_bytes_per_launch": kbytes,
+                           "algorithmic_bytes_by_launch": {k: launch_bytes[k] for k in ("gate_up", "down")},
                            "avg_launch_ms": dom_avg}
     # one more untimed forward of layer 0 with its routing traced, kept for the parity
     # check against the oracle's outputs of the CPU baseline (first tokens only)
