@@ -152,15 +152,17 @@ struct mq_bcol {
 // The loads name the global address space: a generic (flat) load also counts against
 // the LDS counter, so every LDS wait of the column would wait for this prefetch of
 // the next column too.  (Expert bytes are device memory or pinned host memory, both
-// global.)
+// global.)  They are non-temporal: a weight column is read once per work-group, so it
+// should not displace the activation operands and partial sums that other work-groups
+// re-read from the caches.
 template <int BD>
 __device__ __forceinline__ void mq_bcol_load(const mq_u32x4 *__restrict__ src_, int lane, mq_bcol<BD> &c) {
     typedef const __attribute__((address_space(1))) mq_u32x4 *gvec;
     const gvec src = (gvec)src_;
     constexpr int NLD = mq_bcol<BD>::NLD;
 #pragma unroll
-    for (int i = 0; i < NLD - 1; ++i) c.v[i] = src[lane + 64 * i];
-    c.v[NLD - 1] = src[min(lane + 64 * (NLD - 1), mq_bcol<BD>::N - 1)];
+    for (int i = 0; i < NLD - 1; ++i) c.v[i] = __builtin_nontemporal_load(&src[lane + 64 * i]);
+    c.v[NLD - 1] = __builtin_nontemporal_load(&src[min(lane + 64 * (NLD - 1), mq_bcol<BD>::N - 1)]);
 }
 
 template <int BD>
