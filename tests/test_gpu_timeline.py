@@ -15,8 +15,8 @@ TL = os.path.join(ROOT, "bit_quantized_routed_amd", "libmoe_q2_timeline.so")
 
 @pytest.mark.gpu
 def test_timeline_decode1():
-    if not os.path.exists(TL):
-        pytest.fail("libmoe_q2_timeline.so is not built")
+    if not os.path.exists(TL):       # a diagnostic build, not the library the other tests load
+        pytest.skip("libmoe_q2_timeline.so is not built (bit_quantized_routed_amd.build.build(timeline=True))")
     print("timeline: decode1, one call, 2 layers", flush=True)
     p = subprocess.run([sys.executable, "-m", "bit_quantized_routed_amd.timeline", "decode1", "--calls", "1",
                         "--rotate", "2"], cwd=ROOT, capture_output=True, text=True, timeout=240)
